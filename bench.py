@@ -1,0 +1,185 @@
+"""Benchmark of the SSD chunked-scan forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one full forward (ssd_prepare + ssd_scan, i.e. ssd_forward) over the
+workload's batch, with inputs, outputs and workspace already resident in HBM.
+Prints one JSON line: tokens/s over K timed steps, the roofline of the
+dominant kernel (the scan kernel) measured with HIP events on the stream it is
+launched on, and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense
+
+
+def algorithmic_bytes(w, init_nonzero: bool) -> int:
+    """Bytes the method itself must move: x, B, C, dt, A_log, D read once; y and final states written once."""
+    sx = 2 if w.dtype == "bf16" else 4
+    b, T, H, P, N, G = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups
+    nseqs = w.nseqs_packed * b if w.nseqs_packed else b
+    total = sx * (b * T * H * P + 2 * b * T * G * N) + 4 * b * T * H + 8 * H + 4 * b * T * H * P
+    total += 4 * nseqs * H * P * N
+    if init_nonzero:
+        total += 4 * nseqs * H * P * N
+    if w.nseqs_packed:
+        total += 4 * b * T      # seq_idx
+    return total
+
+
+def algorithmic_flops(w) -> int:
+    b, T, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk_len
+    nc = -(-T // Q)
+    return 2 * (b * H * nc * (Q * (Q + 1) // 2 * P + 2 * Q * N * P) + b * G * nc * Q * (Q + 1) // 2 * N)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mamba_ssd_scan_chunked_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(workload: str):
+    """HBM traffic per scan launch from the committed rocprofv3 counter runs, if
+    they were taken on the current kernel sources; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "scan_traffic_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(prob, w):
+    """Time the fp64 oracle on rows 0-1 (all heads, full length) on all host cores."""
+    import numpy as np
+
+    import oracle
+    sub = {k: prob[k] for k in ("x", "dt", "B", "C")}
+    rows = min(2, w.batch)
+    sub = {k: np.ascontiguousarray(v[:rows].to(dtype=__import__("torch").float64).numpy()) for k, v in sub.items()}
+    A_log = prob["A_log"].double().numpy()
+    D = prob["D"].double().numpy() if prob["D"] is not None else None
+    rows = min(2, w.batch)
+    init = prob["init"][:rows].double().numpy() if (prob["init"] is not None and prob["seq_idx"] is None) else None
+    seq = None
+    nseqs = None
+    if prob["seq_idx"] is not None:
+        seq = prob["seq_idx"][:rows].numpy()
+        nseqs = int(seq.max()) + 1
+        init = prob["init"][:nseqs].double().numpy() if prob["init"] is not None else None
+    threads = oracle.max_threads()
+    t0 = time.perf_counter()
+    oracle.recurrence(sub["x"], sub["dt"], A_log, sub["B"], sub["C"], D, init, seq, nseqs, nthreads=threads)
+    dt = time.perf_counter() - t0
+    tokens = rows * w.seqlen    # full rows of the workload, every head
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d rows (all %d heads, %d tokens each), fp64 recurrence, %.2f s wall"
+                      % (rows, w.batch, w.nheads, w.seqlen, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="m2p7_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the SSD forward here has no multi-GPU path "
+              "(sharding over heads or sequence is a design note, not built); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mamba_ssd_scan_chunked_amd as ssd
+    import ssd_inputs as si
+
+    w = si.WORKLOADS[args.workload]
+    prob = si.make_workload(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in prob.items()}
+    dtype = ssd.DTYPE_BF16 if w.dtype == "bf16" else ssd.DTYPE_F32
+    nseqs = prob["nseqs"]
+    p = ssd.problem(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk_len, nseqs, dtype, 0)
+    y = torch.empty((w.batch, w.seqlen, w.nheads, w.headdim), dtype=torch.float32, device=dev)
+    fin = torch.empty((nseqs, w.nheads, w.headdim, w.dstate), dtype=torch.float32, device=dev)
+    ws = torch.empty(ssd.workspace_size(p), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        ssd.prepare(p, d["B"], d["C"], ws, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        ssd.scan(p, d["x"], d["dt"], d["A_log"], d["C"], d["D"], d["init"], d["seq_idx"], y, fin, ws,
+                 stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    prep_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    scan_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    ms_per_step = wall * 1000.0 / args.steps
+    tokens = w.batch * w.seqlen
+    value = tokens / (ms_per_step / 1000.0)
+
+    balg = algorithmic_bytes(w, prob["init"] is not None)
+    falg = algorithmic_flops(w)
+    achieved = balg / (scan_ms / 1000.0) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": committed_traffic(w.name),
+                "kernel": "ssd_scan_kernel", "kernel_ms": round(scan_ms, 5), "prep_kernel_ms": round(prep_ms, 5),
+                "alg_bytes_per_launch": balg, "alg_flops_per_step": falg,
+                "step_frac_of_hbm_roofline": round(balg / (ms_per_step / 1000.0) / 1e9 / HBM_PEAK_GBS, 4)}
+
+    base = None
+    if not args.no_cpu_baseline:
+        base = cpu_baseline(prob, w)
+
+    out = {"metric": "SSD fwd tokens/sec (2.7B-layer shape, T=4096) and % of MFMA/HBM roofline",
+           "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": w.dtype, "data": "synthetic (seeded; random inputs of the layer's shapes)",
+           "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seqlen, "nheads": w.nheads,
+                      "headdim": w.headdim, "dstate": w.dstate, "ngroups": w.ngroups, "chunk_len": w.chunk_len,
+                      "kernel_block": 64 if w.chunk_len >= 64 else w.chunk_len, "outputs": "y fp32 + final fp32",
+                      "parallelism": "single GPU"},
+           "roofline": roofline, "cpu_baseline": base}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

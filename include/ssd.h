@@ -1,0 +1,158 @@
+/*
+ * ssd.h - C ABI of the MI355X (gfx950) Mamba-2 SSD chunked-scan forward.
+ *
+ * The operation (per batch row r and head h):
+ *
+ *     H_t = a_t * H_{t-1} + x_t B_t^T,    y_t = H_t C_t + D_h x_t,
+ *     a_t = exp(dt_t * A_h),  A_h = -exp(A_log_h)
+ *
+ * with the P x N state H carried across tokens.  The recurrence and its
+ * matrix (dual) form Y = [L o (C B^T)] X are defined on "088 Mamba-2: writing
+ * the recurrent state as a structured matrix" (wq-win.github.io), sections 2.1
+ * and 2.2; the chunked evaluation (quadratic diagonal blocks, states passed
+ * between chunks) is its section 2.3 and section 3, and key design 2 of
+ * "Mamba-2 - Transformer and SSM share one algebra" (awesome.papernotes.org).
+ * The decay a = exp(Delta A) is from the selective-SSM section of the "Mamba"
+ * paper story (ai.tomabc.com); the skip term D x from section 2 of "Mamba and
+ * state space models" (wang-x-xia.github.io); B and C shared by groups of heads
+ * from key design 3 of the papernotes page.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers to dense, contiguous, row-major
+ *    arrays in the layouts given below.  The caller allocates and frees every
+ *    buffer, including the workspace; the library allocates no memory.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream).
+ *    No entry point synchronises the stream; errors raised by the kernels
+ *    themselves surface at the caller's next synchronisation.
+ *  - Every function returns SSD_OK (0) or a positive SSD_ERR_* code; nothing
+ *    aborts and no C++ exception crosses the ABI.  Argument checks run on the
+ *    host before any HIP call, so a rejected call has enqueued nothing.
+ *  - The library keeps no per-call state; concurrent calls on different
+ *    streams with disjoint outputs and workspaces are safe.
+ */
+#ifndef SSD_MI355X_H
+#define SSD_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSD_ABI_VERSION 1
+
+/* Element type of x, B and C.  dt, A_log, D, init_state, y and final_state are
+ * always fp32.  BF16: bf16 operands, fp32 accumulation; F32: fp32 throughout. */
+typedef enum { SSD_DTYPE_F32 = 0, SSD_DTYPE_BF16 = 1 } ssd_dtype_t;
+
+/* flags */
+enum {
+    /* Euler input scaling: the state is written with dt_t * x_t instead of x_t
+     * (B-bar = Delta B).  D still multiplies the unscaled x_t.  Off by default:
+     * the recurrence above has no Delta on x. */
+    SSD_FLAG_DT_SCALES_X = 1u << 0
+};
+
+enum {
+    SSD_OK = 0,
+    SSD_ERR_NULL_POINTER = 1,   /* a required pointer is NULL                        */
+    SSD_ERR_BAD_SHAPE = 2,      /* negative size, H % G != 0, nseqs inconsistent ... */
+    SSD_ERR_UNSUPPORTED = 3,    /* (dtype, headdim, dstate, chunk_len) not built      */
+    SSD_ERR_ALIGNMENT = 4,      /* a tensor pointer is not 16-byte aligned            */
+    SSD_ERR_WORKSPACE = 5,      /* workspace NULL or smaller than ssd_workspace_size  */
+    SSD_ERR_ALIAS = 6,          /* an output overlaps an input or the other output    */
+    SSD_ERR_HIP = 7,            /* a HIP runtime call or kernel launch failed         */
+    SSD_ERR_NO_DEVICE = 8       /* no HIP device is available                         */
+};
+
+typedef struct {
+    int64_t batch;      /* b: rows                                                  */
+    int64_t seqlen;     /* T: tokens per row (may be 0)                             */
+    int64_t nheads;     /* H                                                        */
+    int64_t headdim;    /* P: channels per head (x and y)                           */
+    int64_t dstate;     /* N: state size (B and C)                                  */
+    int64_t ngroups;    /* G: B/C groups; head h reads group h / (H / G)            */
+    int64_t chunk_len;  /* Q: chunk length of the block algorithm (see below)      */
+    int64_t nseqs;      /* number of sequences: == batch without seq_idx            */
+    int32_t dtype;      /* ssd_dtype_t                                              */
+    uint32_t flags;     /* SSD_FLAG_*                                               */
+} ssd_problem_t;
+
+/* Host-only check of a problem description (no HIP call).  Supported builds:
+ *   BF16: headdim in {32, 64}, dstate in {64, 128, 256}
+ *   F32 : headdim in {16, 32, 64}, dstate in {16, 32, 64, 128}
+ * chunk_len: 32, or any positive multiple of 64.  The chunk length does not
+ * change the function computed (every chunking of the sequence gives the same
+ * y and final state up to rounding); the kernel evaluates each chunk's
+ * quadratic diagonal block in blocks of min(chunk_len, 64) rows, passing the
+ * state between those blocks (the past-to-future parts of a diagonal block
+ * are low rank, exactly as between chunks). */
+int ssd_validate(const ssd_problem_t* p);
+
+/* Bytes of device workspace ssd_forward / ssd_prepare / ssd_scan need for this
+ * problem (a few MB per row: the per-block C.B^T tiles and a transposed copy
+ * of B).  Returns 0 if the problem is invalid. */
+size_t ssd_workspace_size(const ssd_problem_t* p);
+
+/* Full forward.  Equivalent to ssd_prepare followed by ssd_scan on the same
+ * stream.
+ *   x          (batch, seqlen, nheads, headdim)   dtype
+ *   dt         (batch, seqlen, nheads)            fp32, the step sizes (> 0 after softplus)
+ *   A_log      (nheads)                           fp32; A_h = -exp(A_log[h])
+ *   B, C       (batch, seqlen, ngroups, dstate)   dtype
+ *   D          (nheads)                           fp32, or NULL for no skip term
+ *   init_state (nseqs, nheads, headdim, dstate)   fp32, or NULL for zero initial states
+ *   seq_idx    (batch, seqlen)                    int32 or NULL
+ *   y          (batch, seqlen, nheads, headdim)   fp32 output
+ *   final_state(nseqs, nheads, headdim, dstate)   fp32 output, or NULL
+ *   workspace / workspace_bytes                   >= ssd_workspace_size(p), 256-byte aligned
+ *
+ * seq_idx packs independent sequences into rows: seq_idx[r][t] is the id of
+ * the sequence token t of row r belongs to.  Ids are nondecreasing along each
+ * row, global over the batch (0 .. nseqs-1), and no id appears in two rows.
+ * At the first token of sequence k the state is replaced by init_state[k] (or
+ * zero) and then updated by that token; final_state[k] is the state after the
+ * last token of k.  No state crosses a sequence boundary.  Without seq_idx,
+ * row r is sequence r (nseqs must equal batch).  Ids outside 0..nseqs-1 are
+ * clamped (memory-safe, values undefined).  final_state rows of ids that never
+ * occur are not written.  final_state may be the same buffer as init_state
+ * (in-place state carry); any other overlap between an output and an input
+ * is rejected with SSD_ERR_ALIAS.
+ * A row of seqlen 0 leaves its final state equal to its initial state. */
+int ssd_forward(const ssd_problem_t* p,
+                const void* x, const float* dt, const float* A_log,
+                const void* B, const void* C, const float* D,
+                const float* init_state, const int32_t* seq_idx,
+                float* y, float* final_state,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* First stage alone: for every (row, group, block of min(chunk_len, 64)
+ * tokens) write C_blk B_blk^T (fp32) and B_blk^T into the workspace.  These
+ * depend only on B and C, so they are shared by the nheads / ngroups heads of
+ * a group.  Defined by the intra-chunk C B^T product of the dual form
+ * (section 2.2 of the "088 Mamba-2" page). */
+int ssd_prepare(const ssd_problem_t* p, const void* B, const void* C,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Second stage alone: the chunked scan proper (within-block cumulative decay,
+ * masked diagonal products, state passing, off-diagonal read-out, skip term,
+ * final states), reading the workspace written by ssd_prepare for the same
+ * B, C and problem (C is read again here for the read-out of the carried
+ * state).  Arguments as for ssd_forward. */
+int ssd_scan(const ssd_problem_t* p,
+             const void* x, const float* dt, const float* A_log, const void* C,
+             const float* D, const float* init_state, const int32_t* seq_idx,
+             float* y, float* final_state,
+             const void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of an error code. */
+const char* ssd_strerror(int status);
+
+/* SSD_ABI_VERSION of the loaded library. */
+int ssd_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SSD_MI355X_H */

@@ -1,0 +1,209 @@
+"""Mamba-2 SSD chunked-scan forward on MI355X (gfx950).
+
+A thin ctypes binding over the C ABI in ``include/ssd.h`` (``libssd_mi355x.so``,
+built in-tree by ``mamba_ssd_scan_chunked_amd.build``).  PyTorch only supplies
+device memory and the current stream; every step of the computation runs in
+the library's HIP kernels.  There is no CPU fallback: if the library is not
+built, or no GPU is present, the calls raise.
+
+    y, final = forward(x, dt, A_log, B, C, D=None, chunk_len=256,
+                       init_state=None, seq_idx=None, nseqs=None)
+
+Layouts: x (b,T,H,P) bf16|f32, dt (b,T,H) f32, A_log (H) f32, B/C (b,T,G,N) same
+dtype as x, D (H) f32, init_state (nseqs,H,P,N) f32, seq_idx (b,T) int32.
+Outputs: y (b,T,H,P) f32 and final_state (nseqs,H,P,N) f32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+__all__ = ["forward", "prepare", "scan", "workspace_size", "validate", "problem", "SSDError",
+           "version", "library_path", "load_library", "DTYPE_F32", "DTYPE_BF16", "FLAG_DT_SCALES_X"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libssd_mi355x.so"
+
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+FLAG_DT_SCALES_X = 1
+
+SSD_OK = 0
+ERROR_NAMES = {1: "NULL_POINTER", 2: "BAD_SHAPE", 3: "UNSUPPORTED", 4: "ALIGNMENT", 5: "WORKSPACE",
+               6: "ALIAS", 7: "HIP", 8: "NO_DEVICE"}
+
+
+class SSDError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__("ssd error %d (%s): %s" % (code, ERROR_NAMES.get(code, "?"), msg))
+        self.code = code
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
+                ("headdim", ctypes.c_int64), ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64),
+                ("chunk_len", ctypes.c_int64), ("nseqs", ctypes.c_int64), ("dtype", ctypes.c_int32),
+                ("flags", ctypes.c_uint32)]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+def load_library():
+    """Load libssd_mi355x.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise ImportError("%s is not built; run `python -m mamba_ssd_scan_chunked_amd.build`" % path)
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER(Problem)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    lib.ssd_validate.argtypes = [P]
+    lib.ssd_validate.restype = ctypes.c_int
+    lib.ssd_workspace_size.argtypes = [P]
+    lib.ssd_workspace_size.restype = sz
+    lib.ssd_forward.argtypes = [P] + [vp] * 10 + [vp, sz, vp]
+    lib.ssd_forward.restype = ctypes.c_int
+    lib.ssd_prepare.argtypes = [P, vp, vp, vp, sz, vp]
+    lib.ssd_prepare.restype = ctypes.c_int
+    lib.ssd_scan.argtypes = [P] + [vp] * 9 + [vp, sz, vp]
+    lib.ssd_scan.restype = ctypes.c_int
+    lib.ssd_strerror.argtypes = [ctypes.c_int]
+    lib.ssd_strerror.restype = ctypes.c_char_p
+    lib.ssd_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def version() -> int:
+    return int(load_library().ssd_version())
+
+
+def _check(code: int):
+    if code != SSD_OK:
+        raise SSDError(code, load_library().ssd_strerror(code).decode())
+
+
+def problem(batch, seqlen, nheads, headdim, dstate, ngroups=1, chunk_len=256, nseqs=None,
+            dtype=DTYPE_BF16, flags=0) -> Problem:
+    return Problem(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_len,
+                   batch if nseqs is None else nseqs, dtype, flags)
+
+
+def validate(p: Problem) -> int:
+    return int(load_library().ssd_validate(ctypes.byref(p)))
+
+
+def workspace_size(p: Problem) -> int:
+    return int(load_library().ssd_workspace_size(ctypes.byref(p)))
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream_of(device, stream):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream(device).cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _describe(x, B, dt, A_log, chunk_len, seq_idx, nseqs, dt_scales_x):
+    import torch
+    if x.dim() != 4 or B.dim() != 4:
+        raise ValueError("x must be (b,T,H,P) and B, C (b,T,G,N)")
+    b, T, H, Pd = x.shape
+    G, N = B.shape[2], B.shape[3]
+    if x.dtype == torch.bfloat16:
+        dtype = DTYPE_BF16
+    elif x.dtype == torch.float32:
+        dtype = DTYPE_F32
+    else:
+        raise TypeError("x must be bfloat16 or float32")
+    if seq_idx is None:
+        ns = b
+    else:
+        if nseqs is None:
+            raise ValueError("nseqs is required with seq_idx (it sizes final_state)")
+        ns = int(nseqs)
+    flags = FLAG_DT_SCALES_X if dt_scales_x else 0
+    return problem(b, T, H, Pd, N, G, chunk_len, ns, dtype, flags)
+
+
+def _check_tensors(x, dt, A_log, B, C, D, init_state, seq_idx):
+    import torch
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    for name, t, dt_ in (("dt", dt, torch.float32), ("A_log", A_log, torch.float32), ("D", D, torch.float32),
+                         ("init_state", init_state, torch.float32), ("seq_idx", seq_idx, torch.int32),
+                         ("B", B, x.dtype), ("C", C, x.dtype)):
+        if t is None:
+            continue
+        if t.device != dev:
+            raise ValueError("%s is on %s, x on %s" % (name, t.device, dev))
+        if t.dtype != dt_:
+            raise TypeError("%s must be %s, got %s" % (name, dt_, t.dtype))
+    b, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    if tuple(dt.shape) != (b, T, H) or tuple(A_log.shape) != (H,):
+        raise ValueError("dt must be (b,T,H) and A_log (H,)")
+    if tuple(B.shape) != (b, T, G, N) or tuple(C.shape) != (b, T, G, N):
+        raise ValueError("B and C must be (b,T,G,N)")
+    if D is not None and tuple(D.shape) != (H,):
+        raise ValueError("D must be (H,)")
+    if seq_idx is not None and tuple(seq_idx.shape) != (b, T):
+        raise ValueError("seq_idx must be (b,T)")
+
+
+def forward(x, dt, A_log, B, C, D=None, chunk_len: int = 256, init_state=None, seq_idx=None,
+            nseqs: Optional[int] = None, dt_scales_x: bool = False, y=None, final_state=None,
+            workspace=None, return_final: bool = True, stream=None):
+    """SSD forward through ``ssd_forward``.  Returns (y, final_state or None)."""
+    import torch
+    _check_tensors(x, dt, A_log, B, C, D, init_state, seq_idx)
+    x, dt, A_log, B, C = (t.contiguous() for t in (x, dt, A_log, B, C))
+    D = D.contiguous() if D is not None else None
+    init_state = init_state.contiguous() if init_state is not None else None
+    seq_idx = seq_idx.contiguous() if seq_idx is not None else None
+    p = _describe(x, B, dt, A_log, chunk_len, seq_idx, nseqs, dt_scales_x)
+    lib = load_library()
+    _check(lib.ssd_validate(ctypes.byref(p)))
+    dev = x.device
+    b, T, H, P = x.shape
+    N = B.shape[3]
+    if init_state is not None and tuple(init_state.shape) != (p.nseqs, H, P, N):
+        raise ValueError("init_state must be (nseqs,H,P,N)")
+    if y is None:
+        y = torch.empty((b, T, H, P), dtype=torch.float32, device=dev)
+    if final_state is None and return_final:
+        final_state = torch.empty((p.nseqs, H, P, N), dtype=torch.float32, device=dev)
+    wsb = int(lib.ssd_workspace_size(ctypes.byref(p)))
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+    st = _stream_of(dev, stream)
+    _check(lib.ssd_forward(ctypes.byref(p), _ptr(x), _ptr(dt), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D),
+                           _ptr(init_state), _ptr(seq_idx), _ptr(y), _ptr(final_state),
+                           _ptr(workspace), workspace.numel(), st))
+    return y, final_state
+
+
+def prepare(p: Problem, B, C, workspace, stream=None):
+    """``ssd_prepare``: per-block C B^T tiles and B^T into ``workspace``."""
+    _check(load_library().ssd_prepare(ctypes.byref(p), _ptr(B), _ptr(C), _ptr(workspace), workspace.numel(),
+                                      _stream_of(B.device, stream)))
+
+
+def scan(p: Problem, x, dt, A_log, C, D, init_state, seq_idx, y, final_state, workspace, stream=None):
+    """``ssd_scan``: the chunked scan proper, reading the workspace from :func:`prepare`."""
+    _check(load_library().ssd_scan(ctypes.byref(p), _ptr(x), _ptr(dt), _ptr(A_log), _ptr(C), _ptr(D),
+                                   _ptr(init_state), _ptr(seq_idx), _ptr(y), _ptr(final_state), _ptr(workspace),
+                                   workspace.numel(), _stream_of(x.device, stream)))

@@ -1,0 +1,281 @@
+// Host side of the C ABI declared in include/ssd.h: argument checks, workspace
+// layout, kernel selection and launches.  Every check runs before the first HIP
+// call, so invalid arguments are reported without touching the device.
+#include "ssd.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdlib>
+#include <cstdio>
+
+#include "ssd_kernels.hpp"
+#include "ssd_launch.hpp"
+
+namespace {
+
+constexpr int64_t kMaxDim = int64_t(1) << 31;
+
+int block_len(const ssd_problem_t* p) {
+    if (p->chunk_len == 32) return 32;
+    if (p->chunk_len >= 64 && p->chunk_len % 64 == 0) return 64;
+    return 0;
+}
+
+int64_t elem_size(int32_t dtype) { return dtype == SSD_DTYPE_BF16 ? 2 : 4; }
+
+int64_t nblocks(const ssd_problem_t* p) {
+    const int q = block_len(p);
+    return q ? (p->seqlen + q - 1) / q : 0;
+}
+
+int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
+
+struct WsLayout {
+    int64_t cb_bytes;   // (b, G, nblk, QB, QB) fp32
+    int64_t bt_off;     // offset of (b, G, nblk, N, QB) dtype
+    int64_t total;
+};
+
+WsLayout ws_layout(const ssd_problem_t* p) {
+    const int64_t q = block_len(p);
+    const int64_t units = p->batch * p->ngroups * nblocks(p);
+    WsLayout l;
+    l.cb_bytes = align256(units * q * q * 4);
+    l.bt_off = l.cb_bytes;
+    l.total = l.bt_off + align256(units * p->dstate * q * elem_size(p->dtype));
+    return l;
+}
+
+bool misaligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) != 0; }
+
+bool overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+    if (!a || !b || abytes <= 0 || bbytes <= 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + static_cast<uintptr_t>(bbytes) && b0 < a0 + static_cast<uintptr_t>(abytes);
+}
+
+bool log_enabled() {
+    static const bool on = [] {
+        const char* v = std::getenv("SSD_LOG");
+        return v && v[0] == '1';
+    }();
+    return on;
+}
+
+int check_device() {
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) return SSD_ERR_NO_DEVICE;
+    return SSD_OK;
+}
+
+// Byte sizes of the tensors of a problem.
+struct Sizes {
+    int64_t x, dt, bc, y, state, seq;
+};
+Sizes sizes(const ssd_problem_t* p) {
+    Sizes s;
+    const int64_t bt = p->batch * p->seqlen;
+    s.x = bt * p->nheads * p->headdim * elem_size(p->dtype);
+    s.dt = bt * p->nheads * 4;
+    s.bc = bt * p->ngroups * p->dstate * elem_size(p->dtype);
+    s.y = bt * p->nheads * p->headdim * 4;
+    s.state = p->nseqs * p->nheads * p->headdim * p->dstate * 4;
+    s.seq = bt * 4;
+    return s;
+}
+
+int check_prepare_args(const ssd_problem_t* p, const void* B, const void* C, const void* ws, size_t ws_bytes) {
+    const int v = ssd_validate(p);
+    if (v != SSD_OK) return v;
+    const bool empty = p->batch == 0 || p->seqlen == 0;
+    if (!empty && (!B || !C || !ws)) return SSD_ERR_NULL_POINTER;
+    if (misaligned(B, 16) || misaligned(C, 16) || misaligned(ws, 256)) return SSD_ERR_ALIGNMENT;
+    if (static_cast<int64_t>(ws_bytes) < ws_layout(p).total) return SSD_ERR_WORKSPACE;
+    const Sizes s = sizes(p);
+    const int64_t wsb = ws_layout(p).total;
+    if (overlap(ws, wsb, B, s.bc) || overlap(ws, wsb, C, s.bc)) return SSD_ERR_ALIAS;
+    return SSD_OK;
+}
+
+int check_scan_args(const ssd_problem_t* p, const void* x, const float* dt, const float* A_log, const void* C,
+                    const float* D, const float* init, const int32_t* seq_idx, const float* y, const float* fin,
+                    const void* ws, size_t ws_bytes) {
+    const int v = ssd_validate(p);
+    if (v != SSD_OK) return v;
+    const bool empty_tokens = p->batch == 0 || p->seqlen == 0;
+    if (!A_log) return SSD_ERR_NULL_POINTER;
+    if (!empty_tokens && (!x || !dt || !C || !y || !ws)) return SSD_ERR_NULL_POINTER;
+    if (!seq_idx && p->nseqs != p->batch) return SSD_ERR_BAD_SHAPE;
+    if (misaligned(x, 16) || misaligned(C, 16) || misaligned(y, 16) || misaligned(dt, 4) || misaligned(A_log, 4) ||
+        misaligned(D, 4) || misaligned(init, 16) || misaligned(fin, 16) || misaligned(seq_idx, 4) ||
+        misaligned(ws, 256))
+        return SSD_ERR_ALIGNMENT;
+    if (static_cast<int64_t>(ws_bytes) < ws_layout(p).total) return SSD_ERR_WORKSPACE;
+    const Sizes s = sizes(p);
+    const int64_t wsb = ws_layout(p).total;
+    const int64_t hb = p->nheads * 4;
+    // outputs must not overlap any input, the workspace or each other
+    const void* in_ptr[] = {x, dt, A_log, C, D, seq_idx, ws};
+    const int64_t in_sz[] = {s.x, s.dt, hb, s.bc, hb, s.seq, wsb};
+    for (int i = 0; i < 7; ++i) {
+        if (overlap(y, s.y, in_ptr[i], in_sz[i])) return SSD_ERR_ALIAS;
+        if (overlap(fin, s.state, in_ptr[i], in_sz[i])) return SSD_ERR_ALIAS;
+    }
+    if (overlap(y, s.y, init, s.state) || overlap(y, s.y, fin, s.state)) return SSD_ERR_ALIAS;
+    // final_state may be init_state itself (in-place carry), but not a shifted overlap
+    if (fin && init && fin != init && overlap(fin, s.state, init, s.state)) return SSD_ERR_ALIAS;
+    return SSD_OK;
+}
+
+int launch_prepare(const ssd_problem_t* p, const void* B, const void* C, void* ws, hipStream_t stream) {
+    const int q = block_len(p);
+    const int64_t nblk = nblocks(p);
+    const WsLayout l = ws_layout(p);
+    ssd::PrepParams prm;
+    prm.B = B;
+    prm.C = C;
+    prm.cb = static_cast<float*>(ws);
+    prm.bt = static_cast<char*>(ws) + l.bt_off;
+    prm.T = p->seqlen;
+    prm.G = p->ngroups;
+    prm.nblk = static_cast<int>(nblk);
+    const int64_t grid = p->batch * p->ngroups * nblk;
+    if (grid == 0) return SSD_OK;
+    hipError_t e = p->dtype == SSD_DTYPE_BF16 ? ssd::launch_prep_bf16((int)p->dstate, q, prm, grid, stream)
+                                              : ssd::launch_prep_f32((int)p->dstate, q, prm, grid, stream);
+    if (log_enabled())
+        std::fprintf(stderr, "[ssd] prepare dtype=%d N=%lld QB=%d grid=%lld -> %s\n", p->dtype,
+                     (long long)p->dstate, q, (long long)grid, hipGetErrorString(e));
+    return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+}
+
+int launch_scan(const ssd_problem_t* p, const void* x, const float* dt, const float* A_log, const void* C,
+                const float* D, const float* init, const int32_t* seq_idx, float* y, float* fin, const void* ws,
+                hipStream_t stream) {
+    const int q = block_len(p);
+    const WsLayout l = ws_layout(p);
+    ssd::ScanParams prm;
+    prm.x = x;
+    prm.dt = dt;
+    prm.A_log = A_log;
+    prm.D = D;
+    prm.init = init;
+    prm.seq_idx = seq_idx;
+    prm.y = y;
+    prm.fin = fin;
+    prm.cb = static_cast<const float*>(ws);
+    prm.bt = static_cast<const char*>(ws) + l.bt_off;
+    prm.C = C;
+    prm.batch = p->batch;
+    prm.T = p->seqlen;
+    prm.H = p->nheads;
+    prm.G = p->ngroups;
+    prm.nseqs = p->nseqs;
+    prm.nblk = static_cast<int>(nblocks(p));
+    prm.dt_scales_x = (p->flags & SSD_FLAG_DT_SCALES_X) ? 1 : 0;
+    const int64_t grid = p->batch * p->nheads;
+    if (grid == 0) return SSD_OK;
+    if (p->seqlen == 0 && (seq_idx || !fin)) return SSD_OK;   // no token, no sequence to hand out
+    hipError_t e = p->dtype == SSD_DTYPE_BF16
+                       ? ssd::launch_scan_bf16((int)p->headdim, (int)p->dstate, q, prm, grid, stream)
+                       : ssd::launch_scan_f32((int)p->headdim, (int)p->dstate, q, prm, grid, stream);
+    if (log_enabled())
+        std::fprintf(stderr, "[ssd] scan dtype=%d P=%lld N=%lld QB=%d grid=%lld block=%lld -> %s\n", p->dtype,
+                     (long long)p->headdim, (long long)p->dstate, q, (long long)grid,
+                     (long long)(p->headdim / 16 * 64), hipGetErrorString(e));
+    return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssd_validate(const ssd_problem_t* p) {
+    if (!p) return SSD_ERR_NULL_POINTER;
+    if (p->batch < 0 || p->seqlen < 0 || p->nheads <= 0 || p->headdim <= 0 || p->dstate <= 0 || p->ngroups <= 0 ||
+        p->nseqs < 0)
+        return SSD_ERR_BAD_SHAPE;
+    if (p->batch >= kMaxDim || p->seqlen >= kMaxDim || p->nheads >= kMaxDim || p->nseqs >= kMaxDim)
+        return SSD_ERR_BAD_SHAPE;
+    if (p->nheads % p->ngroups != 0) return SSD_ERR_BAD_SHAPE;
+    if (p->chunk_len <= 0) return SSD_ERR_BAD_SHAPE;
+    if (p->dtype != SSD_DTYPE_BF16 && p->dtype != SSD_DTYPE_F32) return SSD_ERR_UNSUPPORTED;
+    if (p->flags & ~uint32_t(SSD_FLAG_DT_SCALES_X)) return SSD_ERR_UNSUPPORTED;
+    const int q = block_len(p);
+    if (!q) return SSD_ERR_UNSUPPORTED;
+    if (p->headdim > 4096 || p->dstate > 4096) return SSD_ERR_UNSUPPORTED;
+    const int P = (int)p->headdim, N = (int)p->dstate;
+    const bool ok = p->dtype == SSD_DTYPE_BF16 ? ssd::supported_bf16(P, N, q) : ssd::supported_f32(P, N, q);
+    if (!ok) return SSD_ERR_UNSUPPORTED;
+    // element counts must stay far from int64 overflow
+    const double elems = double(p->batch) * double(p->seqlen) * double(p->nheads) * double(p->headdim);
+    const double states = double(p->nseqs) * double(p->nheads) * double(p->headdim) * double(p->dstate);
+    if (elems > 4e18 || states > 4e18) return SSD_ERR_BAD_SHAPE;
+    if (double(p->batch) * double(p->nheads) >= 2147483647.0) return SSD_ERR_BAD_SHAPE;   // grid size
+    return SSD_OK;
+}
+
+size_t ssd_workspace_size(const ssd_problem_t* p) {
+    if (ssd_validate(p) != SSD_OK) return 0;
+    return static_cast<size_t>(ws_layout(p).total);
+}
+
+int ssd_prepare(const ssd_problem_t* p, const void* B, const void* C, void* workspace, size_t workspace_bytes,
+                void* stream) {
+    const int v = check_prepare_args(p, B, C, workspace, workspace_bytes);
+    if (v != SSD_OK) return v;
+    const int d = check_device();
+    if (d != SSD_OK) return d;
+    return launch_prepare(p, B, C, workspace, static_cast<hipStream_t>(stream));
+}
+
+int ssd_scan(const ssd_problem_t* p, const void* x, const float* dt, const float* A_log, const void* C,
+             const float* D, const float* init_state, const int32_t* seq_idx, float* y, float* final_state,
+             const void* workspace, size_t workspace_bytes, void* stream) {
+    const int v = check_scan_args(p, x, dt, A_log, C, D, init_state, seq_idx, y, final_state, workspace,
+                                  workspace_bytes);
+    if (v != SSD_OK) return v;
+    const int d = check_device();
+    if (d != SSD_OK) return d;
+    return launch_scan(p, x, dt, A_log, C, D, init_state, seq_idx, y, final_state, workspace,
+                       static_cast<hipStream_t>(stream));
+}
+
+int ssd_forward(const ssd_problem_t* p, const void* x, const float* dt, const float* A_log, const void* B,
+                const void* C, const float* D, const float* init_state, const int32_t* seq_idx, float* y,
+                float* final_state, void* workspace, size_t workspace_bytes, void* stream) {
+    int v = check_prepare_args(p, B, C, workspace, workspace_bytes);
+    if (v != SSD_OK) return v;
+    v = check_scan_args(p, x, dt, A_log, C, D, init_state, seq_idx, y, final_state, workspace, workspace_bytes);
+    if (v != SSD_OK) return v;
+    {
+        const Sizes s = sizes(p);
+        if (overlap(y, s.y, B, s.bc) || overlap(final_state, s.state, B, s.bc)) return SSD_ERR_ALIAS;
+    }
+    const int d = check_device();
+    if (d != SSD_OK) return d;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    v = launch_prepare(p, B, C, workspace, st);
+    if (v != SSD_OK) return v;
+    return launch_scan(p, x, dt, A_log, C, D, init_state, seq_idx, y, final_state, workspace, st);
+}
+
+const char* ssd_strerror(int status) {
+    switch (status) {
+        case SSD_OK: return "success";
+        case SSD_ERR_NULL_POINTER: return "a required pointer is NULL";
+        case SSD_ERR_BAD_SHAPE: return "invalid problem shape (negative size, nheads % ngroups != 0, or nseqs inconsistent)";
+        case SSD_ERR_UNSUPPORTED: return "unsupported dtype, headdim, dstate, chunk_len or flags";
+        case SSD_ERR_ALIGNMENT: return "a tensor pointer is misaligned (tensors need 16 bytes, the workspace 256)";
+        case SSD_ERR_WORKSPACE: return "workspace missing or smaller than ssd_workspace_size()";
+        case SSD_ERR_ALIAS: return "an output buffer overlaps an input, the workspace or the other output";
+        case SSD_ERR_HIP: return "a HIP runtime call or kernel launch failed";
+        case SSD_ERR_NO_DEVICE: return "no HIP device available";
+        default: return "unknown ssd status code";
+    }
+}
+
+int ssd_version(void) { return SSD_ABI_VERSION; }
+
+}  // extern "C"

@@ -112,6 +112,13 @@ int ssd_oracle_f64(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdi
         }
         if (T > 0 && final_state && cur >= 0)
             memcpy(final_state + (cur * H + h) * P * N, S, (size_t)(P * N) * sizeof(double));
+        if (T == 0 && final_state && seq_idx == NULL) {
+            /* no token, no step of the recurrence: the row's state is its initial state */
+            if (init)
+                memcpy(final_state + (r * H + h) * P * N, init + (r * H + h) * P * N, (size_t)(P * N) * sizeof(double));
+            else
+                memset(final_state + (r * H + h) * P * N, 0, (size_t)(P * N) * sizeof(double));
+        }
         free(S);
         free(xs);
     }

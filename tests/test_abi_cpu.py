@@ -1,0 +1,135 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function include/ssd.h declares, and rejects bad arguments before any
+HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mamba_ssd_scan_chunked_amd as ssd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssd.h")
+
+# fake, 256-byte aligned device addresses: validation must fail before they are used
+A = 0x10000000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssd_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = ssd.load_library()
+    names = declared_functions()
+    assert {"ssd_forward", "ssd_prepare", "ssd_scan", "ssd_validate", "ssd_workspace_size",
+            "ssd_strerror", "ssd_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_strerror():
+    assert ssd.version() == 1
+    lib = ssd.load_library()
+    for code in range(0, 9):
+        assert lib.ssd_strerror(code)
+    assert b"unknown" in lib.ssd_strerror(99)
+
+
+def prob(**kw):
+    base = dict(batch=4, seqlen=4096, nheads=80, headdim=64, dstate=128, ngroups=1, chunk_len=256, nseqs=None,
+                dtype=ssd.DTYPE_BF16, flags=0)
+    base.update(kw)
+    return ssd.problem(**base)
+
+
+def test_validate_accepts_the_measured_shapes():
+    assert ssd.validate(prob()) == 0
+    assert ssd.validate(prob(batch=8, seqlen=2048, nheads=24)) == 0
+    for n in (64, 128, 256):
+        assert ssd.validate(prob(batch=1, seqlen=16384, nheads=32, dstate=n)) == 0
+    assert ssd.validate(prob(batch=1, seqlen=8192, nheads=48, ngroups=8, nseqs=16)) == 0
+    assert ssd.validate(prob(batch=1, seqlen=256, nheads=2, headdim=16, dstate=16, chunk_len=32,
+                             dtype=ssd.DTYPE_F32)) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=-1), 2), (dict(seqlen=-5), 2), (dict(nheads=0), 2), (dict(headdim=0), 2),
+    (dict(ngroups=3), 2), (dict(chunk_len=0), 2), (dict(nseqs=-1), 2),
+    (dict(chunk_len=48), 3), (dict(chunk_len=16), 3), (dict(chunk_len=100), 3),
+    (dict(headdim=48), 3), (dict(dstate=96), 3), (dict(dstate=16), 3), (dict(dtype=7), 3), (dict(flags=2), 3),
+    (dict(dtype=ssd.DTYPE_F32, dstate=256), 3),
+])
+def test_validate_rejects(kw, code):
+    assert ssd.validate(prob(**kw)) == code
+
+
+def test_workspace_size():
+    p = prob()
+    ws = ssd.workspace_size(p)
+    # per (row, group, 64-token block): 64x64 fp32 C.B^T + 128x64 bf16 B^T
+    blocks = 4 * 1 * (4096 // 64)
+    assert ws == blocks * 64 * 64 * 4 + blocks * 128 * 64 * 2
+    assert ssd.workspace_size(prob(headdim=48)) == 0
+    assert ssd.workspace_size(prob(seqlen=0)) == 0 or ssd.workspace_size(prob(seqlen=0)) <= 512
+
+
+def _forward(p, **ptrs):
+    lib = ssd.load_library()
+    names = ["x", "dt", "A_log", "B", "C", "D", "init", "seq", "y", "fin"]
+    vals = {n: A + 0x1000000 * (i + 1) for i, n in enumerate(names)}
+    vals.update({"D": None, "init": None, "seq": None})
+    ws = ptrs.pop("ws", A + 0x40000000)
+    wsb = ptrs.pop("wsb", ssd.workspace_size(p))
+    vals.update(ptrs)
+    return lib.ssd_forward(ctypes.byref(p), *[vals[n] for n in names], ws, wsb, None)
+
+
+def small():
+    return prob(batch=1, seqlen=64, nheads=2, headdim=32, dstate=64, chunk_len=64)
+
+
+def test_forward_rejects_null_pointers():
+    for n in ("x", "dt", "A_log", "B", "C", "y"):
+        assert _forward(small(), **{n: None}) == 1, n
+    assert _forward(small(), ws=None) in (1, 5)
+
+
+def test_forward_rejects_misalignment():
+    assert _forward(small(), x=A + 0x1000000 + 2) == 4
+    assert _forward(small(), y=A + 0x9000000 + 8) == 4
+    assert _forward(small(), ws=A + 0x40000000 + 16) == 4
+
+
+def test_forward_rejects_small_workspace():
+    p = small()
+    assert _forward(p, wsb=ssd.workspace_size(p) - 1) == 5
+
+
+def test_forward_rejects_aliasing():
+    assert _forward(small(), y=A + 0x1000000) == 6          # y on top of x
+    assert _forward(small(), fin=A + 0x3000000) == 6        # final on top of A_log
+    p = small()
+    assert _forward(p, ws=A + 0x9000000) == 6               # workspace on top of y
+
+
+def test_forward_requires_seq_idx_for_packed_nseqs():
+    assert _forward(prob(batch=1, seqlen=64, nheads=2, headdim=32, dstate=64, chunk_len=64, nseqs=3)) == 2
+
+
+def test_forward_without_device_reports_no_device():
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present: this call would launch on fake pointers")
+    assert _forward(small()) == 8
+
+
+def test_binding_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 64, 2, 32, dtype=torch.bfloat16)
+    B = torch.zeros(1, 64, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        ssd.forward(x, torch.zeros(1, 64, 2), torch.zeros(2), B, B)

@@ -323,3 +323,13 @@ def _pin_suite_passes(lib_path) -> bool:
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_planted_mistakes_are_caught(name):
     assert not _pin_suite_passes(_build_mutant(name)), "mutant %s survived the pins" % name
+
+
+def test_zero_tokens_leave_the_initial_state():
+    """No token means no step of the recurrence: the final state is the initial one."""
+    p = _case_problem(dict(b=2, T=0, H=2, P=3, N=4, G=1, init_std=1.0), seed=15)
+    y, f = run(p)
+    assert y.size == 0
+    np.testing.assert_array_equal(f, p["init"].double().numpy())
+    _, f0 = run(dict(p, init=None))
+    assert not f0.any()
