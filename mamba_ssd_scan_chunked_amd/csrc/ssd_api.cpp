@@ -213,6 +213,10 @@ int ssd_validate(const ssd_problem_t* p) {
     const double states = double(p->nseqs) * double(p->nheads) * double(p->headdim) * double(p->dstate);
     if (elems > 4e18 || states > 4e18) return SSD_ERR_BAD_SHAPE;
     if (double(p->batch) * double(p->nheads) >= 2147483647.0) return SSD_ERR_BAD_SHAPE;   // grid size
+    // the kernels address one block of q tokens with 32-bit byte offsets
+    if (double(q) * double(p->nheads) * double(p->headdim) * 4.0 >= 2147483647.0 ||
+        double(q) * double(p->ngroups) * double(p->dstate) * 4.0 >= 2147483647.0)
+        return SSD_ERR_UNSUPPORTED;
     return SSD_OK;
 }
 

@@ -78,15 +78,26 @@ template <> __device__ inline float lds_frag<float>(const float* p) { return *p;
 
 __device__ inline float fast_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
 
-// Number of K steps of the y_off product (K = N, permuted so that the state
-// accumulators feed the B operand directly; see state_frags).
+// Rows of the state tiles.  The state S (P x N) is held transposed, S^T[n][p],
+// as N/16 accumulator tiles per wave; accumulator row rho = 4*(l/16) + i of
+// tile m holds state row n = nrow(m, rho).  For N % 32 == 0 the rows of tile
+// pairs (2k, 2k+1) are interleaved so that lane group l/16 of the pair holds
+// the 8 consecutive rows 32k + 8*(l/16) .. +7: converted to bf16 they are
+// exactly the B operand of the read-out C . S^T for the K step k, and the A
+// operand (C) is one contiguous 16-byte read.  The permutation is applied to
+// the rows of the B^T operand that produces the state, so no data moves.
+template <int N>
+__device__ inline int nrow(int m, int rho) {
+    if constexpr (N % 32 == 0) return 32 * (m >> 1) + 8 * (rho >> 2) + 4 * (m & 1) + (rho & 3);
+    else return 16 * m + rho;
+}
+
+// K steps of the read-out product C . S^T (K = N).
 template <typename TI, int N> struct OffK {
     static constexpr int NK = N / Mfma<TI>::KSTEP;
 };
 
-// B-operand fragments of y_off = C . S^T built from the state accumulators.
-// st[m] holds S^T rows n = 16m + 4*(l/16) + i.  bf16: step k packs tiles 2k and
-// 2k+1 (n = 32k + 16*(e/4) + 4*(l/16) + e%4); fp32: step k = 4m + i.
+// B-operand fragments of the read-out from the state accumulators.
 template <int N>
 __device__ inline void state_frags(const f32x4 (&st)[N / 16], bf16x8 (&sf)[N / 32]) {
 #pragma unroll
@@ -108,13 +119,13 @@ __device__ inline void state_frags(const f32x4 (&st)[N / 16], float (&sf)[N / 4]
         for (int i = 0; i < 4; ++i) sf[4 * m + i] = st[m][i];
 }
 
-// Same fragments from an fp32 state in global memory laid out [p][n] (row p = this lane's channel).
+// Same fragments from an fp32 state row in global memory (row p = this lane's channel).
 template <int N>
 __device__ inline void global_state_frags(const float* row, int lg, bf16x8 (&sf)[N / 32]) {
 #pragma unroll
     for (int k = 0; k < N / 32; ++k) {
-        const float4 lo = *(const float4*)(row + 32 * k + 4 * lg);
-        const float4 hi = *(const float4*)(row + 32 * k + 16 + 4 * lg);
+        const float4 lo = *(const float4*)(row + 32 * k + 8 * lg);
+        const float4 hi = *(const float4*)(row + 32 * k + 8 * lg + 4);
         bf16x8 f;
         f[0] = (__bf16)lo.x; f[1] = (__bf16)lo.y; f[2] = (__bf16)lo.z; f[3] = (__bf16)lo.w;
         f[4] = (__bf16)hi.x; f[5] = (__bf16)hi.y; f[6] = (__bf16)hi.z; f[7] = (__bf16)hi.w;
@@ -125,19 +136,56 @@ template <int N>
 __device__ inline void global_state_frags(const float* row, int lg, float (&sf)[N / 4]) {
 #pragma unroll
     for (int m = 0; m < N / 16; ++m) {
-        const float4 v = *(const float4*)(row + 16 * m + 4 * lg);
+        const float4 v = *(const float4*)(row + nrow<N>(m, 4 * lg));
         sf[4 * m + 0] = v.x; sf[4 * m + 1] = v.y; sf[4 * m + 2] = v.z; sf[4 * m + 3] = v.w;
     }
 }
 
-// A-operand fragment of y_off: row t of the C tile at the permuted K indices.
-__device__ inline bf16x8 c_frag(const __bf16* row, int k, int lg) {
-    const bf16x4 lo = *(const bf16x4*)(row + 32 * k + 4 * lg);
-    const bf16x4 hi = *(const bf16x4*)(row + 32 * k + 16 + 4 * lg);
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+// A-operand fragment of the read-out: row t of the C tile at the K indices of step k.
+template <int N>
+__device__ inline bf16x8 c_frag(const __bf16* row, int k, int lg) { return *(const bf16x8*)(row + 32 * k + 8 * lg); }
+template <int N>
+__device__ inline float c_frag(const float* row, int k, int lg) { return row[nrow<N>(k >> 2, 4 * lg + (k & 3))]; }
+
+// Make this wave's LDS writes visible to its own other lanes.
+__device__ inline void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 }
-__device__ inline float c_frag(const float* row, int k, int lg) {
-    return row[16 * (k >> 2) + 4 * lg + (k & 3)];
+
+// Workgroup barrier that orders LDS only.  __syncthreads() also fences global
+// memory, which makes every wave wait for all of its outstanding global loads
+// (the prefetches of the next blocks) at each barrier; the tiles exchanged
+// through barriers here all live in LDS.
+__device__ inline void block_sync_lds() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Raw buffer resources: loads outside [0, bytes) return zero and stores there
+// are dropped by the hardware range check, so the ragged last block needs no
+// per-element guards (and no divergent branches around memory operations).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ inline rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    const int64_t lim = bytes < 0 ? 0 : (bytes > 0x7fffffffLL ? 0x7fffffffLL : bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)lim, 0x00020000);
+}
+__device__ inline uint4 buf_load16(rsrc_t r, int off) {
+    typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+    const u4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ inline float buf_load_f32(rsrc_t r, int off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ inline int buf_load_i32(rsrc_t r, int off) {
+    return __builtin_bit_cast(int, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ inline void buf_store16(f32x4 v, rsrc_t r, int off) {
+    typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, off, 0, 0);
 }
 
 struct PrepParams {
@@ -235,34 +283,52 @@ template <typename TI> struct CumType { typedef float type; };
 template <> struct CumType<float> { typedef double type; };   // fp32 path: exponent differences in fp64
 
 template <typename TI, int P, int N, int QB>
+struct ScanCfg {
+    static constexpr int NW = P / 16;                 // waves; wave w owns channels 16w .. 16w+15
+    static constexpr int NT = NW * 64;
+    static constexpr int SZ = (int)sizeof(TI);
+    static constexpr int VE = 16 / SZ;                // elements per 16-byte vector
+    static constexpr int LC = N + VE;                 // pitch of C rows (elements)
+    static constexpr int LQ = QB + VE;                // pitch of rows indexed by token s
+    static constexpr int KPL = Mfma<TI>::KPL, KSTEP = Mfma<TI>::KSTEP;
+    static constexpr int NK = OffK<TI, N>::NK;
+    static constexpr int RT = QB / 16;                // token tiles of a block
+    static constexpr int MT = N / 16;                 // state tiles per wave
+    // LDS tiles of one buffer: C, B^T, masked decay L o CB, X^T, weighted X^T
+    static constexpr int OFF_C = 0;
+    static constexpr int OFF_BT = OFF_C + QB * LC;
+    static constexpr int OFF_LM = OFF_BT + N * LQ;
+    static constexpr int OFF_XT = OFF_LM + QB * LQ;
+    static constexpr int OFF_XW = OFF_XT + P * LQ;
+    static constexpr int BUF_ELEMS = OFF_XW + P * LQ;
+    static constexpr int BUF_BYTES = BUF_ELEMS * SZ;
+    static constexpr int NBUF = (2 * BUF_BYTES <= 136 * 1024) ? 2 : 1;
+    // per-thread staging
+    static constexpr int CV = QB * N / VE, CPT = (CV + NT - 1) / NT;           // C tile vectors
+    static constexpr int BV = N * QB / VE, BPT = (BV + NT - 1) / NT;           // B^T tile vectors
+    static constexpr int LMP = QB * (QB / 16), LMPT = (LMP + NT - 1) / NT;     // (row, 16 columns) of L o CB
+    static constexpr int XPR = (QB / 2) * (P / VE), XPT = (XPR + NT - 1) / NT;  // (row pair, VE channels) of X
+};
+
+template <typename TI, int P, int N, int QB>
 __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
+    typedef ScanCfg<TI, P, N, QB> K;
     typedef Mfma<TI> MF;
     typedef typename MF::frag frag;
     typedef typename CumType<TI>::type cum_t;
-    constexpr int NW = P / 16;
-    constexpr int NT = NW * 64;
-    constexpr int VE = 16 / sizeof(TI);
-    constexpr int LC = N + VE;      // sC pitch
-    constexpr int LQ = QB + VE;     // pitch of rows indexed by s
-    constexpr int KPL = MF::KPL, KSTEP = MF::KSTEP;
-    constexpr int NK = OffK<TI, N>::NK;
-    constexpr int RT = QB / 16;     // row tiles per block
-    constexpr int MT = N / 16;      // state tiles per wave
-    static_assert(QB <= 64 && QB % KSTEP == 0, "block length");
+    constexpr int NT = K::NT, VE = K::VE, LC = K::LC, LQ = K::LQ, KPL = K::KPL, KSTEP = K::KSTEP, SZ = K::SZ;
+    constexpr int NK = K::NK, RT = K::RT, MT = K::MT, NBUF = K::NBUF, NW = K::NW;
+    static_assert(QB <= 64 && QB % KSTEP == 0 && QB % 16 == 0, "block length");
     static_assert(N % KSTEP == 0 && N % 16 == 0 && P % 16 == 0, "shape");
 
-    __shared__ __attribute__((aligned(16))) TI sC[QB * LC];
-    __shared__ __attribute__((aligned(16))) TI sBt[N * LQ];
-    __shared__ __attribute__((aligned(16))) TI sLm[QB * LQ];
-    __shared__ __attribute__((aligned(16))) TI sXt[P * LQ];
-    __shared__ __attribute__((aligned(16))) TI sXw[P * LQ];
-    __shared__ cum_t sCum[QB];
-    __shared__ float sRow[QB];
-    __shared__ float sDtf[QB];      // dt_s if x is scaled by dt, else 1
-    __shared__ int sSeg[QB];
-    __shared__ int sStart[QB + 1];
-    __shared__ int sSeqOf[QB + 1];
-    __shared__ int sNstart;
+    __shared__ __attribute__((aligned(16))) TI smem[NBUF * K::BUF_ELEMS];
+    // per-wave copies of the block's per-token scalars (each wave computes its own)
+    __shared__ __attribute__((aligned(16))) cum_t sCum[NW][64];
+    __shared__ __attribute__((aligned(16))) float sRow[NW][64];
+    __shared__ __attribute__((aligned(16))) float sDtf[NW][64];
+    __shared__ int sSeg[NW][64];
+    __shared__ int sStart[NW][65];
+    __shared__ int sSeqOf[NW][65];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -270,26 +336,54 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
 
     // Work-item order: runs of consecutive (row, head) items go to the same
     // XCD (workgroups are dealt round-robin over the 8 XCDs), so the heads of
-    // a row share that row's CB / B^T tiles in one L2.
+    // a row share that row's C, CB and B^T tiles in one L2.
     const int64_t units = prm.batch * prm.H;
     int64_t u = blockIdx.x;
     if (units % 8 == 0) u = (int64_t)(blockIdx.x % 8) * (units / 8) + blockIdx.x / 8;
     const int64_t b = u / prm.H, h = u % prm.H;
     const int64_t g = h / (prm.H / prm.G);
-    const int64_t T = prm.T, H = prm.H;
+    const int64_t T = prm.T, H = prm.H, G = prm.G;
+    const int nblk = prm.nblk;
     const int p0 = 16 * w;
 
-    // A_h in log2 units, so that the decays are exp2 of a cumulative sum
+    // A_h in log2 units, so that every decay is exp2 of a cumulative sum
     cum_t A2;
     if constexpr (sizeof(cum_t) == 8) A2 = -exp((double)prm.A_log[h]) * 1.4426950408889634;
     else A2 = -expf(prm.A_log[h]) * 1.4426950408889634f;
     const float Dh = prm.D ? prm.D[h] : 0.f;
     const TI* xg = (const TI*)prm.x;
+    const TI* Cg = (const TI*)prm.C;
     const TI* btg = (const TI*)prm.bt;
     const int32_t* seqg = prm.seq_idx ? prm.seq_idx + b * T : nullptr;
+    const bool euler = prm.dt_scales_x != 0;
     auto clamp_seq = [&](int s) { return s < 0 ? 0 : (s >= prm.nseqs ? (int)prm.nseqs - 1 : s); };
+    auto rows_of = [&](int blk) { return (int)min((int64_t)QB, T - (int64_t)blk * QB); };
 
-    // ---- initial state of the row's first sequence
+    // byte strides between consecutive tokens (the host keeps QB of them below 2^31)
+    const int xs = (int)(H * P * SZ), ys = (int)(H * P * 4), cs = (int)(G * N * SZ), ds = (int)(H * 4);
+    // per-block buffer resources: everything past the row's last token reads as zero / is not written
+    auto rsrc_x = [&](int blk) {
+        const int64_t t0 = (int64_t)blk * QB;
+        return make_rsrc(xg + ((b * T + t0) * H + h) * P, ((T - 1 - t0) * H + 1) * P * SZ);
+    };
+    auto rsrc_y = [&](int blk) {
+        const int64_t t0 = (int64_t)blk * QB;
+        return make_rsrc(prm.y + ((b * T + t0) * H + h) * P, ((T - 1 - t0) * H + 1) * P * 4);
+    };
+    auto rsrc_c = [&](int blk) {
+        const int64_t t0 = (int64_t)blk * QB;
+        return make_rsrc(Cg + ((b * T + t0) * G + g) * N, ((T - 1 - t0) * G + 1) * N * SZ);
+    };
+    auto rsrc_dt = [&](int blk) {
+        const int64_t t0 = (int64_t)blk * QB;
+        return make_rsrc(prm.dt + (b * T + t0) * H + h, ((T - 1 - t0) * H + 1) * 4);
+    };
+    auto rsrc_seq = [&](int blk) {
+        const int64_t t0 = (int64_t)blk * QB;
+        return make_rsrc(seqg + t0, (T - t0) * 4);
+    };
+
+    // ---- initial state of the row's first sequence (S^T tiles, rows nrow(m, 4*lg+i))
     int prevseq = (int)b;
     if (seqg && T > 0) prevseq = clamp_seq(seqg[0]);
     f32x4 st[MT];
@@ -297,154 +391,233 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
         const float* src = prm.init + (((int64_t)prevseq * H + h) * P + p0 + lr) * N;
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-            const float4 v = *(const float4*)(src + 16 * m + 4 * lg);
+            const float4 v = *(const float4*)(src + nrow<N>(m, 4 * lg));
             st[m] = f32x4{v.x, v.y, v.z, v.w};
         }
     } else {
 #pragma unroll
         for (int m = 0; m < MT; ++m) st[m] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-
     auto write_state = [&](const f32x4 (&s)[MT], int seq) {
         if (!prm.fin) return;
         float* dst = prm.fin + (((int64_t)seq * H + h) * P + p0 + lr) * N;
 #pragma unroll
         for (int m = 0; m < MT; ++m)
-            *(float4*)(dst + 16 * m + 4 * lg) = make_float4(s[m][0], s[m][1], s[m][2], s[m][3]);
+            *(float4*)(dst + nrow<N>(m, 4 * lg)) = make_float4(s[m][0], s[m][1], s[m][2], s[m][3]);
     };
 
-    for (int blk = 0; blk < prm.nblk; ++blk) {
-        const int64_t t0 = (int64_t)blk * QB;
-        const int rows = (int)min((int64_t)QB, T - t0);
+    // ---- staging registers.  C, B^T and CB are shared by all heads of the
+    // group and mostly hit L2: fetched one block ahead.  X, dt and seq_idx are
+    // this head's own HBM traffic: fetched two blocks ahead (sets a and b).
+    uint4 cr[K::CPT], br[K::BPT];
+    uint4 cbr[K::LMPT][4];
+    uint4 xa[K::XPT][2], xb[K::XPT][2];
+    float dta = 0.f, dtb = 0.f;
+    int sqa = 0, sqb = 0;
 
-        __syncthreads();   // the previous block's LDS contents are no longer read
-
-        // ---- stage the C tile and the block's B^T tile
-        {
-            const TI* Cg = (const TI*)prm.C;
-            for (int v = tid; v < QB * (N / VE); v += NT) {
-                const int t = v / (N / VE), c = v % (N / VE);
-                uint4 cv = make_uint4(0, 0, 0, 0);
-                if (t < rows) cv = *(const uint4*)(Cg + ((b * T + t0 + t) * prm.G + g) * N + c * VE);
-                *(uint4*)(sC + t * LC + c * VE) = cv;
-            }
-            const TI* btb = btg + (((b * prm.G + g) * prm.nblk + blk) * N) * QB;
-            for (int v = tid; v < N * (QB / VE); v += NT) {
-                const int n = v / (QB / VE), c = v % (QB / VE);
-                *(uint4*)(sBt + n * LQ + c * VE) = *(const uint4*)(btb + n * QB + c * VE);
-            }
-        }
-        // ---- X tile, stored transposed (rows p, columns t); raw vectors kept
-        //      in registers for the weighted copy
-        constexpr int XV = QB * (P / VE);
-        constexpr int XPT = (XV + NT - 1) / NT;
-        uint4 xr[XPT];
+    auto load_c_bt = [&](int blk) {
+        const rsrc_t rc = rsrc_c(blk);
+        const rsrc_t rb = make_rsrc(btg + (((b * G + g) * nblk + blk) * N) * QB, (int64_t)N * QB * SZ);
 #pragma unroll
-        for (int j = 0; j < XPT; ++j) {
+        for (int j = 0; j < K::CPT; ++j) {
             const int v = tid + j * NT;
-            xr[j] = make_uint4(0, 0, 0, 0);
-            if (v < XV) {
-                const int t = v / (P / VE), c = v % (P / VE);
-                if (t < rows) xr[j] = *(const uint4*)(xg + ((b * T + t0 + t) * H + h) * P + c * VE);
-                const TI* e = (const TI*)&xr[j];
+            if (K::CV % NT == 0 || v < K::CV) cr[j] = buf_load16(rc, (v / (N / VE)) * cs + (v % (N / VE)) * 16);
+        }
 #pragma unroll
-                for (int q = 0; q < VE; ++q) sXt[(c * VE + q) * LQ + t] = e[q];
-            }
+        for (int j = 0; j < K::BPT; ++j) {
+            const int v = tid + j * NT;
+            if (K::BV % NT == 0 || v < K::BV) br[j] = buf_load16(rb, v * 16);
+        }
+    };
+    auto load_cb = [&](int blk) {
+        const rsrc_t rcb = make_rsrc(prm.cb + (((b * G + g) * nblk + blk) * QB) * QB, (int64_t)QB * QB * 4);
+#pragma unroll
+        for (int j = 0; j < K::LMPT; ++j) {
+            const int v = tid + j * NT;
+            const int t = v / (QB / 16), sg = v % (QB / 16);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (K::LMP % NT == 0 || v < K::LMP) cbr[j][q] = buf_load16(rcb, (t * QB + 16 * sg + 4 * q) * 4);
+        }
+    };
+    auto load_x = [&](int blk, uint4 (&xr)[K::XPT][2]) {
+        const rsrc_t rx = rsrc_x(blk);
+#pragma unroll
+        for (int j = 0; j < K::XPT; ++j) {
+            const int v = tid + j * NT;
+            const int q = v / (P / VE), c = v % (P / VE);
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+                if (K::XPR % NT == 0 || v < K::XPR) xr[j][e] = buf_load16(rx, (2 * q + e) * xs + c * 16);
+        }
+    };
+    auto load_tok = [&](int blk, float& dtv, int& sqv) {
+        dtv = buf_load_f32(rsrc_dt(blk), lane * ds);
+        if (seqg) sqv = buf_load_i32(rsrc_seq(blk), lane * 4);
+    };
+
+    if (nblk > 0) {
+        load_c_bt(0);
+        load_cb(0);
+        load_x(0, xa);
+        load_tok(0, dta, sqa);
+        if (nblk > 1) {
+            load_x(1, xb);
+            load_tok(1, dtb, sqb);
+        }
+    }
+
+    auto body = [&](int blk, uint4 (&xr)[K::XPT][2], float& dtv, int& sqv) {
+        TI* buf = smem + (NBUF == 2 ? (blk & 1) : 0) * K::BUF_ELEMS;
+        TI* sC = buf + K::OFF_C;
+        TI* sBt = buf + K::OFF_BT;
+        TI* sLm = buf + K::OFF_LM;
+        TI* sXt = buf + K::OFF_XT;
+        TI* sXw = buf + K::OFF_XW;
+        const int rows = rows_of(blk);
+        if (NBUF == 1) block_sync_lds();     // single buffer: the previous block is no longer read
+
+        // ---- C and B^T tiles into LDS
+#pragma unroll
+        for (int j = 0; j < K::CPT; ++j) {
+            const int v = tid + j * NT;
+            if (K::CV % NT == 0 || v < K::CV) *(uint4*)(sC + (v / (N / VE)) * LC + (v % (N / VE)) * VE) = cr[j];
+        }
+#pragma unroll
+        for (int j = 0; j < K::BPT; ++j) {
+            const int v = tid + j * NT;
+            if (K::BV % NT == 0 || v < K::BV) *(uint4*)(sBt + (v / (QB / VE)) * LQ + (v % (QB / VE)) * VE) = br[j];
         }
 
-        // ---- per-token scalars (wave 0, lane t = token t of the block):
-        //      cumulative log2 decay, sequence segments
-        if (w == 0) {
-            const int t = lane;
-            const bool valid = t < rows;
-            float dtv = 0.f;
-            int sq = prevseq;
-            if (valid) {
-                dtv = prm.dt[(b * T + t0 + t) * H + h];
-                if (seqg) sq = clamp_seq(seqg[t0 + t]);
-            } else if (seqg && rows > 0) {
-                sq = clamp_seq(seqg[t0 + rows - 1]);
-            }
-            cum_t c = (cum_t)dtv * A2;
+        // ---- per-token scalars, computed by every wave for itself:
+        //      cumulative log2 decay over the block, sequence segments
+        cum_t cum = (cum_t)dtv * A2;                 // dt = 0 past the row's end
 #pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                const cum_t o = __shfl_up(c, d);
-                if (lane >= d) c += o;
-            }
-            const int up = __shfl_up(sq, 1);
-            const int prev = (lane == 0) ? prevseq : up;
-            const bool start = valid && (sq != prev);
-            const uint64_t mask = __ballot(start);
+        for (int d = 1; d < 64; d <<= 1) {
+            const cum_t o = __shfl_up(cum, d);
+            if (lane >= d) cum += o;
+        }
+        int sq = prevseq;
+        if (seqg) {
+            const int raw = clamp_seq(sqv);
+            const int lastv = __shfl(raw, rows - 1);
+            sq = lane < rows ? raw : lastv;          // padding tokens continue the last sequence
+        }
+        const int up = __shfl_up(sq, 1);
+        const int prev = (lane == 0) ? prevseq : up;
+        const bool start = lane < rows && sq != prev;
+        const uint64_t mask = __ballot(start);
+        const int nstart = __popcll(mask);
+        const int lastseq = __shfl(sq, QB - 1);
+        const cum_t cend = __shfl(cum, QB - 1);
+        if (lane < QB) {
+            sCum[w][lane] = cum;
+            sDtf[w][lane] = euler ? dtv : 1.f;
+        }
+        if (nstart > 0) {
             const uint64_t upto = (lane == 63) ? ~0ull : ((2ull << lane) - 1ull);
             const int seg = __popcll(mask & upto);
-            if (t < QB) {
-                sCum[t] = c;
-                sSeg[t] = seg;
-                sDtf[t] = prm.dt_scales_x ? dtv : 1.f;
-            }
+            if (lane < QB) sSeg[w][lane] = seg;
             if (start) {
-                sStart[seg] = t;
-                sSeqOf[seg] = sq;
+                sStart[w][seg] = lane;
+                sSeqOf[w][seg] = sq;
             }
             if (lane == 0) {
-                sStart[0] = 0;
-                sSeqOf[0] = prevseq;
-                sNstart = __popcll(mask);
+                sStart[w][0] = 0;
+                sSeqOf[w][0] = prevseq;
             }
         }
-        __syncthreads();
-
-        const int nstart = sNstart;
-        const int lastseq = sSeqOf[nstart];
-        const cum_t cend = sCum[QB - 1];
-
-        // ---- row scales of the incoming-state read-out: exp(cum_t - cum before t's segment)
-        if (tid < QB) {
-            const int a = sStart[sSeg[tid]];
-            const cum_t before = (a == 0) ? (cum_t)0 : sCum[a - 1];
-            sRow[tid] = fast_exp2((float)(sCum[tid] - before));
+        // dt, seq, C and B^T registers are consumed: fetch ahead
+        if (blk + 2 < nblk) load_tok(blk + 2, dtv, sqv);
+        if (blk + 1 < nblk) load_c_bt(blk + 1);
+        wave_sync();
+        // row scale of the incoming-state read-out: exp(cum_t - cum before t's segment)
+        if (lane < QB) {
+            cum_t before = 0;
+            if (nstart > 0) {
+                const int a = sStart[w][sSeg[w][lane]];
+                if (a > 0) before = sCum[w][a - 1];
+            }
+            sRow[w][lane] = fast_exp2((float)(cum - before));
         }
-        // ---- masked decay times C B^T:  Lm[t][s] = exp(cum_t - cum_s) CB[t][s]  (s <= t, same segment)
-        {
-            const float* cbb = prm.cb + (((b * prm.G + g) * prm.nblk + blk) * QB) * QB;
-            for (int v = tid; v < QB * QB / 4; v += NT) {
-                const int t = v / (QB / 4), s4 = (v % (QB / 4)) * 4;
-                const float4 cv = *(const float4*)(cbb + t * QB + s4);
-                const float cvals[4] = {cv.x, cv.y, cv.z, cv.w};
-                const cum_t ct = sCum[t];
-                const int segt = sSeg[t];
-                TI out[4];
+
+        // ---- masked decay times C B^T:  Lm[t][s] = exp(cum_t - cum_s) CB[t][s] (dt_s)  for s <= t
+        //      in the same segment, else 0 (selected, never multiplied, so nothing leaks)
+#pragma unroll
+        for (int j = 0; j < K::LMPT; ++j) {
+            const int v = tid + j * NT;
+            if (K::LMP % NT == 0 || v < K::LMP) {
+                const int t = v / (QB / 16), s0 = 16 * (v % (QB / 16));
+                const cum_t ct = sCum[w][t];
+                const int segt = nstart > 0 ? sSeg[w][t] : 0;
+                TI out[16];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const int s = s4 + q;
-                    float lv = 0.f;
-                    if (s <= t && sSeg[s] == segt) lv = fast_exp2((float)(ct - sCum[s])) * cvals[q] * sDtf[s];
-                    out[q] = to_in<TI>(lv);
+                    const float4 cbv = __builtin_bit_cast(float4, cbr[j][q]);
+                    const float cb4[4] = {cbv.x, cbv.y, cbv.z, cbv.w};
+                    cum_t c4[4];
+                    if constexpr (sizeof(cum_t) == 4) {
+                        const float4 cc = *(const float4*)(&sCum[w][s0 + 4 * q]);
+                        c4[0] = cc.x; c4[1] = cc.y; c4[2] = cc.z; c4[3] = cc.w;
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) c4[e] = sCum[w][s0 + 4 * q + e];
+                    }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int s = s0 + 4 * q + e;
+                        float lv = fast_exp2((float)(ct - c4[e])) * cb4[e];
+                        if (euler) lv *= sDtf[w][s];
+                        bool keep = s <= t;
+                        if (nstart > 0) keep = keep && sSeg[w][s] == segt;
+                        out[4 * q + e] = to_in<TI>(keep ? lv : 0.f);
+                    }
                 }
-                if constexpr (sizeof(TI) == 2) {
-                    *(bf16x4*)(sLm + t * LQ + s4) = bf16x4{out[0], out[1], out[2], out[3]};
-                } else {
-                    *(float4*)(sLm + t * LQ + s4) = make_float4(out[0], out[1], out[2], out[3]);
+#pragma unroll
+                for (int q = 0; q < 16 / VE; ++q) {
+                    uint4 pk;
+                    __builtin_memcpy(&pk, out + q * VE, 16);
+                    *(uint4*)(sLm + t * LQ + s0 + q * VE) = pk;
                 }
             }
         }
-        // ---- weighted X for the end state: exp(cum_end - cum_s) x_s   (single-segment blocks)
-        if (nstart == 0) {
+        // ---- X^T (raw) and, for single-segment blocks, exp(cum_end - cum_s) x_s (dt_s)
 #pragma unroll
-            for (int j = 0; j < XPT; ++j) {
-                const int v = tid + j * NT;
-                if (v < XV) {
-                    const int t = v / (P / VE), c = v % (P / VE);
-                    const float ws = fast_exp2((float)(cend - sCum[t])) * sDtf[t];
-                    const TI* e = (const TI*)&xr[j];
+        for (int j = 0; j < K::XPT; ++j) {
+            const int v = tid + j * NT;
+            if (K::XPR % NT == 0 || v < K::XPR) {
+                const int q = v / (P / VE), c = v % (P / VE);
+                const TI* e0 = (const TI*)&xr[j][0];
+                const TI* e1 = (const TI*)&xr[j][1];
+                float w0 = 0.f, w1 = 0.f;
+                if (nstart == 0) {
+                    w0 = fast_exp2((float)(cend - sCum[w][2 * q])) * sDtf[w][2 * q];
+                    w1 = fast_exp2((float)(cend - sCum[w][2 * q + 1])) * sDtf[w][2 * q + 1];
+                }
 #pragma unroll
-                    for (int q = 0; q < VE; ++q) sXw[(c * VE + q) * LQ + t] = to_in<TI>(ws * to_f32(e[q]));
+                for (int k = 0; k < VE; ++k) {
+                    const int pr = c * VE + k;
+                    TI two[2] = {e0[k], e1[k]};
+                    TI tw[2] = {to_in<TI>(w0 * to_f32(e0[k])), to_in<TI>(w1 * to_f32(e1[k]))};
+                    if constexpr (sizeof(TI) == 2) {
+                        uint32_t a, bw;
+                        __builtin_memcpy(&a, two, 4);
+                        __builtin_memcpy(&bw, tw, 4);
+                        *(uint32_t*)(sXt + pr * LQ + 2 * q) = a;
+                        if (nstart == 0) *(uint32_t*)(sXw + pr * LQ + 2 * q) = bw;
+                    } else {
+                        *(float2*)(sXt + pr * LQ + 2 * q) = make_float2(two[0], two[1]);
+                        if (nstart == 0) *(float2*)(sXw + pr * LQ + 2 * q) = make_float2(tw[0], tw[1]);
+                    }
                 }
             }
         }
-        __syncthreads();
+        // CB and X registers are consumed: fetch ahead
+        if (blk + 1 < nblk) load_cb(blk + 1);
+        if (blk + 2 < nblk) load_x(blk + 2, xr);
+        block_sync_lds();
 
-        // ---- MFMA phase (wave w: channels p0 .. p0+15)
+        // ---- MFMA phase, outputs transposed: y^T tiles (rows p0..p0+15, columns t)
         frag sf[NK];
         state_frags<N>(st, sf);
         f32x4 acc_y[RT], acc_o[RT];
@@ -453,104 +626,93 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
             acc_y[r] = f32x4{0.f, 0.f, 0.f, 0.f};
             acc_o[r] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        // diagonal block (L o CB) X, causal: row tile r needs s < 16 (r + 1)
+        // diagonal block: (L o CB) X, as X^T (L o CB)^T; token tile r only needs s < 16 (r + 1)
 #pragma unroll
-        for (int r = 0; r < RT; ++r) {
+        for (int r = 0; r < RT; ++r)
 #pragma unroll
-            for (int ks = 0; ks < 16 * (r + 1); ks += KSTEP) {
-                const frag a = lds_frag<TI>(sLm + (16 * r + lr) * LQ + ks + KPL * lg);
-                const frag bb = lds_frag<TI>(sXt + (p0 + lr) * LQ + ks + KPL * lg);
-                acc_y[r] = MF::mma(a, bb, acc_y[r]);
-            }
-        }
+            for (int ks = 0; ks < 16 * (r + 1); ks += KSTEP)
+                acc_y[r] = MF::mma(lds_frag<TI>(sXt + (p0 + lr) * LQ + ks + KPL * lg),
+                                   lds_frag<TI>(sLm + (16 * r + lr) * LQ + ks + KPL * lg), acc_y[r]);
         if (nstart == 0) {
-            // incoming state read out by C
+            // carried state read out by C:  S C^T
 #pragma unroll
             for (int r = 0; r < RT; ++r)
 #pragma unroll
                 for (int k = 0; k < NK; ++k)
-                    acc_o[r] = MF::mma(c_frag(sC + (16 * r + lr) * LC, k, lg), sf[k], acc_o[r]);
-            // carried state decayed over the block plus the block's own end state
+                    acc_o[r] = MF::mma(sf[k], c_frag<N>(sC + (16 * r + lr) * LC, k, lg), acc_o[r]);
+            // state <- exp(cum_end) state + B^T (weighted X)
             const float alpha = fast_exp2((float)cend);
 #pragma unroll
             for (int m = 0; m < MT; ++m) st[m] *= alpha;
 #pragma unroll
             for (int m = 0; m < MT; ++m)
 #pragma unroll
-                for (int ks = 0; ks < QB; ks += KSTEP) {
-                    const frag a = lds_frag<TI>(sBt + (16 * m + lr) * LQ + ks + KPL * lg);
-                    const frag bb = lds_frag<TI>(sXw + (p0 + lr) * LQ + ks + KPL * lg);
-                    st[m] = MF::mma(a, bb, st[m]);
-                }
+                for (int ks = 0; ks < QB; ks += KSTEP)
+                    st[m] = MF::mma(lds_frag<TI>(sBt + nrow<N>(m, lr) * LQ + ks + KPL * lg),
+                                    lds_frag<TI>(sXw + (p0 + lr) * LQ + ks + KPL * lg), st[m]);
 #pragma unroll
-            for (int r = 0; r < RT; ++r)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc_o[r][i] *= sRow[16 * r + 4 * lg + i];
+            for (int r = 0; r < RT; ++r) acc_o[r] *= sRow[w][16 * r + lr];
         } else {
-            // ---- block with sequence starts: one segment at a time
+            // ---- block with sequence starts, one segment at a time
             // (1) read-out of each segment's incoming state
             for (int j = 0; j <= nstart; ++j) {
-                const int a = sStart[j];
-                const int e = (j < nstart) ? sStart[j + 1] - 1 : QB - 1;
+                const int a = sStart[w][j];
+                const int e = (j < nstart) ? sStart[w][j + 1] - 1 : QB - 1;
                 if (e < a) continue;                         // empty first segment
                 frag f[NK];
                 if (j == 0) {
 #pragma unroll
                     for (int k = 0; k < NK; ++k) f[k] = sf[k];
                 } else if (prm.init) {
-                    global_state_frags<N>(prm.init + (((int64_t)sSeqOf[j] * H + h) * P + p0 + lr) * N, lg, f);
+                    global_state_frags<N>(prm.init + (((int64_t)sSeqOf[w][j] * H + h) * P + p0 + lr) * N, lg, f);
                 } else {
-                    continue;                                // zero initial state reads out nothing
+                    continue;                                // a zero initial state reads out nothing
                 }
-                f32x4 tmp[RT];
 #pragma unroll
                 for (int r = 0; r < RT; ++r) {
-                    tmp[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    f32x4 tmp = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int k = 0; k < NK; ++k)
-                        tmp[r] = MF::mma(c_frag(sC + (16 * r + lr) * LC, k, lg), f[k], tmp[r]);
+                    for (int k = 0; k < NK; ++k) tmp = MF::mma(f[k], c_frag<N>(sC + (16 * r + lr) * LC, k, lg), tmp);
+                    const int t = 16 * r + lr;
+                    const float sc = (sSeg[w][t] == j) ? sRow[w][t] : 0.f;
+                    acc_o[r] += sc * tmp;
                 }
-#pragma unroll
-                for (int r = 0; r < RT; ++r)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int t = 16 * r + 4 * lg + i;
-                        if (sSeg[t] == j) acc_o[r][i] += sRow[t] * tmp[r][i];
-                    }
             }
             // (2) state at the end of each segment: a sequence that ends inside
             //     the block hands its state to final_state; the last segment's
-            //     state is carried on.
-            if (sStart[1] == 0) write_state(st, sSeqOf[0]);   // previous sequence ended with the previous block
+            //     state is carried on
+            if (sStart[w][1] == 0) write_state(st, sSeqOf[w][0]);   // previous sequence ended with the previous block
             for (int j = 0; j <= nstart; ++j) {
-                const int a = sStart[j];
-                const int e = (j < nstart) ? sStart[j + 1] - 1 : QB - 1;
+                const int a = sStart[w][j];
+                const int e = (j < nstart) ? sStart[w][j + 1] - 1 : QB - 1;
                 if (e < a) continue;
-                __syncthreads();                             // sXw of the previous segment is consumed
+                block_sync_lds();                             // the previous segment's weighted X is consumed
+                for (int v = tid; v < K::XPR; v += NT) {
+                    const int q = v / (P / VE), c = v % (P / VE);
 #pragma unroll
-                for (int jx = 0; jx < XPT; ++jx) {
-                    const int v = tid + jx * NT;
-                    if (v < XV) {
-                        const int t = v / (P / VE), c = v % (P / VE);
-                        const float ws = (sSeg[t] == j) ? fast_exp2((float)(sCum[e] - sCum[t])) * sDtf[t] : 0.f;
-                        const TI* ev = (const TI*)&xr[jx];
+                    for (int ee = 0; ee < 2; ++ee) {
+                        const int t = 2 * q + ee;
+                        const float ws = (sSeg[w][t] == j) ? fast_exp2((float)(sCum[w][e] - sCum[w][t])) * sDtf[w][t] : 0.f;
 #pragma unroll
-                        for (int q = 0; q < VE; ++q) sXw[(c * VE + q) * LQ + t] = to_in<TI>(ws * to_f32(ev[q]));
+                        for (int k = 0; k < VE; ++k) {
+                            const int pr = c * VE + k;
+                            sXw[pr * LQ + t] = to_in<TI>(ws * to_f32(sXt[pr * LQ + t]));
+                        }
                     }
                 }
-                __syncthreads();
-                const cum_t before = (a == 0) ? (cum_t)0 : sCum[a - 1];
-                const float carry = fast_exp2((float)(sCum[e] - before));
+                block_sync_lds();
+                const cum_t before = (a == 0) ? (cum_t)0 : sCum[w][a - 1];
+                const float carry = fast_exp2((float)(sCum[w][e] - before));
                 f32x4 F[MT];
                 if (j == 0) {
 #pragma unroll
                     for (int m = 0; m < MT; ++m) F[m] = st[m] * carry;
                 } else if (prm.init) {
-                    const float* src = prm.init + (((int64_t)sSeqOf[j] * H + h) * P + p0 + lr) * N;
+                    const float* src = prm.init + (((int64_t)sSeqOf[w][j] * H + h) * P + p0 + lr) * N;
 #pragma unroll
                     for (int m = 0; m < MT; ++m) {
-                        const float4 v = *(const float4*)(src + 16 * m + 4 * lg);
-                        F[m] = f32x4{v.x, v.y, v.z, v.w} * carry;
+                        const float4 iv = *(const float4*)(src + nrow<N>(m, 4 * lg));
+                        F[m] = f32x4{iv.x, iv.y, iv.z, iv.w} * carry;
                     }
                 } else {
 #pragma unroll
@@ -559,34 +721,42 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
 #pragma unroll
                 for (int m = 0; m < MT; ++m)
 #pragma unroll
-                    for (int ks = 0; ks < QB; ks += KSTEP) {
-                        const frag a2 = lds_frag<TI>(sBt + (16 * m + lr) * LQ + ks + KPL * lg);
-                        const frag bb = lds_frag<TI>(sXw + (p0 + lr) * LQ + ks + KPL * lg);
-                        F[m] = MF::mma(a2, bb, F[m]);
-                    }
+                    for (int ks = 0; ks < QB; ks += KSTEP)
+                        F[m] = MF::mma(lds_frag<TI>(sBt + nrow<N>(m, lr) * LQ + ks + KPL * lg),
+                                       lds_frag<TI>(sXw + (p0 + lr) * LQ + ks + KPL * lg), F[m]);
                 if (j < nstart) {
-                    write_state(F, sSeqOf[j]);
+                    write_state(F, sSeqOf[w][j]);
                 } else {
 #pragma unroll
                     for (int m = 0; m < MT; ++m) st[m] = F[m];
                 }
             }
+            // Settle this rare path's own memory traffic here, so that the
+            // common path's wait counts stay exact (prefetches stay in flight).
+            __builtin_amdgcn_s_waitcnt(0);
         }
 
-        // ---- y = read-out + diagonal block + D x, one fp32 write per element
+        // ---- y = read-out + diagonal block + D x: lane holds y[t = 16r + lr][p0 + 4lg .. +3],
+        //      one 16-byte store per token tile (past-the-end tokens are dropped by the range check)
+        const rsrc_t ry = rsrc_y(blk);
 #pragma unroll
-        for (int r = 0; r < RT; ++r)
+        for (int r = 0; r < RT; ++r) {
+            const int t = 16 * r + lr;
+            f32x4 out = acc_o[r] + acc_y[r];
+            if (prm.D) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 16 * r + 4 * lg + i;
-                if (t < rows) {
-                    const float xv = to_f32(sXt[(p0 + lr) * LQ + t]);
-                    prm.y[((b * T + t0 + t) * H + h) * P + p0 + lr] = acc_o[r][i] + acc_y[r][i] + Dh * xv;
-                }
+                for (int i = 0; i < 4; ++i) out[i] += Dh * to_f32(sXt[(p0 + 4 * lg + i) * LQ + t]);
             }
+            buf_store16(out, ry, t * ys + (p0 + 4 * lg) * 4);
+        }
         prevseq = lastseq;
+    };
+
+    for (int blk = 0; blk < nblk; blk += 2) {
+        body(blk, xa, dta, sqa);
+        if (blk + 1 < nblk) body(blk + 1, xb, dtb, sqb);
     }
-    // state after the row's last token belongs to its last sequence
+    // the state after the row's last token belongs to its last sequence
     if (T > 0 || !seqg) write_state(st, prevseq);
 }
 
