@@ -17,7 +17,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libssd_mi355x.so")
-SOURCES = ["ssd_api.cpp", "ssd_bf16.hip", "ssd_f32.hip"]
+SOURCES = ["ssd_api.cpp", "ssd_bf16.hip", "ssd_f32.hip"] + [
+    "ssd_%s_s%d_e%d.hip" % (t, sq, eu) for t in ("bf16", "f32") for sq in (0, 1) for eu in (0, 1)]
 
 
 def hipcc() -> str:
@@ -51,7 +52,7 @@ def _compile(src: str, verbose: bool) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp] + objs

@@ -1,0 +1,51 @@
+"""Write the kernel-instantiation sources (ssd_<dtype>.hip, ssd_<dtype>_s<seq>_e<euler>.hip).
+
+Each file instantiates the scan kernel for one (dtype, sequence ids, Euler scaling)
+combination over the supported (headdim, dstate, block) shapes, so the build compiles
+them in parallel.  Run it after changing the shape lists below; the outputs are
+committed sources.
+"""
+import itertools
+def gen(tag, TI, Ps, Ns, QBs, seq, eul):
+    out = ['// Kernel instantiations: %s inputs, %s sequence ids, %s Euler input scaling.\n#include "ssd_kernels.hpp"\n#include "ssd_launch.hpp"\n\nnamespace ssd {\n' % (tag, "with" if seq else "without", "with" if eul else "without")]
+    fn = "launch_scan_%s_s%d_e%d" % (tag, seq, eul)
+    out.append("hipError_t %s(int P, int N, int QB, const ScanParams& prm, int64_t grid, hipStream_t s) {\n" % fn)
+    for P in Ps:
+        for N in Ns:
+            for Q in QBs:
+                out.append("    if (P == %d && N == %d && QB == %d) { hipLaunchKernelGGL((ssd_scan_kernel<%s, %d, %d, %d, %s, %s>), dim3((unsigned)grid), dim3(%d), 0, s, prm); return hipGetLastError(); }\n" % (P, N, Q, TI, P, N, Q, "true" if seq else "false", "true" if eul else "false", P // 16 * 64))
+    out.append("    return hipErrorInvalidValue;\n}\n}  // namespace ssd\n")
+    return "".join(out)
+
+def gen_common(tag, TI, Ps, Ns, QBs):
+    out = ['// Shape table and prologue-kernel instantiations for %s inputs.\n#include "ssd_kernels.hpp"\n#include "ssd_launch.hpp"\n\nnamespace ssd {\n' % tag]
+    out.append("bool supported_%s(int P, int N, int QB) {\n" % tag)
+    out.append("    const bool p = %s;\n" % " || ".join("P == %d" % v for v in Ps))
+    out.append("    const bool n = %s;\n" % " || ".join("N == %d" % v for v in Ns))
+    out.append("    const bool q = %s;\n" % " || ".join("QB == %d" % v for v in QBs))
+    out.append("    return p && n && q;\n}\n\n")
+    out.append("hipError_t launch_prep_%s(int N, int QB, const PrepParams& prm, int64_t grid, hipStream_t s) {\n" % tag)
+    out.append("    if (grid <= 0) return hipSuccess;\n")
+    for N in Ns:
+        for Q in QBs:
+            out.append("    if (N == %d && QB == %d) { hipLaunchKernelGGL((ssd_prep_kernel<%s, %d, %d>), dim3((unsigned)grid), dim3(256), 0, s, prm); return hipGetLastError(); }\n" % (N, Q, TI, N, Q))
+    out.append("    return hipErrorInvalidValue;\n}\n\n")
+    out.append("hipError_t launch_scan_%s(int P, int N, int QB, bool seq, bool euler, const ScanParams& prm, int64_t grid, hipStream_t s) {\n" % tag)
+    out.append("    if (grid <= 0) return hipSuccess;\n")
+    for sq, eu in itertools.product((0, 1), (0, 1)):
+        out.append("    if (seq == %s && euler == %s) return launch_scan_%s_s%d_e%d(P, N, QB, prm, grid, s);\n" % ("true" if sq else "false", "true" if eu else "false", tag, sq, eu))
+    out.append("    return hipErrorInvalidValue;\n}\n}  // namespace ssd\n")
+    return "".join(out)
+
+import os
+d = os.path.dirname(os.path.abspath(__file__)) + "/"
+cfg = {"bf16": ("__bf16", [32, 64], [64, 128, 256], [32, 64]), "f32": ("float", [16, 32, 64], [16, 32, 64, 128], [32, 64])}
+files = []
+for tag, (TI, Ps, Ns, QBs) in cfg.items():
+    open(d + "ssd_%s.hip" % tag, "w").write(gen_common(tag, TI, Ps, Ns, QBs))
+    files.append("ssd_%s.hip" % tag)
+    for sq, eu in itertools.product((0, 1), (0, 1)):
+        fn = "ssd_%s_s%d_e%d.hip" % (tag, sq, eu)
+        open(d + fn, "w").write(gen(tag, TI, Ps, Ns, QBs, sq, eu))
+        files.append(fn)
+print(files)

@@ -177,9 +177,10 @@ int launch_scan(const ssd_problem_t* p, const void* x, const float* dt, const fl
     const int64_t grid = p->batch * p->nheads;
     if (grid == 0) return SSD_OK;
     if (p->seqlen == 0 && (seq_idx || !fin)) return SSD_OK;   // no token, no sequence to hand out
+    const bool seq = seq_idx != nullptr, euler = prm.dt_scales_x != 0;
     hipError_t e = p->dtype == SSD_DTYPE_BF16
-                       ? ssd::launch_scan_bf16((int)p->headdim, (int)p->dstate, q, prm, grid, stream)
-                       : ssd::launch_scan_f32((int)p->headdim, (int)p->dstate, q, prm, grid, stream);
+                       ? ssd::launch_scan_bf16((int)p->headdim, (int)p->dstate, q, seq, euler, prm, grid, stream)
+                       : ssd::launch_scan_f32((int)p->headdim, (int)p->dstate, q, seq, euler, prm, grid, stream);
     if (log_enabled())
         std::fprintf(stderr, "[ssd] scan dtype=%d P=%lld N=%lld QB=%d grid=%lld block=%lld -> %s\n", p->dtype,
                      (long long)p->headdim, (long long)p->dstate, q, (long long)grid,

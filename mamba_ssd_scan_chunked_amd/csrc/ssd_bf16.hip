@@ -1,4 +1,4 @@
-// Kernel instantiations for bf16 inputs.
+// Shape table and prologue-kernel instantiations for bf16 inputs.
 #include "ssd_kernels.hpp"
 #include "ssd_launch.hpp"
 
@@ -21,20 +21,12 @@ hipError_t launch_prep_bf16(int N, int QB, const PrepParams& prm, int64_t grid, 
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_scan_bf16(int P, int N, int QB, const ScanParams& prm, int64_t grid, hipStream_t s) {
+hipError_t launch_scan_bf16(int P, int N, int QB, bool seq, bool euler, const ScanParams& prm, int64_t grid, hipStream_t s) {
     if (grid <= 0) return hipSuccess;
-    if (P == 32 && N == 64 && QB == 32) { hipLaunchKernelGGL((ssd_scan_kernel<__bf16, 32, 64, 32>), dim3((unsigned)grid), dim3(128), 0, s, prm); return hipGetLastError(); }
-    if (P == 32 && N == 64 && QB == 64) { hipLaunchKernelGGL((ssd_scan_kernel<__bf16, 32, 64, 64>), dim3((unsigned)grid), dim3(128), 0, s, prm); return hipGetLastError(); }
-    if (P == 32 && N == 128 && QB == 32) { hipLaunchKernelGGL((ssd_scan_kernel<__bf16, 32, 128, 32>), dim3((unsigned)grid), dim3(128), 0, s, prm); return hipGetLastError(); }
-    if (P == 32 && N == 128 && QB == 64) { hipLaunchKernelGGL((ssd_scan_kernel<__bf16, 32, 128, 64>), dim3((unsigned)grid), dim3(128), 0, s, prm); return hipGetLastError(); }
-    if (P == 32 && N == 256 && QB == 32) { hipLaunchKernelGGL((ssd_scan_kernel<__bf16, 32, 256, 32>), dim3((unsigned)grid), dim3(128), 0, s, prm); return hipGetLastError(); }
-    if (P == 32 && N == 256 && QB == 64) { hipLaunchKernelGGL((ssd_scan_kernel<__bf16, 32, 256, 64>), dim3((unsigned)grid), dim3(128), 0, s, prm); return hipGetLastError(); }
-    if (P == 64 && N == 64 && QB == 32) { hipLaunchKernelGGL((ssd_scan_kernel<__bf16, 64, 64, 32>), dim3((unsigned)grid), dim3(256), 0, s, prm); return hipGetLastError(); }
-    if (P == 64 && N == 64 && QB == 64) { hipLaunchKernelGGL((ssd_scan_kernel<__bf16, 64, 64, 64>), dim3((unsigned)grid), dim3(256), 0, s, prm); return hipGetLastError(); }
-    if (P == 64 && N == 128 && QB == 32) { hipLaunchKernelGGL((ssd_scan_kernel<__bf16, 64, 128, 32>), dim3((unsigned)grid), dim3(256), 0, s, prm); return hipGetLastError(); }
-    if (P == 64 && N == 128 && QB == 64) { hipLaunchKernelGGL((ssd_scan_kernel<__bf16, 64, 128, 64>), dim3((unsigned)grid), dim3(256), 0, s, prm); return hipGetLastError(); }
-    if (P == 64 && N == 256 && QB == 32) { hipLaunchKernelGGL((ssd_scan_kernel<__bf16, 64, 256, 32>), dim3((unsigned)grid), dim3(256), 0, s, prm); return hipGetLastError(); }
-    if (P == 64 && N == 256 && QB == 64) { hipLaunchKernelGGL((ssd_scan_kernel<__bf16, 64, 256, 64>), dim3((unsigned)grid), dim3(256), 0, s, prm); return hipGetLastError(); }
+    if (seq == false && euler == false) return launch_scan_bf16_s0_e0(P, N, QB, prm, grid, s);
+    if (seq == false && euler == true) return launch_scan_bf16_s0_e1(P, N, QB, prm, grid, s);
+    if (seq == true && euler == false) return launch_scan_bf16_s1_e0(P, N, QB, prm, grid, s);
+    if (seq == true && euler == true) return launch_scan_bf16_s1_e1(P, N, QB, prm, grid, s);
     return hipErrorInvalidValue;
 }
 }  // namespace ssd

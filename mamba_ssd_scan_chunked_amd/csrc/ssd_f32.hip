@@ -1,4 +1,4 @@
-// Kernel instantiations for f32 inputs.
+// Shape table and prologue-kernel instantiations for f32 inputs.
 #include "ssd_kernels.hpp"
 #include "ssd_launch.hpp"
 
@@ -23,32 +23,12 @@ hipError_t launch_prep_f32(int N, int QB, const PrepParams& prm, int64_t grid, h
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_scan_f32(int P, int N, int QB, const ScanParams& prm, int64_t grid, hipStream_t s) {
+hipError_t launch_scan_f32(int P, int N, int QB, bool seq, bool euler, const ScanParams& prm, int64_t grid, hipStream_t s) {
     if (grid <= 0) return hipSuccess;
-    if (P == 16 && N == 16 && QB == 32) { hipLaunchKernelGGL((ssd_scan_kernel<float, 16, 16, 32>), dim3((unsigned)grid), dim3(64), 0, s, prm); return hipGetLastError(); }
-    if (P == 16 && N == 16 && QB == 64) { hipLaunchKernelGGL((ssd_scan_kernel<float, 16, 16, 64>), dim3((unsigned)grid), dim3(64), 0, s, prm); return hipGetLastError(); }
-    if (P == 16 && N == 32 && QB == 32) { hipLaunchKernelGGL((ssd_scan_kernel<float, 16, 32, 32>), dim3((unsigned)grid), dim3(64), 0, s, prm); return hipGetLastError(); }
-    if (P == 16 && N == 32 && QB == 64) { hipLaunchKernelGGL((ssd_scan_kernel<float, 16, 32, 64>), dim3((unsigned)grid), dim3(64), 0, s, prm); return hipGetLastError(); }
-    if (P == 16 && N == 64 && QB == 32) { hipLaunchKernelGGL((ssd_scan_kernel<float, 16, 64, 32>), dim3((unsigned)grid), dim3(64), 0, s, prm); return hipGetLastError(); }
-    if (P == 16 && N == 64 && QB == 64) { hipLaunchKernelGGL((ssd_scan_kernel<float, 16, 64, 64>), dim3((unsigned)grid), dim3(64), 0, s, prm); return hipGetLastError(); }
-    if (P == 16 && N == 128 && QB == 32) { hipLaunchKernelGGL((ssd_scan_kernel<float, 16, 128, 32>), dim3((unsigned)grid), dim3(64), 0, s, prm); return hipGetLastError(); }
-    if (P == 16 && N == 128 && QB == 64) { hipLaunchKernelGGL((ssd_scan_kernel<float, 16, 128, 64>), dim3((unsigned)grid), dim3(64), 0, s, prm); return hipGetLastError(); }
-    if (P == 32 && N == 16 && QB == 32) { hipLaunchKernelGGL((ssd_scan_kernel<float, 32, 16, 32>), dim3((unsigned)grid), dim3(128), 0, s, prm); return hipGetLastError(); }
-    if (P == 32 && N == 16 && QB == 64) { hipLaunchKernelGGL((ssd_scan_kernel<float, 32, 16, 64>), dim3((unsigned)grid), dim3(128), 0, s, prm); return hipGetLastError(); }
-    if (P == 32 && N == 32 && QB == 32) { hipLaunchKernelGGL((ssd_scan_kernel<float, 32, 32, 32>), dim3((unsigned)grid), dim3(128), 0, s, prm); return hipGetLastError(); }
-    if (P == 32 && N == 32 && QB == 64) { hipLaunchKernelGGL((ssd_scan_kernel<float, 32, 32, 64>), dim3((unsigned)grid), dim3(128), 0, s, prm); return hipGetLastError(); }
-    if (P == 32 && N == 64 && QB == 32) { hipLaunchKernelGGL((ssd_scan_kernel<float, 32, 64, 32>), dim3((unsigned)grid), dim3(128), 0, s, prm); return hipGetLastError(); }
-    if (P == 32 && N == 64 && QB == 64) { hipLaunchKernelGGL((ssd_scan_kernel<float, 32, 64, 64>), dim3((unsigned)grid), dim3(128), 0, s, prm); return hipGetLastError(); }
-    if (P == 32 && N == 128 && QB == 32) { hipLaunchKernelGGL((ssd_scan_kernel<float, 32, 128, 32>), dim3((unsigned)grid), dim3(128), 0, s, prm); return hipGetLastError(); }
-    if (P == 32 && N == 128 && QB == 64) { hipLaunchKernelGGL((ssd_scan_kernel<float, 32, 128, 64>), dim3((unsigned)grid), dim3(128), 0, s, prm); return hipGetLastError(); }
-    if (P == 64 && N == 16 && QB == 32) { hipLaunchKernelGGL((ssd_scan_kernel<float, 64, 16, 32>), dim3((unsigned)grid), dim3(256), 0, s, prm); return hipGetLastError(); }
-    if (P == 64 && N == 16 && QB == 64) { hipLaunchKernelGGL((ssd_scan_kernel<float, 64, 16, 64>), dim3((unsigned)grid), dim3(256), 0, s, prm); return hipGetLastError(); }
-    if (P == 64 && N == 32 && QB == 32) { hipLaunchKernelGGL((ssd_scan_kernel<float, 64, 32, 32>), dim3((unsigned)grid), dim3(256), 0, s, prm); return hipGetLastError(); }
-    if (P == 64 && N == 32 && QB == 64) { hipLaunchKernelGGL((ssd_scan_kernel<float, 64, 32, 64>), dim3((unsigned)grid), dim3(256), 0, s, prm); return hipGetLastError(); }
-    if (P == 64 && N == 64 && QB == 32) { hipLaunchKernelGGL((ssd_scan_kernel<float, 64, 64, 32>), dim3((unsigned)grid), dim3(256), 0, s, prm); return hipGetLastError(); }
-    if (P == 64 && N == 64 && QB == 64) { hipLaunchKernelGGL((ssd_scan_kernel<float, 64, 64, 64>), dim3((unsigned)grid), dim3(256), 0, s, prm); return hipGetLastError(); }
-    if (P == 64 && N == 128 && QB == 32) { hipLaunchKernelGGL((ssd_scan_kernel<float, 64, 128, 32>), dim3((unsigned)grid), dim3(256), 0, s, prm); return hipGetLastError(); }
-    if (P == 64 && N == 128 && QB == 64) { hipLaunchKernelGGL((ssd_scan_kernel<float, 64, 128, 64>), dim3((unsigned)grid), dim3(256), 0, s, prm); return hipGetLastError(); }
+    if (seq == false && euler == false) return launch_scan_f32_s0_e0(P, N, QB, prm, grid, s);
+    if (seq == false && euler == true) return launch_scan_f32_s0_e1(P, N, QB, prm, grid, s);
+    if (seq == true && euler == false) return launch_scan_f32_s1_e0(P, N, QB, prm, grid, s);
+    if (seq == true && euler == true) return launch_scan_f32_s1_e1(P, N, QB, prm, grid, s);
     return hipErrorInvalidValue;
 }
 }  // namespace ssd

@@ -177,6 +177,11 @@ __device__ inline uint4 buf_load16(rsrc_t r, int off) {
     const u4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
     return make_uint4(v.x, v.y, v.z, v.w);
 }
+__device__ inline uint2 buf_load8(rsrc_t r, int off) {
+    typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+    const u2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    return make_uint2(v.x, v.y);
+}
 __device__ inline float buf_load_f32(rsrc_t r, int off) {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
@@ -282,6 +287,33 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(PrepParams prm) {
 template <typename TI> struct CumType { typedef float type; };
 template <> struct CumType<float> { typedef double type; };   // fp32 path: exponent differences in fp64
 
+// Inclusive prefix sum over the 64 lanes of a wavefront: Hillis-Steele steps
+// inside each row of 16 lanes (DPP row shifts), then the row totals are
+// broadcast into the following rows.
+template <int CTRL, int RMASK>
+__device__ inline float dpp_add(float x) {
+    const int t = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, RMASK, 0xf, true);
+    return x + __builtin_bit_cast(float, t);
+}
+__device__ inline float wave_incl_scan(float x) {
+    x = dpp_add<0x111, 0xf>(x);   // row_shr:1
+    x = dpp_add<0x112, 0xf>(x);   // row_shr:2
+    x = dpp_add<0x114, 0xf>(x);   // row_shr:4
+    x = dpp_add<0x118, 0xf>(x);   // row_shr:8
+    x = dpp_add<0x142, 0xa>(x);   // row_bcast:15 into rows 1 and 3
+    x = dpp_add<0x143, 0xc>(x);   // row_bcast:31 into rows 2 and 3
+    return x;
+}
+__device__ inline double wave_incl_scan(double x) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const double o = __shfl_up(x, d);
+        if (lane >= d) x += o;
+    }
+    return x;
+}
+
 template <typename TI, int P, int N, int QB>
 struct ScanCfg {
     static constexpr int NW = P / 16;                 // waves; wave w owns channels 16w .. 16w+15
@@ -290,45 +322,56 @@ struct ScanCfg {
     static constexpr int VE = 16 / SZ;                // elements per 16-byte vector
     static constexpr int LC = N + VE;                 // pitch of C rows (elements)
     static constexpr int LQ = QB + VE;                // pitch of rows indexed by token s
+    static constexpr int LR = P + VE;                 // pitch of the row-major copy of X
     static constexpr int KPL = Mfma<TI>::KPL, KSTEP = Mfma<TI>::KSTEP;
     static constexpr int NK = OffK<TI, N>::NK;
     static constexpr int RT = QB / 16;                // token tiles of a block
     static constexpr int MT = N / 16;                 // state tiles per wave
-    // LDS tiles of one buffer: C, B^T, masked decay L o CB, X^T, weighted X^T
+    static constexpr int NTILE = RT * (RT + 1) / 2;   // causal 16x16 tiles of the decay mask
+    // LDS tiles: C, B^T, masked decay L o CB, X^T, weighted X^T, X (row-major)
     static constexpr int OFF_C = 0;
     static constexpr int OFF_BT = OFF_C + QB * LC;
     static constexpr int OFF_LM = OFF_BT + N * LQ;
     static constexpr int OFF_XT = OFF_LM + QB * LQ;
     static constexpr int OFF_XW = OFF_XT + P * LQ;
-    static constexpr int BUF_ELEMS = OFF_XW + P * LQ;
-    static constexpr int BUF_BYTES = BUF_ELEMS * SZ;
-    static constexpr int NBUF = (2 * BUF_BYTES <= 136 * 1024) ? 2 : 1;
-    // per-thread staging
+    static constexpr int OFF_XR = OFF_XW + P * LQ;
+    static constexpr int BUF_ELEMS = OFF_XR + QB * LR;
+    // per-thread work units
     static constexpr int CV = QB * N / VE, CPT = (CV + NT - 1) / NT;           // C tile vectors
     static constexpr int BV = N * QB / VE, BPT = (BV + NT - 1) / NT;           // B^T tile vectors
-    static constexpr int LMP = QB * (QB / 16), LMPT = (LMP + NT - 1) / NT;     // (row, 16 columns) of L o CB
-    static constexpr int XPR = (QB / 2) * (P / VE), XPT = (XPR + NT - 1) / NT;  // (row pair, VE channels) of X
+    static constexpr int LMU = NTILE * 64, LMPT = (LMU + NT - 1) / NT;         // 4-element pieces of L o CB
+    static constexpr int XC = 8 / SZ;                                          // channels per 8 bytes
+    static constexpr int XU = (QB / 4) * (P / XC), XPT = (XU + NT - 1) / NT;   // (4 tokens, XC channels) of X
 };
 
-template <typename TI, int P, int N, int QB>
+template <typename TI, int P, int N, int QB, bool SEQ, bool EULER>
 __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
     typedef ScanCfg<TI, P, N, QB> K;
     typedef Mfma<TI> MF;
     typedef typename MF::frag frag;
     typedef typename CumType<TI>::type cum_t;
-    constexpr int NT = K::NT, VE = K::VE, LC = K::LC, LQ = K::LQ, KPL = K::KPL, KSTEP = K::KSTEP, SZ = K::SZ;
-    constexpr int NK = K::NK, RT = K::RT, MT = K::MT, NBUF = K::NBUF, NW = K::NW;
+    constexpr int NT = K::NT, VE = K::VE, LC = K::LC, LQ = K::LQ, LR = K::LR, KPL = K::KPL, KSTEP = K::KSTEP;
+    constexpr int SZ = K::SZ, NK = K::NK, RT = K::RT, MT = K::MT, NW = K::NW, XC = K::XC;
     static_assert(QB <= 64 && QB % KSTEP == 0 && QB % 16 == 0, "block length");
-    static_assert(N % KSTEP == 0 && N % 16 == 0 && P % 16 == 0, "shape");
+    static_assert(N % KSTEP == 0 && N % 16 == 0 && P % 16 == 0 && P % XC == 0, "shape");
 
-    __shared__ __attribute__((aligned(16))) TI smem[NBUF * K::BUF_ELEMS];
+    __shared__ __attribute__((aligned(16))) TI smem[K::BUF_ELEMS];
     // per-wave copies of the block's per-token scalars (each wave computes its own)
-    __shared__ __attribute__((aligned(16))) cum_t sCum[NW][64];
-    __shared__ __attribute__((aligned(16))) float sRow[NW][64];
-    __shared__ __attribute__((aligned(16))) float sDtf[NW][64];
+    __shared__ __attribute__((aligned(16))) cum_t sCum[NW][64];   // cumulative log2 decay
+    __shared__ __attribute__((aligned(16))) float sRow[NW][64];   // read-out row scale
+    __shared__ __attribute__((aligned(16))) float sV[NW][64];     // exp2(cum at end of the token's 16-tile - cum)
+    __shared__ __attribute__((aligned(16))) float sWx[NW][64];    // end-state weight exp2(cum_end - cum) (dt)
+    __shared__ __attribute__((aligned(16))) float sDtf[NW][64];   // dt (Euler input scaling)
     __shared__ int sSeg[NW][64];
     __shared__ int sStart[NW][65];
     __shared__ int sSeqOf[NW][65];
+
+    TI* sC = smem + K::OFF_C;
+    TI* sBt = smem + K::OFF_BT;
+    TI* sLm = smem + K::OFF_LM;
+    TI* sXt = smem + K::OFF_XT;
+    TI* sXw = smem + K::OFF_XW;
+    TI* sXr = smem + K::OFF_XR;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -351,41 +394,26 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
     if constexpr (sizeof(cum_t) == 8) A2 = -exp((double)prm.A_log[h]) * 1.4426950408889634;
     else A2 = -expf(prm.A_log[h]) * 1.4426950408889634f;
     const float Dh = prm.D ? prm.D[h] : 0.f;
-    const TI* xg = (const TI*)prm.x;
-    const TI* Cg = (const TI*)prm.C;
-    const TI* btg = (const TI*)prm.bt;
-    const int32_t* seqg = prm.seq_idx ? prm.seq_idx + b * T : nullptr;
-    const bool euler = prm.dt_scales_x != 0;
+    const bool hasD = prm.D != nullptr;
+    const int32_t* seqg = SEQ ? prm.seq_idx + b * T : nullptr;
     auto clamp_seq = [&](int s) { return s < 0 ? 0 : (s >= prm.nseqs ? (int)prm.nseqs - 1 : s); };
-    auto rows_of = [&](int blk) { return (int)min((int64_t)QB, T - (int64_t)blk * QB); };
 
     // byte strides between consecutive tokens (the host keeps QB of them below 2^31)
     const int xs = (int)(H * P * SZ), ys = (int)(H * P * 4), cs = (int)(G * N * SZ), ds = (int)(H * 4);
-    // per-block buffer resources: everything past the row's last token reads as zero / is not written
-    auto rsrc_x = [&](int blk) {
-        const int64_t t0 = (int64_t)blk * QB;
-        return make_rsrc(xg + ((b * T + t0) * H + h) * P, ((T - 1 - t0) * H + 1) * P * SZ);
-    };
-    auto rsrc_y = [&](int blk) {
-        const int64_t t0 = (int64_t)blk * QB;
-        return make_rsrc(prm.y + ((b * T + t0) * H + h) * P, ((T - 1 - t0) * H + 1) * P * 4);
-    };
-    auto rsrc_c = [&](int blk) {
-        const int64_t t0 = (int64_t)blk * QB;
-        return make_rsrc(Cg + ((b * T + t0) * G + g) * N, ((T - 1 - t0) * G + 1) * N * SZ);
-    };
-    auto rsrc_dt = [&](int blk) {
-        const int64_t t0 = (int64_t)blk * QB;
-        return make_rsrc(prm.dt + (b * T + t0) * H + h, ((T - 1 - t0) * H + 1) * 4);
-    };
-    auto rsrc_seq = [&](int blk) {
-        const int64_t t0 = (int64_t)blk * QB;
-        return make_rsrc(seqg + t0, (T - t0) * 4);
-    };
+    // row bases; block blk starts QB tokens further, and everything past the
+    // row's last token reads as zero / is not written (buffer range check)
+    const char* xrow = (const char*)prm.x + ((b * T) * H + h) * P * SZ;
+    const char* yrow = (const char*)prm.y + ((b * T) * H + h) * P * 4;
+    const char* crow = (const char*)prm.C + ((b * T) * G + g) * N * SZ;
+    const char* drow = (const char*)prm.dt + ((b * T) * H + h) * 4;
+    const char* btb0 = (const char*)prm.bt + ((b * G + g) * nblk) * (int64_t)N * QB * SZ;
+    const char* cbb0 = (const char*)prm.cb + ((b * G + g) * nblk) * (int64_t)QB * QB * 4;
+    const int64_t xrec = ((T - 1) * H + 1) * P * SZ, yrec = ((T - 1) * H + 1) * P * 4;
+    const int64_t crec = ((T - 1) * G + 1) * N * SZ, drec = ((T - 1) * H + 1) * 4;
 
     // ---- initial state of the row's first sequence (S^T tiles, rows nrow(m, 4*lg+i))
     int prevseq = (int)b;
-    if (seqg && T > 0) prevseq = clamp_seq(seqg[0]);
+    if (SEQ && T > 0) prevseq = clamp_seq(seqg[0]);
     f32x4 st[MT];
     if (prm.init) {
         const float* src = prm.init + (((int64_t)prevseq * H + h) * P + p0 + lr) * N;
@@ -406,18 +434,45 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
             *(float4*)(dst + nrow<N>(m, 4 * lg)) = make_float4(s[m][0], s[m][1], s[m][2], s[m][3]);
     };
 
-    // ---- staging registers.  C, B^T and CB are shared by all heads of the
-    // group and mostly hit L2: fetched one block ahead.  X, dt and seq_idx are
-    // this head's own HBM traffic: fetched two blocks ahead (sets a and b).
-    uint4 cr[K::CPT], br[K::BPT];
-    uint4 cbr[K::LMPT][4];
-    uint4 xa[K::XPT][2], xb[K::XPT][2];
-    float dta = 0.f, dtb = 0.f;
-    int sqa = 0, sqb = 0;
+    // The upper 16x16 tile next to an even diagonal tile is read by a 32-wide
+    // K step of the diagonal product; it is zero and never rewritten.
+    if constexpr (KSTEP > 16) {
+        for (int v = tid; v < (RT / 2) * 16 * 16; v += NT) {
+            const int r = 2 * (v / 256), i = (v / 16) % 16, c = v % 16;
+            sLm[(16 * r + i) * LQ + 16 * (r + 1) + c] = to_in<TI>(0.f);
+        }
+    }
 
-    auto load_c_bt = [&](int blk) {
-        const rsrc_t rc = rsrc_c(blk);
-        const rsrc_t rb = make_rsrc(btg + (((b * G + g) * nblk + blk) * N) * QB, (int64_t)N * QB * SZ);
+    // ---- one block of loads, issued at the top of an iteration and consumed
+    // at its bottom (after the MFMA phase of the previous block), so no load
+    // result lives across the loop back-edge and the wait counts stay exact.
+    uint4 cr[K::CPT], br[K::BPT];
+    float4 cbr[K::LMPT];
+    uint2 xr[K::XPT][4];
+    float dtv = 0.f;
+    int sqv = 0;
+    auto tile_ij = [&](int q, int& I, int& J) {      // causal tile q -> (row tile I, column tile J <= I)
+        I = 0;
+        while ((I + 1) * (I + 2) / 2 <= q) ++I;
+        J = q - I * (I + 1) / 2;
+    };
+    auto issue = [&](int blk) {
+        const int64_t t0 = (int64_t)blk * QB;
+        const rsrc_t rx = make_rsrc(xrow + t0 * xs, xrec - t0 * xs);
+        const rsrc_t rc = make_rsrc(crow + t0 * cs, crec - t0 * cs);
+        const rsrc_t rd = make_rsrc(drow + t0 * ds, drec - t0 * ds);
+        const rsrc_t rb = make_rsrc(btb0 + (int64_t)blk * N * QB * SZ, (int64_t)N * QB * SZ);
+        const rsrc_t rcb = make_rsrc(cbb0 + (int64_t)blk * QB * QB * 4, (int64_t)QB * QB * 4);
+        dtv = buf_load_f32(rd, lane * ds);
+        if constexpr (SEQ) sqv = buf_load_i32(make_rsrc(seqg + t0, (T - t0) * 4), lane * 4);
+#pragma unroll
+        for (int j = 0; j < K::XPT; ++j) {
+            const int v = tid + j * NT;
+            const int q4 = v / (P / XC), c4 = v % (P / XC);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (K::XU % NT == 0 || v < K::XU) xr[j][e] = buf_load8(rx, (4 * q4 + e) * xs + c4 * 8);
+        }
 #pragma unroll
         for (int j = 0; j < K::CPT; ++j) {
             const int v = tid + j * NT;
@@ -428,56 +483,26 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
             const int v = tid + j * NT;
             if (K::BV % NT == 0 || v < K::BV) br[j] = buf_load16(rb, v * 16);
         }
-    };
-    auto load_cb = [&](int blk) {
-        const rsrc_t rcb = make_rsrc(prm.cb + (((b * G + g) * nblk + blk) * QB) * QB, (int64_t)QB * QB * 4);
 #pragma unroll
         for (int j = 0; j < K::LMPT; ++j) {
             const int v = tid + j * NT;
-            const int t = v / (QB / 16), sg = v % (QB / 16);
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                if (K::LMP % NT == 0 || v < K::LMP) cbr[j][q] = buf_load16(rcb, (t * QB + 16 * sg + 4 * q) * 4);
+            if (K::LMU % NT == 0 || v < K::LMU) {
+                int I, J;
+                tile_ij(v / 64, I, J);
+                const int t = 16 * I + (v % 64) / 4, s0 = 16 * J + 4 * (v % 4);
+                cbr[j] = __builtin_bit_cast(float4, buf_load16(rcb, (t * QB + s0) * 4));
+            }
         }
     };
-    auto load_x = [&](int blk, uint4 (&xr)[K::XPT][2]) {
-        const rsrc_t rx = rsrc_x(blk);
-#pragma unroll
-        for (int j = 0; j < K::XPT; ++j) {
-            const int v = tid + j * NT;
-            const int q = v / (P / VE), c = v % (P / VE);
-#pragma unroll
-            for (int e = 0; e < 2; ++e)
-                if (K::XPR % NT == 0 || v < K::XPR) xr[j][e] = buf_load16(rx, (2 * q + e) * xs + c * 16);
-        }
-    };
-    auto load_tok = [&](int blk, float& dtv, int& sqv) {
-        dtv = buf_load_f32(rsrc_dt(blk), lane * ds);
-        if (seqg) sqv = buf_load_i32(rsrc_seq(blk), lane * 4);
-    };
 
-    if (nblk > 0) {
-        load_c_bt(0);
-        load_cb(0);
-        load_x(0, xa);
-        load_tok(0, dta, sqa);
-        if (nblk > 1) {
-            load_x(1, xb);
-            load_tok(1, dtb, sqb);
-        }
-    }
+    // per-block values handed from the preparation of a block to its MFMA phase
+    int nstart_c = 0, lastseq_c = prevseq;
+    float cend_f = 0.f;
 
-    auto body = [&](int blk, uint4 (&xr)[K::XPT][2], float& dtv, int& sqv) {
-        TI* buf = smem + (NBUF == 2 ? (blk & 1) : 0) * K::BUF_ELEMS;
-        TI* sC = buf + K::OFF_C;
-        TI* sBt = buf + K::OFF_BT;
-        TI* sLm = buf + K::OFF_LM;
-        TI* sXt = buf + K::OFF_XT;
-        TI* sXw = buf + K::OFF_XW;
-        const int rows = rows_of(blk);
-        if (NBUF == 1) block_sync_lds();     // single buffer: the previous block is no longer read
-
-        // ---- C and B^T tiles into LDS
+    // ---- preparation of a block from the issued loads: tiles into LDS, the
+    //      within-block cumulative decay, segments, L o CB, X^T and weighted X^T
+    auto prep = [&](int blk) {
+        const int rows = (int)min((int64_t)QB, T - (int64_t)blk * QB);
 #pragma unroll
         for (int j = 0; j < K::CPT; ++j) {
             const int v = tid + j * NT;
@@ -488,135 +513,145 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
             const int v = tid + j * NT;
             if (K::BV % NT == 0 || v < K::BV) *(uint4*)(sBt + (v / (QB / VE)) * LQ + (v % (QB / VE)) * VE) = br[j];
         }
-
-        // ---- per-token scalars, computed by every wave for itself:
-        //      cumulative log2 decay over the block, sequence segments
-        cum_t cum = (cum_t)dtv * A2;                 // dt = 0 past the row's end
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const cum_t o = __shfl_up(cum, d);
-            if (lane >= d) cum += o;
-        }
-        int sq = prevseq;
-        if (seqg) {
+        // per-token scalars, computed by every wave for itself (lane = token)
+        const cum_t cum = wave_incl_scan((cum_t)dtv * A2);        // dt = 0 past the row's end
+        const cum_t cend = __shfl(cum, QB - 1);
+        const cum_t c16 = __shfl(cum, lane | 15);                // cum at the end of this token's 16-tile
+        int nstart = 0;
+        int segl = 0;
+        cum_t before = 0;
+        if constexpr (SEQ) {
             const int raw = clamp_seq(sqv);
             const int lastv = __shfl(raw, rows - 1);
-            sq = lane < rows ? raw : lastv;          // padding tokens continue the last sequence
+            const int sq = lane < rows ? raw : lastv;            // padding tokens continue the last sequence
+            const int up = __shfl_up(sq, 1);
+            const int prev = (lane == 0) ? prevseq : up;
+            const bool start = lane < rows && sq != prev;
+            const uint64_t mask = __ballot(start);
+            nstart = __popcll(mask);
+            lastseq_c = __shfl(sq, QB - 1);
+            if (nstart > 0) {
+                const uint64_t upto = (lane == 63) ? ~0ull : ((2ull << lane) - 1ull);
+                segl = __popcll(mask & upto);
+                if (lane < QB) sSeg[w][lane] = segl;
+                if (start) {
+                    sStart[w][segl] = lane;
+                    sSeqOf[w][segl] = sq;
+                }
+                if (lane == 0) {
+                    sStart[w][0] = 0;
+                    sSeqOf[w][0] = prevseq;
+                }
+            }
         }
-        const int up = __shfl_up(sq, 1);
-        const int prev = (lane == 0) ? prevseq : up;
-        const bool start = lane < rows && sq != prev;
-        const uint64_t mask = __ballot(start);
-        const int nstart = __popcll(mask);
-        const int lastseq = __shfl(sq, QB - 1);
-        const cum_t cend = __shfl(cum, QB - 1);
+        nstart_c = nstart;
+        cend_f = (float)cend;
+        const float dtf = EULER ? dtv : 1.f;
         if (lane < QB) {
             sCum[w][lane] = cum;
-            sDtf[w][lane] = euler ? dtv : 1.f;
+            sV[w][lane] = fast_exp2((float)(c16 - cum));
+            sWx[w][lane] = fast_exp2((float)(cend - cum)) * dtf;
+            if constexpr (EULER) sDtf[w][lane] = dtv;
         }
-        if (nstart > 0) {
-            const uint64_t upto = (lane == 63) ? ~0ull : ((2ull << lane) - 1ull);
-            const int seg = __popcll(mask & upto);
-            if (lane < QB) sSeg[w][lane] = seg;
-            if (start) {
-                sStart[w][seg] = lane;
-                sSeqOf[w][seg] = sq;
-            }
-            if (lane == 0) {
-                sStart[w][0] = 0;
-                sSeqOf[w][0] = prevseq;
-            }
-        }
-        // dt, seq, C and B^T registers are consumed: fetch ahead
-        if (blk + 2 < nblk) load_tok(blk + 2, dtv, sqv);
-        if (blk + 1 < nblk) load_c_bt(blk + 1);
         wave_sync();
-        // row scale of the incoming-state read-out: exp(cum_t - cum before t's segment)
-        if (lane < QB) {
-            cum_t before = 0;
+        if constexpr (SEQ) {
             if (nstart > 0) {
-                const int a = sStart[w][sSeg[w][lane]];
+                const int a = sStart[w][segl];
                 if (a > 0) before = sCum[w][a - 1];
             }
-            sRow[w][lane] = fast_exp2((float)(cum - before));
         }
+        if (lane < QB) sRow[w][lane] = fast_exp2((float)(cum - before));
 
-        // ---- masked decay times C B^T:  Lm[t][s] = exp(cum_t - cum_s) CB[t][s] (dt_s)  for s <= t
-        //      in the same segment, else 0 (selected, never multiplied, so nothing leaks)
+        // masked decay times C B^T over the causal tiles, 4 consecutive tokens s per piece:
+        //   diagonal tile:  exp2(cum_t - cum_s) CB[t][s] for s <= t, else 0
+        //   below it:       exp2(cum_t - cum_r) exp2(cum_r - cum_s) CB[t][s], r = last token of s's tile
+        // (times dt_s with Euler input scaling; zero across sequence segments)
 #pragma unroll
         for (int j = 0; j < K::LMPT; ++j) {
             const int v = tid + j * NT;
-            if (K::LMP % NT == 0 || v < K::LMP) {
-                const int t = v / (QB / 16), s0 = 16 * (v % (QB / 16));
+            if (K::LMU % NT == 0 || v < K::LMU) {
+                int I, J;
+                tile_ij(v / 64, I, J);                           // uniform over the wave
+                const int t = 16 * I + (v % 64) / 4, s0 = 16 * J + 4 * (v % 4);
+                const float cb4[4] = {cbr[j].x, cbr[j].y, cbr[j].z, cbr[j].w};
                 const cum_t ct = sCum[w][t];
-                const int segt = nstart > 0 ? sSeg[w][t] : 0;
-                TI out[16];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float4 cbv = __builtin_bit_cast(float4, cbr[j][q]);
-                    const float cb4[4] = {cbv.x, cbv.y, cbv.z, cbv.w};
+                float val[4];
+                if (I == J) {
                     cum_t c4[4];
                     if constexpr (sizeof(cum_t) == 4) {
-                        const float4 cc = *(const float4*)(&sCum[w][s0 + 4 * q]);
+                        const float4 cc = *(const float4*)(&sCum[w][s0]);
                         c4[0] = cc.x; c4[1] = cc.y; c4[2] = cc.z; c4[3] = cc.w;
                     } else {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) c4[e] = sCum[w][s0 + 4 * q + e];
+                        for (int e = 0; e < 4; ++e) c4[e] = sCum[w][s0 + e];
                     }
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const int s = s0 + 4 * q + e;
-                        float lv = fast_exp2((float)(ct - c4[e])) * cb4[e];
-                        if (euler) lv *= sDtf[w][s];
-                        bool keep = s <= t;
-                        if (nstart > 0) keep = keep && sSeg[w][s] == segt;
-                        out[4 * q + e] = to_in<TI>(keep ? lv : 0.f);
+                        const float lv = fast_exp2((float)(ct - c4[e])) * cb4[e];
+                        val[e] = (s0 + e <= t) ? lv : 0.f;
+                    }
+                } else {
+                    const float ut = fast_exp2((float)(ct - sCum[w][16 * J + 15]));
+                    const float4 v4 = *(const float4*)(&sV[w][s0]);
+                    val[0] = ut * v4.x * cb4[0];
+                    val[1] = ut * v4.y * cb4[1];
+                    val[2] = ut * v4.z * cb4[2];
+                    val[3] = ut * v4.w * cb4[3];
+                }
+                if constexpr (EULER) {
+                    const float4 d4 = *(const float4*)(&sDtf[w][s0]);
+                    val[0] *= d4.x; val[1] *= d4.y; val[2] *= d4.z; val[3] *= d4.w;
+                }
+                if constexpr (SEQ) {
+                    if (nstart > 0) {
+                        const int segt = sSeg[w][t];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (sSeg[w][s0 + e] != segt) val[e] = 0.f;
                     }
                 }
-#pragma unroll
-                for (int q = 0; q < 16 / VE; ++q) {
-                    uint4 pk;
-                    __builtin_memcpy(&pk, out + q * VE, 16);
-                    *(uint4*)(sLm + t * LQ + s0 + q * VE) = pk;
+                if constexpr (sizeof(TI) == 2) {
+                    *(bf16x4*)(sLm + t * LQ + s0) = bf16x4{(__bf16)val[0], (__bf16)val[1], (__bf16)val[2], (__bf16)val[3]};
+                } else {
+                    *(float4*)(sLm + t * LQ + s0) = make_float4(val[0], val[1], val[2], val[3]);
                 }
             }
         }
-        // ---- X^T (raw) and, for single-segment blocks, exp(cum_end - cum_s) x_s (dt_s)
+        // X^T (raw), X (row-major, for the skip term) and, for single-segment
+        // blocks, the end-state weighted X^T
 #pragma unroll
         for (int j = 0; j < K::XPT; ++j) {
             const int v = tid + j * NT;
-            if (K::XPR % NT == 0 || v < K::XPR) {
-                const int q = v / (P / VE), c = v % (P / VE);
-                const TI* e0 = (const TI*)&xr[j][0];
-                const TI* e1 = (const TI*)&xr[j][1];
-                float w0 = 0.f, w1 = 0.f;
-                if (nstart == 0) {
-                    w0 = fast_exp2((float)(cend - sCum[w][2 * q])) * sDtf[w][2 * q];
-                    w1 = fast_exp2((float)(cend - sCum[w][2 * q + 1])) * sDtf[w][2 * q + 1];
-                }
+            if (K::XU % NT == 0 || v < K::XU) {
+                const int q4 = v / (P / XC), c4 = v % (P / XC);
+                const int t0l = 4 * q4;
 #pragma unroll
-                for (int k = 0; k < VE; ++k) {
-                    const int pr = c * VE + k;
-                    TI two[2] = {e0[k], e1[k]};
-                    TI tw[2] = {to_in<TI>(w0 * to_f32(e0[k])), to_in<TI>(w1 * to_f32(e1[k]))};
+                for (int e = 0; e < 4; ++e) *(uint2*)(sXr + (t0l + e) * LR + c4 * XC) = xr[j][e];
+                const float4 w4 = *(const float4*)(&sWx[w][t0l]);
+                const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+                for (int k = 0; k < XC; ++k) {
+                    const int pr = c4 * XC + k;
+                    TI col[4], colw[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        col[e] = ((const TI*)&xr[j][e])[k];
+                        colw[e] = to_in<TI>(wv[e] * to_f32(col[e]));
+                    }
                     if constexpr (sizeof(TI) == 2) {
-                        uint32_t a, bw;
-                        __builtin_memcpy(&a, two, 4);
-                        __builtin_memcpy(&bw, tw, 4);
-                        *(uint32_t*)(sXt + pr * LQ + 2 * q) = a;
-                        if (nstart == 0) *(uint32_t*)(sXw + pr * LQ + 2 * q) = bw;
+                        *(bf16x4*)(sXt + pr * LQ + t0l) = bf16x4{col[0], col[1], col[2], col[3]};
+                        if (!SEQ || nstart == 0) *(bf16x4*)(sXw + pr * LQ + t0l) = bf16x4{colw[0], colw[1], colw[2], colw[3]};
                     } else {
-                        *(float2*)(sXt + pr * LQ + 2 * q) = make_float2(two[0], two[1]);
-                        if (nstart == 0) *(float2*)(sXw + pr * LQ + 2 * q) = make_float2(tw[0], tw[1]);
+                        *(float4*)(sXt + pr * LQ + t0l) = make_float4(col[0], col[1], col[2], col[3]);
+                        if (!SEQ || nstart == 0) *(float4*)(sXw + pr * LQ + t0l) = make_float4(colw[0], colw[1], colw[2], colw[3]);
                     }
                 }
             }
         }
-        // CB and X registers are consumed: fetch ahead
-        if (blk + 1 < nblk) load_cb(blk + 1);
-        if (blk + 2 < nblk) load_x(blk + 2, xr);
-        block_sync_lds();
+    };
 
+    auto mfma_phase = [&](int blk) {
+        const int nstart = nstart_c;
         // ---- MFMA phase, outputs transposed: y^T tiles (rows p0..p0+15, columns t)
         frag sf[NK];
         state_frags<N>(st, sf);
@@ -633,7 +668,7 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
             for (int ks = 0; ks < 16 * (r + 1); ks += KSTEP)
                 acc_y[r] = MF::mma(lds_frag<TI>(sXt + (p0 + lr) * LQ + ks + KPL * lg),
                                    lds_frag<TI>(sLm + (16 * r + lr) * LQ + ks + KPL * lg), acc_y[r]);
-        if (nstart == 0) {
+        if (!SEQ || nstart == 0) {
             // carried state read out by C:  S C^T
 #pragma unroll
             for (int r = 0; r < RT; ++r)
@@ -641,7 +676,7 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
                 for (int k = 0; k < NK; ++k)
                     acc_o[r] = MF::mma(sf[k], c_frag<N>(sC + (16 * r + lr) * LC, k, lg), acc_o[r]);
             // state <- exp(cum_end) state + B^T (weighted X)
-            const float alpha = fast_exp2((float)cend);
+            const float alpha = fast_exp2(cend_f);
 #pragma unroll
             for (int m = 0; m < MT; ++m) st[m] *= alpha;
 #pragma unroll
@@ -652,7 +687,7 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
                                     lds_frag<TI>(sXw + (p0 + lr) * LQ + ks + KPL * lg), st[m]);
 #pragma unroll
             for (int r = 0; r < RT; ++r) acc_o[r] *= sRow[w][16 * r + lr];
-        } else {
+        } else if constexpr (SEQ) {
             // ---- block with sequence starts, one segment at a time
             // (1) read-out of each segment's incoming state
             for (int j = 0; j <= nstart; ++j) {
@@ -687,18 +722,11 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
                 const int e = (j < nstart) ? sStart[w][j + 1] - 1 : QB - 1;
                 if (e < a) continue;
                 block_sync_lds();                             // the previous segment's weighted X is consumed
-                for (int v = tid; v < K::XPR; v += NT) {
-                    const int q = v / (P / VE), c = v % (P / VE);
-#pragma unroll
-                    for (int ee = 0; ee < 2; ++ee) {
-                        const int t = 2 * q + ee;
-                        const float ws = (sSeg[w][t] == j) ? fast_exp2((float)(sCum[w][e] - sCum[w][t])) * sDtf[w][t] : 0.f;
-#pragma unroll
-                        for (int k = 0; k < VE; ++k) {
-                            const int pr = c * VE + k;
-                            sXw[pr * LQ + t] = to_in<TI>(ws * to_f32(sXt[pr * LQ + t]));
-                        }
-                    }
+                for (int v = tid; v < P * QB; v += NT) {
+                    const int t = v % QB, pr = v / QB;
+                    const float ws = (sSeg[w][t] == j)
+                        ? fast_exp2((float)(sCum[w][e] - sCum[w][t])) * (EULER ? sDtf[w][t] : 1.f) : 0.f;
+                    sXw[pr * LQ + t] = to_in<TI>(ws * to_f32(sXt[pr * LQ + t]));
                 }
                 block_sync_lds();
                 const cum_t before = (a == 0) ? (cum_t)0 : sCum[w][a - 1];
@@ -738,26 +766,49 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
 
         // ---- y = read-out + diagonal block + D x: lane holds y[t = 16r + lr][p0 + 4lg .. +3],
         //      one 16-byte store per token tile (past-the-end tokens are dropped by the range check)
-        const rsrc_t ry = rsrc_y(blk);
+        const int64_t t0 = (int64_t)blk * QB;
+        const rsrc_t ry = make_rsrc(yrow + t0 * ys, yrec - t0 * ys);
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
             const int t = 16 * r + lr;
             f32x4 out = acc_o[r] + acc_y[r];
-            if (prm.D) {
+            if (hasD) {
+                float xv[4];
+                if constexpr (sizeof(TI) == 2) {
+                    const bf16x4 x4 = *(const bf16x4*)(sXr + t * LR + p0 + 4 * lg);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) out[i] += Dh * to_f32(sXt[(p0 + 4 * lg + i) * LQ + t]);
+                    for (int i = 0; i < 4; ++i) xv[i] = (float)x4[i];
+                } else {
+                    const float4 x4 = *(const float4*)(sXr + t * LR + p0 + 4 * lg);
+                    xv[0] = x4.x; xv[1] = x4.y; xv[2] = x4.z; xv[3] = x4.w;
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) out[i] += Dh * xv[i];
             }
             buf_store16(out, ry, t * ys + (p0 + 4 * lg) * 4);
         }
-        prevseq = lastseq;
+        if constexpr (SEQ) prevseq = lastseq_c;
     };
 
-    for (int blk = 0; blk < nblk; blk += 2) {
-        body(blk, xa, dta, sqa);
-        if (blk + 1 < nblk) body(blk + 1, xb, dtb, sqb);
+    if (nblk > 0) {
+        issue(0);
+        prep(0);
+        block_sync_lds();
+    }
+    // The initial state (loaded at entry) is carried through the loop; settle
+    // its loads here so the loop header does not wait on memory each iteration.
+    __builtin_amdgcn_s_waitcnt(0);
+    for (int blk = 0; blk < nblk; ++blk) {
+        if (blk + 1 < nblk) issue(blk + 1);
+        mfma_phase(blk);
+        if (blk + 1 < nblk) {
+            block_sync_lds();        // block blk's tiles are no longer read
+            prep(blk + 1);
+            block_sync_lds();        // block blk+1's tiles are complete
+        }
     }
     // the state after the row's last token belongs to its last sequence
-    if (T > 0 || !seqg) write_state(st, prevseq);
+    if (T > 0 || !SEQ) write_state(st, prevseq);
 }
 
 }  // namespace ssd
