@@ -147,6 +147,24 @@ __device__ inline bf16x8 c_frag(const __bf16* row, int k, int lg) { return *(con
 template <int N>
 __device__ inline float c_frag(const float* row, int k, int lg) { return row[nrow<N>(k >> 2, 4 * lg + (k & 3))]; }
 
+// Operand fragment of X^T (row = channel p0 + l%16, K = tokens ks + KPL*(l/16) ..)
+// read from a row-major tile sX[t][p] (pitch lp elements).  bf16: the LDS
+// transpose read; within each group of 16 lanes, lane j reads 4 channels
+// p0 + 4(j%4) .. of token row R + j/4, and the hardware hands lane i channel
+// p0 + i of rows R .. R+3; two reads give the 8 tokens of one K step.
+// fp32: one value per lane, no transpose needed.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ inline bf16x8 x_frag(const __bf16* sX, int lp, int ks, int p0, int lr, int lg) {
+    const __bf16* a = sX + (ks + 8 * lg + (lr >> 2)) * lp + p0 + 4 * (lr & 3);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)a);
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(a + 4 * lp));
+    const bf16x4 l4 = __builtin_bit_cast(bf16x4, lo), h4 = __builtin_bit_cast(bf16x4, hi);
+    return __builtin_shufflevector(l4, h4, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ inline float x_frag(const float* sX, int lp, int ks, int p0, int lr, int lg) {
+    return sX[(ks + lg) * lp + p0 + lr];
+}
+
 // Make this wave's LDS writes visible to its own other lanes.
 __device__ inline void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
@@ -322,26 +340,32 @@ struct ScanCfg {
     static constexpr int VE = 16 / SZ;                // elements per 16-byte vector
     static constexpr int LC = N + VE;                 // pitch of C rows (elements)
     static constexpr int LQ = QB + VE;                // pitch of rows indexed by token s
-    static constexpr int LR = P + VE;                 // pitch of the row-major copy of X
+    static constexpr int LR = P + 32 / SZ;            // pitch of the row-major X tiles (32 bytes of pad:
+                                                      // the four rows of a transposed read fall in
+                                                      // distinct banks)
     static constexpr int KPL = Mfma<TI>::KPL, KSTEP = Mfma<TI>::KSTEP;
     static constexpr int NK = OffK<TI, N>::NK;
     static constexpr int RT = QB / 16;                // token tiles of a block
     static constexpr int MT = N / 16;                 // state tiles per wave
     static constexpr int NTILE = RT * (RT + 1) / 2;   // causal 16x16 tiles of the decay mask
-    // LDS tiles: C, B^T, masked decay L o CB, X^T, weighted X^T, X (row-major)
+    // LDS tiles: C, B^T, masked decay L o CB, X and end-state-weighted X (both row-major)
     static constexpr int OFF_C = 0;
     static constexpr int OFF_BT = OFF_C + QB * LC;
     static constexpr int OFF_LM = OFF_BT + N * LQ;
-    static constexpr int OFF_XT = OFF_LM + QB * LQ;
-    static constexpr int OFF_XW = OFF_XT + P * LQ;
-    static constexpr int OFF_XR = OFF_XW + P * LQ;
-    static constexpr int BUF_ELEMS = OFF_XR + QB * LR;
+    static constexpr int OFF_XR = OFF_LM + QB * LQ;
+    static constexpr int OFF_XW = OFF_XR + QB * LR;
+    static constexpr int BUF_ELEMS = OFF_XW + QB * LR;
     // per-thread work units
     static constexpr int CV = QB * N / VE, CPT = (CV + NT - 1) / NT;           // C tile vectors
     static constexpr int BV = N * QB / VE, BPT = (BV + NT - 1) / NT;           // B^T tile vectors
     static constexpr int LMU = NTILE * 64, LMPT = (LMU + NT - 1) / NT;         // 4-element pieces of L o CB
     static constexpr int XC = 8 / SZ;                                          // channels per 8 bytes
     static constexpr int XU = (QB / 4) * (P / XC), XPT = (XU + NT - 1) / NT;   // (4 tokens, XC channels) of X
+    // B^T rows n and n + 8 would share LDS banks in the permuted-row reads of
+    // the state update; for bf16 64-token blocks the two 64-byte halves of
+    // every row with bit 3 of n set are swapped (XOR swizzle, element offset).
+    static constexpr bool BT_SWZ = (SZ == 2 && QB == 64);
+    __device__ static inline int bt_col(int n, int col) { return BT_SWZ ? (col ^ (((n >> 3) & 1) * 32)) : col; }
 };
 
 template <typename TI, int P, int N, int QB, bool SEQ, bool EULER>
@@ -369,9 +393,8 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
     TI* sC = smem + K::OFF_C;
     TI* sBt = smem + K::OFF_BT;
     TI* sLm = smem + K::OFF_LM;
-    TI* sXt = smem + K::OFF_XT;
-    TI* sXw = smem + K::OFF_XW;
     TI* sXr = smem + K::OFF_XR;
+    TI* sXw = smem + K::OFF_XW;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -394,7 +417,6 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
     if constexpr (sizeof(cum_t) == 8) A2 = -exp((double)prm.A_log[h]) * 1.4426950408889634;
     else A2 = -expf(prm.A_log[h]) * 1.4426950408889634f;
     const float Dh = prm.D ? prm.D[h] : 0.f;
-    const bool hasD = prm.D != nullptr;
     const int32_t* seqg = SEQ ? prm.seq_idx + b * T : nullptr;
     auto clamp_seq = [&](int s) { return s < 0 ? 0 : (s >= prm.nseqs ? (int)prm.nseqs - 1 : s); };
 
@@ -451,11 +473,17 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
     uint2 xr[K::XPT][4];
     float dtv = 0.f;
     int sqv = 0;
-    auto tile_ij = [&](int q, int& I, int& J) {      // causal tile q -> (row tile I, column tile J <= I)
-        I = 0;
+    // Causal tile of each of this thread's L o CB pieces (row tile I, column tile
+    // J <= I); the tile index v / 64 is uniform over the wave.
+    int tI[K::LMPT], tJ[K::LMPT];
+#pragma unroll
+    for (int j = 0; j < K::LMPT; ++j) {
+        const int q = (tid + j * NT) / 64;
+        int I = 0;
         while ((I + 1) * (I + 2) / 2 <= q) ++I;
-        J = q - I * (I + 1) / 2;
-    };
+        tI[j] = I;
+        tJ[j] = q - I * (I + 1) / 2;
+    }
     auto issue = [&](int blk) {
         const int64_t t0 = (int64_t)blk * QB;
         const rsrc_t rx = make_rsrc(xrow + t0 * xs, xrec - t0 * xs);
@@ -487,9 +515,7 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
         for (int j = 0; j < K::LMPT; ++j) {
             const int v = tid + j * NT;
             if (K::LMU % NT == 0 || v < K::LMU) {
-                int I, J;
-                tile_ij(v / 64, I, J);
-                const int t = 16 * I + (v % 64) / 4, s0 = 16 * J + 4 * (v % 4);
+                const int t = 16 * tI[j] + (v % 64) / 4, s0 = 16 * tJ[j] + 4 * (v % 4);
                 cbr[j] = __builtin_bit_cast(float4, buf_load16(rcb, (t * QB + s0) * 4));
             }
         }
@@ -511,7 +537,7 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
 #pragma unroll
         for (int j = 0; j < K::BPT; ++j) {
             const int v = tid + j * NT;
-            if (K::BV % NT == 0 || v < K::BV) *(uint4*)(sBt + (v / (QB / VE)) * LQ + (v % (QB / VE)) * VE) = br[j];
+            if (K::BV % NT == 0 || v < K::BV) *(uint4*)(sBt + (v / (QB / VE)) * LQ + K::bt_col(v / (QB / VE), (v % (QB / VE)) * VE)) = br[j];
         }
         // per-token scalars, computed by every wave for itself (lane = token)
         const cum_t cum = wave_incl_scan((cum_t)dtv * A2);        // dt = 0 past the row's end
@@ -570,8 +596,7 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
         for (int j = 0; j < K::LMPT; ++j) {
             const int v = tid + j * NT;
             if (K::LMU % NT == 0 || v < K::LMU) {
-                int I, J;
-                tile_ij(v / 64, I, J);                           // uniform over the wave
+                const int I = tI[j], J = tJ[j];                 // uniform over the wave
                 const int t = 16 * I + (v % 64) / 4, s0 = 16 * J + 4 * (v % 4);
                 const float cb4[4] = {cbr[j].x, cbr[j].y, cbr[j].z, cbr[j].w};
                 const cum_t ct = sCum[w][t];
@@ -617,33 +642,25 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
                 }
             }
         }
-        // X^T (raw), X (row-major, for the skip term) and, for single-segment
-        // blocks, the end-state weighted X^T
+        // X (row-major) and, for single-segment blocks, the end-state weighted X
 #pragma unroll
         for (int j = 0; j < K::XPT; ++j) {
             const int v = tid + j * NT;
             if (K::XU % NT == 0 || v < K::XU) {
                 const int q4 = v / (P / XC), c4 = v % (P / XC);
                 const int t0l = 4 * q4;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) *(uint2*)(sXr + (t0l + e) * LR + c4 * XC) = xr[j][e];
                 const float4 w4 = *(const float4*)(&sWx[w][t0l]);
                 const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
 #pragma unroll
-                for (int k = 0; k < XC; ++k) {
-                    const int pr = c4 * XC + k;
-                    TI col[4], colw[4];
+                for (int e = 0; e < 4; ++e) {
+                    *(uint2*)(sXr + (t0l + e) * LR + c4 * XC) = xr[j][e];
+                    if (!SEQ || nstart == 0) {
+                        TI wx[XC];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        col[e] = ((const TI*)&xr[j][e])[k];
-                        colw[e] = to_in<TI>(wv[e] * to_f32(col[e]));
-                    }
-                    if constexpr (sizeof(TI) == 2) {
-                        *(bf16x4*)(sXt + pr * LQ + t0l) = bf16x4{col[0], col[1], col[2], col[3]};
-                        if (!SEQ || nstart == 0) *(bf16x4*)(sXw + pr * LQ + t0l) = bf16x4{colw[0], colw[1], colw[2], colw[3]};
-                    } else {
-                        *(float4*)(sXt + pr * LQ + t0l) = make_float4(col[0], col[1], col[2], col[3]);
-                        if (!SEQ || nstart == 0) *(float4*)(sXw + pr * LQ + t0l) = make_float4(colw[0], colw[1], colw[2], colw[3]);
+                        for (int k = 0; k < XC; ++k) wx[k] = to_in<TI>(wv[e] * to_f32(((const TI*)&xr[j][e])[k]));
+                        uint2 pk;
+                        __builtin_memcpy(&pk, wx, 8);
+                        *(uint2*)(sXw + (t0l + e) * LR + c4 * XC) = pk;
                     }
                 }
             }
@@ -661,12 +678,21 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
             acc_y[r] = f32x4{0.f, 0.f, 0.f, 0.f};
             acc_o[r] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
+        constexpr int KS = QB / KSTEP;           // K steps over the tokens of a block
+        // B^T fragment (state tile m, K step ks): row nrow(m, lr) = nrow(m, 0) + nrow(0, lr),
+        // and the row swizzle depends on the lane only (bit 3 of nrow(0, lr)), so every
+        // fragment is a per-K-step lane base plus a compile-time row offset
+        const TI* bt_lane[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            bt_lane[ks] = sBt + nrow<N>(0, lr) * LQ + K::bt_col(nrow<N>(0, lr), ks * KSTEP + KPL * lg);
+        auto bt_frag = [&](int m, int ks) { return lds_frag<TI>(bt_lane[ks / KSTEP] + nrow<N>(m, 0) * LQ); };
         // diagonal block: (L o CB) X, as X^T (L o CB)^T; token tile r only needs s < 16 (r + 1)
 #pragma unroll
         for (int r = 0; r < RT; ++r)
 #pragma unroll
             for (int ks = 0; ks < 16 * (r + 1); ks += KSTEP)
-                acc_y[r] = MF::mma(lds_frag<TI>(sXt + (p0 + lr) * LQ + ks + KPL * lg),
+                acc_y[r] = MF::mma(x_frag(sXr, LR, ks, p0, lr, lg),
                                    lds_frag<TI>(sLm + (16 * r + lr) * LQ + ks + KPL * lg), acc_y[r]);
         if (!SEQ || nstart == 0) {
             // carried state read out by C:  S C^T
@@ -682,9 +708,7 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
 #pragma unroll
             for (int m = 0; m < MT; ++m)
 #pragma unroll
-                for (int ks = 0; ks < QB; ks += KSTEP)
-                    st[m] = MF::mma(lds_frag<TI>(sBt + nrow<N>(m, lr) * LQ + ks + KPL * lg),
-                                    lds_frag<TI>(sXw + (p0 + lr) * LQ + ks + KPL * lg), st[m]);
+                for (int ks = 0; ks < KS; ++ks) st[m] = MF::mma(bt_frag(m, ks * KSTEP), x_frag(sXw, LR, ks * KSTEP, p0, lr, lg), st[m]);
 #pragma unroll
             for (int r = 0; r < RT; ++r) acc_o[r] *= sRow[w][16 * r + lr];
         } else if constexpr (SEQ) {
@@ -723,10 +747,10 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
                 if (e < a) continue;
                 block_sync_lds();                             // the previous segment's weighted X is consumed
                 for (int v = tid; v < P * QB; v += NT) {
-                    const int t = v % QB, pr = v / QB;
+                    const int t = v / P, pr = v % P;
                     const float ws = (sSeg[w][t] == j)
                         ? fast_exp2((float)(sCum[w][e] - sCum[w][t])) * (EULER ? sDtf[w][t] : 1.f) : 0.f;
-                    sXw[pr * LQ + t] = to_in<TI>(ws * to_f32(sXt[pr * LQ + t]));
+                    sXw[t * LR + pr] = to_in<TI>(ws * to_f32(sXr[t * LR + pr]));
                 }
                 block_sync_lds();
                 const cum_t before = (a == 0) ? (cum_t)0 : sCum[w][a - 1];
@@ -750,8 +774,8 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
                 for (int m = 0; m < MT; ++m)
 #pragma unroll
                     for (int ks = 0; ks < QB; ks += KSTEP)
-                        F[m] = MF::mma(lds_frag<TI>(sBt + nrow<N>(m, lr) * LQ + ks + KPL * lg),
-                                       lds_frag<TI>(sXw + (p0 + lr) * LQ + ks + KPL * lg), F[m]);
+                        F[m] = MF::mma(lds_frag<TI>(sBt + nrow<N>(m, lr) * LQ + K::bt_col(nrow<N>(m, lr), ks + KPL * lg)),
+                                       x_frag(sXw, LR, ks, p0, lr, lg), F[m]);
                 if (j < nstart) {
                     write_state(F, sSeqOf[w][j]);
                 } else {
@@ -772,7 +796,7 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
         for (int r = 0; r < RT; ++r) {
             const int t = 16 * r + lr;
             f32x4 out = acc_o[r] + acc_y[r];
-            if (hasD) {
+            {
                 float xv[4];
                 if constexpr (sizeof(TI) == 2) {
                     const bf16x4 x4 = *(const bf16x4*)(sXr + t * LR + p0 + 4 * lg);
