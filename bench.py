@@ -22,6 +22,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+COPY_BYTES = 1 << 30           # size of the calibration copy (read and written once each)
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense
 
 
@@ -68,16 +69,15 @@ def committed_traffic(workload: str):
 
 
 def cpu_baseline(prob, w):
-    """Time the fp64 oracle on rows 0-1 (all heads, full length) on all host cores."""
+    """Time the fp64 oracle on every row of the workload (all heads, full length) on all host cores."""
     import numpy as np
 
     import oracle
     sub = {k: prob[k] for k in ("x", "dt", "B", "C")}
-    rows = min(2, w.batch)
+    rows = w.batch
     sub = {k: np.ascontiguousarray(v[:rows].to(dtype=__import__("torch").float64).numpy()) for k, v in sub.items()}
     A_log = prob["A_log"].double().numpy()
     D = prob["D"].double().numpy() if prob["D"] is not None else None
-    rows = min(2, w.batch)
     init = prob["init"][:rows].double().numpy() if (prob["init"] is not None and prob["seq_idx"] is None) else None
     seq = None
     nseqs = None
@@ -102,6 +102,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="m2p7_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain device copy of known size (reference for the HBM traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the SSD forward here has no multi-GPU path "
@@ -113,6 +115,18 @@ def main():
 
     import mamba_ssd_scan_chunked_amd as ssd
     import ssd_inputs as si
+
+    if args.copy_calibration:
+        # A plain copy of COPY_BYTES: FETCH_SIZE / WRITE_SIZE of this dispatch give
+        # the counters' scale (bytes of HBM traffic per counted KiB).
+        n = COPY_BYTES // 4
+        src = torch.arange(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(max(1, args.steps)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": COPY_BYTES}), flush=True)
+        return
 
     w = si.WORKLOADS[args.workload]
     prob = si.make_workload(w)
