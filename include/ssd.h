@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 1
+#define SSD_ABI_VERSION 2
 
 /* Element type of x, B and C.  dt, A_log, D, init_state, y and final_state are
  * always fp32.  BF16: bf16 operands, fp32 accumulation; F32: fp32 throughout. */
@@ -90,13 +90,13 @@ typedef struct {
  * are low rank, exactly as between chunks). */
 int ssd_validate(const ssd_problem_t* p);
 
-/* Bytes of device workspace ssd_forward / ssd_prepare / ssd_scan need for this
- * problem (a few MB per row: the per-block C.B^T tiles and a transposed copy
- * of B).  Returns 0 if the problem is invalid. */
+/* Bytes of device workspace ssd_forward needs for this problem; 0 when it needs
+ * none (then workspace may be NULL) or when the problem is invalid.  The
+ * single-pass scan keeps its intermediates (C.B^T tiles, decays, the carried
+ * state) on chip and needs no workspace. */
 size_t ssd_workspace_size(const ssd_problem_t* p);
 
-/* Full forward.  Equivalent to ssd_prepare followed by ssd_scan on the same
- * stream.
+/* Full forward, one kernel launch on `stream`.
  *   x          (batch, seqlen, nheads, headdim)   dtype
  *   dt         (batch, seqlen, nheads)            fp32, the step sizes (> 0 after softplus)
  *   A_log      (nheads)                           fp32; A_h = -exp(A_log[h])
@@ -106,7 +106,8 @@ size_t ssd_workspace_size(const ssd_problem_t* p);
  *   seq_idx    (batch, seqlen)                    int32 or NULL
  *   y          (batch, seqlen, nheads, headdim)   fp32 output
  *   final_state(nseqs, nheads, headdim, dstate)   fp32 output, or NULL
- *   workspace / workspace_bytes                   >= ssd_workspace_size(p), 256-byte aligned
+ *   workspace / workspace_bytes                   >= ssd_workspace_size(p) bytes, 256-byte aligned
+ *                                                 (NULL / 0 when that size is 0)
  *
  * seq_idx packs independent sequences into rows: seq_idx[r][t] is the id of
  * the sequence token t of row r belongs to.  Ids are nondecreasing along each
@@ -126,25 +127,6 @@ int ssd_forward(const ssd_problem_t* p,
                 const float* init_state, const int32_t* seq_idx,
                 float* y, float* final_state,
                 void* workspace, size_t workspace_bytes, void* stream);
-
-/* First stage alone: for every (row, group, block of min(chunk_len, 64)
- * tokens) write C_blk B_blk^T (fp32) and B_blk^T into the workspace.  These
- * depend only on B and C, so they are shared by the nheads / ngroups heads of
- * a group.  Defined by the intra-chunk C B^T product of the dual form
- * (section 2.2 of the "088 Mamba-2" page). */
-int ssd_prepare(const ssd_problem_t* p, const void* B, const void* C,
-                void* workspace, size_t workspace_bytes, void* stream);
-
-/* Second stage alone: the chunked scan proper (within-block cumulative decay,
- * masked diagonal products, state passing, off-diagonal read-out, skip term,
- * final states), reading the workspace written by ssd_prepare for the same
- * B, C and problem (C is read again here for the read-out of the carried
- * state).  Arguments as for ssd_forward. */
-int ssd_scan(const ssd_problem_t* p,
-             const void* x, const float* dt, const float* A_log, const void* C,
-             const float* D, const float* init_state, const int32_t* seq_idx,
-             float* y, float* final_state,
-             const void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static description of an error code. */
 const char* ssd_strerror(int status);

@@ -19,7 +19,7 @@ import ctypes
 import os
 from typing import Optional
 
-__all__ = ["forward", "prepare", "scan", "workspace_size", "validate", "problem", "SSDError",
+__all__ = ["forward", "forward_into", "workspace_size", "validate", "problem", "SSDError",
            "version", "library_path", "load_library", "DTYPE_F32", "DTYPE_BF16", "FLAG_DT_SCALES_X"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -71,10 +71,6 @@ def load_library():
     lib.ssd_workspace_size.restype = sz
     lib.ssd_forward.argtypes = [P] + [vp] * 10 + [vp, sz, vp]
     lib.ssd_forward.restype = ctypes.c_int
-    lib.ssd_prepare.argtypes = [P, vp, vp, vp, sz, vp]
-    lib.ssd_prepare.restype = ctypes.c_int
-    lib.ssd_scan.argtypes = [P] + [vp] * 9 + [vp, sz, vp]
-    lib.ssd_scan.restype = ctypes.c_int
     lib.ssd_strerror.argtypes = [ctypes.c_int]
     lib.ssd_strerror.restype = ctypes.c_char_p
     lib.ssd_version.restype = ctypes.c_int
@@ -187,23 +183,18 @@ def forward(x, dt, A_log, B, C, D=None, chunk_len: int = 256, init_state=None, s
     if final_state is None and return_final:
         final_state = torch.empty((p.nseqs, H, P, N), dtype=torch.float32, device=dev)
     wsb = int(lib.ssd_workspace_size(ctypes.byref(p)))
-    if workspace is None:
-        workspace = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
-    st = _stream_of(dev, stream)
-    _check(lib.ssd_forward(ctypes.byref(p), _ptr(x), _ptr(dt), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D),
-                           _ptr(init_state), _ptr(seq_idx), _ptr(y), _ptr(final_state),
-                           _ptr(workspace), workspace.numel(), st))
+    if workspace is None and wsb > 0:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    forward_into(p, x, dt, A_log, B, C, D, init_state, seq_idx, y, final_state, workspace, stream)
     return y, final_state
 
 
-def prepare(p: Problem, B, C, workspace, stream=None):
-    """``ssd_prepare``: per-block C B^T tiles and B^T into ``workspace``."""
-    _check(load_library().ssd_prepare(ctypes.byref(p), _ptr(B), _ptr(C), _ptr(workspace), workspace.numel(),
-                                      _stream_of(B.device, stream)))
-
-
-def scan(p: Problem, x, dt, A_log, C, D, init_state, seq_idx, y, final_state, workspace, stream=None):
-    """``ssd_scan``: the chunked scan proper, reading the workspace from :func:`prepare`."""
-    _check(load_library().ssd_scan(ctypes.byref(p), _ptr(x), _ptr(dt), _ptr(A_log), _ptr(C), _ptr(D),
-                                   _ptr(init_state), _ptr(seq_idx), _ptr(y), _ptr(final_state), _ptr(workspace),
-                                   workspace.numel(), _stream_of(x.device, stream)))
+def forward_into(p: Problem, x, dt, A_log, B, C, D, init_state, seq_idx, y, final_state, workspace=None,
+                 stream=None):
+    """``ssd_forward`` on caller-provided contiguous tensors and problem description
+    (no checks beyond the library's own; ``workspace`` may be None when
+    :func:`workspace_size` is 0)."""
+    wsn = workspace.numel() if workspace is not None else 0
+    _check(load_library().ssd_forward(ctypes.byref(p), _ptr(x), _ptr(dt), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D),
+                                      _ptr(init_state), _ptr(seq_idx), _ptr(y), _ptr(final_state),
+                                      _ptr(workspace), wsn, _stream_of(x.device, stream)))

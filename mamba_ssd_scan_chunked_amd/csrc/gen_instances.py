@@ -18,18 +18,12 @@ def gen(tag, TI, Ps, Ns, QBs, seq, eul):
     return "".join(out)
 
 def gen_common(tag, TI, Ps, Ns, QBs):
-    out = ['// Shape table and prologue-kernel instantiations for %s inputs.\n#include "ssd_kernels.hpp"\n#include "ssd_launch.hpp"\n\nnamespace ssd {\n' % tag]
+    out = ['// Shape table and variant dispatch for %s inputs.\n#include "ssd_kernels.hpp"\n#include "ssd_launch.hpp"\n\nnamespace ssd {\n' % tag]
     out.append("bool supported_%s(int P, int N, int QB) {\n" % tag)
     out.append("    const bool p = %s;\n" % " || ".join("P == %d" % v for v in Ps))
     out.append("    const bool n = %s;\n" % " || ".join("N == %d" % v for v in Ns))
     out.append("    const bool q = %s;\n" % " || ".join("QB == %d" % v for v in QBs))
     out.append("    return p && n && q;\n}\n\n")
-    out.append("hipError_t launch_prep_%s(int N, int QB, const PrepParams& prm, int64_t grid, hipStream_t s) {\n" % tag)
-    out.append("    if (grid <= 0) return hipSuccess;\n")
-    for N in Ns:
-        for Q in QBs:
-            out.append("    if (N == %d && QB == %d) { hipLaunchKernelGGL((ssd_prep_kernel<%s, %d, %d>), dim3((unsigned)grid), dim3(256), 0, s, prm); return hipGetLastError(); }\n" % (N, Q, TI, N, Q))
-    out.append("    return hipErrorInvalidValue;\n}\n\n")
     out.append("hipError_t launch_scan_%s(int P, int N, int QB, bool seq, bool euler, const ScanParams& prm, int64_t grid, hipStream_t s) {\n" % tag)
     out.append("    if (grid <= 0) return hipSuccess;\n")
     for sq, eu in itertools.product((0, 1), (0, 1)):

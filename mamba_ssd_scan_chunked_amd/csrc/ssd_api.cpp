@@ -1,5 +1,5 @@
-// Host side of the C ABI declared in include/ssd.h: argument checks, workspace
-// layout, kernel selection and launches.  Every check runs before the first HIP
+// Host side of the C ABI declared in include/ssd.h: argument checks, kernel
+// selection and the launch.  Every check runs before the first HIP
 // call, so invalid arguments are reported without touching the device.
 #include "ssd.h"
 
@@ -29,23 +29,9 @@ int64_t nblocks(const ssd_problem_t* p) {
     return q ? (p->seqlen + q - 1) / q : 0;
 }
 
-int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
-
-struct WsLayout {
-    int64_t cb_bytes;   // (b, G, nblk, QB, QB) fp32
-    int64_t bt_off;     // offset of (b, G, nblk, N, QB) dtype
-    int64_t total;
-};
-
-WsLayout ws_layout(const ssd_problem_t* p) {
-    const int64_t q = block_len(p);
-    const int64_t units = p->batch * p->ngroups * nblocks(p);
-    WsLayout l;
-    l.cb_bytes = align256(units * q * q * 4);
-    l.bt_off = l.cb_bytes;
-    l.total = l.bt_off + align256(units * p->dstate * q * elem_size(p->dtype));
-    return l;
-}
+// Workspace bytes the forward pass needs.  The single-pass scan keeps every
+// intermediate in registers and LDS, so none.
+int64_t workspace_bytes(const ssd_problem_t*) { return 0; }
 
 bool misaligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) != 0; }
 
@@ -85,40 +71,29 @@ Sizes sizes(const ssd_problem_t* p) {
     return s;
 }
 
-int check_prepare_args(const ssd_problem_t* p, const void* B, const void* C, const void* ws, size_t ws_bytes) {
-    const int v = ssd_validate(p);
-    if (v != SSD_OK) return v;
-    const bool empty = p->batch == 0 || p->seqlen == 0;
-    if (!empty && (!B || !C || !ws)) return SSD_ERR_NULL_POINTER;
-    if (misaligned(B, 16) || misaligned(C, 16) || misaligned(ws, 256)) return SSD_ERR_ALIGNMENT;
-    if (static_cast<int64_t>(ws_bytes) < ws_layout(p).total) return SSD_ERR_WORKSPACE;
-    const Sizes s = sizes(p);
-    const int64_t wsb = ws_layout(p).total;
-    if (overlap(ws, wsb, B, s.bc) || overlap(ws, wsb, C, s.bc)) return SSD_ERR_ALIAS;
-    return SSD_OK;
-}
-
-int check_scan_args(const ssd_problem_t* p, const void* x, const float* dt, const float* A_log, const void* C,
-                    const float* D, const float* init, const int32_t* seq_idx, const float* y, const float* fin,
-                    const void* ws, size_t ws_bytes) {
+int check_args(const ssd_problem_t* p, const void* x, const float* dt, const float* A_log, const void* B,
+               const void* C, const float* D, const float* init, const int32_t* seq_idx, const float* y,
+               const float* fin, const void* ws, size_t ws_bytes) {
     const int v = ssd_validate(p);
     if (v != SSD_OK) return v;
     const bool empty_tokens = p->batch == 0 || p->seqlen == 0;
     if (!A_log) return SSD_ERR_NULL_POINTER;
-    if (!empty_tokens && (!x || !dt || !C || !y || !ws)) return SSD_ERR_NULL_POINTER;
+    const int64_t wsb = workspace_bytes(p);
+    if (!empty_tokens && (!x || !dt || !B || !C || !y)) return SSD_ERR_NULL_POINTER;
+    if (wsb > 0 && !ws) return SSD_ERR_WORKSPACE;
     if (!seq_idx && p->nseqs != p->batch) return SSD_ERR_BAD_SHAPE;
-    if (misaligned(x, 16) || misaligned(C, 16) || misaligned(y, 16) || misaligned(dt, 4) || misaligned(A_log, 4) ||
+    if (misaligned(x, 16) || misaligned(B, 16) || misaligned(C, 16) || misaligned(y, 16) || misaligned(dt, 4) ||
+        misaligned(A_log, 4) ||
         misaligned(D, 4) || misaligned(init, 16) || misaligned(fin, 16) || misaligned(seq_idx, 4) ||
         misaligned(ws, 256))
         return SSD_ERR_ALIGNMENT;
-    if (static_cast<int64_t>(ws_bytes) < ws_layout(p).total) return SSD_ERR_WORKSPACE;
+    if (static_cast<int64_t>(ws_bytes) < wsb) return SSD_ERR_WORKSPACE;
     const Sizes s = sizes(p);
-    const int64_t wsb = ws_layout(p).total;
     const int64_t hb = p->nheads * 4;
     // outputs must not overlap any input, the workspace or each other
-    const void* in_ptr[] = {x, dt, A_log, C, D, seq_idx, ws};
-    const int64_t in_sz[] = {s.x, s.dt, hb, s.bc, hb, s.seq, wsb};
-    for (int i = 0; i < 7; ++i) {
+    const void* in_ptr[] = {x, dt, A_log, B, C, D, seq_idx, ws};
+    const int64_t in_sz[] = {s.x, s.dt, hb, s.bc, s.bc, hb, s.seq, wsb};
+    for (int i = 0; i < 8; ++i) {
         if (overlap(y, s.y, in_ptr[i], in_sz[i])) return SSD_ERR_ALIAS;
         if (overlap(fin, s.state, in_ptr[i], in_sz[i])) return SSD_ERR_ALIAS;
     }
@@ -128,33 +103,10 @@ int check_scan_args(const ssd_problem_t* p, const void* x, const float* dt, cons
     return SSD_OK;
 }
 
-int launch_prepare(const ssd_problem_t* p, const void* B, const void* C, void* ws, hipStream_t stream) {
-    const int q = block_len(p);
-    const int64_t nblk = nblocks(p);
-    const WsLayout l = ws_layout(p);
-    ssd::PrepParams prm;
-    prm.B = B;
-    prm.C = C;
-    prm.cb = static_cast<float*>(ws);
-    prm.bt = static_cast<char*>(ws) + l.bt_off;
-    prm.T = p->seqlen;
-    prm.G = p->ngroups;
-    prm.nblk = static_cast<int>(nblk);
-    const int64_t grid = p->batch * p->ngroups * nblk;
-    if (grid == 0) return SSD_OK;
-    hipError_t e = p->dtype == SSD_DTYPE_BF16 ? ssd::launch_prep_bf16((int)p->dstate, q, prm, grid, stream)
-                                              : ssd::launch_prep_f32((int)p->dstate, q, prm, grid, stream);
-    if (log_enabled())
-        std::fprintf(stderr, "[ssd] prepare dtype=%d N=%lld QB=%d grid=%lld -> %s\n", p->dtype,
-                     (long long)p->dstate, q, (long long)grid, hipGetErrorString(e));
-    return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
-}
-
-int launch_scan(const ssd_problem_t* p, const void* x, const float* dt, const float* A_log, const void* C,
-                const float* D, const float* init, const int32_t* seq_idx, float* y, float* fin, const void* ws,
+int launch_scan(const ssd_problem_t* p, const void* x, const float* dt, const float* A_log, const void* B,
+                const void* C, const float* D, const float* init, const int32_t* seq_idx, float* y, float* fin,
                 hipStream_t stream) {
     const int q = block_len(p);
-    const WsLayout l = ws_layout(p);
     ssd::ScanParams prm;
     prm.x = x;
     prm.dt = dt;
@@ -164,8 +116,7 @@ int launch_scan(const ssd_problem_t* p, const void* x, const float* dt, const fl
     prm.seq_idx = seq_idx;
     prm.y = y;
     prm.fin = fin;
-    prm.cb = static_cast<const float*>(ws);
-    prm.bt = static_cast<const char*>(ws) + l.bt_off;
+    prm.B = B;
     prm.C = C;
     prm.batch = p->batch;
     prm.T = p->seqlen;
@@ -223,47 +174,19 @@ int ssd_validate(const ssd_problem_t* p) {
 
 size_t ssd_workspace_size(const ssd_problem_t* p) {
     if (ssd_validate(p) != SSD_OK) return 0;
-    return static_cast<size_t>(ws_layout(p).total);
-}
-
-int ssd_prepare(const ssd_problem_t* p, const void* B, const void* C, void* workspace, size_t workspace_bytes,
-                void* stream) {
-    const int v = check_prepare_args(p, B, C, workspace, workspace_bytes);
-    if (v != SSD_OK) return v;
-    const int d = check_device();
-    if (d != SSD_OK) return d;
-    return launch_prepare(p, B, C, workspace, static_cast<hipStream_t>(stream));
-}
-
-int ssd_scan(const ssd_problem_t* p, const void* x, const float* dt, const float* A_log, const void* C,
-             const float* D, const float* init_state, const int32_t* seq_idx, float* y, float* final_state,
-             const void* workspace, size_t workspace_bytes, void* stream) {
-    const int v = check_scan_args(p, x, dt, A_log, C, D, init_state, seq_idx, y, final_state, workspace,
-                                  workspace_bytes);
-    if (v != SSD_OK) return v;
-    const int d = check_device();
-    if (d != SSD_OK) return d;
-    return launch_scan(p, x, dt, A_log, C, D, init_state, seq_idx, y, final_state, workspace,
-                       static_cast<hipStream_t>(stream));
+    return static_cast<size_t>(workspace_bytes(p));
 }
 
 int ssd_forward(const ssd_problem_t* p, const void* x, const float* dt, const float* A_log, const void* B,
                 const void* C, const float* D, const float* init_state, const int32_t* seq_idx, float* y,
                 float* final_state, void* workspace, size_t workspace_bytes, void* stream) {
-    int v = check_prepare_args(p, B, C, workspace, workspace_bytes);
+    const int v = check_args(p, x, dt, A_log, B, C, D, init_state, seq_idx, y, final_state, workspace,
+                             workspace_bytes);
     if (v != SSD_OK) return v;
-    v = check_scan_args(p, x, dt, A_log, C, D, init_state, seq_idx, y, final_state, workspace, workspace_bytes);
-    if (v != SSD_OK) return v;
-    {
-        const Sizes s = sizes(p);
-        if (overlap(y, s.y, B, s.bc) || overlap(final_state, s.state, B, s.bc)) return SSD_ERR_ALIAS;
-    }
     const int d = check_device();
     if (d != SSD_OK) return d;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    v = launch_prepare(p, B, C, workspace, st);
-    if (v != SSD_OK) return v;
-    return launch_scan(p, x, dt, A_log, C, D, init_state, seq_idx, y, final_state, workspace, st);
+    return launch_scan(p, x, dt, A_log, B, C, D, init_state, seq_idx, y, final_state,
+                       static_cast<hipStream_t>(stream));
 }
 
 const char* ssd_strerror(int status) {

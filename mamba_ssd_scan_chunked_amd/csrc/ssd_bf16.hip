@@ -1,4 +1,4 @@
-// Shape table and prologue-kernel instantiations for bf16 inputs.
+// Shape table and variant dispatch for bf16 inputs.
 #include "ssd_kernels.hpp"
 #include "ssd_launch.hpp"
 
@@ -8,17 +8,6 @@ bool supported_bf16(int P, int N, int QB) {
     const bool n = N == 64 || N == 128 || N == 256;
     const bool q = QB == 32 || QB == 64;
     return p && n && q;
-}
-
-hipError_t launch_prep_bf16(int N, int QB, const PrepParams& prm, int64_t grid, hipStream_t s) {
-    if (grid <= 0) return hipSuccess;
-    if (N == 64 && QB == 32) { hipLaunchKernelGGL((ssd_prep_kernel<__bf16, 64, 32>), dim3((unsigned)grid), dim3(256), 0, s, prm); return hipGetLastError(); }
-    if (N == 64 && QB == 64) { hipLaunchKernelGGL((ssd_prep_kernel<__bf16, 64, 64>), dim3((unsigned)grid), dim3(256), 0, s, prm); return hipGetLastError(); }
-    if (N == 128 && QB == 32) { hipLaunchKernelGGL((ssd_prep_kernel<__bf16, 128, 32>), dim3((unsigned)grid), dim3(256), 0, s, prm); return hipGetLastError(); }
-    if (N == 128 && QB == 64) { hipLaunchKernelGGL((ssd_prep_kernel<__bf16, 128, 64>), dim3((unsigned)grid), dim3(256), 0, s, prm); return hipGetLastError(); }
-    if (N == 256 && QB == 32) { hipLaunchKernelGGL((ssd_prep_kernel<__bf16, 256, 32>), dim3((unsigned)grid), dim3(256), 0, s, prm); return hipGetLastError(); }
-    if (N == 256 && QB == 64) { hipLaunchKernelGGL((ssd_prep_kernel<__bf16, 256, 64>), dim3((unsigned)grid), dim3(256), 0, s, prm); return hipGetLastError(); }
-    return hipErrorInvalidValue;
 }
 
 hipError_t launch_scan_bf16(int P, int N, int QB, bool seq, bool euler, const ScanParams& prm, int64_t grid, hipStream_t s) {

@@ -1,42 +1,41 @@
-// SSD chunked-scan forward kernels for gfx950 (MI355X).
+// SSD chunked-scan forward kernel for gfx950 (MI355X).
 //
-// Two kernels make one forward pass:
-//
-//  1. ssd_prep_kernel, one workgroup per (row, group, block of QB tokens):
-//       CB[t][s] = C_t . B_s   for t, s in the block (fp32), and B^T of the block.
-//     These depend only on B and C, so every head of the group reuses them;
-//     they are the intra-chunk C B^T products of the dual form Y = [L o (C B^T)] X
-//     ("088 Mamba-2", section 2.2; the diagonal-block step of key design 2 on
-//     the "Mamba-2 - Transformer and SSM share one algebra" page).
-//
-//  2. ssd_scan_kernel, one workgroup per (row, head), P/16 waves; wave w owns
-//     channels p in [16w, 16w+16).  The workgroup walks its row block by block
-//     (QB = 32 or 64 tokens) with the P x N state held in MFMA accumulator
-//     registers for the whole row.  Per block:
-//       a. log-decay l_t = dt_t A_h (kept in log2 units) and its inclusive
-//          cumulative sum within the block, by a wavefront scan
-//          (the within-chunk cumsum of the chunked algorithm);
-//       b. masked decay L[t][s] = exp(cum_t - cum_s) for s <= t in the same
-//          sequence, else 0, multiplied into CB (segment sum, section 2.2);
-//       c. y_diag = (L o CB) X on bf16 MFMA (diagonal block, section 2.3);
-//       d. y_off  = exp(cum_t) C_t H_prev, the incoming state read out by C and
-//          decayed to each position (left factor, section 3 of "088 Mamba-2");
-//       e. H <- exp(cum_end) H + X^T (exp(cum_end - cum_s) o B), the block's end
-//          state combined with the carried one (right factor and the
-//          inter-chunk scan step real_end = block_decay * prev + local_end);
-//       f. y = y_off + y_diag + D x, written once to HBM in fp32.
-//     Sequence boundaries inside a block (seq_idx) split it into segments:
-//     L is masked across segments, each segment's incoming state is either the
-//     carried state or its own initial state, and the state of a sequence that
-//     ends inside the block is written to final_state on the spot.
+// ssd_scan_kernel, one workgroup per (row, head), P/16 waves; wave w owns
+// channels p in [16w, 16w+16).  The workgroup walks its row block by block
+// (QB = 32 or 64 tokens) with the P x N state held in MFMA accumulator
+// registers for the whole row.  Per block:
+//   a. log-decay l_t = dt_t A_h (kept in log2 units) and its inclusive
+//      cumulative sum within the block, by a wavefront scan
+//      (the within-chunk cumsum of the chunked algorithm);
+//   b. C B^T over the causal 16x16 tiles of the block on bf16 MFMA, from the
+//      C and B tiles staged in LDS, shared out over the waves (the intra-chunk
+//      C B^T products of the dual form Y = [L o (C B^T)] X, "088 Mamba-2",
+//      section 2.2; the diagonal-block step of key design 2 on the
+//      "Mamba-2 - Transformer and SSM share one algebra" page);
+//   c. masked decay L[t][s] = exp(cum_t - cum_s) for s <= t in the same
+//      sequence, else 0, applied to those tiles in registers (segment sum,
+//      section 2.2) and left in LDS as bf16;
+//   d. y_diag = (L o CB) X on bf16 MFMA (diagonal block, section 2.3);
+//   e. y_off  = exp(cum_t) C_t H_prev, the incoming state read out by C and
+//      decayed to each position (left factor, section 3 of "088 Mamba-2");
+//   f. H <- exp(cum_end) H + X^T (exp(cum_end - cum_s) o B), the block's end
+//      state combined with the carried one (right factor and the
+//      inter-chunk scan step real_end = block_decay * prev + local_end);
+//   g. y = y_off + y_diag + D x, written once to HBM in fp32.
+// Sequence boundaries inside a block (seq_idx) split it into segments:
+// L is masked across segments, each segment's incoming state is either the
+// carried state or its own initial state, and the state of a sequence that
+// ends inside the block is written to final_state on the spot.
 //
 // Because the state stays in registers, x is read once and y written once;
-// the only other traffic is dt and the per-block CB / B^T tiles, which all
-// heads of a group share through L2.
+// the only other traffic is dt and the per-block B and C tiles, which all
+// heads of a group read through L2.
 
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 namespace ssd {
 
@@ -165,6 +164,63 @@ __device__ inline float x_frag(const float* sX, int lp, int ks, int p0, int lr, 
     return sX[(ks + lg) * lp + p0 + lr];
 }
 
+// B tile in LDS, bf16: row t holds the N values of token t at element offset
+// t * bpitch(N) + boff(t).  A transposing read of the state update has each
+// half-wave touch 8 token rows (t0 .. t0+3 and t0+8 .. t0+11) and, in each, four
+// 8-byte chunks spaced 16 bytes apart; with a row pitch of 8 or 24 (mod 32)
+// chunks and one extra chunk for rows with bit 3 of t set, those 8 rows start
+// on chunk offsets {0, 8, 16, 24} and {1, 9, 17, 25} (mod 32) and the 32
+// chunks cover all 64 banks once.  The offsets are additive, so every
+// fragment is a per-lane base plus a compile-time immediate.  fp32 tiles use
+// a plain padded pitch.
+template <int N>
+constexpr int bpitch() {
+    int c = N / 4 + 1;
+    while (c % 32 != 8 && c % 32 != 24) ++c;
+    return 4 * c;
+}
+__device__ inline int boff(int t) { return 4 * ((t >> 3) & 1); }
+
+// A operand of the state update for state tile m and the K step of tokens
+// ks .. ks+KSTEP-1: row rho = l % 16 is state row n = nrow(m, rho), K values are
+// tokens ks + KPL*(l/16) + 0 .. KPL-1.  bf16: two transposing reads of the
+// token-major B tile; lane j of each 16-lane group loads the four values
+// n = nrow(m, 4(j%4)) .. +3 of token ks + 8(l/16) + j/4 (+4 for the second read)
+// and the hardware hands lane i row nrow(m, i) of those four tokens.
+template <int N>
+__device__ inline bf16x8 bt_frag(const __bf16* sB, int m, int ks, int lr, int lg) {
+    constexpr int LB = bpitch<N>();
+    const int t0 = ks + 8 * lg + (lr >> 2);
+    const __bf16* lo = sB + t0 * LB + boff(t0) + nrow<N>(m, 4 * (lr & 3));
+    const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)lo);
+    const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(lo + 4 * LB));
+    return __builtin_shufflevector(__builtin_bit_cast(bf16x4, a), __builtin_bit_cast(bf16x4, b), 0, 1, 2, 3, 4, 5, 6, 7);
+}
+template <int N>
+__device__ inline float bt_frag(const float* sB, int m, int ks, int lr, int lg) {
+    return sB[(ks + lg) * (N + 4) + nrow<N>(m, lr)];
+}
+
+// Operand of C B^T holding B row s at the K indices n of step k (natural order):
+// bf16 n = 32k + 8(l/16) .. +7 (two 8-byte reads); fp32 n = 4k + l/16.
+template <int N>
+__device__ inline bf16x8 brow_frag(const __bf16* sB, int s, int k, int lg) {
+    constexpr int LB = bpitch<N>();
+    const __bf16* r = sB + s * LB + boff(s) + 32 * k + 8 * lg;
+    const bf16x4 a = *(const bf16x4*)r;
+    const bf16x4 b = *(const bf16x4*)(r + 4);
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+template <int N>
+__device__ inline float brow_frag(const float* sB, int s, int k, int lg) {
+    return sB[s * (N + 4) + 4 * k + lg];
+}
+// Operand of C B^T holding C row t at the same K indices (natural order).
+template <int N>
+__device__ inline bf16x8 crow_frag(const __bf16* row, int k, int lg) { return *(const bf16x8*)(row + 32 * k + 8 * lg); }
+template <int N>
+__device__ inline float crow_frag(const float* row, int k, int lg) { return row[4 * k + lg]; }
+
 // Make this wave's LDS writes visible to its own other lanes.
 __device__ inline void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
@@ -211,14 +267,19 @@ __device__ inline void buf_store16(f32x4 v, rsrc_t r, int off) {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, off, 0, 0);
 }
 
-struct PrepParams {
-    const void* B;
-    const void* C;
-    float* cb;          // (b, G, nblk, QB, QB) fp32
-    void* bt;           // (b, G, nblk, N, QB) input dtype
-    int64_t T, G;
-    int nblk;
-};
+// Scheduling hint for a straight-line stretch of LDS-fed MFMAs: keep LEAD LDS
+// reads ahead of the MFMA that consumes them, then alternate one MFMA with RPM
+// reads.  Without it the scheduler issues each operand read right before its
+// MFMA and waits for it, exposing the full LDS latency on every product.
+template <int LEAD, int NMFMA, int RPM>
+__device__ inline void pipeline_lds_mfma() {
+    __builtin_amdgcn_sched_group_barrier(0x100, LEAD, 0);
+#pragma unroll
+    for (int i = 0; i < NMFMA; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
+    }
+}
 
 struct ScanParams {
     const void* x;
@@ -229,77 +290,12 @@ struct ScanParams {
     const int32_t* seq_idx;
     float* y;
     float* fin;
-    const float* cb;
-    const void* bt;
+    const void* B;
     const void* C;
     int64_t batch, T, H, G, nseqs;
     int nblk;
     int dt_scales_x;
 };
-
-// ============================================================== prep kernel
-template <typename TI, int N, int QB>
-__global__ __launch_bounds__(256) void ssd_prep_kernel(PrepParams prm) {
-    constexpr int VE = 16 / sizeof(TI);         // elements per 16-byte vector
-    constexpr int LP = N + VE;                  // padded row pitch (elements)
-    __shared__ __attribute__((aligned(16))) TI sB[QB * LP];
-    __shared__ __attribute__((aligned(16))) TI sC[QB * LP];
-
-    const int tid = threadIdx.x;
-    const int blk = blockIdx.x % prm.nblk;
-    const int64_t bg = blockIdx.x / prm.nblk;   // b * G + g
-    const int64_t b = bg / prm.G, g = bg % prm.G;
-    const int64_t t0 = (int64_t)blk * QB;
-    const int rows = (int)min((int64_t)QB, prm.T - t0);
-
-    const TI* Bg = (const TI*)prm.B;
-    const TI* Cg = (const TI*)prm.C;
-    for (int v = tid; v < QB * N / VE; v += 256) {
-        const int t = v / (N / VE), c = v % (N / VE);
-        uint4 bv = make_uint4(0, 0, 0, 0), cv = make_uint4(0, 0, 0, 0);
-        if (t < rows) {
-            const int64_t off = ((b * prm.T + t0 + t) * prm.G + g) * N + c * VE;
-            bv = *(const uint4*)(Bg + off);
-            cv = *(const uint4*)(Cg + off);
-        }
-        *(uint4*)(sB + t * LP + c * VE) = bv;
-        *(uint4*)(sC + t * LP + c * VE) = cv;
-    }
-    __syncthreads();
-
-    // CB = C B^T over the block, 4x4 outputs per thread.
-    constexpr int G4 = QB / 4;
-    if (tid < G4 * G4) {
-        const int tg = tid / G4, sg = tid % G4;
-        float acc[4][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
-        for (int n = 0; n < N; ++n) {
-            float cv[4], bv[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                cv[i] = to_f32(sC[(4 * tg + i) * LP + n]);
-                bv[i] = to_f32(sB[(4 * sg + i) * LP + n]);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(cv[i], bv[j], acc[i][j]);
-        }
-        float* out = prm.cb + ((bg * prm.nblk + blk) * QB) * QB;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *(float4*)(out + (4 * tg + i) * QB + 4 * sg) = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
-    }
-    // B^T of the block (rows n, columns s), in the input dtype.
-    TI* bt = (TI*)prm.bt + ((bg * prm.nblk + blk) * N) * QB;
-    for (int v = tid; v < N * QB; v += 256) {
-        const int n = v / QB, s = v % QB;
-        bt[v] = sB[s * LP + n];
-    }
-}
 
 // ============================================================== scan kernel
 template <typename TI> struct CumType { typedef float type; };
@@ -339,33 +335,30 @@ struct ScanCfg {
     static constexpr int SZ = (int)sizeof(TI);
     static constexpr int VE = 16 / SZ;                // elements per 16-byte vector
     static constexpr int LC = N + VE;                 // pitch of C rows (elements)
-    static constexpr int LQ = QB + VE;                // pitch of rows indexed by token s
+    static constexpr int LB = SZ == 2 ? bpitch<N>() : N + 4;   // pitch of B rows (see bpitch)
+    static constexpr int LQ = QB + VE;                // pitch of the rows of L o CB (indexed by token s)
     static constexpr int LR = P + 32 / SZ;            // pitch of the row-major X tiles (32 bytes of pad:
                                                       // the four rows of a transposed read fall in
                                                       // distinct banks)
     static constexpr int KPL = Mfma<TI>::KPL, KSTEP = Mfma<TI>::KSTEP;
-    static constexpr int NK = OffK<TI, N>::NK;
+    static constexpr int NK = OffK<TI, N>::NK;        // K steps over the state dimension
     static constexpr int RT = QB / 16;                // token tiles of a block
     static constexpr int MT = N / 16;                 // state tiles per wave
-    static constexpr int NTILE = RT * (RT + 1) / 2;   // causal 16x16 tiles of the decay mask
-    // LDS tiles: C, B^T, masked decay L o CB, X and end-state-weighted X (both row-major)
+    static constexpr int NTILE = RT * (RT + 1) / 2;   // causal 16x16 tiles of L o CB
+    static constexpr int TPW = (NTILE + NW - 1) / NW; // causal tiles per wave (surplus slots repeat a tile)
+    // LDS tiles: C, B (both token-major), masked decay L o CB, X (row-major, two
+    // buffers: block k+1 is staged while the diagonal product of block k reads
+    // block k) and the end-state-weighted X
     static constexpr int OFF_C = 0;
-    static constexpr int OFF_BT = OFF_C + QB * LC;
-    static constexpr int OFF_LM = OFF_BT + N * LQ;
+    static constexpr int OFF_B = OFF_C + QB * LC;
+    static constexpr int OFF_LM = OFF_B + QB * LB;
     static constexpr int OFF_XR = OFF_LM + QB * LQ;
-    static constexpr int OFF_XW = OFF_XR + QB * LR;
+    static constexpr int OFF_XW = OFF_XR + 2 * QB * LR;
     static constexpr int BUF_ELEMS = OFF_XW + QB * LR;
     // per-thread work units
-    static constexpr int CV = QB * N / VE, CPT = (CV + NT - 1) / NT;           // C tile vectors
-    static constexpr int BV = N * QB / VE, BPT = (BV + NT - 1) / NT;           // B^T tile vectors
-    static constexpr int LMU = NTILE * 64, LMPT = (LMU + NT - 1) / NT;         // 4-element pieces of L o CB
+    static constexpr int CV = QB * N / VE, CPT = (CV + NT - 1) / NT;           // C (and B) tile vectors
     static constexpr int XC = 8 / SZ;                                          // channels per 8 bytes
     static constexpr int XU = (QB / 4) * (P / XC), XPT = (XU + NT - 1) / NT;   // (4 tokens, XC channels) of X
-    // B^T rows n and n + 8 would share LDS banks in the permuted-row reads of
-    // the state update; for bf16 64-token blocks the two 64-byte halves of
-    // every row with bit 3 of n set are swapped (XOR swizzle, element offset).
-    static constexpr bool BT_SWZ = (SZ == 2 && QB == 64);
-    __device__ static inline int bt_col(int n, int col) { return BT_SWZ ? (col ^ (((n >> 3) & 1) * 32)) : col; }
 };
 
 template <typename TI, int P, int N, int QB, bool SEQ, bool EULER>
@@ -374,26 +367,27 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
     typedef Mfma<TI> MF;
     typedef typename MF::frag frag;
     typedef typename CumType<TI>::type cum_t;
-    constexpr int NT = K::NT, VE = K::VE, LC = K::LC, LQ = K::LQ, LR = K::LR, KPL = K::KPL, KSTEP = K::KSTEP;
-    constexpr int SZ = K::SZ, NK = K::NK, RT = K::RT, MT = K::MT, NW = K::NW, XC = K::XC;
+    constexpr int NT = K::NT, VE = K::VE, LC = K::LC, LB = K::LB, LQ = K::LQ, LR = K::LR, KPL = K::KPL;
+    constexpr int KSTEP = K::KSTEP, SZ = K::SZ, NK = K::NK, RT = K::RT, MT = K::MT, NW = K::NW, XC = K::XC;
     static_assert(QB <= 64 && QB % KSTEP == 0 && QB % 16 == 0, "block length");
     static_assert(N % KSTEP == 0 && N % 16 == 0 && P % 16 == 0 && P % XC == 0, "shape");
 
     __shared__ __attribute__((aligned(16))) TI smem[K::BUF_ELEMS];
     // per-wave copies of the block's per-token scalars (each wave computes its own)
+    constexpr int SQW = SEQ ? NW : 1, EUW = EULER ? NW : 1;        // arrays only the variant uses
     __shared__ __attribute__((aligned(16))) cum_t sCum[NW][64];   // cumulative log2 decay
     __shared__ __attribute__((aligned(16))) float sRow[NW][64];   // read-out row scale
-    __shared__ __attribute__((aligned(16))) float sV[NW][64];     // exp2(cum at end of the token's 16-tile - cum)
     __shared__ __attribute__((aligned(16))) float sWx[NW][64];    // end-state weight exp2(cum_end - cum) (dt)
-    __shared__ __attribute__((aligned(16))) float sDtf[NW][64];   // dt (Euler input scaling)
-    __shared__ int sSeg[NW][64];
-    __shared__ int sStart[NW][65];
-    __shared__ int sSeqOf[NW][65];
+    __shared__ __attribute__((aligned(16))) float sDtf[EUW][64];  // dt (Euler input scaling)
+    __shared__ __attribute__((aligned(16))) int sSeg[SQW][64];    // segment of each token
+    __shared__ int sStart[SQW][65];
+    __shared__ int sSeqOf[SQW][65];
+    const int wq = SEQ ? (int)(threadIdx.x >> 6) : 0, we = EULER ? (int)(threadIdx.x >> 6) : 0;
 
     TI* sC = smem + K::OFF_C;
-    TI* sBt = smem + K::OFF_BT;
+    TI* sB = smem + K::OFF_B;
     TI* sLm = smem + K::OFF_LM;
-    TI* sXr = smem + K::OFF_XR;
+    auto sXr_of = [&](int blk) { return smem + K::OFF_XR + (blk & 1) * QB * K::LR; };
     TI* sXw = smem + K::OFF_XW;
 
     const int tid = threadIdx.x;
@@ -402,7 +396,7 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
 
     // Work-item order: runs of consecutive (row, head) items go to the same
     // XCD (workgroups are dealt round-robin over the 8 XCDs), so the heads of
-    // a row share that row's C, CB and B^T tiles in one L2.
+    // a row share that row's B and C tiles in one L2.
     const int64_t units = prm.batch * prm.H;
     int64_t u = blockIdx.x;
     if (units % 8 == 0) u = (int64_t)(blockIdx.x % 8) * (units / 8) + blockIdx.x / 8;
@@ -427,9 +421,8 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
     const char* xrow = (const char*)prm.x + ((b * T) * H + h) * P * SZ;
     const char* yrow = (const char*)prm.y + ((b * T) * H + h) * P * 4;
     const char* crow = (const char*)prm.C + ((b * T) * G + g) * N * SZ;
+    const char* brow = (const char*)prm.B + ((b * T) * G + g) * N * SZ;
     const char* drow = (const char*)prm.dt + ((b * T) * H + h) * 4;
-    const char* btb0 = (const char*)prm.bt + ((b * G + g) * nblk) * (int64_t)N * QB * SZ;
-    const char* cbb0 = (const char*)prm.cb + ((b * G + g) * nblk) * (int64_t)QB * QB * 4;
     const int64_t xrec = ((T - 1) * H + 1) * P * SZ, yrec = ((T - 1) * H + 1) * P * 4;
     const int64_t crec = ((T - 1) * G + 1) * N * SZ, drec = ((T - 1) * H + 1) * 4;
 
@@ -464,33 +457,31 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
             sLm[(16 * r + i) * LQ + 16 * (r + 1) + c] = to_in<TI>(0.f);
         }
     }
-
-    // ---- one block of loads, issued at the top of an iteration and consumed
-    // at its bottom (after the MFMA phase of the previous block), so no load
-    // result lives across the loop back-edge and the wait counts stay exact.
-    uint4 cr[K::CPT], br[K::BPT];
-    float4 cbr[K::LMPT];
-    uint2 xr[K::XPT][4];
-    float dtv = 0.f;
-    int sqv = 0;
-    // Causal tile of each of this thread's L o CB pieces (row tile I, column tile
-    // J <= I); the tile index v / 64 is uniform over the wave.
-    int tI[K::LMPT], tJ[K::LMPT];
+    // Causal tiles (row tile I, column tile J <= I) of L o CB computed by this
+    // wave: q = w, w + NW, ..., q = I (I + 1) / 2 + J.
+    int tI[K::TPW], tJ[K::TPW];
 #pragma unroll
-    for (int j = 0; j < K::LMPT; ++j) {
-        const int q = (tid + j * NT) / 64;
+    for (int j = 0; j < K::TPW; ++j) {
+        const int q = (w + j * NW) % K::NTILE;
         int I = 0;
         while ((I + 1) * (I + 2) / 2 <= q) ++I;
         tI[j] = I;
         tJ[j] = q - I * (I + 1) / 2;
     }
+
+    // ---- one block of loads, issued at the top of an iteration and consumed
+    // at its bottom (after the MFMA phase of the previous block), so no load
+    // result lives across the loop back-edge and the wait counts stay exact.
+    uint4 cr[K::CPT], br[K::CPT];
+    uint2 xr[K::XPT][4];
+    float dtv = 0.f;
+    int sqv = 0;
     auto issue = [&](int blk) {
         const int64_t t0 = (int64_t)blk * QB;
         const rsrc_t rx = make_rsrc(xrow + t0 * xs, xrec - t0 * xs);
         const rsrc_t rc = make_rsrc(crow + t0 * cs, crec - t0 * cs);
+        const rsrc_t rb = make_rsrc(brow + t0 * cs, crec - t0 * cs);
         const rsrc_t rd = make_rsrc(drow + t0 * ds, drec - t0 * ds);
-        const rsrc_t rb = make_rsrc(btb0 + (int64_t)blk * N * QB * SZ, (int64_t)N * QB * SZ);
-        const rsrc_t rcb = make_rsrc(cbb0 + (int64_t)blk * QB * QB * 4, (int64_t)QB * QB * 4);
         dtv = buf_load_f32(rd, lane * ds);
         if constexpr (SEQ) sqv = buf_load_i32(make_rsrc(seqg + t0, (T - t0) * 4), lane * 4);
 #pragma unroll
@@ -504,45 +495,42 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
 #pragma unroll
         for (int j = 0; j < K::CPT; ++j) {
             const int v = tid + j * NT;
-            if (K::CV % NT == 0 || v < K::CV) cr[j] = buf_load16(rc, (v / (N / VE)) * cs + (v % (N / VE)) * 16);
-        }
-#pragma unroll
-        for (int j = 0; j < K::BPT; ++j) {
-            const int v = tid + j * NT;
-            if (K::BV % NT == 0 || v < K::BV) br[j] = buf_load16(rb, v * 16);
-        }
-#pragma unroll
-        for (int j = 0; j < K::LMPT; ++j) {
-            const int v = tid + j * NT;
-            if (K::LMU % NT == 0 || v < K::LMU) {
-                const int t = 16 * tI[j] + (v % 64) / 4, s0 = 16 * tJ[j] + 4 * (v % 4);
-                cbr[j] = __builtin_bit_cast(float4, buf_load16(rcb, (t * QB + s0) * 4));
+            if (K::CV % NT == 0 || v < K::CV) {
+                const int off = (v / (N / VE)) * cs + (v % (N / VE)) * 16;
+                cr[j] = buf_load16(rc, off);
+                br[j] = buf_load16(rb, off);
             }
         }
     };
 
-    // per-block values handed from the preparation of a block to its MFMA phase
+    // per-block values handed from the preparation of a block to its MFMA phases
     int nstart_c = 0, lastseq_c = prevseq;
     float cend_f = 0.f;
 
     // ---- preparation of a block from the issued loads: tiles into LDS, the
-    //      within-block cumulative decay, segments, L o CB, X^T and weighted X^T
+    //      within-block cumulative decay, segments, X and weighted X
     auto prep = [&](int blk) {
         const int rows = (int)min((int64_t)QB, T - (int64_t)blk * QB);
+        TI* sXr = sXr_of(blk);
 #pragma unroll
         for (int j = 0; j < K::CPT; ++j) {
             const int v = tid + j * NT;
-            if (K::CV % NT == 0 || v < K::CV) *(uint4*)(sC + (v / (N / VE)) * LC + (v % (N / VE)) * VE) = cr[j];
-        }
-#pragma unroll
-        for (int j = 0; j < K::BPT; ++j) {
-            const int v = tid + j * NT;
-            if (K::BV % NT == 0 || v < K::BV) *(uint4*)(sBt + (v / (QB / VE)) * LQ + K::bt_col(v / (QB / VE), (v % (QB / VE)) * VE)) = br[j];
+            if (K::CV % NT == 0 || v < K::CV) {
+                const int t = v / (N / VE), c = v % (N / VE);
+                *(uint4*)(sC + t * LC + c * VE) = cr[j];
+                if constexpr (SZ == 2) {
+                    // 8-byte aligned (row offset boff), so two 8-byte writes
+                    TI* d = sB + t * LB + boff(t) + c * VE;
+                    *(uint2*)d = make_uint2(br[j].x, br[j].y);
+                    *(uint2*)(d + 4) = make_uint2(br[j].z, br[j].w);
+                } else {
+                    *(uint4*)(sB + t * LB + c * VE) = br[j];
+                }
+            }
         }
         // per-token scalars, computed by every wave for itself (lane = token)
         const cum_t cum = wave_incl_scan((cum_t)dtv * A2);        // dt = 0 past the row's end
         const cum_t cend = __shfl(cum, QB - 1);
-        const cum_t c16 = __shfl(cum, lane | 15);                // cum at the end of this token's 16-tile
         int nstart = 0;
         int segl = 0;
         cum_t before = 0;
@@ -556,17 +544,19 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
             const uint64_t mask = __ballot(start);
             nstart = __popcll(mask);
             lastseq_c = __shfl(sq, QB - 1);
-            if (nstart > 0) {
+            {
                 const uint64_t upto = (lane == 63) ? ~0ull : ((2ull << lane) - 1ull);
                 segl = __popcll(mask & upto);
-                if (lane < QB) sSeg[w][lane] = segl;
+                if (lane < QB) sSeg[wq][lane] = segl;        // all zero for a single-segment block
+            }
+            if (nstart > 0) {
                 if (start) {
-                    sStart[w][segl] = lane;
-                    sSeqOf[w][segl] = sq;
+                    sStart[wq][segl] = lane;
+                    sSeqOf[wq][segl] = sq;
                 }
                 if (lane == 0) {
-                    sStart[w][0] = 0;
-                    sSeqOf[w][0] = prevseq;
+                    sStart[wq][0] = 0;
+                    sSeqOf[wq][0] = prevseq;
                 }
             }
         }
@@ -575,73 +565,18 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
         const float dtf = EULER ? dtv : 1.f;
         if (lane < QB) {
             sCum[w][lane] = cum;
-            sV[w][lane] = fast_exp2((float)(c16 - cum));
             sWx[w][lane] = fast_exp2((float)(cend - cum)) * dtf;
-            if constexpr (EULER) sDtf[w][lane] = dtv;
+            if constexpr (EULER) sDtf[we][lane] = dtv;
         }
         wave_sync();
         if constexpr (SEQ) {
             if (nstart > 0) {
-                const int a = sStart[w][segl];
+                const int a = sStart[wq][segl];
                 if (a > 0) before = sCum[w][a - 1];
             }
         }
         if (lane < QB) sRow[w][lane] = fast_exp2((float)(cum - before));
 
-        // masked decay times C B^T over the causal tiles, 4 consecutive tokens s per piece:
-        //   diagonal tile:  exp2(cum_t - cum_s) CB[t][s] for s <= t, else 0
-        //   below it:       exp2(cum_t - cum_r) exp2(cum_r - cum_s) CB[t][s], r = last token of s's tile
-        // (times dt_s with Euler input scaling; zero across sequence segments)
-#pragma unroll
-        for (int j = 0; j < K::LMPT; ++j) {
-            const int v = tid + j * NT;
-            if (K::LMU % NT == 0 || v < K::LMU) {
-                const int I = tI[j], J = tJ[j];                 // uniform over the wave
-                const int t = 16 * I + (v % 64) / 4, s0 = 16 * J + 4 * (v % 4);
-                const float cb4[4] = {cbr[j].x, cbr[j].y, cbr[j].z, cbr[j].w};
-                const cum_t ct = sCum[w][t];
-                float val[4];
-                if (I == J) {
-                    cum_t c4[4];
-                    if constexpr (sizeof(cum_t) == 4) {
-                        const float4 cc = *(const float4*)(&sCum[w][s0]);
-                        c4[0] = cc.x; c4[1] = cc.y; c4[2] = cc.z; c4[3] = cc.w;
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) c4[e] = sCum[w][s0 + e];
-                    }
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float lv = fast_exp2((float)(ct - c4[e])) * cb4[e];
-                        val[e] = (s0 + e <= t) ? lv : 0.f;
-                    }
-                } else {
-                    const float ut = fast_exp2((float)(ct - sCum[w][16 * J + 15]));
-                    const float4 v4 = *(const float4*)(&sV[w][s0]);
-                    val[0] = ut * v4.x * cb4[0];
-                    val[1] = ut * v4.y * cb4[1];
-                    val[2] = ut * v4.z * cb4[2];
-                    val[3] = ut * v4.w * cb4[3];
-                }
-                if constexpr (EULER) {
-                    const float4 d4 = *(const float4*)(&sDtf[w][s0]);
-                    val[0] *= d4.x; val[1] *= d4.y; val[2] *= d4.z; val[3] *= d4.w;
-                }
-                if constexpr (SEQ) {
-                    if (nstart > 0) {
-                        const int segt = sSeg[w][t];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (sSeg[w][s0 + e] != segt) val[e] = 0.f;
-                    }
-                }
-                if constexpr (sizeof(TI) == 2) {
-                    *(bf16x4*)(sLm + t * LQ + s0) = bf16x4{(__bf16)val[0], (__bf16)val[1], (__bf16)val[2], (__bf16)val[3]};
-                } else {
-                    *(float4*)(sLm + t * LQ + s0) = make_float4(val[0], val[1], val[2], val[3]);
-                }
-            }
-        }
         // X (row-major) and, for single-segment blocks, the end-state weighted X
 #pragma unroll
         for (int j = 0; j < K::XPT; ++j) {
@@ -667,33 +602,75 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
         }
     };
 
-    auto mfma_phase = [&](int blk) {
+    // ---- this wave's causal tiles of L o CB: C B^T on MFMA (as (C B^T)^T, rows s,
+    //      columns t, so that each lane holds 4 consecutive s of one token t), then
+    //      the masked decay exp2(cum_t - cum_s) for s <= t (else 0) in registers
+    //      (times dt_s with Euler input scaling; zero across sequence segments) and
+    //      one 8- or 16-byte LDS write per lane.  Every wave does TPW tiles; surplus
+    //      slots recompute a tile another wave owns and write the same values.
+    // The values are held in registers (lmv) and written after the state update,
+    // so that no LDS write separates the operand reads of the MFMA phase (the
+    // compiler cannot move a read above a write to the same array).
+    typedef typename std::conditional<SZ == 2, bf16x4, f32x4>::type lm_t;
+    lm_t lmv[K::TPW];
+    auto lm_phase = [&]() {
+#pragma unroll
+        for (int j = 0; j < K::TPW; ++j) {
+            const int I = tI[j], J = tJ[j];                      // uniform over the wave
+            const int t = 16 * I + lr, s0 = 16 * J + 4 * lg;
+            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k = 0; k < NK; ++k)
+                acc = MF::mma(brow_frag<N>(sB, 16 * J + lr, k, lg), crow_frag<N>(sC + t * LC, k, lg), acc);
+            const cum_t ct = sCum[w][t];
+            cum_t cs[4];
+            if constexpr (sizeof(cum_t) == 4) {
+                const float4 c4 = *(const float4*)(&sCum[w][s0]);
+                cs[0] = c4.x; cs[1] = c4.y; cs[2] = c4.z; cs[3] = c4.w;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) cs[e] = sCum[w][s0 + e];
+            }
+            float val[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float lv = fast_exp2((float)(ct - cs[e])) * acc[e];
+                val[e] = (s0 + e <= t) ? lv : 0.f;
+            }
+            if constexpr (EULER) {
+                const float4 d4 = *(const float4*)(&sDtf[we][s0]);
+                val[0] *= d4.x; val[1] *= d4.y; val[2] *= d4.z; val[3] *= d4.w;
+            }
+            if constexpr (SEQ) {
+                const int segt = sSeg[wq][t];
+                const int4 sg = *(const int4*)(&sSeg[wq][s0]);
+                if (sg.x != segt) val[0] = 0.f;
+                if (sg.y != segt) val[1] = 0.f;
+                if (sg.z != segt) val[2] = 0.f;
+                if (sg.w != segt) val[3] = 0.f;
+            }
+            if constexpr (SZ == 2) lmv[j] = bf16x4{(__bf16)val[0], (__bf16)val[1], (__bf16)val[2], (__bf16)val[3]};
+            else lmv[j] = f32x4{val[0], val[1], val[2], val[3]};
+        }
+    };
+    auto lm_store = [&]() {
+#pragma unroll
+        for (int j = 0; j < K::TPW; ++j) *(lm_t*)(sLm + (16 * tI[j] + lr) * LQ + 16 * tJ[j] + 4 * lg) = lmv[j];
+    };
+
+    // ---- MFMA phases, outputs transposed: y^T tiles (rows p0..p0+15, columns t);
+    //      acc holds the scaled read-out of the carried state, then the diagonal block
+    f32x4 acc_o[RT];
+    constexpr int KS = QB / KSTEP;           // K steps over the tokens of a block
+
+    // carried-state read-out and state update (both independent of L o CB)
+    auto state_phase = [&](int blk) {
         const int nstart = nstart_c;
-        // ---- MFMA phase, outputs transposed: y^T tiles (rows p0..p0+15, columns t)
+        const TI* sXr = sXr_of(blk);
         frag sf[NK];
         state_frags<N>(st, sf);
-        f32x4 acc_y[RT], acc_o[RT];
 #pragma unroll
-        for (int r = 0; r < RT; ++r) {
-            acc_y[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-            acc_o[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-        constexpr int KS = QB / KSTEP;           // K steps over the tokens of a block
-        // B^T fragment (state tile m, K step ks): row nrow(m, lr) = nrow(m, 0) + nrow(0, lr),
-        // and the row swizzle depends on the lane only (bit 3 of nrow(0, lr)), so every
-        // fragment is a per-K-step lane base plus a compile-time row offset
-        const TI* bt_lane[KS];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            bt_lane[ks] = sBt + nrow<N>(0, lr) * LQ + K::bt_col(nrow<N>(0, lr), ks * KSTEP + KPL * lg);
-        auto bt_frag = [&](int m, int ks) { return lds_frag<TI>(bt_lane[ks / KSTEP] + nrow<N>(m, 0) * LQ); };
-        // diagonal block: (L o CB) X, as X^T (L o CB)^T; token tile r only needs s < 16 (r + 1)
-#pragma unroll
-        for (int r = 0; r < RT; ++r)
-#pragma unroll
-            for (int ks = 0; ks < 16 * (r + 1); ks += KSTEP)
-                acc_y[r] = MF::mma(x_frag(sXr, LR, ks, p0, lr, lg),
-                                   lds_frag<TI>(sLm + (16 * r + lr) * LQ + ks + KPL * lg), acc_y[r]);
+        for (int r = 0; r < RT; ++r) acc_o[r] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (!SEQ || nstart == 0) {
             // carried state read out by C:  S C^T
 #pragma unroll
@@ -708,22 +685,24 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
 #pragma unroll
             for (int m = 0; m < MT; ++m)
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) st[m] = MF::mma(bt_frag(m, ks * KSTEP), x_frag(sXw, LR, ks * KSTEP, p0, lr, lg), st[m]);
+                for (int ks = 0; ks < KS; ++ks)
+                    st[m] = MF::mma(bt_frag<N>(sB, m, ks * KSTEP, lr, lg), x_frag(sXw, LR, ks * KSTEP, p0, lr, lg), st[m]);
 #pragma unroll
             for (int r = 0; r < RT; ++r) acc_o[r] *= sRow[w][16 * r + lr];
+            if constexpr (!SEQ && SZ == 2) pipeline_lds_mfma<8, K::TPW * NK + RT * NK + MT * KS, 2>();
         } else if constexpr (SEQ) {
             // ---- block with sequence starts, one segment at a time
             // (1) read-out of each segment's incoming state
             for (int j = 0; j <= nstart; ++j) {
-                const int a = sStart[w][j];
-                const int e = (j < nstart) ? sStart[w][j + 1] - 1 : QB - 1;
+                const int a = sStart[wq][j];
+                const int e = (j < nstart) ? sStart[wq][j + 1] - 1 : QB - 1;
                 if (e < a) continue;                         // empty first segment
                 frag f[NK];
                 if (j == 0) {
 #pragma unroll
                     for (int k = 0; k < NK; ++k) f[k] = sf[k];
                 } else if (prm.init) {
-                    global_state_frags<N>(prm.init + (((int64_t)sSeqOf[w][j] * H + h) * P + p0 + lr) * N, lg, f);
+                    global_state_frags<N>(prm.init + (((int64_t)sSeqOf[wq][j] * H + h) * P + p0 + lr) * N, lg, f);
                 } else {
                     continue;                                // a zero initial state reads out nothing
                 }
@@ -733,23 +712,24 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
 #pragma unroll
                     for (int k = 0; k < NK; ++k) tmp = MF::mma(f[k], c_frag<N>(sC + (16 * r + lr) * LC, k, lg), tmp);
                     const int t = 16 * r + lr;
-                    const float sc = (sSeg[w][t] == j) ? sRow[w][t] : 0.f;
+                    const float sc = (sSeg[wq][t] == j) ? sRow[w][t] : 0.f;
                     acc_o[r] += sc * tmp;
                 }
             }
             // (2) state at the end of each segment: a sequence that ends inside
             //     the block hands its state to final_state; the last segment's
             //     state is carried on
-            if (sStart[w][1] == 0) write_state(st, sSeqOf[w][0]);   // previous sequence ended with the previous block
+            if (sStart[wq][1] == 0) write_state(st, sSeqOf[wq][0]);   // previous sequence ended with the previous block
             for (int j = 0; j <= nstart; ++j) {
-                const int a = sStart[w][j];
-                const int e = (j < nstart) ? sStart[w][j + 1] - 1 : QB - 1;
+                const int a = sStart[wq][j];
+                const int e = (j < nstart) ? sStart[wq][j + 1] - 1 : QB - 1;
                 if (e < a) continue;
                 block_sync_lds();                             // the previous segment's weighted X is consumed
                 for (int v = tid; v < P * QB; v += NT) {
                     const int t = v / P, pr = v % P;
-                    const float ws = (sSeg[w][t] == j)
-                        ? fast_exp2((float)(sCum[w][e] - sCum[w][t])) * (EULER ? sDtf[w][t] : 1.f) : 0.f;
+                    float df = 1.f;
+                    if constexpr (EULER) df = sDtf[we][t];
+                    const float ws = (sSeg[wq][t] == j) ? fast_exp2((float)(sCum[w][e] - sCum[w][t])) * df : 0.f;
                     sXw[t * LR + pr] = to_in<TI>(ws * to_f32(sXr[t * LR + pr]));
                 }
                 block_sync_lds();
@@ -760,7 +740,7 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
 #pragma unroll
                     for (int m = 0; m < MT; ++m) F[m] = st[m] * carry;
                 } else if (prm.init) {
-                    const float* src = prm.init + (((int64_t)sSeqOf[w][j] * H + h) * P + p0 + lr) * N;
+                    const float* src = prm.init + (((int64_t)sSeqOf[wq][j] * H + h) * P + p0 + lr) * N;
 #pragma unroll
                     for (int m = 0; m < MT; ++m) {
                         const float4 iv = *(const float4*)(src + nrow<N>(m, 4 * lg));
@@ -773,11 +753,10 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
 #pragma unroll
                 for (int m = 0; m < MT; ++m)
 #pragma unroll
-                    for (int ks = 0; ks < QB; ks += KSTEP)
-                        F[m] = MF::mma(lds_frag<TI>(sBt + nrow<N>(m, lr) * LQ + K::bt_col(nrow<N>(m, lr), ks + KPL * lg)),
-                                       x_frag(sXw, LR, ks, p0, lr, lg), F[m]);
+                    for (int ks = 0; ks < KS; ++ks)
+                        F[m] = MF::mma(bt_frag<N>(sB, m, ks * KSTEP, lr, lg), x_frag(sXw, LR, ks * KSTEP, p0, lr, lg), F[m]);
                 if (j < nstart) {
-                    write_state(F, sSeqOf[w][j]);
+                    write_state(F, sSeqOf[wq][j]);
                 } else {
 #pragma unroll
                     for (int m = 0; m < MT; ++m) st[m] = F[m];
@@ -787,18 +766,28 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
             // common path's wait counts stay exact (prefetches stay in flight).
             __builtin_amdgcn_s_waitcnt(0);
         }
+    };
 
-        // ---- y = read-out + diagonal block + D x: lane holds y[t = 16r + lr][p0 + 4lg .. +3],
-        //      one 16-byte store per token tile (past-the-end tokens are dropped by the range check)
+    // diagonal block (L o CB) X, as X^T (L o CB)^T (token tile r only needs s < 16 (r + 1)),
+    // then y = read-out + diagonal block + D x: lane holds y[t = 16r + lr][p0 + 4lg .. +3],
+    // one 16-byte store per token tile (past-the-end tokens are dropped by the range check)
+    auto diag_phase = [&](int blk) {
+        const TI* sXr = sXr_of(blk);
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+#pragma unroll
+            for (int ks = 0; ks < 16 * (r + 1); ks += KSTEP)
+                acc_o[r] = MF::mma(x_frag(sXr, LR, ks, p0, lr, lg),
+                                   lds_frag<TI>(sLm + (16 * r + lr) * LQ + ks + KPL * lg), acc_o[r]);
         const int64_t t0 = (int64_t)blk * QB;
         const rsrc_t ry = make_rsrc(yrow + t0 * ys, yrec - t0 * ys);
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
             const int t = 16 * r + lr;
-            f32x4 out = acc_o[r] + acc_y[r];
+            f32x4 out = acc_o[r];
             {
                 float xv[4];
-                if constexpr (sizeof(TI) == 2) {
+                if constexpr (SZ == 2) {
                     const bf16x4 x4 = *(const bf16x4*)(sXr + t * LR + p0 + 4 * lg);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) xv[i] = (float)x4[i];
@@ -824,9 +813,15 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
     __builtin_amdgcn_s_waitcnt(0);
     for (int blk = 0; blk < nblk; ++blk) {
         if (blk + 1 < nblk) issue(blk + 1);
-        mfma_phase(blk);
+        lm_phase();
+        state_phase(blk);
+        lm_store();
+        // every wave's tiles of L o CB are written, and block blk's C, B, weighted X
+        // and per-token scalars are no longer read: block blk+1 may be staged
+        // (its X into the other buffer) while the diagonal product reads block blk
+        block_sync_lds();
+        diag_phase(blk);
         if (blk + 1 < nblk) {
-            block_sync_lds();        // block blk's tiles are no longer read
             prep(blk + 1);
             block_sync_lds();        // block blk+1's tiles are complete
         }

@@ -5,13 +5,10 @@
 #include <stdint.h>
 
 namespace ssd {
-struct PrepParams;
 struct ScanParams;
 
 // Return hipSuccess, hipErrorInvalidValue for a shape with no instantiation,
 // or the launch error.
-hipError_t launch_prep_bf16(int N, int QB, const PrepParams& prm, int64_t grid, hipStream_t s);
-hipError_t launch_prep_f32(int N, int QB, const PrepParams& prm, int64_t grid, hipStream_t s);
 // seq: sequence ids present (segment handling compiled in); euler: dt scales x
 hipError_t launch_scan_bf16(int P, int N, int QB, bool seq, bool euler, const ScanParams& prm, int64_t grid,
                             hipStream_t s);

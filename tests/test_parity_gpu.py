@@ -174,18 +174,18 @@ def test_sequences_do_not_leak():
     np.testing.assert_array_equal(f[2], f2[2])
 
 
-def test_prepare_then_scan_equals_forward():
+def test_forward_into_preallocated_outputs():
+    """The raw entry point on caller-owned outputs, with no workspace, equals forward()."""
     import mamba_ssd_scan_chunked_amd as ssd
     prob = si.make_problem(2, 160, 4, 64, 128, 2, dtype="bf16", seed=71, d_skip=True, init_std=0.5)
     d = to_device(prob)
-    announce("prepare+scan")
+    announce("forward_into")
     y1, f1 = ssd.forward(d["x"], d["dt"], d["A_log"], d["B"], d["C"], d["D"], chunk_len=64, init_state=d["init"])
     p = ssd.problem(2, 160, 4, 64, 128, 2, 64, 2, ssd.DTYPE_BF16, 0)
-    ws = torch.empty(ssd.workspace_size(p), dtype=torch.uint8, device="cuda")
+    assert ssd.workspace_size(p) == 0
     y2 = torch.empty_like(y1)
     f2 = torch.empty_like(f1)
-    ssd.prepare(p, d["B"], d["C"], ws)
-    ssd.scan(p, d["x"], d["dt"], d["A_log"], d["C"], d["D"], d["init"], None, y2, f2, ws)
+    ssd.forward_into(p, d["x"], d["dt"], d["A_log"], d["B"], d["C"], d["D"], d["init"], None, y2, f2, None)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2) and torch.equal(f1, f2)
 
