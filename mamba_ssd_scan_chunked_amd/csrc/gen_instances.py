@@ -13,7 +13,7 @@ def gen(tag, TI, Ps, Ns, QBs, seq, eul):
     for P in Ps:
         for N in Ns:
             for Q in QBs:
-                out.append("    if (P == %d && N == %d && QB == %d) { hipLaunchKernelGGL((ssd_scan_kernel<%s, %d, %d, %d, %s, %s>), dim3((unsigned)grid), dim3(%d), 0, s, prm); return hipGetLastError(); }\n" % (P, N, Q, TI, P, N, Q, "true" if seq else "false", "true" if eul else "false", P // 16 * 64))
+                out.append("    if (P == %d && N == %d && QB == %d) { hipLaunchKernelGGL((ssd_scan_kernel<%s, %d, %d, %d, %s, %s>), dim3((unsigned)grid), dim3(ScanCfg<%s, %d, %d, %d>::NT), 0, s, prm); return hipGetLastError(); }\n" % (P, N, Q, TI, P, N, Q, "true" if seq else "false", "true" if eul else "false", TI, P, N, Q))
     out.append("    return hipErrorInvalidValue;\n}\n}  // namespace ssd\n")
     return "".join(out)
 

@@ -133,9 +133,8 @@ int launch_scan(const ssd_problem_t* p, const void* x, const float* dt, const fl
                        ? ssd::launch_scan_bf16((int)p->headdim, (int)p->dstate, q, seq, euler, prm, grid, stream)
                        : ssd::launch_scan_f32((int)p->headdim, (int)p->dstate, q, seq, euler, prm, grid, stream);
     if (log_enabled())
-        std::fprintf(stderr, "[ssd] scan dtype=%d P=%lld N=%lld QB=%d grid=%lld block=%lld -> %s\n", p->dtype,
-                     (long long)p->headdim, (long long)p->dstate, q, (long long)grid,
-                     (long long)(p->headdim / 16 * 64), hipGetErrorString(e));
+        std::fprintf(stderr, "[ssd] scan dtype=%d P=%lld N=%lld QB=%d grid=%lld -> %s\n", p->dtype,
+                     (long long)p->headdim, (long long)p->dstate, q, (long long)grid, hipGetErrorString(e));
     return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
 }
 

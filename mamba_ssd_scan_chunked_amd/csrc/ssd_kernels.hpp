@@ -96,11 +96,13 @@ template <typename TI, int N> struct OffK {
     static constexpr int NK = N / Mfma<TI>::KSTEP;
 };
 
-// B-operand fragments of the read-out from the state accumulators.
-template <int N>
-__device__ inline void state_frags(const f32x4 (&st)[N / 16], bf16x8 (&sf)[N / 32]) {
+// B-operand fragments of the read-out from MT state accumulator tiles (a whole
+// state or the half a wave owns): bf16 tile pair (2k, 2k+1) is fragment k;
+// fp32 element i of tile m is fragment 4m + i.
+template <int MT>
+__device__ inline void state_frags(const f32x4 (&st)[MT], bf16x8 (&sf)[MT / 2]) {
 #pragma unroll
-    for (int k = 0; k < N / 32; ++k) {
+    for (int k = 0; k < MT / 2; ++k) {
         bf16x8 f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -110,10 +112,10 @@ __device__ inline void state_frags(const f32x4 (&st)[N / 16], bf16x8 (&sf)[N / 3
         sf[k] = f;
     }
 }
-template <int N>
-__device__ inline void state_frags(const f32x4 (&st)[N / 16], float (&sf)[N / 4]) {
+template <int MT>
+__device__ inline void state_frags(const f32x4 (&st)[MT], float (&sf)[4 * MT]) {
 #pragma unroll
-    for (int m = 0; m < N / 16; ++m)
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int i = 0; i < 4; ++i) sf[4 * m + i] = st[m][i];
 }
@@ -164,22 +166,9 @@ __device__ inline float x_frag(const float* sX, int lp, int ks, int p0, int lr, 
     return sX[(ks + lg) * lp + p0 + lr];
 }
 
-// B tile in LDS, bf16: row t holds the N values of token t at element offset
-// t * bpitch(N) + boff(t).  A transposing read of the state update has each
-// half-wave touch 8 token rows (t0 .. t0+3 and t0+8 .. t0+11) and, in each, four
-// 8-byte chunks spaced 16 bytes apart; with a row pitch of 8 or 24 (mod 32)
-// chunks and one extra chunk for rows with bit 3 of t set, those 8 rows start
-// on chunk offsets {0, 8, 16, 24} and {1, 9, 17, 25} (mod 32) and the 32
-// chunks cover all 64 banks once.  The offsets are additive, so every
-// fragment is a per-lane base plus a compile-time immediate.  fp32 tiles use
-// a plain padded pitch.
-template <int N>
-constexpr int bpitch() {
-    int c = N / 4 + 1;
-    while (c % 32 != 8 && c % 32 != 24) ++c;
-    return 4 * c;
-}
-__device__ inline int boff(int t) { return 4 * ((t >> 3) & 1); }
+// B tile in LDS: row t holds the N values of token t, pitch LB = N + 4
+// elements (8-byte aligned rows for bf16).  The transposing reads of the state
+// update and the row reads of C B^T see at most 2-way bank conflicts.
 
 // A operand of the state update for state tile m and the K step of tokens
 // ks .. ks+KSTEP-1: row rho = l % 16 is state row n = nrow(m, rho), K values are
@@ -187,33 +176,30 @@ __device__ inline int boff(int t) { return 4 * ((t >> 3) & 1); }
 // token-major B tile; lane j of each 16-lane group loads the four values
 // n = nrow(m, 4(j%4)) .. +3 of token ks + 8(l/16) + j/4 (+4 for the second read)
 // and the hardware hands lane i row nrow(m, i) of those four tokens.
-template <int N>
+template <int N, int LB>
 __device__ inline bf16x8 bt_frag(const __bf16* sB, int m, int ks, int lr, int lg) {
-    constexpr int LB = bpitch<N>();
-    const int t0 = ks + 8 * lg + (lr >> 2);
-    const __bf16* lo = sB + t0 * LB + boff(t0) + nrow<N>(m, 4 * (lr & 3));
+    const __bf16* lo = sB + (ks + 8 * lg + (lr >> 2)) * LB + nrow<N>(m, 4 * (lr & 3));
     const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)lo);
     const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(lo + 4 * LB));
     return __builtin_shufflevector(__builtin_bit_cast(bf16x4, a), __builtin_bit_cast(bf16x4, b), 0, 1, 2, 3, 4, 5, 6, 7);
 }
-template <int N>
+template <int N, int LB>
 __device__ inline float bt_frag(const float* sB, int m, int ks, int lr, int lg) {
-    return sB[(ks + lg) * (N + 4) + nrow<N>(m, lr)];
+    return sB[(ks + lg) * LB + nrow<N>(m, lr)];
 }
 
 // Operand of C B^T holding B row s at the K indices n of step k (natural order):
 // bf16 n = 32k + 8(l/16) .. +7 (two 8-byte reads); fp32 n = 4k + l/16.
-template <int N>
+template <int N, int LB>
 __device__ inline bf16x8 brow_frag(const __bf16* sB, int s, int k, int lg) {
-    constexpr int LB = bpitch<N>();
-    const __bf16* r = sB + s * LB + boff(s) + 32 * k + 8 * lg;
+    const __bf16* r = sB + s * LB + 32 * k + 8 * lg;
     const bf16x4 a = *(const bf16x4*)r;
     const bf16x4 b = *(const bf16x4*)(r + 4);
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
-template <int N>
+template <int N, int LB>
 __device__ inline float brow_frag(const float* sB, int s, int k, int lg) {
-    return sB[s * (N + 4) + 4 * k + lg];
+    return sB[s * LB + 4 * k + lg];
 }
 // Operand of C B^T holding C row t at the same K indices (natural order).
 template <int N>
@@ -330,69 +316,94 @@ __device__ inline double wave_incl_scan(double x) {
 
 template <typename TI, int P, int N, int QB>
 struct ScanCfg {
-    static constexpr int NW = P / 16;                 // waves; wave w owns channels 16w .. 16w+15
-    static constexpr int NT = NW * 64;
     static constexpr int SZ = (int)sizeof(TI);
     static constexpr int VE = 16 / SZ;                // elements per 16-byte vector
+    static constexpr int KPL = Mfma<TI>::KPL, KSTEP = Mfma<TI>::KSTEP;
+    static constexpr int NK = OffK<TI, N>::NK;        // K steps of the read-out over the state dimension
+    static constexpr int RT = QB / 16;                // token tiles of a block
+    static constexpr int MT = N / 16;                 // state tiles of one 16-channel slice
+    static constexpr int NPT = P / 16;                // 16-channel slices of a head
+    // Each slice is shared by NH waves: wave (slice pt, half nh) owns state tiles
+    // [nh MT/NH, (nh+1) MT/NH) (whole K steps of the read-out) and token tiles
+    // own_tile(nh, i) of the outputs.
+    static constexpr int NH = (SZ == 2 ? MT % 4 == 0 : MT % 2 == 0) && RT % 2 == 0 ? 2 : 1;
+    static constexpr int NW = NPT * NH;
+    static constexpr int NT = NW * 64;
+    static constexpr int WPE = NW >= 8 ? NW / 2 : 2;   // waves per SIMD for two workgroups per CU
+    static constexpr int MTH = MT / NH, NKH = NK / NH, RTH = RT / NH;
     static constexpr int LC = N + VE;                 // pitch of C rows (elements)
-    static constexpr int LB = SZ == 2 ? bpitch<N>() : N + 4;   // pitch of B rows (see bpitch)
+    static constexpr int LB = N + 4;                  // pitch of B rows
     static constexpr int LQ = QB + VE;                // pitch of the rows of L o CB (indexed by token s)
     static constexpr int LR = P + 32 / SZ;            // pitch of the row-major X tiles (32 bytes of pad:
                                                       // the four rows of a transposed read fall in
                                                       // distinct banks)
-    static constexpr int KPL = Mfma<TI>::KPL, KSTEP = Mfma<TI>::KSTEP;
-    static constexpr int NK = OffK<TI, N>::NK;        // K steps over the state dimension
-    static constexpr int RT = QB / 16;                // token tiles of a block
-    static constexpr int MT = N / 16;                 // state tiles per wave
     static constexpr int NTILE = RT * (RT + 1) / 2;   // causal 16x16 tiles of L o CB
     static constexpr int TPW = (NTILE + NW - 1) / NW; // causal tiles per wave (surplus slots repeat a tile)
-    // LDS tiles: C, B (both token-major), masked decay L o CB, X (row-major, two
-    // buffers: block k+1 is staged while the diagonal product of block k reads
-    // block k) and the end-state-weighted X
+    // LDS tiles: C, B (both token-major), masked decay L o CB, X and end-state-weighted X
+    // (row-major) and, with NH = 2, each wave's half of the state as read-out operands
     static constexpr int OFF_C = 0;
     static constexpr int OFF_B = OFF_C + QB * LC;
     static constexpr int OFF_LM = OFF_B + QB * LB;
     static constexpr int OFF_XR = OFF_LM + QB * LQ;
-    static constexpr int OFF_XW = OFF_XR + 2 * QB * LR;
-    static constexpr int BUF_ELEMS = OFF_XW + QB * LR;
+    static constexpr int OFF_XW = OFF_XR + QB * LR;
+    static constexpr int OFF_SX = OFF_XW + QB * LR;
+    static constexpr int BUF_ELEMS = OFF_SX + (NH > 1 ? NW * NKH * 64 * KPL : 0);
     // per-thread work units
     static constexpr int CV = QB * N / VE, CPT = (CV + NT - 1) / NT;           // C (and B) tile vectors
     static constexpr int XC = 8 / SZ;                                          // channels per 8 bytes
     static constexpr int XU = (QB / 4) * (P / XC), XPT = (XU + NT - 1) / NT;   // (4 tokens, XC channels) of X
+    // token tile i of the outputs of half nh: the causal work of the diagonal
+    // block is split evenly ({0, 3} and {1, 2} of four tiles)
+    __device__ static inline int own_tile(int nh, int i) {
+        if constexpr (NH == 1) return i;
+        else if constexpr (RT == 2) return nh;
+        else return i == 0 ? nh : 3 - nh;
+    }
 };
 
 template <typename TI, int P, int N, int QB, bool SEQ, bool EULER>
-__global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
+__global__ __attribute__((amdgpu_flat_work_group_size(1, ScanCfg<TI, P, N, QB>::NT),
+                          amdgpu_waves_per_eu(ScanCfg<TI, P, N, QB>::WPE)))
+void ssd_scan_kernel(ScanParams prm) {
     typedef ScanCfg<TI, P, N, QB> K;
     typedef Mfma<TI> MF;
     typedef typename MF::frag frag;
     typedef typename CumType<TI>::type cum_t;
     constexpr int NT = K::NT, VE = K::VE, LC = K::LC, LB = K::LB, LQ = K::LQ, LR = K::LR, KPL = K::KPL;
     constexpr int KSTEP = K::KSTEP, SZ = K::SZ, NK = K::NK, RT = K::RT, MT = K::MT, NW = K::NW, XC = K::XC;
+    constexpr int NH = K::NH, NPT = K::NPT, MTH = K::MTH, NKH = K::NKH, RTH = K::RTH;
+    constexpr int NFH = SZ == 2 ? MTH / 2 : 4 * MTH;               // read-out fragments of a state half
+    static_assert(NFH == NKH, "fragments of a state half are whole K steps");
     static_assert(QB <= 64 && QB % KSTEP == 0 && QB % 16 == 0, "block length");
     static_assert(N % KSTEP == 0 && N % 16 == 0 && P % 16 == 0 && P % XC == 0, "shape");
 
     __shared__ __attribute__((aligned(16))) TI smem[K::BUF_ELEMS];
-    // per-wave copies of the block's per-token scalars (each wave computes its own)
-    constexpr int SQW = SEQ ? NW : 1, EUW = EULER ? NW : 1;        // arrays only the variant uses
-    __shared__ __attribute__((aligned(16))) cum_t sCum[NW][64];   // cumulative log2 decay
-    __shared__ __attribute__((aligned(16))) float sRow[NW][64];   // read-out row scale
-    __shared__ __attribute__((aligned(16))) float sWx[NW][64];    // end-state weight exp2(cum_end - cum) (dt)
-    __shared__ __attribute__((aligned(16))) float sDtf[EUW][64];  // dt (Euler input scaling)
-    __shared__ __attribute__((aligned(16))) int sSeg[SQW][64];    // segment of each token
-    __shared__ int sStart[SQW][65];
-    __shared__ int sSeqOf[SQW][65];
-    const int wq = SEQ ? (int)(threadIdx.x >> 6) : 0, we = EULER ? (int)(threadIdx.x >> 6) : 0;
+    // per-token scalars of the block, shared by all waves (written by wave 0)
+    constexpr int SQ = SEQ ? 1 : 0, EU = EULER ? 1 : 0;
+    __shared__ __attribute__((aligned(16))) cum_t sCum[64];       // cumulative log2 decay
+    __shared__ __attribute__((aligned(16))) float sRow[64];       // read-out row scale
+    __shared__ __attribute__((aligned(16))) float sDtf[64 * EU + 4];   // dt (Euler input scaling)
+    __shared__ __attribute__((aligned(16))) int sSeg[64 * SQ + 4];     // segment of each token
+    __shared__ int sStart[65 * SQ + 1];
+    __shared__ int sSeqOf[65 * SQ + 1];
 
     TI* sC = smem + K::OFF_C;
     TI* sB = smem + K::OFF_B;
     TI* sLm = smem + K::OFF_LM;
-    auto sXr_of = [&](int blk) { return smem + K::OFF_XR + (blk & 1) * QB * K::LR; };
+    TI* sXr = smem + K::OFF_XR;
     TI* sXw = smem + K::OFF_XW;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: wave-level values stay scalar
     const int lr = lane & 15, lg = lane >> 4;
+    const int pt = w % NPT, nh = w / NPT;
+    const int p0 = 16 * pt;
+    const int mb = nh * MTH;                  // first state tile this wave owns
+    const int kbo = nh * NKH, kbp = (1 - nh) * NKH;   // read-out K steps of its half and of the partner's
+    // this wave's and its partner's read-out fragments in the exchange area (16-byte slots per lane)
+    TI* sxo = smem + K::OFF_SX + ((pt * NH + nh) * NKH * 64 + lane) * KPL;
+    const TI* sxp = smem + K::OFF_SX + ((pt * NH + (NH - 1 - nh)) * NKH * 64 + lane) * KPL;
 
     // Work-item order: runs of consecutive (row, head) items go to the same
     // XCD (workgroups are dealt round-robin over the 8 XCDs), so the heads of
@@ -404,7 +415,6 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
     const int64_t g = h / (prm.H / prm.G);
     const int64_t T = prm.T, H = prm.H, G = prm.G;
     const int nblk = prm.nblk;
-    const int p0 = 16 * w;
 
     // A_h in log2 units, so that every decay is exp2 of a cumulative sum
     cum_t A2;
@@ -426,27 +436,37 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
     const int64_t xrec = ((T - 1) * H + 1) * P * SZ, yrec = ((T - 1) * H + 1) * P * 4;
     const int64_t crec = ((T - 1) * G + 1) * N * SZ, drec = ((T - 1) * H + 1) * 4;
 
-    // ---- initial state of the row's first sequence (S^T tiles, rows nrow(m, 4*lg+i))
+    // ---- initial state of the row's first sequence: this wave's tiles of S^T,
+    //      rows nrow(mb + j, 4*lg+i) of channel p0 + lr
     int prevseq = (int)b;
     if (SEQ && T > 0) prevseq = clamp_seq(seqg[0]);
-    f32x4 st[MT];
+    f32x4 st[MTH];
     if (prm.init) {
         const float* src = prm.init + (((int64_t)prevseq * H + h) * P + p0 + lr) * N;
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            const float4 v = *(const float4*)(src + nrow<N>(m, 4 * lg));
-            st[m] = f32x4{v.x, v.y, v.z, v.w};
+        for (int j = 0; j < MTH; ++j) {
+            const float4 v = *(const float4*)(src + nrow<N>(mb + j, 4 * lg));
+            st[j] = f32x4{v.x, v.y, v.z, v.w};
         }
     } else {
 #pragma unroll
-        for (int m = 0; m < MT; ++m) st[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < MTH; ++j) st[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    auto write_state = [&](const f32x4 (&s)[MT], int seq) {
+    auto write_state = [&](const f32x4 (&s)[MTH], int seq) {
         if (!prm.fin) return;
         float* dst = prm.fin + (((int64_t)seq * H + h) * P + p0 + lr) * N;
 #pragma unroll
-        for (int m = 0; m < MT; ++m)
-            *(float4*)(dst + nrow<N>(m, 4 * lg)) = make_float4(s[m][0], s[m][1], s[m][2], s[m][3]);
+        for (int j = 0; j < MTH; ++j)
+            *(float4*)(dst + nrow<N>(mb + j, 4 * lg)) = make_float4(s[j][0], s[j][1], s[j][2], s[j][3]);
+    };
+    // this wave's half of the state, as read-out operands, for its partner
+    auto sx_store = [&]() {
+        if constexpr (NH > 1) {
+            frag f[NKH];
+            state_frags<MTH>(st, f);
+#pragma unroll
+            for (int j = 0; j < NKH; ++j) *(frag*)(sxo + j * 64 * KPL) = f[j];
+        }
     };
 
     // The upper 16x16 tile next to an even diagonal tile is read by a 32-wide
@@ -458,7 +478,7 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
         }
     }
     // Causal tiles (row tile I, column tile J <= I) of L o CB computed by this
-    // wave: q = w, w + NW, ..., q = I (I + 1) / 2 + J.
+    // wave: q = w, w + NW, ... (mod NTILE), q = I (I + 1) / 2 + J.
     int tI[K::TPW], tJ[K::TPW];
 #pragma unroll
     for (int j = 0; j < K::TPW; ++j) {
@@ -470,7 +490,7 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
     }
 
     // ---- one block of loads, issued at the top of an iteration and consumed
-    // at its bottom (after the MFMA phase of the previous block), so no load
+    // at its bottom (after the MFMA phases of the previous block), so no load
     // result lives across the loop back-edge and the wait counts stay exact.
     uint4 cr[K::CPT], br[K::CPT];
     uint2 xr[K::XPT][4];
@@ -508,10 +528,11 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
     float cend_f = 0.f;
 
     // ---- preparation of a block from the issued loads: tiles into LDS, the
-    //      within-block cumulative decay, segments, X and weighted X
+    //      within-block cumulative decay, segments, X and weighted X.  Every wave
+    //      computes the per-token scalars in registers (lane = token); wave 0
+    //      publishes them for the MFMA phases.
     auto prep = [&](int blk) {
         const int rows = (int)min((int64_t)QB, T - (int64_t)blk * QB);
-        TI* sXr = sXr_of(blk);
 #pragma unroll
         for (int j = 0; j < K::CPT; ++j) {
             const int v = tid + j * NT;
@@ -519,8 +540,7 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
                 const int t = v / (N / VE), c = v % (N / VE);
                 *(uint4*)(sC + t * LC + c * VE) = cr[j];
                 if constexpr (SZ == 2) {
-                    // 8-byte aligned (row offset boff), so two 8-byte writes
-                    TI* d = sB + t * LB + boff(t) + c * VE;
+                    TI* d = sB + t * LB + c * VE;          // 8-byte aligned rows
                     *(uint2*)d = make_uint2(br[j].x, br[j].y);
                     *(uint2*)(d + 4) = make_uint2(br[j].z, br[j].w);
                 } else {
@@ -528,11 +548,9 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
                 }
             }
         }
-        // per-token scalars, computed by every wave for itself (lane = token)
         const cum_t cum = wave_incl_scan((cum_t)dtv * A2);        // dt = 0 past the row's end
         const cum_t cend = __shfl(cum, QB - 1);
         int nstart = 0;
-        int segl = 0;
         cum_t before = 0;
         if constexpr (SEQ) {
             const int raw = clamp_seq(sqv);
@@ -544,57 +562,53 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
             const uint64_t mask = __ballot(start);
             nstart = __popcll(mask);
             lastseq_c = __shfl(sq, QB - 1);
-            {
-                const uint64_t upto = (lane == 63) ? ~0ull : ((2ull << lane) - 1ull);
-                segl = __popcll(mask & upto);
-                if (lane < QB) sSeg[wq][lane] = segl;        // all zero for a single-segment block
-            }
-            if (nstart > 0) {
+            const uint64_t upto = (lane == 63) ? ~0ull : ((2ull << lane) - 1ull);
+            const uint64_t mine = mask & upto;
+            const int segl = __popcll(mine);
+            const int a = mine ? 63 - __clzll(mine) : 0;         // first token of this token's segment
+            const cum_t cprev = __shfl(cum, a > 0 ? a - 1 : 0);
+            before = a > 0 ? cprev : (cum_t)0;
+            if (w == 0) {
+                if (lane < QB) sSeg[lane] = segl;                // all zero for a single-segment block
                 if (start) {
-                    sStart[wq][segl] = lane;
-                    sSeqOf[wq][segl] = sq;
+                    sStart[segl] = lane;
+                    sSeqOf[segl] = sq;
                 }
                 if (lane == 0) {
-                    sStart[wq][0] = 0;
-                    sSeqOf[wq][0] = prevseq;
+                    sStart[0] = 0;
+                    sSeqOf[0] = prevseq;
                 }
             }
         }
         nstart_c = nstart;
         cend_f = (float)cend;
         const float dtf = EULER ? dtv : 1.f;
-        if (lane < QB) {
-            sCum[w][lane] = cum;
-            sWx[w][lane] = fast_exp2((float)(cend - cum)) * dtf;
-            if constexpr (EULER) sDtf[we][lane] = dtv;
+        const float wx = fast_exp2((float)(cend - cum)) * dtf;  // end-state weight of token lane
+        if (w == 0 && lane < QB) {
+            sCum[lane] = cum;
+            sRow[lane] = fast_exp2((float)(cum - before));
+            if constexpr (EULER) sDtf[lane] = dtv;
         }
-        wave_sync();
-        if constexpr (SEQ) {
-            if (nstart > 0) {
-                const int a = sStart[wq][segl];
-                if (a > 0) before = sCum[w][a - 1];
-            }
-        }
-        if (lane < QB) sRow[w][lane] = fast_exp2((float)(cum - before));
 
         // X (row-major) and, for single-segment blocks, the end-state weighted X
 #pragma unroll
         for (int j = 0; j < K::XPT; ++j) {
             const int v = tid + j * NT;
+            const int q4 = v / (P / XC), c4 = v % (P / XC);
+            const int t0l = 4 * q4;
+            float wv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) wv[e] = __shfl(wx, (t0l + e) & 63);
             if (K::XU % NT == 0 || v < K::XU) {
-                const int q4 = v / (P / XC), c4 = v % (P / XC);
-                const int t0l = 4 * q4;
-                const float4 w4 = *(const float4*)(&sWx[w][t0l]);
-                const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     *(uint2*)(sXr + (t0l + e) * LR + c4 * XC) = xr[j][e];
                     if (!SEQ || nstart == 0) {
-                        TI wx[XC];
+                        TI wxv[XC];
 #pragma unroll
-                        for (int k = 0; k < XC; ++k) wx[k] = to_in<TI>(wv[e] * to_f32(((const TI*)&xr[j][e])[k]));
+                        for (int k = 0; k < XC; ++k) wxv[k] = to_in<TI>(wv[e] * to_f32(((const TI*)&xr[j][e])[k]));
                         uint2 pk;
-                        __builtin_memcpy(&pk, wx, 8);
+                        __builtin_memcpy(&pk, wxv, 8);
                         *(uint2*)(sXw + (t0l + e) * LR + c4 * XC) = pk;
                     }
                 }
@@ -605,12 +619,11 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
     // ---- this wave's causal tiles of L o CB: C B^T on MFMA (as (C B^T)^T, rows s,
     //      columns t, so that each lane holds 4 consecutive s of one token t), then
     //      the masked decay exp2(cum_t - cum_s) for s <= t (else 0) in registers
-    //      (times dt_s with Euler input scaling; zero across sequence segments) and
-    //      one 8- or 16-byte LDS write per lane.  Every wave does TPW tiles; surplus
-    //      slots recompute a tile another wave owns and write the same values.
-    // The values are held in registers (lmv) and written after the state update,
-    // so that no LDS write separates the operand reads of the MFMA phase (the
-    // compiler cannot move a read above a write to the same array).
+    //      (times dt_s with Euler input scaling; zero across sequence segments).
+    //      Surplus slots recompute a tile another wave owns and write the same values.
+    //      The values are held in registers and written after the state update, so
+    //      that no LDS write separates the operand reads of the MFMA phase (the
+    //      compiler cannot move a read above a write to the same array).
     typedef typename std::conditional<SZ == 2, bf16x4, f32x4>::type lm_t;
     lm_t lmv[K::TPW];
     auto lm_phase = [&]() {
@@ -621,29 +634,29 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
             f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int k = 0; k < NK; ++k)
-                acc = MF::mma(brow_frag<N>(sB, 16 * J + lr, k, lg), crow_frag<N>(sC + t * LC, k, lg), acc);
-            const cum_t ct = sCum[w][t];
-            cum_t cs[4];
+                acc = MF::mma(brow_frag<N, LB>(sB, 16 * J + lr, k, lg), crow_frag<N>(sC + t * LC, k, lg), acc);
+            const cum_t ct = sCum[t];
+            cum_t csv[4];
             if constexpr (sizeof(cum_t) == 4) {
-                const float4 c4 = *(const float4*)(&sCum[w][s0]);
-                cs[0] = c4.x; cs[1] = c4.y; cs[2] = c4.z; cs[3] = c4.w;
+                const float4 c4 = *(const float4*)(&sCum[s0]);
+                csv[0] = c4.x; csv[1] = c4.y; csv[2] = c4.z; csv[3] = c4.w;
             } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) cs[e] = sCum[w][s0 + e];
+                for (int e = 0; e < 4; ++e) csv[e] = sCum[s0 + e];
             }
             float val[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float lv = fast_exp2((float)(ct - cs[e])) * acc[e];
+                const float lv = fast_exp2((float)(ct - csv[e])) * acc[e];
                 val[e] = (s0 + e <= t) ? lv : 0.f;
             }
             if constexpr (EULER) {
-                const float4 d4 = *(const float4*)(&sDtf[we][s0]);
+                const float4 d4 = *(const float4*)(&sDtf[s0]);
                 val[0] *= d4.x; val[1] *= d4.y; val[2] *= d4.z; val[3] *= d4.w;
             }
             if constexpr (SEQ) {
-                const int segt = sSeg[wq][t];
-                const int4 sg = *(const int4*)(&sSeg[wq][s0]);
+                const int segt = sSeg[t];
+                const int4 sg = *(const int4*)(&sSeg[s0]);
                 if (sg.x != segt) val[0] = 0.f;
                 if (sg.y != segt) val[1] = 0.f;
                 if (sg.z != segt) val[2] = 0.f;
@@ -658,108 +671,123 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
         for (int j = 0; j < K::TPW; ++j) *(lm_t*)(sLm + (16 * tI[j] + lr) * LQ + 16 * tJ[j] + 4 * lg) = lmv[j];
     };
 
-    // ---- MFMA phases, outputs transposed: y^T tiles (rows p0..p0+15, columns t);
-    //      acc holds the scaled read-out of the carried state, then the diagonal block
-    f32x4 acc_o[RT];
+    // ---- MFMA phases, outputs transposed: y^T tiles (rows p0..p0+15, columns t) of
+    //      this wave's token tiles; acc holds the scaled read-out of the carried state,
+    //      then the diagonal block
+    f32x4 acc[RTH];
     constexpr int KS = QB / KSTEP;           // K steps over the tokens of a block
 
-    // carried-state read-out and state update (both independent of L o CB)
-    auto state_phase = [&](int blk) {
+    // read-out of the carried state over all N (this wave's half from its registers,
+    // the partner's from the exchange area) and the update of this wave's half
+    auto state_phase = [&]() {
         const int nstart = nstart_c;
-        const TI* sXr = sXr_of(blk);
-        frag sf[NK];
-        state_frags<N>(st, sf);
+        frag sfo[NKH], sfp[NKH];
+        state_frags<MTH>(st, sfo);
+        if constexpr (NH > 1) {
 #pragma unroll
-        for (int r = 0; r < RT; ++r) acc_o[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < NKH; ++j) sfp[j] = *(const frag*)(sxp + j * 64 * KPL);
+        }
+#pragma unroll
+        for (int i = 0; i < RTH; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (!SEQ || nstart == 0) {
             // carried state read out by C:  S C^T
 #pragma unroll
-            for (int r = 0; r < RT; ++r)
+            for (int i = 0; i < RTH; ++i) {
+                const TI* crw = sC + (16 * K::own_tile(nh, i) + lr) * LC;
 #pragma unroll
-                for (int k = 0; k < NK; ++k)
-                    acc_o[r] = MF::mma(sf[k], c_frag<N>(sC + (16 * r + lr) * LC, k, lg), acc_o[r]);
+                for (int j = 0; j < NKH; ++j) acc[i] = MF::mma(sfo[j], c_frag<N>(crw, kbo + j, lg), acc[i]);
+                if constexpr (NH > 1) {
+#pragma unroll
+                    for (int j = 0; j < NKH; ++j) acc[i] = MF::mma(sfp[j], c_frag<N>(crw, kbp + j, lg), acc[i]);
+                }
+            }
             // state <- exp(cum_end) state + B^T (weighted X)
             const float alpha = fast_exp2(cend_f);
 #pragma unroll
-            for (int m = 0; m < MT; ++m) st[m] *= alpha;
+            for (int j = 0; j < MTH; ++j) st[j] *= alpha;
 #pragma unroll
-            for (int m = 0; m < MT; ++m)
+            for (int j = 0; j < MTH; ++j)
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
-                    st[m] = MF::mma(bt_frag<N>(sB, m, ks * KSTEP, lr, lg), x_frag(sXw, LR, ks * KSTEP, p0, lr, lg), st[m]);
+                    st[j] = MF::mma(bt_frag<N, LB>(sB, mb + j, ks * KSTEP, lr, lg),
+                                    x_frag(sXw, LR, ks * KSTEP, p0, lr, lg), st[j]);
 #pragma unroll
-            for (int r = 0; r < RT; ++r) acc_o[r] *= sRow[w][16 * r + lr];
-            if constexpr (!SEQ && SZ == 2) pipeline_lds_mfma<8, K::TPW * NK + RT * NK + MT * KS, 2>();
+            for (int i = 0; i < RTH; ++i) acc[i] *= sRow[16 * K::own_tile(nh, i) + lr];
         } else if constexpr (SEQ) {
             // ---- block with sequence starts, one segment at a time
             // (1) read-out of each segment's incoming state
             for (int j = 0; j <= nstart; ++j) {
-                const int a = sStart[wq][j];
-                const int e = (j < nstart) ? sStart[wq][j + 1] - 1 : QB - 1;
+                const int a = sStart[j];
+                const int e = (j < nstart) ? sStart[j + 1] - 1 : QB - 1;
                 if (e < a) continue;                         // empty first segment
+                if (j > 0 && !prm.init) continue;            // a zero initial state reads out nothing
                 frag f[NK];
-                if (j == 0) {
+                if (j > 0) global_state_frags<N>(prm.init + (((int64_t)sSeqOf[j] * H + h) * P + p0 + lr) * N, lg, f);
 #pragma unroll
-                    for (int k = 0; k < NK; ++k) f[k] = sf[k];
-                } else if (prm.init) {
-                    global_state_frags<N>(prm.init + (((int64_t)sSeqOf[wq][j] * H + h) * P + p0 + lr) * N, lg, f);
-                } else {
-                    continue;                                // a zero initial state reads out nothing
-                }
-#pragma unroll
-                for (int r = 0; r < RT; ++r) {
+                for (int i = 0; i < RTH; ++i) {
+                    const int t = 16 * K::own_tile(nh, i) + lr;
+                    const TI* crw = sC + t * LC;
                     f32x4 tmp = f32x4{0.f, 0.f, 0.f, 0.f};
+                    if (j == 0) {
 #pragma unroll
-                    for (int k = 0; k < NK; ++k) tmp = MF::mma(f[k], c_frag<N>(sC + (16 * r + lr) * LC, k, lg), tmp);
-                    const int t = 16 * r + lr;
-                    const float sc = (sSeg[wq][t] == j) ? sRow[w][t] : 0.f;
-                    acc_o[r] += sc * tmp;
+                        for (int q = 0; q < NKH; ++q) tmp = MF::mma(sfo[q], c_frag<N>(crw, kbo + q, lg), tmp);
+                        if constexpr (NH > 1) {
+#pragma unroll
+                            for (int q = 0; q < NKH; ++q) tmp = MF::mma(sfp[q], c_frag<N>(crw, kbp + q, lg), tmp);
+                        }
+                    } else {
+#pragma unroll
+                        for (int k = 0; k < NK; ++k) tmp = MF::mma(f[k], c_frag<N>(crw, k, lg), tmp);
+                    }
+                    const float sc = (sSeg[t] == j) ? sRow[t] : 0.f;
+                    acc[i] += sc * tmp;
                 }
             }
             // (2) state at the end of each segment: a sequence that ends inside
             //     the block hands its state to final_state; the last segment's
             //     state is carried on
-            if (sStart[wq][1] == 0) write_state(st, sSeqOf[wq][0]);   // previous sequence ended with the previous block
+            if (sStart[1] == 0) write_state(st, sSeqOf[0]);   // previous sequence ended with the previous block
             for (int j = 0; j <= nstart; ++j) {
-                const int a = sStart[wq][j];
-                const int e = (j < nstart) ? sStart[wq][j + 1] - 1 : QB - 1;
+                const int a = sStart[j];
+                const int e = (j < nstart) ? sStart[j + 1] - 1 : QB - 1;
                 if (e < a) continue;
                 block_sync_lds();                             // the previous segment's weighted X is consumed
                 for (int v = tid; v < P * QB; v += NT) {
                     const int t = v / P, pr = v % P;
                     float df = 1.f;
-                    if constexpr (EULER) df = sDtf[we][t];
-                    const float ws = (sSeg[wq][t] == j) ? fast_exp2((float)(sCum[w][e] - sCum[w][t])) * df : 0.f;
+                    if constexpr (EULER) df = sDtf[t];
+                    const float ws = (sSeg[t] == j) ? fast_exp2((float)(sCum[e] - sCum[t])) * df : 0.f;
                     sXw[t * LR + pr] = to_in<TI>(ws * to_f32(sXr[t * LR + pr]));
                 }
                 block_sync_lds();
-                const cum_t before = (a == 0) ? (cum_t)0 : sCum[w][a - 1];
-                const float carry = fast_exp2((float)(sCum[w][e] - before));
-                f32x4 F[MT];
+                const cum_t before = (a == 0) ? (cum_t)0 : sCum[a - 1];
+                const float carry = fast_exp2((float)(sCum[e] - before));
+                f32x4 F[MTH];
                 if (j == 0) {
 #pragma unroll
-                    for (int m = 0; m < MT; ++m) F[m] = st[m] * carry;
+                    for (int q = 0; q < MTH; ++q) F[q] = st[q] * carry;
                 } else if (prm.init) {
-                    const float* src = prm.init + (((int64_t)sSeqOf[wq][j] * H + h) * P + p0 + lr) * N;
+                    const float* src = prm.init + (((int64_t)sSeqOf[j] * H + h) * P + p0 + lr) * N;
 #pragma unroll
-                    for (int m = 0; m < MT; ++m) {
-                        const float4 iv = *(const float4*)(src + nrow<N>(m, 4 * lg));
-                        F[m] = f32x4{iv.x, iv.y, iv.z, iv.w} * carry;
+                    for (int q = 0; q < MTH; ++q) {
+                        const float4 iv = *(const float4*)(src + nrow<N>(mb + q, 4 * lg));
+                        F[q] = f32x4{iv.x, iv.y, iv.z, iv.w} * carry;
                     }
                 } else {
 #pragma unroll
-                    for (int m = 0; m < MT; ++m) F[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    for (int q = 0; q < MTH; ++q) F[q] = f32x4{0.f, 0.f, 0.f, 0.f};
                 }
 #pragma unroll
-                for (int m = 0; m < MT; ++m)
+                for (int q = 0; q < MTH; ++q)
 #pragma unroll
                     for (int ks = 0; ks < KS; ++ks)
-                        F[m] = MF::mma(bt_frag<N>(sB, m, ks * KSTEP, lr, lg), x_frag(sXw, LR, ks * KSTEP, p0, lr, lg), F[m]);
+                        F[q] = MF::mma(bt_frag<N, LB>(sB, mb + q, ks * KSTEP, lr, lg),
+                                       x_frag(sXw, LR, ks * KSTEP, p0, lr, lg), F[q]);
                 if (j < nstart) {
-                    write_state(F, sSeqOf[wq][j]);
+                    write_state(F, sSeqOf[j]);
                 } else {
 #pragma unroll
-                    for (int m = 0; m < MT; ++m) st[m] = F[m];
+                    for (int q = 0; q < MTH; ++q) st[q] = F[q];
                 }
             }
             // Settle this rare path's own memory traffic here, so that the
@@ -768,62 +796,81 @@ __global__ __launch_bounds__(P / 16 * 64) void ssd_scan_kernel(ScanParams prm) {
         }
     };
 
-    // diagonal block (L o CB) X, as X^T (L o CB)^T (token tile r only needs s < 16 (r + 1)),
-    // then y = read-out + diagonal block + D x: lane holds y[t = 16r + lr][p0 + 4lg .. +3],
-    // one 16-byte store per token tile (past-the-end tokens are dropped by the range check)
+    // diagonal block (L o CB) X of this wave's token tiles, as X^T (L o CB)^T (token
+    // tile r only needs s < 16 (r + 1)), then y = read-out + diagonal block + D x:
+    // lane holds y[t = 16r + lr][p0 + 4lg .. +3], one 16-byte store per token tile
+    // (past-the-end tokens are dropped by the range check).  Everything read from
+    // X (the skip term and the X operands) is taken before the barrier that ends
+    // the MFMA phase, so the next block's X may be staged right after it.
+    constexpr int DKS = (KSTEP == 32 && NH == 2) ? 2 : 0;          // X operands kept across the barrier
+    frag xd[DKS > 0 ? DKS : 1];
+    auto diag_pre = [&]() {
+#pragma unroll
+        for (int i = 0; i < RTH; ++i) {
+            const int t = 16 * K::own_tile(nh, i) + lr;
+            float xv[4];
+            if constexpr (SZ == 2) {
+                const bf16x4 x4 = *(const bf16x4*)(sXr + t * LR + p0 + 4 * lg);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) xv[q] = (float)x4[q];
+            } else {
+                const float4 x4 = *(const float4*)(sXr + t * LR + p0 + 4 * lg);
+                xv[0] = x4.x; xv[1] = x4.y; xv[2] = x4.z; xv[3] = x4.w;
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[i][q] += Dh * xv[q];
+        }
+        if constexpr (DKS > 0) {
+#pragma unroll
+            for (int q = 0; q < DKS; ++q) xd[q] = x_frag(sXr, LR, 32 * q, p0, lr, lg);
+        }
+    };
     auto diag_phase = [&](int blk) {
-        const TI* sXr = sXr_of(blk);
 #pragma unroll
-        for (int r = 0; r < RT; ++r)
+        for (int i = 0; i < RTH; ++i) {
+            const int r = K::own_tile(nh, i);
+            const TI* lrow = sLm + (16 * r + lr) * LQ + KPL * lg;
+            if constexpr (DKS > 0) {
+                // tiles {0, 3} or {1, 2} (or {0} / {1}): one K step for the first, two for the second
 #pragma unroll
-            for (int ks = 0; ks < 16 * (r + 1); ks += KSTEP)
-                acc_o[r] = MF::mma(x_frag(sXr, LR, ks, p0, lr, lg),
-                                   lds_frag<TI>(sLm + (16 * r + lr) * LQ + ks + KPL * lg), acc_o[r]);
+                for (int q = 0; q < (i == 0 ? 1 : 2); ++q) acc[i] = MF::mma(xd[q], lds_frag<TI>(lrow + 32 * q), acc[i]);
+            } else {
+                for (int ks = 0; ks < 16 * (r + 1); ks += KSTEP)
+                    acc[i] = MF::mma(x_frag(sXr, LR, ks, p0, lr, lg), lds_frag<TI>(lrow + ks), acc[i]);
+            }
+        }
         const int64_t t0 = (int64_t)blk * QB;
         const rsrc_t ry = make_rsrc(yrow + t0 * ys, yrec - t0 * ys);
 #pragma unroll
-        for (int r = 0; r < RT; ++r) {
-            const int t = 16 * r + lr;
-            f32x4 out = acc_o[r];
-            {
-                float xv[4];
-                if constexpr (SZ == 2) {
-                    const bf16x4 x4 = *(const bf16x4*)(sXr + t * LR + p0 + 4 * lg);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) xv[i] = (float)x4[i];
-                } else {
-                    const float4 x4 = *(const float4*)(sXr + t * LR + p0 + 4 * lg);
-                    xv[0] = x4.x; xv[1] = x4.y; xv[2] = x4.z; xv[3] = x4.w;
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) out[i] += Dh * xv[i];
-            }
-            buf_store16(out, ry, t * ys + (p0 + 4 * lg) * 4);
-        }
+        for (int i = 0; i < RTH; ++i) buf_store16(acc[i], ry, (16 * K::own_tile(nh, i) + lr) * ys + (p0 + 4 * lg) * 4);
         if constexpr (SEQ) prevseq = lastseq_c;
     };
 
+    sx_store();                      // the initial state, for the first read-out
     if (nblk > 0) {
         issue(0);
         prep(0);
-        block_sync_lds();
     }
+    block_sync_lds();
     // The initial state (loaded at entry) is carried through the loop; settle
     // its loads here so the loop header does not wait on memory each iteration.
     __builtin_amdgcn_s_waitcnt(0);
     for (int blk = 0; blk < nblk; ++blk) {
         if (blk + 1 < nblk) issue(blk + 1);
         lm_phase();
-        state_phase(blk);
+        state_phase();
         lm_store();
-        // every wave's tiles of L o CB are written, and block blk's C, B, weighted X
-        // and per-token scalars are no longer read: block blk+1 may be staged
-        // (its X into the other buffer) while the diagonal product reads block blk
+        diag_pre();
+        // every wave's tiles of L o CB are written; the exchange area and block blk's
+        // C, B, X and weighted X are no longer read (f32 without paired halves still
+        // reads X in the diagonal product: it keeps a barrier before the next staging)
         block_sync_lds();
+        sx_store();
         diag_phase(blk);
         if (blk + 1 < nblk) {
+            if constexpr (DKS == 0) block_sync_lds();
             prep(blk + 1);
-            block_sync_lds();        // block blk+1's tiles are complete
+            block_sync_lds();        // block blk+1's tiles (and the exchanged state) are complete
         }
     }
     // the state after the row's last token belongs to its last sequence
