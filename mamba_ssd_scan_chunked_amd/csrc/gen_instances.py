@@ -1,19 +1,19 @@
-"""Write the kernel-instantiation sources (ssd_<dtype>.hip, ssd_<dtype>_s<seq>_e<euler>.hip).
+"""Write the kernel-instantiation sources (ssd_<dtype>.hip, ssd_<dtype>_s<seq>_e<euler>_l<local>.hip).
 
-Each file instantiates the scan kernel for one (dtype, sequence ids, Euler scaling)
-combination over the supported (headdim, dstate, block) shapes, so the build compiles
+Each file instantiates the scan kernel for one (dtype, sequence ids, Euler scaling,
+local pass or scan) combination over the supported (headdim, dstate, block) shapes, so the build compiles
 them in parallel.  Run it after changing the shape lists below; the outputs are
 committed sources.
 """
 import itertools
-def gen(tag, TI, Ps, Ns, QBs, seq, eul):
-    out = ['// Kernel instantiations: %s inputs, %s sequence ids, %s Euler input scaling.\n#include "ssd_kernels.hpp"\n#include "ssd_launch.hpp"\n\nnamespace ssd {\n' % (tag, "with" if seq else "without", "with" if eul else "without")]
-    fn = "launch_scan_%s_s%d_e%d" % (tag, seq, eul)
+def gen(tag, TI, Ps, Ns, QBs, seq, eul, loc):
+    out = ['// Kernel instantiations: %s inputs, %s sequence ids, %s Euler input scaling, %s.\n#include "ssd_kernels.hpp"\n#include "ssd_launch.hpp"\n\nnamespace ssd {\n' % (tag, "with" if seq else "without", "with" if eul else "without", "local pass" if loc else "scan")]
+    fn = "launch_scan_%s_s%d_e%d_l%d" % (tag, seq, eul, loc)
     out.append("hipError_t %s(int P, int N, int QB, const ScanParams& prm, int64_t grid, hipStream_t s) {\n" % fn)
     for P in Ps:
         for N in Ns:
             for Q in QBs:
-                out.append("    if (P == %d && N == %d && QB == %d) { hipLaunchKernelGGL((ssd_scan_kernel<%s, %d, %d, %d, %s, %s>), dim3((unsigned)grid), dim3(ScanCfg<%s, %d, %d, %d>::NT), 0, s, prm); return hipGetLastError(); }\n" % (P, N, Q, TI, P, N, Q, "true" if seq else "false", "true" if eul else "false", TI, P, N, Q))
+                out.append("    if (P == %d && N == %d && QB == %d) { hipLaunchKernelGGL((ssd_scan_kernel<%s, %d, %d, %d, %s, %s, %s>), dim3((unsigned)grid), dim3(ScanCfg<%s, %d, %d, %d>::NT), 0, s, prm); return hipGetLastError(); }\n" % (P, N, Q, TI, P, N, Q, "true" if seq else "false", "true" if eul else "false", "true" if loc else "false", TI, P, N, Q))
     out.append("    return hipErrorInvalidValue;\n}\n}  // namespace ssd\n")
     return "".join(out)
 
@@ -24,10 +24,10 @@ def gen_common(tag, TI, Ps, Ns, QBs):
     out.append("    const bool n = %s;\n" % " || ".join("N == %d" % v for v in Ns))
     out.append("    const bool q = %s;\n" % " || ".join("QB == %d" % v for v in QBs))
     out.append("    return p && n && q;\n}\n\n")
-    out.append("hipError_t launch_scan_%s(int P, int N, int QB, bool seq, bool euler, const ScanParams& prm, int64_t grid, hipStream_t s) {\n" % tag)
+    out.append("hipError_t launch_scan_%s(int P, int N, int QB, bool seq, bool euler, bool local, const ScanParams& prm, int64_t grid, hipStream_t s) {\n" % tag)
     out.append("    if (grid <= 0) return hipSuccess;\n")
-    for sq, eu in itertools.product((0, 1), (0, 1)):
-        out.append("    if (seq == %s && euler == %s) return launch_scan_%s_s%d_e%d(P, N, QB, prm, grid, s);\n" % ("true" if sq else "false", "true" if eu else "false", tag, sq, eu))
+    for sq, eu, lo in itertools.product((0, 1), (0, 1), (0, 1)):
+        out.append("    if (seq == %s && euler == %s && local == %s) return launch_scan_%s_s%d_e%d_l%d(P, N, QB, prm, grid, s);\n" % ("true" if sq else "false", "true" if eu else "false", "true" if lo else "false", tag, sq, eu, lo))
     out.append("    return hipErrorInvalidValue;\n}\n}  // namespace ssd\n")
     return "".join(out)
 
@@ -38,8 +38,8 @@ files = []
 for tag, (TI, Ps, Ns, QBs) in cfg.items():
     open(d + "ssd_%s.hip" % tag, "w").write(gen_common(tag, TI, Ps, Ns, QBs))
     files.append("ssd_%s.hip" % tag)
-    for sq, eu in itertools.product((0, 1), (0, 1)):
-        fn = "ssd_%s_s%d_e%d.hip" % (tag, sq, eu)
-        open(d + fn, "w").write(gen(tag, TI, Ps, Ns, QBs, sq, eu))
+    for sq, eu, lo in itertools.product((0, 1), (0, 1), (0, 1)):
+        fn = "ssd_%s_s%d_e%d_l%d.hip" % (tag, sq, eu, lo)
+        open(d + fn, "w").write(gen(tag, TI, Ps, Ns, QBs, sq, eu, lo))
         files.append(fn)
 print(files)

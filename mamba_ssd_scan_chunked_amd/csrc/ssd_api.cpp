@@ -12,6 +12,47 @@
 #include "ssd_kernels.hpp"
 #include "ssd_launch.hpp"
 
+#include <algorithm>
+
+namespace ssd {
+// Incoming state of every segment from the local pass: for each (row, head) and
+// state element, S_in(0) = the row's initial state and
+// S_in(s+1) = carry(s) S_in(s) + local(s), written over local(s) (the
+// inter-chunk state recurrence real_end = block_decay * prev + local_end at
+// segment granularity).  One thread per 4 consecutive elements.
+__global__ __launch_bounds__(256) void ssd_combine_kernel(CombineParams prm) {
+    const int64_t pn4 = (int64_t)prm.P * prm.N / 4;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t bh = idx / pn4, e = idx % pn4;
+    if (bh >= prm.batch * prm.H) return;
+    const int64_t b = bh / prm.H, h = bh % prm.H;
+    float4 st = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (prm.init) {
+        int64_t seq0 = b;
+        if (prm.seq_idx) {
+            const int32_t s0 = prm.seq_idx[b * prm.T];
+            seq0 = s0 < 0 ? 0 : (s0 >= prm.nseqs ? prm.nseqs - 1 : s0);
+        }
+        st = *(const float4*)(prm.init + (seq0 * prm.H + h) * prm.P * prm.N + 4 * e);
+    }
+    const int ns = prm.nseg - 1;
+    for (int sg = 0; sg < ns; ++sg) {
+        const float c = prm.seg_carry[bh * ns + sg];
+        float4* slot = (float4*)(prm.seg_state + ((bh * ns + sg) * prm.P * prm.N)) + e;
+        const float4 l = *slot;
+        st = make_float4(c * st.x + l.x, c * st.y + l.y, c * st.z + l.z, c * st.w + l.w);
+        *slot = st;
+    }
+}
+
+hipError_t launch_combine(const CombineParams& prm, hipStream_t s) {
+    const int64_t threads = prm.batch * prm.H * (int64_t)prm.P * prm.N / 4;
+    if (threads <= 0) return hipSuccess;
+    hipLaunchKernelGGL(ssd_combine_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, prm);
+    return hipGetLastError();
+}
+}  // namespace ssd
+
 namespace {
 
 constexpr int64_t kMaxDim = int64_t(1) << 31;
@@ -29,9 +70,50 @@ int64_t nblocks(const ssd_problem_t* p) {
     return q ? (p->seqlen + q - 1) / q : 0;
 }
 
-// Workspace bytes the forward pass needs.  The single-pass scan keeps every
-// intermediate in registers and LDS, so none.
-int64_t workspace_bytes(const ssd_problem_t*) { return 0; }
+int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
+
+// Segments per row.  With fewer (row, head) items than twice the 256 compute
+// units, rows are split into segments that run in parallel (a local pass, a
+// combine step, then the scan of every segment from its incoming state), down
+// to 4 blocks per segment.  A function of the problem alone (no device query),
+// so the workspace size is known on the host; SSD_SEGMENTS=<n> overrides it.
+struct Segs {
+    int nseg, seg_blocks;
+};
+Segs segments(const ssd_problem_t* p) {
+    const int64_t nblk = nblocks(p);
+    Segs r{1, (int)(nblk > 0 ? nblk : 1)};
+    if (nblk <= 1 || p->batch == 0) return r;
+    int64_t S = 1;
+    const char* env = std::getenv("SSD_SEGMENTS");
+    if (env && std::atoi(env) > 0) {
+        S = std::atoi(env);
+    } else {
+        const int64_t units = p->batch * p->nheads;
+        if (units < 256) S = std::min<int64_t>(512 / units, nblk / 4);
+    }
+    S = std::max<int64_t>(1, std::min<int64_t>(S, nblk));
+    const int64_t sb = (nblk + S - 1) / S;
+    r.seg_blocks = (int)sb;
+    r.nseg = (int)((nblk + sb - 1) / sb);
+    return r;
+}
+
+// Workspace bytes the forward pass needs: for a row split into S segments, the
+// S-1 segment states (fp32 P x N per row and head) and their carried decays.
+struct WsLayout {
+    int64_t state_bytes, carry_off, total;
+};
+WsLayout ws_layout(const ssd_problem_t* p) {
+    const Segs sg = segments(p);
+    const int64_t n = p->batch * p->nheads * (sg.nseg - 1);
+    WsLayout l;
+    l.state_bytes = align256(n * p->headdim * p->dstate * 4);
+    l.carry_off = l.state_bytes;
+    l.total = n > 0 ? l.state_bytes + align256(n * 4) : 0;
+    return l;
+}
+int64_t workspace_bytes(const ssd_problem_t* p) { return ws_layout(p).total; }
 
 bool misaligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) != 0; }
 
@@ -105,8 +187,10 @@ int check_args(const ssd_problem_t* p, const void* x, const float* dt, const flo
 
 int launch_scan(const ssd_problem_t* p, const void* x, const float* dt, const float* A_log, const void* B,
                 const void* C, const float* D, const float* init, const int32_t* seq_idx, float* y, float* fin,
-                hipStream_t stream) {
+                void* ws, hipStream_t stream) {
     const int q = block_len(p);
+    const Segs sg = segments(p);
+    const WsLayout wl = ws_layout(p);
     ssd::ScanParams prm;
     prm.x = x;
     prm.dt = dt;
@@ -125,16 +209,42 @@ int launch_scan(const ssd_problem_t* p, const void* x, const float* dt, const fl
     prm.nseqs = p->nseqs;
     prm.nblk = static_cast<int>(nblocks(p));
     prm.dt_scales_x = (p->flags & SSD_FLAG_DT_SCALES_X) ? 1 : 0;
-    const int64_t grid = p->batch * p->nheads;
-    if (grid == 0) return SSD_OK;
+    prm.seg_blocks = sg.seg_blocks;
+    prm.nseg = sg.nseg;
+    prm.seg_state = sg.nseg > 1 ? static_cast<float*>(ws) : nullptr;
+    prm.seg_carry = sg.nseg > 1 ? reinterpret_cast<float*>(static_cast<char*>(ws) + wl.carry_off) : nullptr;
+    const int64_t rows = p->batch * p->nheads;
+    if (rows == 0) return SSD_OK;
     if (p->seqlen == 0 && (seq_idx || !fin)) return SSD_OK;   // no token, no sequence to hand out
     const bool seq = seq_idx != nullptr, euler = prm.dt_scales_x != 0;
-    hipError_t e = p->dtype == SSD_DTYPE_BF16
-                       ? ssd::launch_scan_bf16((int)p->headdim, (int)p->dstate, q, seq, euler, prm, grid, stream)
-                       : ssd::launch_scan_f32((int)p->headdim, (int)p->dstate, q, seq, euler, prm, grid, stream);
+    const int P = (int)p->headdim, N = (int)p->dstate;
+    auto scan = [&](bool local, int64_t grid) {
+        return p->dtype == SSD_DTYPE_BF16 ? ssd::launch_scan_bf16(P, N, q, seq, euler, local, prm, grid, stream)
+                                          : ssd::launch_scan_f32(P, N, q, seq, euler, local, prm, grid, stream);
+    };
+    hipError_t e = hipSuccess;
+    if (sg.nseg > 1) {
+        e = scan(true, rows * (sg.nseg - 1));
+        if (e == hipSuccess) {
+            ssd::CombineParams cp;
+            cp.init = init;
+            cp.seq_idx = seq_idx;
+            cp.seg_state = prm.seg_state;
+            cp.seg_carry = prm.seg_carry;
+            cp.batch = p->batch;
+            cp.T = p->seqlen;
+            cp.H = p->nheads;
+            cp.nseqs = p->nseqs;
+            cp.P = P;
+            cp.N = N;
+            cp.nseg = sg.nseg;
+            e = ssd::launch_combine(cp, stream);
+        }
+    }
+    if (e == hipSuccess) e = scan(false, rows * sg.nseg);
     if (log_enabled())
-        std::fprintf(stderr, "[ssd] scan dtype=%d P=%lld N=%lld QB=%d grid=%lld -> %s\n", p->dtype,
-                     (long long)p->headdim, (long long)p->dstate, q, (long long)grid, hipGetErrorString(e));
+        std::fprintf(stderr, "[ssd] scan dtype=%d P=%d N=%d QB=%d rows=%lld segments=%d x %d blocks -> %s\n",
+                     p->dtype, P, N, q, (long long)rows, sg.nseg, sg.seg_blocks, hipGetErrorString(e));
     return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
 }
 
@@ -184,7 +294,7 @@ int ssd_forward(const ssd_problem_t* p, const void* x, const float* dt, const fl
     if (v != SSD_OK) return v;
     const int d = check_device();
     if (d != SSD_OK) return d;
-    return launch_scan(p, x, dt, A_log, B, C, D, init_state, seq_idx, y, final_state,
+    return launch_scan(p, x, dt, A_log, B, C, D, init_state, seq_idx, y, final_state, workspace,
                        static_cast<hipStream_t>(stream));
 }
 

@@ -281,6 +281,24 @@ struct ScanParams {
     int64_t batch, T, H, G, nseqs;
     int nblk;
     int dt_scales_x;
+    // A row may be split into nseg segments of seg_blocks blocks that run in
+    // parallel: a local pass gives each segment but the last its end state from
+    // a zero incoming state and the decay it carries across, a combine step
+    // turns those into every segment's incoming state, and the scan proper then
+    // starts each segment from it.
+    int seg_blocks;     // blocks per segment (the whole row when nseg == 1)
+    int nseg;           // segments per row
+    float* seg_state;   // (batch, H, nseg-1, P, N): local end states, then incoming states of segments 1..
+    float* seg_carry;   // (batch, H, nseg-1): decay factor across each segment (0 if a sequence starts in it)
+};
+
+struct CombineParams {
+    const float* init;
+    const int32_t* seq_idx;
+    float* seg_state;
+    const float* seg_carry;
+    int64_t batch, T, H, nseqs;
+    int P, N, nseg;
 };
 
 // ============================================================== scan kernel
@@ -330,6 +348,8 @@ struct ScanCfg {
     static constexpr int NW = NPT * NH;
     static constexpr int NT = NW * 64;
     static constexpr int WPE = NW >= 8 ? NW / 2 : 2;   // waves per SIMD for two workgroups per CU
+                                                      // (the sequence-id variants, whose segment path
+                                                      // needs more registers, are left at two)
     static constexpr int MTH = MT / NH, NKH = NK / NH, RTH = RT / NH;
     static constexpr int LC = N + VE;                 // pitch of C rows (elements)
     static constexpr int LB = N + 4;                  // pitch of B rows
@@ -361,9 +381,11 @@ struct ScanCfg {
     }
 };
 
-template <typename TI, int P, int N, int QB, bool SEQ, bool EULER>
+// LOCAL: the local pass over segments 0 .. nseg-2 (end state from a zero incoming
+// state and the carried decay, no outputs); otherwise the scan proper.
+template <typename TI, int P, int N, int QB, bool SEQ, bool EULER, bool LOCAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, ScanCfg<TI, P, N, QB>::NT),
-                          amdgpu_waves_per_eu(ScanCfg<TI, P, N, QB>::WPE)))
+                          amdgpu_waves_per_eu(SEQ ? 2 : ScanCfg<TI, P, N, QB>::WPE)))
 void ssd_scan_kernel(ScanParams prm) {
     typedef ScanCfg<TI, P, N, QB> K;
     typedef Mfma<TI> MF;
@@ -408,13 +430,18 @@ void ssd_scan_kernel(ScanParams prm) {
     // Work-item order: runs of consecutive (row, head) items go to the same
     // XCD (workgroups are dealt round-robin over the 8 XCDs), so the heads of
     // a row share that row's B and C tiles in one L2.
-    const int64_t units = prm.batch * prm.H;
+    const int nsl = LOCAL ? prm.nseg - 1 : prm.nseg;             // segments this launch covers
+    const int64_t units = prm.batch * prm.H * nsl;
     int64_t u = blockIdx.x;
     if (units % 8 == 0) u = (int64_t)(blockIdx.x % 8) * (units / 8) + blockIdx.x / 8;
-    const int64_t b = u / prm.H, h = u % prm.H;
+    const int64_t h = u % prm.H, rowseg = u / prm.H;
+    const int sg = (int)(rowseg % nsl);
+    const int64_t b = rowseg / nsl;
     const int64_t g = h / (prm.H / prm.G);
     const int64_t T = prm.T, H = prm.H, G = prm.G;
-    const int nblk = prm.nblk;
+    const int blk0 = sg * prm.seg_blocks;
+    const int blk1 = min(prm.nblk, blk0 + prm.seg_blocks);
+    const int64_t slot = (b * H + h) * (prm.nseg - 1) + sg;     // this segment's local-pass slot
 
     // A_h in log2 units, so that every decay is exp2 of a cumulative sum
     cum_t A2;
@@ -438,11 +465,18 @@ void ssd_scan_kernel(ScanParams prm) {
 
     // ---- initial state of the row's first sequence: this wave's tiles of S^T,
     //      rows nrow(mb + j, 4*lg+i) of channel p0 + lr
+    // (a later segment continues the sequence of the token before it; its incoming
+    // state is the combined one, and the local pass starts from zero)
     int prevseq = (int)b;
-    if (SEQ && T > 0) prevseq = clamp_seq(seqg[0]);
+    if (SEQ && T > 0) prevseq = clamp_seq(seqg[blk0 > 0 ? (int64_t)blk0 * QB - 1 : 0]);
     f32x4 st[MTH];
-    if (prm.init) {
-        const float* src = prm.init + (((int64_t)prevseq * H + h) * P + p0 + lr) * N;
+    const float* src0 = nullptr;
+    if constexpr (!LOCAL) {
+        if (sg > 0) src0 = prm.seg_state + ((slot - 1) * P + p0 + lr) * N;
+        else if (prm.init) src0 = prm.init + (((int64_t)prevseq * H + h) * P + p0 + lr) * N;
+    }
+    if (src0) {
+        const float* src = src0;
 #pragma unroll
         for (int j = 0; j < MTH; ++j) {
             const float4 v = *(const float4*)(src + nrow<N>(mb + j, 4 * lg));
@@ -517,7 +551,7 @@ void ssd_scan_kernel(ScanParams prm) {
             const int v = tid + j * NT;
             if (K::CV % NT == 0 || v < K::CV) {
                 const int off = (v / (N / VE)) * cs + (v % (N / VE)) * 16;
-                cr[j] = buf_load16(rc, off);
+                if constexpr (!LOCAL) cr[j] = buf_load16(rc, off);
                 br[j] = buf_load16(rb, off);
             }
         }
@@ -526,6 +560,8 @@ void ssd_scan_kernel(ScanParams prm) {
     // per-block values handed from the preparation of a block to its MFMA phases
     int nstart_c = 0, lastseq_c = prevseq;
     float cend_f = 0.f;
+    cum_t seg_total = 0;          // log2 decay across the blocks staged so far
+    bool seg_reset = false;       // a sequence started in them
 
     // ---- preparation of a block from the issued loads: tiles into LDS, the
     //      within-block cumulative decay, segments, X and weighted X.  Every wave
@@ -538,7 +574,7 @@ void ssd_scan_kernel(ScanParams prm) {
             const int v = tid + j * NT;
             if (K::CV % NT == 0 || v < K::CV) {
                 const int t = v / (N / VE), c = v % (N / VE);
-                *(uint4*)(sC + t * LC + c * VE) = cr[j];
+                if constexpr (!LOCAL) *(uint4*)(sC + t * LC + c * VE) = cr[j];
                 if constexpr (SZ == 2) {
                     TI* d = sB + t * LB + c * VE;          // 8-byte aligned rows
                     *(uint2*)d = make_uint2(br[j].x, br[j].y);
@@ -582,6 +618,8 @@ void ssd_scan_kernel(ScanParams prm) {
         }
         nstart_c = nstart;
         cend_f = (float)cend;
+        seg_total += cend;
+        seg_reset |= nstart > 0;
         const float dtf = EULER ? dtv : 1.f;
         const float wx = fast_exp2((float)(cend - cum)) * dtf;  // end-state weight of token lane
         if (w == 0 && lane < QB) {
@@ -682,8 +720,8 @@ void ssd_scan_kernel(ScanParams prm) {
     auto state_phase = [&]() {
         const int nstart = nstart_c;
         frag sfo[NKH], sfp[NKH];
-        state_frags<MTH>(st, sfo);
-        if constexpr (NH > 1) {
+        if constexpr (!LOCAL) state_frags<MTH>(st, sfo);
+        if constexpr (NH > 1 && !LOCAL) {
 #pragma unroll
             for (int j = 0; j < NKH; ++j) sfp[j] = *(const frag*)(sxp + j * 64 * KPL);
         }
@@ -692,7 +730,7 @@ void ssd_scan_kernel(ScanParams prm) {
         if (!SEQ || nstart == 0) {
             // carried state read out by C:  S C^T
 #pragma unroll
-            for (int i = 0; i < RTH; ++i) {
+            for (int i = 0; i < (LOCAL ? 0 : RTH); ++i) {
                 const TI* crw = sC + (16 * K::own_tile(nh, i) + lr) * LC;
 #pragma unroll
                 for (int j = 0; j < NKH; ++j) acc[i] = MF::mma(sfo[j], c_frag<N>(crw, kbo + j, lg), acc[i]);
@@ -712,11 +750,11 @@ void ssd_scan_kernel(ScanParams prm) {
                     st[j] = MF::mma(bt_frag<N, LB>(sB, mb + j, ks * KSTEP, lr, lg),
                                     x_frag(sXw, LR, ks * KSTEP, p0, lr, lg), st[j]);
 #pragma unroll
-            for (int i = 0; i < RTH; ++i) acc[i] *= sRow[16 * K::own_tile(nh, i) + lr];
+            for (int i = 0; i < (LOCAL ? 0 : RTH); ++i) acc[i] *= sRow[16 * K::own_tile(nh, i) + lr];
         } else if constexpr (SEQ) {
             // ---- block with sequence starts, one segment at a time
             // (1) read-out of each segment's incoming state
-            for (int j = 0; j <= nstart; ++j) {
+            for (int j = 0; j <= (LOCAL ? -1 : nstart); ++j) {
                 const int a = sStart[j];
                 const int e = (j < nstart) ? sStart[j + 1] - 1 : QB - 1;
                 if (e < a) continue;                         // empty first segment
@@ -746,7 +784,7 @@ void ssd_scan_kernel(ScanParams prm) {
             // (2) state at the end of each segment: a sequence that ends inside
             //     the block hands its state to final_state; the last segment's
             //     state is carried on
-            if (sStart[1] == 0) write_state(st, sSeqOf[0]);   // previous sequence ended with the previous block
+            if (!LOCAL && sStart[1] == 0) write_state(st, sSeqOf[0]);   // previous sequence ended with the previous block
             for (int j = 0; j <= nstart; ++j) {
                 const int a = sStart[j];
                 const int e = (j < nstart) ? sStart[j + 1] - 1 : QB - 1;
@@ -784,7 +822,7 @@ void ssd_scan_kernel(ScanParams prm) {
                         F[q] = MF::mma(bt_frag<N, LB>(sB, mb + q, ks * KSTEP, lr, lg),
                                        x_frag(sXw, LR, ks * KSTEP, p0, lr, lg), F[q]);
                 if (j < nstart) {
-                    write_state(F, sSeqOf[j]);
+                    if constexpr (!LOCAL) write_state(F, sSeqOf[j]);
                 } else {
 #pragma unroll
                     for (int q = 0; q < MTH; ++q) st[q] = F[q];
@@ -846,35 +884,51 @@ void ssd_scan_kernel(ScanParams prm) {
         if constexpr (SEQ) prevseq = lastseq_c;
     };
 
-    sx_store();                      // the initial state, for the first read-out
-    if (nblk > 0) {
-        issue(0);
-        prep(0);
+    if constexpr (!LOCAL) sx_store();    // the initial state, for the first read-out
+    if (blk1 > blk0) {
+        issue(blk0);
+        prep(blk0);
     }
     block_sync_lds();
     // The initial state (loaded at entry) is carried through the loop; settle
     // its loads here so the loop header does not wait on memory each iteration.
     __builtin_amdgcn_s_waitcnt(0);
-    for (int blk = 0; blk < nblk; ++blk) {
-        if (blk + 1 < nblk) issue(blk + 1);
-        lm_phase();
+    for (int blk = blk0; blk < blk1; ++blk) {
+        if (blk + 1 < blk1) issue(blk + 1);
+        if constexpr (!LOCAL) lm_phase();
         state_phase();
-        lm_store();
-        diag_pre();
+        if constexpr (!LOCAL) {
+            lm_store();
+            diag_pre();
+        }
         // every wave's tiles of L o CB are written; the exchange area and block blk's
         // C, B, X and weighted X are no longer read (f32 without paired halves still
         // reads X in the diagonal product: it keeps a barrier before the next staging)
         block_sync_lds();
-        sx_store();
-        diag_phase(blk);
-        if (blk + 1 < nblk) {
-            if constexpr (DKS == 0) block_sync_lds();
+        if constexpr (!LOCAL) {
+            sx_store();
+            diag_phase(blk);
+        } else if constexpr (SEQ) {
+            prevseq = lastseq_c;
+        }
+        if (blk + 1 < blk1) {
+            if constexpr (DKS == 0 && !LOCAL) block_sync_lds();
             prep(blk + 1);
             block_sync_lds();        // block blk+1's tiles (and the exchanged state) are complete
         }
     }
-    // the state after the row's last token belongs to its last sequence
-    if (T > 0 || !SEQ) write_state(st, prevseq);
+    if constexpr (LOCAL) {
+        // this segment's end state from a zero incoming state, and the decay it
+        // applies to an incoming state (none past a sequence start)
+        float* dst = prm.seg_state + (slot * P + p0 + lr) * N;
+#pragma unroll
+        for (int j = 0; j < MTH; ++j)
+            *(float4*)(dst + nrow<N>(mb + j, 4 * lg)) = make_float4(st[j][0], st[j][1], st[j][2], st[j][3]);
+        if (tid == 0) prm.seg_carry[slot] = seg_reset ? 0.f : fast_exp2((float)seg_total);
+    } else if (sg == prm.nseg - 1) {
+        // the state after the row's last token belongs to its last sequence
+        if (T > 0 || !SEQ) write_state(st, prevseq);
+    }
 }
 
 }  // namespace ssd

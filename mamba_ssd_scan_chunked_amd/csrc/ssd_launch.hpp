@@ -6,24 +6,29 @@
 
 namespace ssd {
 struct ScanParams;
+struct CombineParams;
 
 // Return hipSuccess, hipErrorInvalidValue for a shape with no instantiation,
 // or the launch error.
-// seq: sequence ids present (segment handling compiled in); euler: dt scales x
-hipError_t launch_scan_bf16(int P, int N, int QB, bool seq, bool euler, const ScanParams& prm, int64_t grid,
-                            hipStream_t s);
-hipError_t launch_scan_f32(int P, int N, int QB, bool seq, bool euler, const ScanParams& prm, int64_t grid,
-                           hipStream_t s);
-#define SSD_DECLARE_SCAN(tag, sq, eu) \
-    hipError_t launch_scan_##tag##_s##sq##_e##eu(int P, int N, int QB, const ScanParams& prm, int64_t grid, hipStream_t s);
-SSD_DECLARE_SCAN(bf16, 0, 0)
-SSD_DECLARE_SCAN(bf16, 0, 1)
-SSD_DECLARE_SCAN(bf16, 1, 0)
-SSD_DECLARE_SCAN(bf16, 1, 1)
-SSD_DECLARE_SCAN(f32, 0, 0)
-SSD_DECLARE_SCAN(f32, 0, 1)
-SSD_DECLARE_SCAN(f32, 1, 0)
-SSD_DECLARE_SCAN(f32, 1, 1)
+// seq: sequence ids present (segment handling compiled in); euler: dt scales x;
+// local: the local pass of a row split into segments (else the scan proper)
+hipError_t launch_scan_bf16(int P, int N, int QB, bool seq, bool euler, bool local, const ScanParams& prm,
+                            int64_t grid, hipStream_t s);
+hipError_t launch_scan_f32(int P, int N, int QB, bool seq, bool euler, bool local, const ScanParams& prm,
+                           int64_t grid, hipStream_t s);
+hipError_t launch_combine(const CombineParams& prm, hipStream_t s);
+#define SSD_DECLARE_SCAN(tag, sq, eu, lo) \
+    hipError_t launch_scan_##tag##_s##sq##_e##eu##_l##lo(int P, int N, int QB, const ScanParams& prm, int64_t grid, hipStream_t s);
+#define SSD_DECLARE_SCAN2(tag, sq, eu) SSD_DECLARE_SCAN(tag, sq, eu, 0) SSD_DECLARE_SCAN(tag, sq, eu, 1)
+SSD_DECLARE_SCAN2(bf16, 0, 0)
+SSD_DECLARE_SCAN2(bf16, 0, 1)
+SSD_DECLARE_SCAN2(bf16, 1, 0)
+SSD_DECLARE_SCAN2(bf16, 1, 1)
+SSD_DECLARE_SCAN2(f32, 0, 0)
+SSD_DECLARE_SCAN2(f32, 0, 1)
+SSD_DECLARE_SCAN2(f32, 1, 0)
+SSD_DECLARE_SCAN2(f32, 1, 1)
+#undef SSD_DECLARE_SCAN2
 #undef SSD_DECLARE_SCAN
 
 bool supported_bf16(int P, int N, int QB);

@@ -67,10 +67,24 @@ def test_validate_rejects(kw, code):
 
 
 def test_workspace_size():
-    # the single-pass scan keeps its intermediates on chip
+    # enough (row, head) items: one pass per row, intermediates on chip
     assert ssd.workspace_size(prob()) == 0
     assert ssd.workspace_size(prob(headdim=48)) == 0            # invalid problem
     assert ssd.workspace_size(prob(seqlen=0)) == 0
+    # 32 items and 256 blocks of 64 tokens: 16 segments per row, 15 segment states
+    # (fp32 64 x 128) and decays per (row, head), each region 256-byte aligned
+    p = prob(batch=1, seqlen=16384, nheads=32)
+    n = 32 * 15
+    assert ssd.workspace_size(p) == n * 64 * 128 * 4 + ((n * 4 + 255) // 256) * 256
+
+
+def test_workspace_size_follows_forced_segments(monkeypatch):
+    p = prob(batch=1, seqlen=1000, nheads=2, headdim=32, dstate=64, chunk_len=64)   # 16 blocks
+    monkeypatch.setenv("SSD_SEGMENTS", "1")
+    assert ssd.workspace_size(p) == 0
+    monkeypatch.setenv("SSD_SEGMENTS", "5")      # 4 blocks per segment -> 4 segments
+    n = 2 * 3
+    assert ssd.workspace_size(p) == n * 32 * 64 * 4 + 256
 
 
 def _forward(p, **ptrs):
