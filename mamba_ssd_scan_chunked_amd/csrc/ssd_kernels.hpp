@@ -370,8 +370,7 @@ struct ScanCfg {
     static constexpr int BUF_ELEMS = OFF_SX + (NH > 1 ? NW * NKH * 64 * KPL : 0);
     // per-thread work units
     static constexpr int CV = QB * N / VE, CPT = (CV + NT - 1) / NT;           // C (and B) tile vectors
-    static constexpr int XC = 8 / SZ;                                          // channels per 8 bytes
-    static constexpr int XU = (QB / 4) * (P / XC), XPT = (XU + NT - 1) / NT;   // (4 tokens, XC channels) of X
+    static constexpr int XU = QB * P / VE, XPT = (XU + NT - 1) / NT;            // 16-byte pieces of the X tile
     // token tile i of the outputs of half nh: the causal work of the diagonal
     // block is split evenly ({0, 3} and {1, 2} of four tiles)
     __device__ static inline int own_tile(int nh, int i) {
@@ -392,12 +391,12 @@ void ssd_scan_kernel(ScanParams prm) {
     typedef typename MF::frag frag;
     typedef typename CumType<TI>::type cum_t;
     constexpr int NT = K::NT, VE = K::VE, LC = K::LC, LB = K::LB, LQ = K::LQ, LR = K::LR, KPL = K::KPL;
-    constexpr int KSTEP = K::KSTEP, SZ = K::SZ, NK = K::NK, RT = K::RT, MT = K::MT, NW = K::NW, XC = K::XC;
+    constexpr int KSTEP = K::KSTEP, SZ = K::SZ, NK = K::NK, RT = K::RT, MT = K::MT, NW = K::NW;
     constexpr int NH = K::NH, NPT = K::NPT, MTH = K::MTH, NKH = K::NKH, RTH = K::RTH;
     constexpr int NFH = SZ == 2 ? MTH / 2 : 4 * MTH;               // read-out fragments of a state half
     static_assert(NFH == NKH, "fragments of a state half are whole K steps");
     static_assert(QB <= 64 && QB % KSTEP == 0 && QB % 16 == 0, "block length");
-    static_assert(N % KSTEP == 0 && N % 16 == 0 && P % 16 == 0 && P % XC == 0, "shape");
+    static_assert(N % KSTEP == 0 && N % 16 == 0 && P % 16 == 0, "shape");
 
     __shared__ __attribute__((aligned(16))) TI smem[K::BUF_ELEMS];
     // per-token scalars of the block, shared by all waves (written by wave 0)
@@ -527,25 +526,27 @@ void ssd_scan_kernel(ScanParams prm) {
     // at its bottom (after the MFMA phases of the previous block), so no load
     // result lives across the loop back-edge and the wait counts stay exact.
     uint4 cr[K::CPT], br[K::CPT];
-    uint2 xr[K::XPT][4];
+    uint4 xr[K::XPT];
     float dtv = 0.f;
     int sqv = 0;
-    auto issue = [&](int blk) {
+    // (two groups: the B and C tiles, then dt and X, so that the waves do not all
+    // queue every load of the block at the same moment)
+    auto issue_x = [&](int blk) {
         const int64_t t0 = (int64_t)blk * QB;
         const rsrc_t rx = make_rsrc(xrow + t0 * xs, xrec - t0 * xs);
-        const rsrc_t rc = make_rsrc(crow + t0 * cs, crec - t0 * cs);
-        const rsrc_t rb = make_rsrc(brow + t0 * cs, crec - t0 * cs);
         const rsrc_t rd = make_rsrc(drow + t0 * ds, drec - t0 * ds);
         dtv = buf_load_f32(rd, lane * ds);
         if constexpr (SEQ) sqv = buf_load_i32(make_rsrc(seqg + t0, (T - t0) * 4), lane * 4);
 #pragma unroll
         for (int j = 0; j < K::XPT; ++j) {
             const int v = tid + j * NT;
-            const int q4 = v / (P / XC), c4 = v % (P / XC);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (K::XU % NT == 0 || v < K::XU) xr[j][e] = buf_load8(rx, (4 * q4 + e) * xs + c4 * 8);
+            if (K::XU % NT == 0 || v < K::XU) xr[j] = buf_load16(rx, (v / (P / VE)) * xs + (v % (P / VE)) * 16);
         }
+    };
+    auto issue_bc = [&](int blk) {
+        const int64_t t0 = (int64_t)blk * QB;
+        const rsrc_t rc = make_rsrc(crow + t0 * cs, crec - t0 * cs);
+        const rsrc_t rb = make_rsrc(brow + t0 * cs, crec - t0 * cs);
 #pragma unroll
         for (int j = 0; j < K::CPT; ++j) {
             const int v = tid + j * NT;
@@ -629,26 +630,21 @@ void ssd_scan_kernel(ScanParams prm) {
         }
 
         // X (row-major) and, for single-segment blocks, the end-state weighted X
+        // (each thread holds VE channels of one token)
 #pragma unroll
         for (int j = 0; j < K::XPT; ++j) {
             const int v = tid + j * NT;
-            const int q4 = v / (P / XC), c4 = v % (P / XC);
-            const int t0l = 4 * q4;
-            float wv[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) wv[e] = __shfl(wx, (t0l + e) & 63);
+            const int t = (v / (P / VE)) & 63, c = v % (P / VE);
+            const float wt = __shfl(wx, t);
             if (K::XU % NT == 0 || v < K::XU) {
+                *(uint4*)(sXr + t * LR + c * VE) = xr[j];
+                if (!SEQ || nstart == 0) {
+                    TI wxv[VE];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    *(uint2*)(sXr + (t0l + e) * LR + c4 * XC) = xr[j][e];
-                    if (!SEQ || nstart == 0) {
-                        TI wxv[XC];
-#pragma unroll
-                        for (int k = 0; k < XC; ++k) wxv[k] = to_in<TI>(wv[e] * to_f32(((const TI*)&xr[j][e])[k]));
-                        uint2 pk;
-                        __builtin_memcpy(&pk, wxv, 8);
-                        *(uint2*)(sXw + (t0l + e) * LR + c4 * XC) = pk;
-                    }
+                    for (int k = 0; k < VE; ++k) wxv[k] = to_in<TI>(wt * to_f32(((const TI*)&xr[j])[k]));
+                    uint4 pk;
+                    __builtin_memcpy(&pk, wxv, 16);
+                    *(uint4*)(sXw + t * LR + c * VE) = pk;
                 }
             }
         }
@@ -886,7 +882,8 @@ void ssd_scan_kernel(ScanParams prm) {
 
     if constexpr (!LOCAL) sx_store();    // the initial state, for the first read-out
     if (blk1 > blk0) {
-        issue(blk0);
+        issue_bc(blk0);
+        issue_x(blk0);
         prep(blk0);
     }
     block_sync_lds();
@@ -894,8 +891,9 @@ void ssd_scan_kernel(ScanParams prm) {
     // its loads here so the loop header does not wait on memory each iteration.
     __builtin_amdgcn_s_waitcnt(0);
     for (int blk = blk0; blk < blk1; ++blk) {
-        if (blk + 1 < blk1) issue(blk + 1);
+        if (blk + 1 < blk1) issue_bc(blk + 1);
         if constexpr (!LOCAL) lm_phase();
+        if (blk + 1 < blk1) issue_x(blk + 1);
         state_phase();
         if constexpr (!LOCAL) {
             lm_store();
