@@ -91,12 +91,20 @@ typedef struct {
 int ssd_validate(const ssd_problem_t* p);
 
 /* Bytes of device workspace ssd_forward needs for this problem; 0 when it needs
- * none (then workspace may be NULL) or when the problem is invalid.  The
- * single-pass scan keeps its intermediates (C.B^T tiles, decays, the carried
- * state) on chip and needs no workspace. */
+ * none (then workspace may be NULL) or when the problem is invalid.  A row is
+ * scanned in one pass with every intermediate (C.B^T tiles, decays, the
+ * carried state) on chip, unless there are fewer than 256 (row, head) items:
+ * then rows are cut into segments that run in parallel, and the workspace holds
+ * each segment's state (fp32 P x N) and carried decay, (batch, nheads,
+ * segments - 1) of each.  The chunked algorithm's inter-chunk state passing at
+ * segment granularity (section 3 of "088 Mamba-2"; key design 2 on the
+ * papernotes page).  Depends on the problem only (and on the SSD_SEGMENTS
+ * environment variable, which forces the number of segments per row); the
+ * contents need no initialisation. */
 size_t ssd_workspace_size(const ssd_problem_t* p);
 
-/* Full forward, one kernel launch on `stream`.
+/* Full forward on `stream`: one kernel launch, or three when rows are split
+ * into segments (see ssd_workspace_size).
  *   x          (batch, seqlen, nheads, headdim)   dtype
  *   dt         (batch, seqlen, nheads)            fp32, the step sizes (> 0 after softplus)
  *   A_log      (nheads)                           fp32; A_h = -exp(A_log[h])

@@ -747,6 +747,7 @@ void ssd_scan_kernel(ScanParams prm) {
                                     x_frag(sXw, LR, ks * KSTEP, p0, lr, lg), st[j]);
 #pragma unroll
             for (int i = 0; i < (LOCAL ? 0 : RTH); ++i) acc[i] *= sRow[16 * K::own_tile(nh, i) + lr];
+            if constexpr (!SEQ && !LOCAL && SZ == 2) pipeline_lds_mfma<6, K::TPW * NK + RTH * NK + MTH * KS, 2>();
         } else if constexpr (SEQ) {
             // ---- block with sequence starts, one segment at a time
             // (1) read-out of each segment's incoming state
