@@ -136,6 +136,28 @@ int ssd_forward(const ssd_problem_t* p,
                 float* y, float* final_state,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* One token of the recurrence (decoding), for every row and head, on the
+ * fp32 state in place:
+ *     state <- a * state + x B^T,   y = state C + D x,   a = exp(dt * A_h)
+ * exactly ssd_forward with seqlen 1, init_state = final_state = state (the
+ * recurrence of "088 Mamba-2", section 2.1, one step at a time; a chunked
+ * prefill followed by steps continues the same sequence).
+ *   p          problem with seqlen == 1 and nseqs == batch (chunk_len any valid value)
+ *   x          (batch, 1, nheads, headdim)   dtype
+ *   dt         (batch, 1, nheads)            fp32
+ *   A_log      (nheads)                      fp32
+ *   B, C       (batch, 1, ngroups, dstate)   dtype
+ *   D          (nheads) fp32, or NULL
+ *   state      (batch, nheads, headdim, dstate) fp32, read and written (required)
+ *   y          (batch, 1, nheads, headdim)   fp32 output
+ * SSD_FLAG_DT_SCALES_X applies as in ssd_forward.  One kernel launch; bound by
+ * reading and writing the state once.  y and state must not overlap each other
+ * or any input (SSD_ERR_ALIAS). */
+int ssd_step(const ssd_problem_t* p,
+             const void* x, const float* dt, const float* A_log,
+             const void* B, const void* C, const float* D,
+             float* state, float* y, void* stream);
+
 /* Static description of an error code. */
 const char* ssd_strerror(int status);
 

@@ -19,7 +19,7 @@ import ctypes
 import os
 from typing import Optional
 
-__all__ = ["forward", "forward_into", "workspace_size", "validate", "problem", "SSDError",
+__all__ = ["forward", "forward_into", "step", "workspace_size", "validate", "problem", "SSDError",
            "version", "library_path", "load_library", "DTYPE_F32", "DTYPE_BF16", "FLAG_DT_SCALES_X"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -67,6 +67,8 @@ def load_library():
     vp, sz = ctypes.c_void_p, ctypes.c_size_t
     lib.ssd_validate.argtypes = [P]
     lib.ssd_validate.restype = ctypes.c_int
+    lib.ssd_step.argtypes = [P] + [vp] * 9
+    lib.ssd_step.restype = ctypes.c_int
     lib.ssd_workspace_size.argtypes = [P]
     lib.ssd_workspace_size.restype = sz
     lib.ssd_forward.argtypes = [P] + [vp] * 10 + [vp, sz, vp]
@@ -198,3 +200,27 @@ def forward_into(p: Problem, x, dt, A_log, B, C, D, init_state, seq_idx, y, fina
     _check(load_library().ssd_forward(ctypes.byref(p), _ptr(x), _ptr(dt), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D),
                                       _ptr(init_state), _ptr(seq_idx), _ptr(y), _ptr(final_state),
                                       _ptr(workspace), wsn, _stream_of(x.device, stream)))
+
+
+def step(x, dt, A_log, B, C, D, state, y=None, dt_scales_x: bool = False, stream=None):
+    """``ssd_step``: one token per (row, head).  x (b,1,H,P) or (b,H,P), dt (b,1,H) or
+    (b,H), B/C (b,1,G,N) or (b,G,N); ``state`` (b,H,P,N) fp32 is updated in place.
+    Returns y (b,1,H,P) fp32."""
+    import torch
+    b = x.shape[0]
+    H, P = x.shape[-2], x.shape[-1]
+    G, N = B.shape[-2], B.shape[-1]
+    x = x.reshape(b, 1, H, P).contiguous()
+    dt = dt.reshape(b, 1, H).contiguous()
+    B = B.reshape(b, 1, G, N).contiguous()
+    C = C.reshape(b, 1, G, N).contiguous()
+    _check_tensors(x, dt, A_log, B, C, D, state, None)
+    if not state.is_contiguous() or tuple(state.shape) != (b, H, P, N) or state.dtype != torch.float32:
+        raise ValueError("state must be a contiguous fp32 (b,H,P,N) tensor")
+    p = _describe(x, B, dt, A_log, 64, None, None, dt_scales_x)
+    if y is None:
+        y = torch.empty((b, 1, H, P), dtype=torch.float32, device=x.device)
+    _check(load_library().ssd_step(ctypes.byref(p), _ptr(x), _ptr(dt), _ptr(A_log.contiguous()), _ptr(B), _ptr(C),
+                                   _ptr(D.contiguous() if D is not None else None), _ptr(state), _ptr(y),
+                                   _stream_of(x.device, stream)))
+    return y

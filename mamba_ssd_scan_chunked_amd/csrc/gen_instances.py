@@ -28,6 +28,12 @@ def gen_common(tag, TI, Ps, Ns, QBs):
     out.append("    if (grid <= 0) return hipSuccess;\n")
     for sq, eu, lo in itertools.product((0, 1), (0, 1), (0, 1)):
         out.append("    if (seq == %s && euler == %s && local == %s) return launch_scan_%s_s%d_e%d_l%d(P, N, QB, prm, grid, s);\n" % ("true" if sq else "false", "true" if eu else "false", "true" if lo else "false", tag, sq, eu, lo))
+    out.append("    return hipErrorInvalidValue;\n}\n\n")
+    out.append("hipError_t launch_step_%s(int P, int N, const StepParams& prm, int64_t grid, hipStream_t s) {\n" % tag)
+    out.append("    if (grid <= 0) return hipSuccess;\n")
+    for P in Ps:
+        for N in Ns:
+            out.append("    if (P == %d && N == %d) { hipLaunchKernelGGL((ssd_step_kernel<%s, %d, %d>), dim3((unsigned)grid), dim3(256), 0, s, prm); return hipGetLastError(); }\n" % (P, N, TI, P, N))
     out.append("    return hipErrorInvalidValue;\n}\n}  // namespace ssd\n")
     return "".join(out)
 

@@ -298,6 +298,50 @@ int ssd_forward(const ssd_problem_t* p, const void* x, const float* dt, const fl
                        static_cast<hipStream_t>(stream));
 }
 
+int ssd_step(const ssd_problem_t* p, const void* x, const float* dt, const float* A_log, const void* B,
+             const void* C, const float* D, float* state, float* y, void* stream) {
+    if (!p) return SSD_ERR_NULL_POINTER;
+    if (p->seqlen != 1 || p->nseqs != p->batch) return SSD_ERR_BAD_SHAPE;
+    const int v = ssd_validate(p);
+    if (v != SSD_OK) return v;
+    if (!A_log) return SSD_ERR_NULL_POINTER;
+    if (p->batch > 0 && (!x || !dt || !B || !C || !state || !y)) return SSD_ERR_NULL_POINTER;
+    if (misaligned(x, 16) || misaligned(B, 16) || misaligned(C, 16) || misaligned(state, 16) ||
+        misaligned(y, 4) || misaligned(dt, 4) || misaligned(A_log, 4) || misaligned(D, 4))
+        return SSD_ERR_ALIGNMENT;
+    const Sizes s = sizes(p);
+    const int64_t hb = p->nheads * 4;
+    const void* in_ptr[] = {x, dt, A_log, B, C, D};
+    const int64_t in_sz[] = {s.x, s.dt, hb, s.bc, s.bc, hb};
+    for (int i = 0; i < 6; ++i)
+        if (overlap(y, s.y, in_ptr[i], in_sz[i]) || overlap(state, s.state, in_ptr[i], in_sz[i])) return SSD_ERR_ALIAS;
+    if (overlap(y, s.y, state, s.state)) return SSD_ERR_ALIAS;
+    const int d = check_device();
+    if (d != SSD_OK) return d;
+    ssd::StepParams prm;
+    prm.x = x;
+    prm.dt = dt;
+    prm.A_log = A_log;
+    prm.B = B;
+    prm.C = C;
+    prm.D = D;
+    prm.state = state;
+    prm.y = y;
+    prm.batch = p->batch;
+    prm.H = p->nheads;
+    prm.G = p->ngroups;
+    prm.dt_scales_x = (p->flags & SSD_FLAG_DT_SCALES_X) ? 1 : 0;
+    const int64_t grid = p->batch * p->nheads;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const hipError_t e = p->dtype == SSD_DTYPE_BF16
+                             ? ssd::launch_step_bf16((int)p->headdim, (int)p->dstate, prm, grid, st)
+                             : ssd::launch_step_f32((int)p->headdim, (int)p->dstate, prm, grid, st);
+    if (log_enabled())
+        std::fprintf(stderr, "[ssd] step dtype=%d P=%lld N=%lld grid=%lld -> %s\n", p->dtype, (long long)p->headdim,
+                     (long long)p->dstate, (long long)grid, hipGetErrorString(e));
+    return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+}
+
 const char* ssd_strerror(int status) {
     switch (status) {
         case SSD_OK: return "success";

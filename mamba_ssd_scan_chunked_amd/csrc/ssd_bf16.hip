@@ -22,4 +22,15 @@ hipError_t launch_scan_bf16(int P, int N, int QB, bool seq, bool euler, bool loc
     if (seq == true && euler == true && local == true) return launch_scan_bf16_s1_e1_l1(P, N, QB, prm, grid, s);
     return hipErrorInvalidValue;
 }
+
+hipError_t launch_step_bf16(int P, int N, const StepParams& prm, int64_t grid, hipStream_t s) {
+    if (grid <= 0) return hipSuccess;
+    if (P == 32 && N == 64) { hipLaunchKernelGGL((ssd_step_kernel<__bf16, 32, 64>), dim3((unsigned)grid), dim3(256), 0, s, prm); return hipGetLastError(); }
+    if (P == 32 && N == 128) { hipLaunchKernelGGL((ssd_step_kernel<__bf16, 32, 128>), dim3((unsigned)grid), dim3(256), 0, s, prm); return hipGetLastError(); }
+    if (P == 32 && N == 256) { hipLaunchKernelGGL((ssd_step_kernel<__bf16, 32, 256>), dim3((unsigned)grid), dim3(256), 0, s, prm); return hipGetLastError(); }
+    if (P == 64 && N == 64) { hipLaunchKernelGGL((ssd_step_kernel<__bf16, 64, 64>), dim3((unsigned)grid), dim3(256), 0, s, prm); return hipGetLastError(); }
+    if (P == 64 && N == 128) { hipLaunchKernelGGL((ssd_step_kernel<__bf16, 64, 128>), dim3((unsigned)grid), dim3(256), 0, s, prm); return hipGetLastError(); }
+    if (P == 64 && N == 256) { hipLaunchKernelGGL((ssd_step_kernel<__bf16, 64, 256>), dim3((unsigned)grid), dim3(256), 0, s, prm); return hipGetLastError(); }
+    return hipErrorInvalidValue;
+}
 }  // namespace ssd

@@ -301,6 +301,75 @@ struct CombineParams {
     int P, N, nseg;
 };
 
+// ============================================================== recurrent step
+// One token of the recurrence per (row, head), on the fp32 state in place:
+// S <- a S + x B^T, y = S C + D x, a = exp(dt A) (the recurrence of "088
+// Mamba-2", section 2.1, one step; the decay of the selective-SSM section of
+// the Mamba story; the skip term of section 2 of "Mamba and state space
+// models").  Bound by the state's HBM read and write.
+struct StepParams {
+    const void* x;          // (batch, H, P)
+    const float* dt;        // (batch, H)
+    const float* A_log;     // (H)
+    const void* B;          // (batch, G, N)
+    const void* C;          // (batch, G, N)
+    const float* D;         // (H) or null
+    float* state;           // (batch, H, P, N), updated in place
+    float* y;               // (batch, H, P)
+    int64_t batch, H, G;
+    int dt_scales_x;
+};
+
+// One workgroup of 256 threads per (row, head).  Thread t owns state row
+// p = t / R (R = 256 / P threads per row) and the NPT = N / R consecutive
+// values n in [q NPT, (q + 1) NPT), q = t % R; the read-out of row p is summed
+// over its R lanes (consecutive in the wave) in a fixed order.
+template <typename TI, int P, int N>
+__global__ __launch_bounds__(256) void ssd_step_kernel(StepParams prm) {
+    constexpr int R = 256 / P, NPT = N / R;
+    static_assert(256 % P == 0 && R <= 64 && N % R == 0, "step shape");
+    const int64_t bh = blockIdx.x;
+    const int64_t b = bh / prm.H, h = bh % prm.H;
+    const int64_t g = h / (prm.H / prm.G);
+    const int tid = threadIdx.x, p = tid / R, q = tid % R;
+    const float xv = to_f32(((const TI*)prm.x)[bh * P + p]);
+    const float dtv = prm.dt[bh];
+    const float a = expf(dtv * -expf(prm.A_log[h]));
+    const float xs = prm.dt_scales_x ? dtv * xv : xv;        // Euler input scaling (D uses x)
+    const TI* Bg = (const TI*)prm.B + (b * prm.G + g) * N + q * NPT;
+    const TI* Cg = (const TI*)prm.C + (b * prm.G + g) * N + q * NPT;
+    float* srow = prm.state + (bh * P + p) * N + q * NPT;
+    float acc = 0.f;
+    if constexpr (NPT % 4 == 0) {
+#pragma unroll
+        for (int j = 0; j < NPT; j += 4) {
+            float4 sv = *(const float4*)(srow + j);
+            float bv[4], cv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                bv[e] = to_f32(Bg[j + e]);
+                cv[e] = to_f32(Cg[j + e]);
+            }
+            sv.x = a * sv.x + xs * bv[0];
+            sv.y = a * sv.y + xs * bv[1];
+            sv.z = a * sv.z + xs * bv[2];
+            sv.w = a * sv.w + xs * bv[3];
+            *(float4*)(srow + j) = sv;
+            acc += cv[0] * sv.x + cv[1] * sv.y + cv[2] * sv.z + cv[3] * sv.w;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < NPT; ++j) {
+            const float sv = a * srow[j] + xs * to_f32(Bg[j]);
+            srow[j] = sv;
+            acc += to_f32(Cg[j]) * sv;
+        }
+    }
+#pragma unroll
+    for (int d = R / 2; d >= 1; d >>= 1) acc += __shfl_xor(acc, d);
+    if (q == 0) prm.y[bh * P + p] = acc + (prm.D ? prm.D[h] : 0.f) * xv;
+}
+
 // ============================================================== scan kernel
 template <typename TI> struct CumType { typedef float type; };
 template <> struct CumType<float> { typedef double type; };   // fp32 path: exponent differences in fp64

@@ -7,6 +7,7 @@
 namespace ssd {
 struct ScanParams;
 struct CombineParams;
+struct StepParams;
 
 // Return hipSuccess, hipErrorInvalidValue for a shape with no instantiation,
 // or the launch error.
@@ -17,6 +18,8 @@ hipError_t launch_scan_bf16(int P, int N, int QB, bool seq, bool euler, bool loc
 hipError_t launch_scan_f32(int P, int N, int QB, bool seq, bool euler, bool local, const ScanParams& prm,
                            int64_t grid, hipStream_t s);
 hipError_t launch_combine(const CombineParams& prm, hipStream_t s);
+hipError_t launch_step_bf16(int P, int N, const StepParams& prm, int64_t grid, hipStream_t s);
+hipError_t launch_step_f32(int P, int N, const StepParams& prm, int64_t grid, hipStream_t s);
 #define SSD_DECLARE_SCAN(tag, sq, eu, lo) \
     hipError_t launch_scan_##tag##_s##sq##_e##eu##_l##lo(int P, int N, int QB, const ScanParams& prm, int64_t grid, hipStream_t s);
 #define SSD_DECLARE_SCAN2(tag, sq, eu) SSD_DECLARE_SCAN(tag, sq, eu, 0) SSD_DECLARE_SCAN(tag, sq, eu, 1)

@@ -139,3 +139,32 @@ def test_binding_refuses_cpu_tensors():
     B = torch.zeros(1, 64, 1, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         ssd.forward(x, torch.zeros(1, 64, 2), torch.zeros(2), B, B)
+
+
+def _step(p, **ptrs):
+    lib = ssd.load_library()
+    names = ["x", "dt", "A_log", "B", "C", "D", "state", "y"]
+    vals = {n: A + 0x1000000 * (i + 1) for i, n in enumerate(names)}
+    vals.update({"D": None})
+    vals.update(ptrs)
+    return lib.ssd_step(ctypes.byref(p), *[vals[n] for n in names], None)
+
+
+def test_step_rejects_bad_arguments():
+    one = prob(batch=2, seqlen=1, nheads=4, headdim=64, dstate=128)
+    assert _step(prob(batch=2, seqlen=2, nheads=4)) == 2                  # one token only
+    assert _step(prob(batch=2, seqlen=1, nheads=4, nseqs=3)) == 2         # no packed sequences
+    assert _step(prob(batch=2, seqlen=1, nheads=4, headdim=48)) == 3      # unsupported shape
+    for n in ("x", "dt", "A_log", "B", "C", "state", "y"):
+        assert _step(one, **{n: None}) == 1, n
+    assert _step(one, state=A + 0x7000000 + 8) == 4                      # misaligned state
+    assert _step(one, y=A + 0x1000000) == 6                               # y on top of x
+    assert _step(one, state=A + 0x4000000) == 6                           # state on top of B
+    assert _step(one, y=A + 0x7000000) == 6                               # y on top of the state
+
+
+def test_step_without_device_reports_no_device():
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present: this call would launch on fake pointers")
+    assert _step(prob(batch=2, seqlen=1, nheads=4, headdim=64, dstate=128)) == 8
