@@ -730,14 +730,21 @@ void ssd_scan_kernel(ScanParams prm) {
     typedef typename std::conditional<SZ == 2, bf16x4, f32x4>::type lm_t;
     lm_t lmv[K::TPW];
     auto lm_phase = [&]() {
+        // K step outer, tile inner: consecutive MFMAs go to independent accumulators
+        f32x4 cbt[K::TPW];
+#pragma unroll
+        for (int j = 0; j < K::TPW; ++j) cbt[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < NK; ++k)
+#pragma unroll
+            for (int j = 0; j < K::TPW; ++j)
+                cbt[j] = MF::mma(brow_frag<N, LB>(sB, 16 * tJ[j] + lr, k, lg),
+                                 crow_frag<N>(sC + (16 * tI[j] + lr) * LC, k, lg), cbt[j]);
 #pragma unroll
         for (int j = 0; j < K::TPW; ++j) {
             const int I = tI[j], J = tJ[j];                      // uniform over the wave
             const int t = 16 * I + lr, s0 = 16 * J + 4 * lg;
-            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int k = 0; k < NK; ++k)
-                acc = MF::mma(brow_frag<N, LB>(sB, 16 * J + lr, k, lg), crow_frag<N>(sC + t * LC, k, lg), acc);
+            const f32x4 acc = cbt[j];
             const cum_t ct = sCum[t];
             cum_t csv[4];
             if constexpr (sizeof(cum_t) == 4) {
@@ -793,15 +800,21 @@ void ssd_scan_kernel(ScanParams prm) {
 #pragma unroll
         for (int i = 0; i < RTH; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (!SEQ || nstart == 0) {
-            // carried state read out by C:  S C^T
+            // carried state read out by C:  S C^T (K step outer: the token tiles'
+            // accumulators alternate, so consecutive MFMAs are independent)
+            if constexpr (!LOCAL) {
+                const TI* crw[RTH];
 #pragma unroll
-            for (int i = 0; i < (LOCAL ? 0 : RTH); ++i) {
-                const TI* crw = sC + (16 * K::own_tile(nh, i) + lr) * LC;
+                for (int i = 0; i < RTH; ++i) crw[i] = sC + (16 * K::own_tile(nh, i) + lr) * LC;
 #pragma unroll
-                for (int j = 0; j < NKH; ++j) acc[i] = MF::mma(sfo[j], c_frag<N>(crw, kbo + j, lg), acc[i]);
+                for (int j = 0; j < NKH; ++j)
+#pragma unroll
+                    for (int i = 0; i < RTH; ++i) acc[i] = MF::mma(sfo[j], c_frag<N>(crw[i], kbo + j, lg), acc[i]);
                 if constexpr (NH > 1) {
 #pragma unroll
-                    for (int j = 0; j < NKH; ++j) acc[i] = MF::mma(sfp[j], c_frag<N>(crw, kbp + j, lg), acc[i]);
+                    for (int j = 0; j < NKH; ++j)
+#pragma unroll
+                        for (int i = 0; i < RTH; ++i) acc[i] = MF::mma(sfp[j], c_frag<N>(crw[i], kbp + j, lg), acc[i]);
                 }
             }
             // state <- exp(cum_end) state + B^T (weighted X)
@@ -809,11 +822,11 @@ void ssd_scan_kernel(ScanParams prm) {
 #pragma unroll
             for (int j = 0; j < MTH; ++j) st[j] *= alpha;
 #pragma unroll
-            for (int j = 0; j < MTH; ++j)
+            for (int ks = 0; ks < KS; ++ks) {
+                const frag xw = x_frag(sXw, LR, ks * KSTEP, p0, lr, lg);
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    st[j] = MF::mma(bt_frag<N, LB>(sB, mb + j, ks * KSTEP, lr, lg),
-                                    x_frag(sXw, LR, ks * KSTEP, p0, lr, lg), st[j]);
+                for (int j = 0; j < MTH; ++j) st[j] = MF::mma(bt_frag<N, LB>(sB, mb + j, ks * KSTEP, lr, lg), xw, st[j]);
+            }
 #pragma unroll
             for (int i = 0; i < (LOCAL ? 0 : RTH); ++i) acc[i] *= sRow[16 * K::own_tile(nh, i) + lr];
             if constexpr (!SEQ && !LOCAL && SZ == 2) pipeline_lds_mfma<6, K::TPW * NK + RTH * NK + MTH * KS, 2>();
