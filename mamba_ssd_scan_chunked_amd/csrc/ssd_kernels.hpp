@@ -166,6 +166,21 @@ __device__ inline float x_frag(const float* sX, int lp, int ks, int p0, int lr, 
     return sX[(ks + lg) * lp + p0 + lr];
 }
 
+// The same operand with every token t scaled by wt(t) (and rounded once to the
+// input type): the K values a lane holds are tokens ks + KPL*(l/16) + e.
+template <typename F>
+__device__ inline bf16x8 weighted_x_frag(const __bf16* sX, int lp, int ks, int p0, int lr, int lg, F wt) {
+    const bf16x8 x = x_frag(sX, lp, ks, p0, lr, lg);
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = (__bf16)(wt(ks + 8 * lg + e) * (float)x[e]);
+    return r;
+}
+template <typename F>
+__device__ inline float weighted_x_frag(const float* sX, int lp, int ks, int p0, int lr, int lg, F wt) {
+    return wt(ks + lg) * x_frag(sX, lp, ks, p0, lr, lg);
+}
+
 // B tile in LDS: row t holds the N values of token t, pitch LB = N + 4
 // elements (8-byte aligned rows for bf16).  The transposing reads of the state
 // update and the row reads of C B^T see at most 2-way bank conflicts.
@@ -428,14 +443,14 @@ struct ScanCfg {
                                                       // distinct banks)
     static constexpr int NTILE = RT * (RT + 1) / 2;   // causal 16x16 tiles of L o CB
     static constexpr int TPW = (NTILE + NW - 1) / NW; // causal tiles per wave (surplus slots repeat a tile)
-    // LDS tiles: C, B (both token-major), masked decay L o CB, X and end-state-weighted X
-    // (row-major) and, with NH = 2, each wave's half of the state as read-out operands
+    // LDS tiles: C, B (both token-major), masked decay L o CB, X (row-major; the
+    // state update weights it per token in registers) and, with NH = 2, each wave's
+    // half of the state as read-out operands
     static constexpr int OFF_C = 0;
     static constexpr int OFF_B = OFF_C + QB * LC;
     static constexpr int OFF_LM = OFF_B + QB * LB;
     static constexpr int OFF_XR = OFF_LM + QB * LQ;
-    static constexpr int OFF_XW = OFF_XR + QB * LR;
-    static constexpr int OFF_SX = OFF_XW + QB * LR;
+    static constexpr int OFF_SX = OFF_XR + QB * LR;
     static constexpr int BUF_ELEMS = OFF_SX + (NH > 1 ? NW * NKH * 64 * KPL : 0);
     // per-thread work units
     static constexpr int CV = QB * N / VE, CPT = (CV + NT - 1) / NT;           // C (and B) tile vectors
@@ -472,6 +487,7 @@ void ssd_scan_kernel(ScanParams prm) {
     constexpr int SQ = SEQ ? 1 : 0, EU = EULER ? 1 : 0;
     __shared__ __attribute__((aligned(16))) cum_t sCum[64];       // cumulative log2 decay
     __shared__ __attribute__((aligned(16))) float sRow[64];       // read-out row scale
+    __shared__ __attribute__((aligned(16))) float sWx[64];        // end-state weight exp2(cum_end - cum) (dt)
     __shared__ __attribute__((aligned(16))) float sDtf[64 * EU + 4];   // dt (Euler input scaling)
     __shared__ __attribute__((aligned(16))) int sSeg[64 * SQ + 4];     // segment of each token
     __shared__ int sStart[65 * SQ + 1];
@@ -481,7 +497,6 @@ void ssd_scan_kernel(ScanParams prm) {
     TI* sB = smem + K::OFF_B;
     TI* sLm = smem + K::OFF_LM;
     TI* sXr = smem + K::OFF_XR;
-    TI* sXw = smem + K::OFF_XW;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -691,31 +706,18 @@ void ssd_scan_kernel(ScanParams prm) {
         seg_total += cend;
         seg_reset |= nstart > 0;
         const float dtf = EULER ? dtv : 1.f;
-        const float wx = fast_exp2((float)(cend - cum)) * dtf;  // end-state weight of token lane
         if (w == 0 && lane < QB) {
             sCum[lane] = cum;
             sRow[lane] = fast_exp2((float)(cum - before));
+            sWx[lane] = fast_exp2((float)(cend - cum)) * dtf;  // end-state weight of token lane
             if constexpr (EULER) sDtf[lane] = dtv;
         }
 
-        // X (row-major) and, for single-segment blocks, the end-state weighted X
-        // (each thread holds VE channels of one token)
+        // X (row-major; each thread holds VE channels of one token)
 #pragma unroll
         for (int j = 0; j < K::XPT; ++j) {
             const int v = tid + j * NT;
-            const int t = (v / (P / VE)) & 63, c = v % (P / VE);
-            const float wt = __shfl(wx, t);
-            if (K::XU % NT == 0 || v < K::XU) {
-                *(uint4*)(sXr + t * LR + c * VE) = xr[j];
-                if (!SEQ || nstart == 0) {
-                    TI wxv[VE];
-#pragma unroll
-                    for (int k = 0; k < VE; ++k) wxv[k] = to_in<TI>(wt * to_f32(((const TI*)&xr[j])[k]));
-                    uint4 pk;
-                    __builtin_memcpy(&pk, wxv, 16);
-                    *(uint4*)(sXw + t * LR + c * VE) = pk;
-                }
-            }
+            if (K::XU % NT == 0 || v < K::XU) *(uint4*)(sXr + (v / (P / VE)) * LR + (v % (P / VE)) * VE) = xr[j];
         }
     };
 
@@ -823,7 +825,7 @@ void ssd_scan_kernel(ScanParams prm) {
             for (int j = 0; j < MTH; ++j) st[j] *= alpha;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const frag xw = x_frag(sXw, LR, ks * KSTEP, p0, lr, lg);
+                const frag xw = weighted_x_frag(sXr, LR, ks * KSTEP, p0, lr, lg, [&](int t) { return sWx[t]; });
 #pragma unroll
                 for (int j = 0; j < MTH; ++j) st[j] = MF::mma(bt_frag<N, LB>(sB, mb + j, ks * KSTEP, lr, lg), xw, st[j]);
             }
@@ -868,15 +870,13 @@ void ssd_scan_kernel(ScanParams prm) {
                 const int a = sStart[j];
                 const int e = (j < nstart) ? sStart[j + 1] - 1 : QB - 1;
                 if (e < a) continue;
-                block_sync_lds();                             // the previous segment's weighted X is consumed
-                for (int v = tid; v < P * QB; v += NT) {
-                    const int t = v / P, pr = v % P;
+                // end-of-segment weights: exp2(cum_e - cum_t) (dt) for the segment's tokens, else 0
+                const cum_t ce = sCum[e];
+                auto wseg = [&](int t) {
                     float df = 1.f;
                     if constexpr (EULER) df = sDtf[t];
-                    const float ws = (sSeg[t] == j) ? fast_exp2((float)(sCum[e] - sCum[t])) * df : 0.f;
-                    sXw[t * LR + pr] = to_in<TI>(ws * to_f32(sXr[t * LR + pr]));
-                }
-                block_sync_lds();
+                    return (sSeg[t] == j) ? fast_exp2((float)(ce - sCum[t])) * df : 0.f;
+                };
                 const cum_t before = (a == 0) ? (cum_t)0 : sCum[a - 1];
                 const float carry = fast_exp2((float)(sCum[e] - before));
                 f32x4 F[MTH];
@@ -895,11 +895,11 @@ void ssd_scan_kernel(ScanParams prm) {
                     for (int q = 0; q < MTH; ++q) F[q] = f32x4{0.f, 0.f, 0.f, 0.f};
                 }
 #pragma unroll
-                for (int q = 0; q < MTH; ++q)
+                for (int ks = 0; ks < KS; ++ks) {
+                    const frag xw = weighted_x_frag(sXr, LR, ks * KSTEP, p0, lr, lg, wseg);
 #pragma unroll
-                    for (int ks = 0; ks < KS; ++ks)
-                        F[q] = MF::mma(bt_frag<N, LB>(sB, mb + q, ks * KSTEP, lr, lg),
-                                       x_frag(sXw, LR, ks * KSTEP, p0, lr, lg), F[q]);
+                    for (int q = 0; q < MTH; ++q) F[q] = MF::mma(bt_frag<N, LB>(sB, mb + q, ks * KSTEP, lr, lg), xw, F[q]);
+                }
                 if (j < nstart) {
                     if constexpr (!LOCAL) write_state(F, sSeqOf[j]);
                 } else {
