@@ -9,11 +9,15 @@ import itertools
 def gen(tag, TI, Ps, Ns, QBs, seq, eul, loc):
     out = ['// Kernel instantiations: %s inputs, %s sequence ids, %s Euler input scaling, %s.\n#include "ssd_kernels.hpp"\n#include "ssd_launch.hpp"\n\nnamespace ssd {\n' % (tag, "with" if seq else "without", "with" if eul else "without", "local pass" if loc else "scan")]
     fn = "launch_scan_%s_s%d_e%d_l%d" % (tag, seq, eul, loc)
-    out.append("hipError_t %s(int P, int N, int QB, const ScanParams& prm, int64_t grid, hipStream_t s) {\n" % fn)
+    out.append("hipError_t %s(int P, int N, int QB, int spw, const ScanParams& prm, int64_t grid, hipStream_t s) {\n" % fn)
+    b = lambda v: "true" if v else "false"
     for P in Ps:
         for N in Ns:
             for Q in QBs:
-                out.append("    if (P == %d && N == %d && QB == %d) { hipLaunchKernelGGL((ssd_scan_kernel<%s, %d, %d, %d, %s, %s, %s>), dim3((unsigned)grid), dim3(ScanCfg<%s, %d, %d, %d>::NT), 0, s, prm); return hipGetLastError(); }\n" % (P, N, Q, TI, P, N, Q, "true" if seq else "false", "true" if eul else "false", "true" if loc else "false", TI, P, N, Q))
+                spws = [P // 16] + ([P // 16 + 1] if (tag, P, seq, loc) == ("bf16", 64, 0, 0) else [])
+                for spw in spws:
+                    out.append("    if (P == %d && N == %d && QB == %d && spw == %d) { hipLaunchKernelGGL((ssd_scan_kernel<%s, %d, %d, %d, %s, %s, %s, %d>), dim3((unsigned)grid), dim3(ScanCfg<%s, %d, %d, %d, %d>::NT), 0, s, prm); return hipGetLastError(); }\n"
+                               % (P, N, Q, spw, TI, P, N, Q, b(seq), b(eul), b(loc), spw, TI, P, N, Q, spw))
     out.append("    return hipErrorInvalidValue;\n}\n}  // namespace ssd\n")
     return "".join(out)
 
@@ -24,10 +28,10 @@ def gen_common(tag, TI, Ps, Ns, QBs):
     out.append("    const bool n = %s;\n" % " || ".join("N == %d" % v for v in Ns))
     out.append("    const bool q = %s;\n" % " || ".join("QB == %d" % v for v in QBs))
     out.append("    return p && n && q;\n}\n\n")
-    out.append("hipError_t launch_scan_%s(int P, int N, int QB, bool seq, bool euler, bool local, const ScanParams& prm, int64_t grid, hipStream_t s) {\n" % tag)
+    out.append("hipError_t launch_scan_%s(int P, int N, int QB, bool seq, bool euler, bool local, int spw, const ScanParams& prm, int64_t grid, hipStream_t s) {\n" % tag)
     out.append("    if (grid <= 0) return hipSuccess;\n")
     for sq, eu, lo in itertools.product((0, 1), (0, 1), (0, 1)):
-        out.append("    if (seq == %s && euler == %s && local == %s) return launch_scan_%s_s%d_e%d_l%d(P, N, QB, prm, grid, s);\n" % ("true" if sq else "false", "true" if eu else "false", "true" if lo else "false", tag, sq, eu, lo))
+        out.append("    if (seq == %s && euler == %s && local == %s) return launch_scan_%s_s%d_e%d_l%d(P, N, QB, spw, prm, grid, s);\n" % ("true" if sq else "false", "true" if eu else "false", "true" if lo else "false", tag, sq, eu, lo))
     out.append("    return hipErrorInvalidValue;\n}\n\n")
     out.append("hipError_t launch_step_%s(int P, int N, const StepParams& prm, int64_t grid, hipStream_t s) {\n" % tag)
     out.append("    if (grid <= 0) return hipSuccess;\n")

@@ -115,6 +115,20 @@ WsLayout ws_layout(const ssd_problem_t* p) {
 }
 int64_t workspace_bytes(const ssd_problem_t* p) { return ws_layout(p).total; }
 
+// 16-channel slices per scan workgroup.  One head (P / 16) by default.  With
+// between 256 and 320 (row, head) items of 64 channels (bf16, no sequence ids,
+// unsplit rows), five slices per workgroup spread the items evenly over 256
+// workgroups (one per compute unit) instead of leaving some units with two
+// heads; the slices of a workgroup must then lie in one B/C group.
+int slices_per_workgroup(const ssd_problem_t* p, bool seq, int nseg) {
+    const int npt = (int)(p->headdim / 16);
+    const int64_t items = p->batch * p->nheads;
+    if (p->dtype == SSD_DTYPE_BF16 && p->headdim == 64 && !seq && nseg == 1 && items > 256 && items <= 320 &&
+        ((p->nheads / p->ngroups) * npt) % (npt + 1) == 0)
+        return npt + 1;
+    return npt;
+}
+
 bool misaligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) != 0; }
 
 bool overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
@@ -218,13 +232,15 @@ int launch_scan(const ssd_problem_t* p, const void* x, const float* dt, const fl
     if (p->seqlen == 0 && (seq_idx || !fin)) return SSD_OK;   // no token, no sequence to hand out
     const bool seq = seq_idx != nullptr, euler = prm.dt_scales_x != 0;
     const int P = (int)p->headdim, N = (int)p->dstate;
-    auto scan = [&](bool local, int64_t grid) {
-        return p->dtype == SSD_DTYPE_BF16 ? ssd::launch_scan_bf16(P, N, q, seq, euler, local, prm, grid, stream)
-                                          : ssd::launch_scan_f32(P, N, q, seq, euler, local, prm, grid, stream);
+    const int npt = P / 16;
+    auto scan = [&](bool local, int spw, int64_t grid) {
+        return p->dtype == SSD_DTYPE_BF16 ? ssd::launch_scan_bf16(P, N, q, seq, euler, local, spw, prm, grid, stream)
+                                          : ssd::launch_scan_f32(P, N, q, seq, euler, local, spw, prm, grid, stream);
     };
+    const int spw = slices_per_workgroup(p, seq, sg.nseg);
     hipError_t e = hipSuccess;
     if (sg.nseg > 1) {
-        e = scan(true, rows * (sg.nseg - 1));
+        e = scan(true, npt, rows * (sg.nseg - 1));
         if (e == hipSuccess) {
             ssd::CombineParams cp;
             cp.init = init;
@@ -241,10 +257,10 @@ int launch_scan(const ssd_problem_t* p, const void* x, const float* dt, const fl
             e = ssd::launch_combine(cp, stream);
         }
     }
-    if (e == hipSuccess) e = scan(false, rows * sg.nseg);
+    if (e == hipSuccess) e = scan(false, spw, p->batch * (p->nheads * npt / spw) * sg.nseg);
     if (log_enabled())
-        std::fprintf(stderr, "[ssd] scan dtype=%d P=%d N=%d QB=%d rows=%lld segments=%d x %d blocks -> %s\n",
-                     p->dtype, P, N, q, (long long)rows, sg.nseg, sg.seg_blocks, hipGetErrorString(e));
+        std::fprintf(stderr, "[ssd] scan dtype=%d P=%d N=%d QB=%d rows=%lld segments=%d x %d blocks, %d slices/wg -> %s\n",
+                     p->dtype, P, N, q, (long long)rows, sg.nseg, sg.seg_blocks, spw, hipGetErrorString(e));
     return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
 }
 

@@ -416,7 +416,11 @@ __device__ inline double wave_incl_scan(double x) {
     return x;
 }
 
-template <typename TI, int P, int N, int QB>
+// SPW: 16-channel slices per workgroup.  By default a workgroup holds one head
+// (SPW = P / 16); with more, it holds SPW consecutive slices of a row, which
+// may belong to two heads (consecutive slices are consecutive channels of the
+// flattened (head, channel) dimension).
+template <typename TI, int P, int N, int QB, int SPW_ = P / 16>
 struct ScanCfg {
     static constexpr int SZ = (int)sizeof(TI);
     static constexpr int VE = 16 / SZ;                // elements per 16-byte vector
@@ -425,20 +429,24 @@ struct ScanCfg {
     static constexpr int RT = QB / 16;                // token tiles of a block
     static constexpr int MT = N / 16;                 // state tiles of one 16-channel slice
     static constexpr int NPT = P / 16;                // 16-channel slices of a head
+    static constexpr int SPW = SPW_;                  // slices of this workgroup
+    static constexpr int MLH = SPW % NPT == 0 ? SPW / NPT : (SPW + NPT - 2) / NPT + 1;   // heads it may touch
+    static constexpr int XW = 16 * SPW;               // channels of the workgroup's X tile
     // Each slice is shared by NH waves: wave (slice pt, half nh) owns state tiles
     // [nh MT/NH, (nh+1) MT/NH) (whole K steps of the read-out) and token tiles
     // own_tile(nh, i) of the outputs.
     static constexpr int NH = (SZ == 2 ? MT % 4 == 0 : MT % 2 == 0) && RT % 2 == 0 ? 2 : 1;
-    static constexpr int NW = NPT * NH;
+    static constexpr int NW = SPW * NH;
     static constexpr int NT = NW * 64;
-    static constexpr int WPE = NW >= 8 ? NW / 2 : 2;   // waves per SIMD for two workgroups per CU
+    static constexpr int WPE = SPW != NPT ? (NW + 3) / 4   // one workgroup per CU
+                             : NW >= 8 ? NW / 2 : 2;       // waves per SIMD for two workgroups per CU
                                                       // (the sequence-id variants, whose segment path
                                                       // needs more registers, are left at two)
     static constexpr int MTH = MT / NH, NKH = NK / NH, RTH = RT / NH;
     static constexpr int LC = N + VE;                 // pitch of C rows (elements)
     static constexpr int LB = N + 4;                  // pitch of B rows
     static constexpr int LQ = QB + VE;                // pitch of the rows of L o CB (indexed by token s)
-    static constexpr int LR = P + 32 / SZ;            // pitch of the row-major X tiles (32 bytes of pad:
+    static constexpr int LR = XW + 32 / SZ;           // pitch of the row-major X tile (32 bytes of pad:
                                                       // the four rows of a transposed read fall in
                                                       // distinct banks)
     static constexpr int NTILE = RT * (RT + 1) / 2;   // causal 16x16 tiles of L o CB
@@ -449,12 +457,12 @@ struct ScanCfg {
     static constexpr int OFF_C = 0;
     static constexpr int OFF_B = OFF_C + QB * LC;
     static constexpr int OFF_LM = OFF_B + QB * LB;
-    static constexpr int OFF_XR = OFF_LM + QB * LQ;
+    static constexpr int OFF_XR = OFF_LM + MLH * QB * LQ;            // L o CB of each head
     static constexpr int OFF_SX = OFF_XR + QB * LR;
     static constexpr int BUF_ELEMS = OFF_SX + (NH > 1 ? NW * NKH * 64 * KPL : 0);
     // per-thread work units
     static constexpr int CV = QB * N / VE, CPT = (CV + NT - 1) / NT;           // C (and B) tile vectors
-    static constexpr int XU = QB * P / VE, XPT = (XU + NT - 1) / NT;            // 16-byte pieces of the X tile
+    static constexpr int XU = QB * XW / VE, XPT = (XU + NT - 1) / NT;           // 16-byte pieces of the X tile
     // token tile i of the outputs of half nh: the causal work of the diagonal
     // block is split evenly ({0, 3} and {1, 2} of four tiles)
     __device__ static inline int own_tile(int nh, int i) {
@@ -466,17 +474,17 @@ struct ScanCfg {
 
 // LOCAL: the local pass over segments 0 .. nseg-2 (end state from a zero incoming
 // state and the carried decay, no outputs); otherwise the scan proper.
-template <typename TI, int P, int N, int QB, bool SEQ, bool EULER, bool LOCAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(1, ScanCfg<TI, P, N, QB>::NT),
-                          amdgpu_waves_per_eu(SEQ ? 2 : ScanCfg<TI, P, N, QB>::WPE)))
+template <typename TI, int P, int N, int QB, bool SEQ, bool EULER, bool LOCAL, int SPW = P / 16>
+__global__ __attribute__((amdgpu_flat_work_group_size(1, ScanCfg<TI, P, N, QB, SPW>::NT),
+                          amdgpu_waves_per_eu(SEQ && SPW == P / 16 ? 2 : ScanCfg<TI, P, N, QB, SPW>::WPE)))
 void ssd_scan_kernel(ScanParams prm) {
-    typedef ScanCfg<TI, P, N, QB> K;
+    typedef ScanCfg<TI, P, N, QB, SPW> K;
     typedef Mfma<TI> MF;
     typedef typename MF::frag frag;
     typedef typename CumType<TI>::type cum_t;
     constexpr int NT = K::NT, VE = K::VE, LC = K::LC, LB = K::LB, LQ = K::LQ, LR = K::LR, KPL = K::KPL;
     constexpr int KSTEP = K::KSTEP, SZ = K::SZ, NK = K::NK, RT = K::RT, MT = K::MT, NW = K::NW;
-    constexpr int NH = K::NH, NPT = K::NPT, MTH = K::MTH, NKH = K::NKH, RTH = K::RTH;
+    constexpr int NH = K::NH, NPT = K::NPT, MTH = K::MTH, NKH = K::NKH, RTH = K::RTH, MLH = K::MLH, XW = K::XW;
     constexpr int NFH = SZ == 2 ? MTH / 2 : 4 * MTH;               // read-out fragments of a state half
     static_assert(NFH == NKH, "fragments of a state half are whole K steps");
     static_assert(QB <= 64 && QB % KSTEP == 0 && QB % 16 == 0, "block length");
@@ -485,43 +493,56 @@ void ssd_scan_kernel(ScanParams prm) {
     __shared__ __attribute__((aligned(16))) TI smem[K::BUF_ELEMS];
     // per-token scalars of the block, shared by all waves (written by wave 0)
     constexpr int SQ = SEQ ? 1 : 0, EU = EULER ? 1 : 0;
-    __shared__ __attribute__((aligned(16))) cum_t sCum[64];       // cumulative log2 decay
-    __shared__ __attribute__((aligned(16))) float sRow[64];       // read-out row scale
-    __shared__ __attribute__((aligned(16))) float sWx[64];        // end-state weight exp2(cum_end - cum) (dt)
-    __shared__ __attribute__((aligned(16))) float sDtf[64 * EU + 4];   // dt (Euler input scaling)
+    // (one copy per head of the workgroup, written by that head's first wave)
+    __shared__ __attribute__((aligned(16))) cum_t sCumH[MLH][64];      // cumulative log2 decay
+    __shared__ __attribute__((aligned(16))) float sRowH[MLH][64];      // read-out row scale
+    __shared__ __attribute__((aligned(16))) float sWxH[MLH][64];       // end-state weight exp2(cum_end - cum) (dt)
+    __shared__ __attribute__((aligned(16))) float sDtfH[MLH][64 * EU + 4];   // dt (Euler input scaling)
     __shared__ __attribute__((aligned(16))) int sSeg[64 * SQ + 4];     // segment of each token
     __shared__ int sStart[65 * SQ + 1];
     __shared__ int sSeqOf[65 * SQ + 1];
 
     TI* sC = smem + K::OFF_C;
     TI* sB = smem + K::OFF_B;
-    TI* sLm = smem + K::OFF_LM;
     TI* sXr = smem + K::OFF_XR;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: wave-level values stay scalar
     const int lr = lane & 15, lg = lane >> 4;
-    const int pt = w % NPT, nh = w / NPT;
-    const int p0 = 16 * pt;
+    const int ls = w % SPW, nh = w / SPW;     // this wave's slice of the workgroup, and its half of the state
+    const int xc = 16 * ls;                   // its channels in the X tile
     const int mb = nh * MTH;                  // first state tile this wave owns
     const int kbo = nh * NKH, kbp = (1 - nh) * NKH;   // read-out K steps of its half and of the partner's
     // this wave's and its partner's read-out fragments in the exchange area (16-byte slots per lane)
-    TI* sxo = smem + K::OFF_SX + ((pt * NH + nh) * NKH * 64 + lane) * KPL;
-    const TI* sxp = smem + K::OFF_SX + ((pt * NH + (NH - 1 - nh)) * NKH * 64 + lane) * KPL;
+    TI* sxo = smem + K::OFF_SX + ((ls * NH + nh) * NKH * 64 + lane) * KPL;
+    const TI* sxp = smem + K::OFF_SX + ((ls * NH + (NH - 1 - nh)) * NKH * 64 + lane) * KPL;
 
-    // Work-item order: runs of consecutive (row, head) items go to the same
+    // Work-item order: runs of consecutive (row, slice group) items go to the same
     // XCD (workgroups are dealt round-robin over the 8 XCDs), so the heads of
     // a row share that row's B and C tiles in one L2.
+    const int64_t T = prm.T, H = prm.H, G = prm.G;
+    const int64_t nsg = H * NPT / SPW;                           // slice groups per row
     const int nsl = LOCAL ? prm.nseg - 1 : prm.nseg;             // segments this launch covers
-    const int64_t units = prm.batch * prm.H * nsl;
+    const int64_t units = prm.batch * nsg * nsl;
     int64_t u = blockIdx.x;
     if (units % 8 == 0) u = (int64_t)(blockIdx.x % 8) * (units / 8) + blockIdx.x / 8;
-    const int64_t h = u % prm.H, rowseg = u / prm.H;
+    const int64_t grp = u % nsg, rowseg = u / nsg;
     const int sg = (int)(rowseg % nsl);
     const int64_t b = rowseg / nsl;
-    const int64_t g = h / (prm.H / prm.G);
-    const int64_t T = prm.T, H = prm.H, G = prm.G;
+    const int64_t gs0 = grp * SPW;                               // first slice of the workgroup in its row
+    const int64_t h = (gs0 + ls) / NPT;                          // this wave's head and channels
+    const int pt = (int)((gs0 + ls) % NPT), p0 = 16 * pt;
+    const int64_t hf = gs0 / NPT;                                // first head of the workgroup
+    const int lh = (int)(h - hf), nlh = (int)((gs0 + SPW - 1) / NPT - hf) + 1;
+    const bool head_leader = nh == 0 && (ls == 0 || pt == 0);   // publishes its head's per-token scalars
+    const int64_t g = hf / (H / G);
+    cum_t* sCum = sCumH[lh];
+    float* sRow = sRowH[lh];
+    float* sWx = sWxH[lh];
+    float* sDtf = sDtfH[lh];
+    TI* sLmH = smem + K::OFF_LM;                                 // L o CB of local head l at l * QB * LQ
+    TI* sLm = sLmH + lh * QB * LQ;
     const int blk0 = sg * prm.seg_blocks;
     const int blk1 = min(prm.nblk, blk0 + prm.seg_blocks);
     const int64_t slot = (b * H + h) * (prm.nseg - 1) + sg;     // this segment's local-pass slot
@@ -538,12 +559,12 @@ void ssd_scan_kernel(ScanParams prm) {
     const int xs = (int)(H * P * SZ), ys = (int)(H * P * 4), cs = (int)(G * N * SZ), ds = (int)(H * 4);
     // row bases; block blk starts QB tokens further, and everything past the
     // row's last token reads as zero / is not written (buffer range check)
-    const char* xrow = (const char*)prm.x + ((b * T) * H + h) * P * SZ;
-    const char* yrow = (const char*)prm.y + ((b * T) * H + h) * P * 4;
+    const char* xrow = (const char*)prm.x + ((b * T) * H * P + gs0 * 16) * SZ;
+    const char* yrow = (const char*)prm.y + ((b * T) * H * P + gs0 * 16) * 4;
     const char* crow = (const char*)prm.C + ((b * T) * G + g) * N * SZ;
     const char* brow = (const char*)prm.B + ((b * T) * G + g) * N * SZ;
     const char* drow = (const char*)prm.dt + ((b * T) * H + h) * 4;
-    const int64_t xrec = ((T - 1) * H + 1) * P * SZ, yrec = ((T - 1) * H + 1) * P * 4;
+    const int64_t xrec = ((T - 1) * H * P + XW) * SZ, yrec = ((T - 1) * H * P + XW) * 4;
     const int64_t crec = ((T - 1) * G + 1) * N * SZ, drec = ((T - 1) * H + 1) * 4;
 
     // ---- initial state of the row's first sequence: this wave's tiles of S^T,
@@ -589,9 +610,10 @@ void ssd_scan_kernel(ScanParams prm) {
     // The upper 16x16 tile next to an even diagonal tile is read by a 32-wide
     // K step of the diagonal product; it is zero and never rewritten.
     if constexpr (KSTEP > 16) {
-        for (int v = tid; v < (RT / 2) * 16 * 16; v += NT) {
-            const int r = 2 * (v / 256), i = (v / 16) % 16, c = v % 16;
-            sLm[(16 * r + i) * LQ + 16 * (r + 1) + c] = to_in<TI>(0.f);
+        for (int v = tid; v < MLH * (RT / 2) * 16 * 16; v += NT) {
+            const int l = v / ((RT / 2) * 256), vv = v % ((RT / 2) * 256);
+            const int r = 2 * (vv / 256), i = (vv / 16) % 16, c = vv % 16;
+            sLmH[l * QB * LQ + (16 * r + i) * LQ + 16 * (r + 1) + c] = to_in<TI>(0.f);
         }
     }
     // Causal tiles (row tile I, column tile J <= I) of L o CB computed by this
@@ -624,7 +646,7 @@ void ssd_scan_kernel(ScanParams prm) {
 #pragma unroll
         for (int j = 0; j < K::XPT; ++j) {
             const int v = tid + j * NT;
-            if (K::XU % NT == 0 || v < K::XU) xr[j] = buf_load16(rx, (v / (P / VE)) * xs + (v % (P / VE)) * 16);
+            if (K::XU % NT == 0 || v < K::XU) xr[j] = buf_load16(rx, (v / (XW / VE)) * xs + (v % (XW / VE)) * 16);
         }
     };
     auto issue_bc = [&](int blk) {
@@ -706,7 +728,7 @@ void ssd_scan_kernel(ScanParams prm) {
         seg_total += cend;
         seg_reset |= nstart > 0;
         const float dtf = EULER ? dtv : 1.f;
-        if (w == 0 && lane < QB) {
+        if (head_leader && lane < QB) {
             sCum[lane] = cum;
             sRow[lane] = fast_exp2((float)(cum - before));
             sWx[lane] = fast_exp2((float)(cend - cum)) * dtf;  // end-state weight of token lane
@@ -717,7 +739,7 @@ void ssd_scan_kernel(ScanParams prm) {
 #pragma unroll
         for (int j = 0; j < K::XPT; ++j) {
             const int v = tid + j * NT;
-            if (K::XU % NT == 0 || v < K::XU) *(uint4*)(sXr + (v / (P / VE)) * LR + (v % (P / VE)) * VE) = xr[j];
+            if (K::XU % NT == 0 || v < K::XU) *(uint4*)(sXr + (v / (XW / VE)) * LR + (v % (XW / VE)) * VE) = xr[j];
         }
     };
 
@@ -730,7 +752,7 @@ void ssd_scan_kernel(ScanParams prm) {
     //      that no LDS write separates the operand reads of the MFMA phase (the
     //      compiler cannot move a read above a write to the same array).
     typedef typename std::conditional<SZ == 2, bf16x4, f32x4>::type lm_t;
-    lm_t lmv[K::TPW];
+    lm_t lmv[K::TPW][MLH];
     auto lm_phase = [&]() {
         // K step outer, tile inner: consecutive MFMAs go to independent accumulators
         f32x4 cbt[K::TPW];
@@ -742,45 +764,55 @@ void ssd_scan_kernel(ScanParams prm) {
             for (int j = 0; j < K::TPW; ++j)
                 cbt[j] = MF::mma(brow_frag<N, LB>(sB, 16 * tJ[j] + lr, k, lg),
                                  crow_frag<N>(sC + (16 * tI[j] + lr) * LC, k, lg), cbt[j]);
+        // the same C B^T tile under the decay of each head of the workgroup
 #pragma unroll
         for (int j = 0; j < K::TPW; ++j) {
             const int I = tI[j], J = tJ[j];                      // uniform over the wave
             const int t = 16 * I + lr, s0 = 16 * J + 4 * lg;
             const f32x4 acc = cbt[j];
-            const cum_t ct = sCum[t];
-            cum_t csv[4];
-            if constexpr (sizeof(cum_t) == 4) {
-                const float4 c4 = *(const float4*)(&sCum[s0]);
-                csv[0] = c4.x; csv[1] = c4.y; csv[2] = c4.z; csv[3] = c4.w;
-            } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) csv[e] = sCum[s0 + e];
-            }
-            float val[4];
+            for (int l = 0; l < MLH; ++l) {
+                if (MLH > 1 && l >= nlh) break;
+                const cum_t ct = sCumH[l][t];
+                cum_t csv[4];
+                if constexpr (sizeof(cum_t) == 4) {
+                    const float4 c4 = *(const float4*)(&sCumH[l][s0]);
+                    csv[0] = c4.x; csv[1] = c4.y; csv[2] = c4.z; csv[3] = c4.w;
+                } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float lv = fast_exp2((float)(ct - csv[e])) * acc[e];
-                val[e] = (s0 + e <= t) ? lv : 0.f;
+                    for (int e = 0; e < 4; ++e) csv[e] = sCumH[l][s0 + e];
+                }
+                float val[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float lv = fast_exp2((float)(ct - csv[e])) * acc[e];
+                    val[e] = (s0 + e <= t) ? lv : 0.f;
+                }
+                if constexpr (EULER) {
+                    const float4 d4 = *(const float4*)(&sDtfH[l][s0]);
+                    val[0] *= d4.x; val[1] *= d4.y; val[2] *= d4.z; val[3] *= d4.w;
+                }
+                if constexpr (SEQ) {
+                    const int segt = sSeg[t];
+                    const int4 sgv = *(const int4*)(&sSeg[s0]);
+                    if (sgv.x != segt) val[0] = 0.f;
+                    if (sgv.y != segt) val[1] = 0.f;
+                    if (sgv.z != segt) val[2] = 0.f;
+                    if (sgv.w != segt) val[3] = 0.f;
+                }
+                if constexpr (SZ == 2) lmv[j][l] = bf16x4{(__bf16)val[0], (__bf16)val[1], (__bf16)val[2], (__bf16)val[3]};
+                else lmv[j][l] = f32x4{val[0], val[1], val[2], val[3]};
             }
-            if constexpr (EULER) {
-                const float4 d4 = *(const float4*)(&sDtf[s0]);
-                val[0] *= d4.x; val[1] *= d4.y; val[2] *= d4.z; val[3] *= d4.w;
-            }
-            if constexpr (SEQ) {
-                const int segt = sSeg[t];
-                const int4 sg = *(const int4*)(&sSeg[s0]);
-                if (sg.x != segt) val[0] = 0.f;
-                if (sg.y != segt) val[1] = 0.f;
-                if (sg.z != segt) val[2] = 0.f;
-                if (sg.w != segt) val[3] = 0.f;
-            }
-            if constexpr (SZ == 2) lmv[j] = bf16x4{(__bf16)val[0], (__bf16)val[1], (__bf16)val[2], (__bf16)val[3]};
-            else lmv[j] = f32x4{val[0], val[1], val[2], val[3]};
         }
     };
     auto lm_store = [&]() {
 #pragma unroll
-        for (int j = 0; j < K::TPW; ++j) *(lm_t*)(sLm + (16 * tI[j] + lr) * LQ + 16 * tJ[j] + 4 * lg) = lmv[j];
+        for (int j = 0; j < K::TPW; ++j)
+#pragma unroll
+            for (int l = 0; l < MLH; ++l) {
+                if (MLH > 1 && l >= nlh) break;
+                *(lm_t*)(sLmH + l * QB * LQ + (16 * tI[j] + lr) * LQ + 16 * tJ[j] + 4 * lg) = lmv[j][l];
+            }
     };
 
     // ---- MFMA phases, outputs transposed: y^T tiles (rows p0..p0+15, columns t) of
@@ -825,7 +857,7 @@ void ssd_scan_kernel(ScanParams prm) {
             for (int j = 0; j < MTH; ++j) st[j] *= alpha;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const frag xw = weighted_x_frag(sXr, LR, ks * KSTEP, p0, lr, lg, [&](int t) { return sWx[t]; });
+                const frag xw = weighted_x_frag(sXr, LR, ks * KSTEP, xc, lr, lg, [&](int t) { return sWx[t]; });
 #pragma unroll
                 for (int j = 0; j < MTH; ++j) st[j] = MF::mma(bt_frag<N, LB>(sB, mb + j, ks * KSTEP, lr, lg), xw, st[j]);
             }
@@ -896,7 +928,7 @@ void ssd_scan_kernel(ScanParams prm) {
                 }
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    const frag xw = weighted_x_frag(sXr, LR, ks * KSTEP, p0, lr, lg, wseg);
+                    const frag xw = weighted_x_frag(sXr, LR, ks * KSTEP, xc, lr, lg, wseg);
 #pragma unroll
                     for (int q = 0; q < MTH; ++q) F[q] = MF::mma(bt_frag<N, LB>(sB, mb + q, ks * KSTEP, lr, lg), xw, F[q]);
                 }
@@ -927,11 +959,11 @@ void ssd_scan_kernel(ScanParams prm) {
             const int t = 16 * K::own_tile(nh, i) + lr;
             float xv[4];
             if constexpr (SZ == 2) {
-                const bf16x4 x4 = *(const bf16x4*)(sXr + t * LR + p0 + 4 * lg);
+                const bf16x4 x4 = *(const bf16x4*)(sXr + t * LR + xc + 4 * lg);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) xv[q] = (float)x4[q];
             } else {
-                const float4 x4 = *(const float4*)(sXr + t * LR + p0 + 4 * lg);
+                const float4 x4 = *(const float4*)(sXr + t * LR + xc + 4 * lg);
                 xv[0] = x4.x; xv[1] = x4.y; xv[2] = x4.z; xv[3] = x4.w;
             }
 #pragma unroll
@@ -939,7 +971,7 @@ void ssd_scan_kernel(ScanParams prm) {
         }
         if constexpr (DKS > 0) {
 #pragma unroll
-            for (int q = 0; q < DKS; ++q) xd[q] = x_frag(sXr, LR, 32 * q, p0, lr, lg);
+            for (int q = 0; q < DKS; ++q) xd[q] = x_frag(sXr, LR, 32 * q, xc, lr, lg);
         }
     };
     auto diag_phase = [&](int blk) {
@@ -953,13 +985,13 @@ void ssd_scan_kernel(ScanParams prm) {
                 for (int q = 0; q < (i == 0 ? 1 : 2); ++q) acc[i] = MF::mma(xd[q], lds_frag<TI>(lrow + 32 * q), acc[i]);
             } else {
                 for (int ks = 0; ks < 16 * (r + 1); ks += KSTEP)
-                    acc[i] = MF::mma(x_frag(sXr, LR, ks, p0, lr, lg), lds_frag<TI>(lrow + ks), acc[i]);
+                    acc[i] = MF::mma(x_frag(sXr, LR, ks, xc, lr, lg), lds_frag<TI>(lrow + ks), acc[i]);
             }
         }
         const int64_t t0 = (int64_t)blk * QB;
         const rsrc_t ry = make_rsrc(yrow + t0 * ys, yrec - t0 * ys);
 #pragma unroll
-        for (int i = 0; i < RTH; ++i) buf_store16(acc[i], ry, (16 * K::own_tile(nh, i) + lr) * ys + (p0 + 4 * lg) * 4);
+        for (int i = 0; i < RTH; ++i) buf_store16(acc[i], ry, (16 * K::own_tile(nh, i) + lr) * ys + (xc + 4 * lg) * 4);
         if constexpr (SEQ) prevseq = lastseq_c;
     };
 
@@ -1005,7 +1037,7 @@ void ssd_scan_kernel(ScanParams prm) {
 #pragma unroll
         for (int j = 0; j < MTH; ++j)
             *(float4*)(dst + nrow<N>(mb + j, 4 * lg)) = make_float4(st[j][0], st[j][1], st[j][2], st[j][3]);
-        if (tid == 0) prm.seg_carry[slot] = seg_reset ? 0.f : fast_exp2((float)seg_total);
+        if (head_leader && lane == 0) prm.seg_carry[slot] = seg_reset ? 0.f : fast_exp2((float)seg_total);
     } else if (sg == prm.nseg - 1) {
         // the state after the row's last token belongs to its last sequence
         if (T > 0 || !SEQ) write_state(st, prevseq);

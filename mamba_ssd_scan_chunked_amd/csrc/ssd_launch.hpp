@@ -12,16 +12,17 @@ struct StepParams;
 // Return hipSuccess, hipErrorInvalidValue for a shape with no instantiation,
 // or the launch error.
 // seq: sequence ids present (segment handling compiled in); euler: dt scales x;
-// local: the local pass of a row split into segments (else the scan proper)
-hipError_t launch_scan_bf16(int P, int N, int QB, bool seq, bool euler, bool local, const ScanParams& prm,
+// local: the local pass of a row split into segments (else the scan proper);
+// spw: 16-channel slices per workgroup (P / 16: one head per workgroup)
+hipError_t launch_scan_bf16(int P, int N, int QB, bool seq, bool euler, bool local, int spw, const ScanParams& prm,
                             int64_t grid, hipStream_t s);
-hipError_t launch_scan_f32(int P, int N, int QB, bool seq, bool euler, bool local, const ScanParams& prm,
+hipError_t launch_scan_f32(int P, int N, int QB, bool seq, bool euler, bool local, int spw, const ScanParams& prm,
                            int64_t grid, hipStream_t s);
 hipError_t launch_combine(const CombineParams& prm, hipStream_t s);
 hipError_t launch_step_bf16(int P, int N, const StepParams& prm, int64_t grid, hipStream_t s);
 hipError_t launch_step_f32(int P, int N, const StepParams& prm, int64_t grid, hipStream_t s);
 #define SSD_DECLARE_SCAN(tag, sq, eu, lo) \
-    hipError_t launch_scan_##tag##_s##sq##_e##eu##_l##lo(int P, int N, int QB, const ScanParams& prm, int64_t grid, hipStream_t s);
+    hipError_t launch_scan_##tag##_s##sq##_e##eu##_l##lo(int P, int N, int QB, int spw, const ScanParams& prm, int64_t grid, hipStream_t s);
 #define SSD_DECLARE_SCAN2(tag, sq, eu) SSD_DECLARE_SCAN(tag, sq, eu, 0) SSD_DECLARE_SCAN(tag, sq, eu, 1)
 SSD_DECLARE_SCAN2(bf16, 0, 0)
 SSD_DECLARE_SCAN2(bf16, 0, 1)

@@ -225,3 +225,20 @@ def test_workload_sampled(name, k):
     for (b, h), (yr, fr, seqs) in zip(pairs, oracle_pairs(prob, pairs)):
         assert_parity(y[b, :, h], yr, tol, "y[%d,:,%d]" % (b, h))
         assert_parity(f[seqs, h], fr, tol, "final[%s,%d]" % (seqs[:3], h))
+
+
+# ------------------------------------------------------------------ five slices per workgroup
+# Between 256 and 320 (row, head) items of 64 channels: the library packs five
+# 16-channel slices into a workgroup, so a workgroup may hold parts of two heads.
+
+@pytest.mark.parametrize("case", [
+    # b, T, H, N, G, chunk, euler
+    (1, 130, 260, 64, 1, 64, False),
+    (2, 70, 150, 128, 1, 64, True),
+    (1, 100, 300, 64, 5, 32, False),      # (H/G)*4 = 240 slices per group: still five per workgroup
+    (1, 90, 265, 64, 5, 64, False),       # (H/G)*4 = 212: not a multiple of five, one head per workgroup
+])
+def test_five_slice_workgroups(case):
+    b, T, H, N, G, Q, euler = case
+    prob = si.make_problem(b, T, H, 64, N, G, dtype="bf16", seed=H + T, d_skip=True, init_std=0.5)
+    check_full(prob, Q, dt_scales_x=euler, label="five slices b=%d H=%d G=%d" % (b, H, G))
