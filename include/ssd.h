@@ -93,7 +93,7 @@ int ssd_validate(const ssd_problem_t* p);
 /* Bytes of device workspace ssd_forward needs for this problem; 0 when it needs
  * none (then workspace may be NULL) or when the problem is invalid.  A row is
  * scanned in one pass with every intermediate (C.B^T tiles, decays, the
- * carried state) on chip, unless there are fewer than 256 (row, head) items:
+ * carried state) on chip, unless there are at most 128 (row, head) items:
  * then rows are cut into segments that run in parallel, and the workspace holds
  * each segment's state (fp32 P x N) and carried decay, (batch, nheads,
  * segments - 1) of each.  The chunked algorithm's inter-chunk state passing at

@@ -14,7 +14,9 @@ def gen(tag, TI, Ps, Ns, QBs, seq, eul, loc):
     for P in Ps:
         for N in Ns:
             for Q in QBs:
-                spws = [P // 16] + ([P // 16 + 1] if (tag, P, seq, loc) == ("bf16", 64, 0, 0) else [])
+                # one head per workgroup, and for bf16 64-channel heads without sequence
+                # ids, in the scan proper, also five slices per workgroup
+                spws = [P // 16] + ([5] if (tag, P, seq, loc) == ("bf16", 64, 0, 0) else [])
                 for spw in spws:
                     out.append("    if (P == %d && N == %d && QB == %d && spw == %d) { hipLaunchKernelGGL((ssd_scan_kernel<%s, %d, %d, %d, %s, %s, %s, %d>), dim3((unsigned)grid), dim3(ScanCfg<%s, %d, %d, %d, %d>::NT), 0, s, prm); return hipGetLastError(); }\n"
                                % (P, N, Q, spw, TI, P, N, Q, b(seq), b(eul), b(loc), spw, TI, P, N, Q, spw))

@@ -72,10 +72,11 @@ int64_t nblocks(const ssd_problem_t* p) {
 
 int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
 
-// Segments per row.  With fewer (row, head) items than twice the 256 compute
-// units, rows are split into segments that run in parallel (a local pass, a
-// combine step, then the scan of every segment from its incoming state), down
-// to 4 blocks per segment.  A function of the problem alone (no device query),
+// Segments per row.  With at most 128 (row, head) items, rows are split into
+// up to 512 / items segments that run in parallel (a local pass, a combine
+// step, then the scan of every segment from its incoming state), down to 4
+// blocks per segment.  (Measured on MI355X: 32 items of 256 blocks run best as
+// 16 segments; 192 items of 32 blocks run best unsplit.)  A function of the problem alone (no device query),
 // so the workspace size is known on the host; SSD_SEGMENTS=<n> overrides it.
 struct Segs {
     int nseg, seg_blocks;
@@ -90,7 +91,7 @@ Segs segments(const ssd_problem_t* p) {
         S = std::atoi(env);
     } else {
         const int64_t units = p->batch * p->nheads;
-        if (units < 256) S = std::min<int64_t>(512 / units, nblk / 4);
+        if (units <= 128) S = std::min<int64_t>(512 / units, nblk / 4);
     }
     S = std::max<int64_t>(1, std::min<int64_t>(S, nblk));
     const int64_t sb = (nblk + S - 1) / S;
@@ -123,6 +124,11 @@ int64_t workspace_bytes(const ssd_problem_t* p) { return ws_layout(p).total; }
 int slices_per_workgroup(const ssd_problem_t* p, bool seq, int nseg) {
     const int npt = (int)(p->headdim / 16);
     const int64_t items = p->batch * p->nheads;
+    const char* env = std::getenv("SSD_SPW");          // forced (measurements and tests)
+    if (env && std::atoi(env) > 0 && p->dtype == SSD_DTYPE_BF16 && p->headdim == 64 && !seq) {
+        const int v = std::atoi(env);
+        if ((v == npt || (v == npt + 1 && nseg == 1)) && ((p->nheads / p->ngroups) * npt) % v == 0) return v;
+    }
     if (p->dtype == SSD_DTYPE_BF16 && p->headdim == 64 && !seq && nseg == 1 && items > 256 && items <= 320 &&
         ((p->nheads / p->ngroups) * npt) % (npt + 1) == 0)
         return npt + 1;
@@ -233,14 +239,15 @@ int launch_scan(const ssd_problem_t* p, const void* x, const float* dt, const fl
     const bool seq = seq_idx != nullptr, euler = prm.dt_scales_x != 0;
     const int P = (int)p->headdim, N = (int)p->dstate;
     const int npt = P / 16;
+    const int spw = slices_per_workgroup(p, seq, sg.nseg);
     auto scan = [&](bool local, int spw, int64_t grid) {
         return p->dtype == SSD_DTYPE_BF16 ? ssd::launch_scan_bf16(P, N, q, seq, euler, local, spw, prm, grid, stream)
                                           : ssd::launch_scan_f32(P, N, q, seq, euler, local, spw, prm, grid, stream);
     };
-    const int spw = slices_per_workgroup(p, seq, sg.nseg);
+
     hipError_t e = hipSuccess;
     if (sg.nseg > 1) {
-        e = scan(true, npt, rows * (sg.nseg - 1));
+        e = scan(true, spw, p->batch * (p->nheads * npt / spw) * (sg.nseg - 1));
         if (e == hipSuccess) {
             ssd::CombineParams cp;
             cp.init = init;

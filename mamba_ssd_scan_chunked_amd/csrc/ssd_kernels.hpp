@@ -438,8 +438,6 @@ struct ScanCfg {
     static constexpr int NH = (SZ == 2 ? MT % 4 == 0 : MT % 2 == 0) && RT % 2 == 0 ? 2 : 1;
     static constexpr int NW = SPW * NH;
     static constexpr int NT = NW * 64;
-    static constexpr int WPE = SPW != NPT ? (NW + 3) / 4   // one workgroup per CU
-                             : NW >= 8 ? NW / 2 : 2;       // waves per SIMD for two workgroups per CU
                                                       // (the sequence-id variants, whose segment path
                                                       // needs more registers, are left at two)
     static constexpr int MTH = MT / NH, NKH = NK / NH, RTH = RT / NH;
@@ -460,6 +458,12 @@ struct ScanCfg {
     static constexpr int OFF_XR = OFF_LM + MLH * QB * LQ;            // L o CB of each head
     static constexpr int OFF_SX = OFF_XR + QB * LR;
     static constexpr int BUF_ELEMS = OFF_SX + (NH > 1 ? NW * NKH * 64 * KPL : 0);
+    // workgroups per CU that the LDS footprint allows (the tiles plus about 1 KB per
+    // head and 1.5 KB of other per-token arrays), at most 2; and the waves per SIMD
+    // to plan registers for: one head per workgroup, two workgroups per CU, else
+    // that many workgroups
+    static constexpr int WGPC = 163840 / (BUF_ELEMS * SZ + MLH * 1024 + 1536) >= 2 ? 2 : 1;
+    static constexpr int WPE = SPW == NPT ? (NW >= 8 ? NW / 2 : 2) : (WGPC * NW + 3) / 4;
     // per-thread work units
     static constexpr int CV = QB * N / VE, CPT = (CV + NT - 1) / NT;           // C (and B) tile vectors
     static constexpr int XU = QB * XW / VE, XPT = (XU + NT - 1) / NT;           // 16-byte pieces of the X tile
