@@ -32,8 +32,9 @@ def _load():
     f = lib.ssd_oracle_f64
     i64 = ctypes.c_int64
     vp = ctypes.c_void_p
-    f.argtypes = [i64, i64, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int,
-                  vp, vp, ctypes.c_int]
+    ci = ctypes.c_int
+    f.argtypes = [i64, i64, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci,
+                  vp, vp, ci]
     f.restype = ctypes.c_int
     lib.ssd_oracle_max_threads.restype = ctypes.c_int
     _lib = lib
@@ -54,16 +55,23 @@ def _f64(a):
 
 
 def recurrence(x, dt, A_log, B, C, D=None, init=None, seq_idx=None, nseqs: Optional[int] = None,
-               dt_scales_x: bool = False, nthreads: int = 0):
+               dt_scales_x: bool = False, nthreads: int = 0, dt_bias=None, dt_softplus: bool = False,
+               zoh: bool = False):
     """Run the fp64 recurrence.  Arrays may be numpy or torch (any float dtype).
 
     Shapes: x (b,T,H,P), dt (b,T,H), A_log (H), B/C (b,T,G,N), D (H), init (nseqs,H,P,N),
-    seq_idx (b,T) int32.  Returns (y (b,T,H,P), final (nseqs,H,P,N)) as float64.
+    seq_idx (b,T) int32, dt_bias (H).  The step size is dt + dt_bias, passed through
+    softplus when ``dt_softplus``; x is written to the state unscaled, times the step
+    size (``dt_scales_x``, Euler) or times (exp(step A) - 1) / A (``zoh``, exact
+    zero-order hold).  Returns (y (b,T,H,P), final (nseqs,H,P,N)) as float64.
     """
+    if dt_scales_x and zoh:
+        raise ValueError("Euler and zero-order-hold input scaling are exclusive")
     lib = _load()
     x, dt, A_log, B, C = (_f64(v) for v in (x, dt, A_log, B, C))
     D = _f64(D)
     init = _f64(init)
+    dt_bias = _f64(dt_bias)
     b, T, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
     if seq_idx is not None:
@@ -75,6 +83,7 @@ def recurrence(x, dt, A_log, B, C, D=None, init=None, seq_idx=None, nseqs: Optio
     else:
         nseqs = b
     assert dt.shape == (b, T, H) and A_log.shape == (H,)
+    assert dt_bias is None or dt_bias.shape == (H,)
     assert B.shape == (b, T, G, N) and C.shape == (b, T, G, N)
     y = np.empty((b, T, H, P), dtype=np.float64)
     final = np.zeros((nseqs, H, P, N), dtype=np.float64)
@@ -83,7 +92,8 @@ def recurrence(x, dt, A_log, B, C, D=None, init=None, seq_idx=None, nseqs: Optio
         return a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
 
     rc = lib.ssd_oracle_f64(b, T, H, P, N, G, nseqs, p(x), p(dt), p(A_log), p(B), p(C), p(D), p(init),
-                            p(seq_idx), int(bool(dt_scales_x)), p(y), p(final), int(nthreads))
+                            p(seq_idx), p(dt_bias), int(bool(dt_softplus)), 2 if zoh else int(bool(dt_scales_x)),
+                            p(y), p(final), int(nthreads))
     if rc != 0:
         raise ValueError("oracle rejected its arguments (code %d)" % rc)
     return y, final

@@ -31,10 +31,19 @@
  *    2.3 and 5.  At the first token of sequence k the state is replaced by
  *    init_k and then updated by that token as usual (decayed by a_t, written by
  *    x_t B_t^T), so a carried state continues a split run exactly.
- *  - optional Euler input scaling (x_t -> dt_t x_t, i.e. B-bar = Delta B): the
- *    pages name the zero-order hold without giving B-bar; the default follows
- *    the recurrence above, with no Delta on x.  D always multiplies the
- *    unscaled x.
+ *  - optional input scaling.  The pages name the zero-order hold (ZOH) as the
+ *    discretisation ("Mamba and state space models", section 2 "formal
+ *    definition") without giving B-bar; the default follows the recurrence
+ *    above, with no Delta on x.  Two opt-in readings:
+ *      Euler: x_t -> Delta_t x_t  (B-bar = Delta B);
+ *      ZOH:   x_t -> (exp(Delta_t A) - 1) / A * x_t, the exact solution over
+ *             one step of h' = A h + B x with x and B held constant (for the
+ *             scalar A here: h(Delta) = e^{Delta A} h(0) + (e^{Delta A} - 1)/A B x).
+ *    D always multiplies the unscaled x.
+ *  - optional step-size map Delta = softplus(dt + dt_bias_h): the "Mamba"
+ *    paper story (ai.tomabc.com), the simplified Mamba block pseudocode, where
+ *    the step size is the softplus of a projection plus a learned per-channel
+ *    parameter.  Without the flag Delta = dt + dt_bias_h (dt_bias NULL = 0).
  *
  * Layouts (all contiguous, row-major):
  *   x (b,T,H,P)  dt (b,T,H)  A_log (H)  B, C (b,T,G,N)  D (H) or NULL
@@ -54,13 +63,16 @@ int ssd_oracle_f64(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdi
                    int64_t dstate, int64_t ngroups, int64_t nseqs,
                    const double* x, const double* dt, const double* A_log,
                    const double* B, const double* C, const double* D,
-                   const double* init, const int32_t* seq_idx, int dt_scales_x,
+                   const double* init, const int32_t* seq_idx,
+                   const double* dt_bias, int dt_softplus, int input_scaling,
                    double* y, double* final_state, int nthreads)
 {
     const int64_t T = seqlen, H = nheads, P = headdim, N = dstate, G = ngroups;
     if (batch < 0 || T < 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0 || H % G != 0)
         return 1;
     if (seq_idx == NULL && nseqs != batch)
+        return 1;
+    if (input_scaling < 0 || input_scaling > 2)
         return 1;
     const int64_t heads_per_group = H / G;
     const int64_t units = batch * H;
@@ -90,14 +102,18 @@ int ssd_oracle_f64(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdi
                     memset(S, 0, (size_t)(P * N) * sizeof(double));
                 cur = k;
             }
-            const double dtv = dt[(r * T + t) * H + h];
+            double dtv = dt[(r * T + t) * H + h] + (dt_bias ? dt_bias[h] : 0.0);
+            if (dt_softplus)   /* log(1 + e^v), written so that neither branch overflows */
+                dtv = dtv > 0.0 ? dtv + log1p(exp(-dtv)) : log1p(exp(dtv));
             const double a = exp(dtv * A);
+            /* factor on x_t in the state write (1, Delta, or the ZOH (e^{Delta A} - 1) / A) */
+            const double xf = input_scaling == 1 ? dtv : (input_scaling == 2 ? expm1(dtv * A) / A : 1.0);
             const double* xt = x + ((r * T + t) * H + h) * P;
             const double* Bt = B + ((r * T + t) * G + g) * N;
             const double* Ct = C + ((r * T + t) * G + g) * N;
             double* yt = y + ((r * T + t) * H + h) * P;
             for (int64_t p = 0; p < P; ++p)
-                xs[p] = dt_scales_x ? dtv * xt[p] : xt[p];
+                xs[p] = xf * xt[p];
             /* decay, then write: H_t = a_t H_{t-1} + x_t B_t^T */
             for (int64_t p = 0; p < P; ++p)
                 for (int64_t n = 0; n < N; ++n)

@@ -268,6 +268,96 @@ def test_group_mapping_contiguous_heads():
     np.testing.assert_allclose(run(rep)[0], run(one)[0], atol=1e-12)
 
 
+# ------------------------------------------- step-size map and input discretisation
+
+def _w1_with_step_map(dt_raw, dt_bias, A_log, **kw):
+    g = golden("w1_three_steps.json")
+    p = scalar_problem(g["a"], g["x"], g["B"], g["C"])
+    T = len(g["x"])
+    p = dict(p, dt=np.full((1, T, 1), float(dt_raw)), A_log=np.array([float(A_log)]))
+    y, fin = run(p, dt_bias=np.array([float(dt_bias)]), **kw)
+    return g, y, fin
+
+
+def test_softplus_step_size_reproduces_w1():
+    """softplus(v) == 1 exactly at v = ln(e - 1): with the bias carrying part of v and
+    A = -ln 2 the decay is 1/2 again and the printed three-step example comes back."""
+    v = math.log(math.e - 1.0)
+    g, y, fin = _w1_with_step_map(v - 0.25, 0.25, math.log(math.log(2.0)), dt_softplus=True)
+    np.testing.assert_allclose(y.ravel(), g["h"], rtol=0, atol=1e-12)
+    assert abs(fin.item() - g["h"][-1]) < 1e-12
+
+
+def test_softplus_at_zero_is_ln2():
+    """softplus(0) = ln 2, so with A = -1 the decay is exp(-ln 2) = 1/2: the printed example."""
+    g, y, _ = _w1_with_step_map(-0.5, 0.5, 0.0, dt_softplus=True)
+    np.testing.assert_allclose(y.ravel(), g["h"], rtol=0, atol=1e-12)
+
+
+def test_softplus_tails():
+    """softplus(v) - v -> 0 for large v (about e^-v), and softplus(v) -> 0 for very
+    negative v: then a = 1 and the map is a prefix sum."""
+    p = _case_problem(dict(b=1, T=12, H=2, P=3, N=2, G=1), seed=21)
+    big = dict(p, dt=np.full((1, 12, 2), 36.0))
+    y_sp, f_sp = run(big, dt_softplus=True)
+    y_id, f_id = run(big)
+    np.testing.assert_allclose(y_sp, y_id, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(f_sp, f_id, rtol=1e-12, atol=1e-14)
+    neg = dict(p, dt=np.full((1, 12, 2), -800.0))
+    y0, _ = run(neg, dt_softplus=True)
+    x = p["x"].double().numpy()
+    B = p["B"].double().numpy()
+    C = p["C"].double().numpy()
+    cb = np.einsum("btgn,bsgn->bts", C, B)[0]           # (t, s), one group
+    expect = np.einsum("ts,shp->thp", np.tril(cb), x[0])
+    np.testing.assert_allclose(y0[0], expect, atol=1e-12)
+
+
+def test_zoh_scales_w1_by_the_hold_factor():
+    """Exact zero-order hold with a = 1/2, dt = 1, A = -ln 2: every write is scaled by
+    (1/2 - 1) / (-ln 2) = 1 / (2 ln 2), and the map is linear in the writes."""
+    g = golden("w1_three_steps.json")
+    y, fin = run(scalar_problem(g["a"], g["x"], g["B"], g["C"]), zoh=True)
+    k = 1.0 / (2.0 * math.log(2.0))
+    np.testing.assert_allclose(y.ravel(), np.array(g["h"]) * k, rtol=1e-14, atol=0)
+    assert abs(fin.item() - g["h"][-1] * k) < 1e-12
+
+
+def test_zoh_steps_compose():
+    """With x and B held for two steps, the exact hold over dt1 then dt2 equals one
+    step over dt1 + dt2 (the solution operator of h' = A h + B x is a semigroup);
+    Euler scaling does not have this property, which shows the check can fail."""
+    rng = np.random.default_rng(22)
+    H, P, N = 3, 4, 5
+    x1 = rng.standard_normal((1, 1, H, P))
+    B1 = rng.standard_normal((1, 1, 1, N))
+    C1 = rng.standard_normal((1, 1, 1, N))
+    init = rng.standard_normal((1, H, P, N))
+    A_log = rng.uniform(-1.0, 1.0, H)
+    dt1, dt2 = rng.uniform(0.1, 1.5, (1, 1, H)), rng.uniform(0.1, 1.5, (1, 1, H))
+    two = dict(x=np.concatenate([x1, x1], 1), dt=np.concatenate([dt1, dt2], 1), A_log=A_log,
+               B=np.concatenate([B1, B1], 1), C=np.concatenate([C1, C1], 1), init=init)
+    one = dict(x=x1, dt=dt1 + dt2, A_log=A_log, B=B1, C=C1, init=init)
+    _, f2 = run(two, zoh=True)
+    _, f1 = run(one, zoh=True)
+    np.testing.assert_allclose(f2, f1, rtol=1e-12, atol=1e-12)
+    _, e2 = run(two, dt_scales_x=True)
+    _, e1 = run(one, dt_scales_x=True)
+    assert not np.allclose(e2, e1, rtol=1e-6, atol=1e-6)
+
+
+def test_zoh_tends_to_euler_as_A_vanishes():
+    """(e^{dt A} - 1) / A = dt (1 + dt A / 2 + ...): as A -> 0 the hold becomes Euler."""
+    p = _case_problem(dict(b=1, T=16, H=2, P=3, N=4, G=1, init_std=1.0), seed=23)
+    p = dict(p, A_log=np.full(2, -25.0))
+    yz, fz = run(p, zoh=True)
+    ye, fe = run(p, dt_scales_x=True)
+    np.testing.assert_allclose(yz, ye, rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(fz, fe, rtol=1e-9, atol=1e-12)
+    yn, _ = run(p)
+    assert not np.allclose(yz, yn, rtol=1e-3)
+
+
 # ---------------------------------------------------------------- planted mistakes
 
 MUTANTS = {
@@ -281,6 +371,11 @@ MUTANTS = {
     "group_interleaved": ("g = h / heads_per_group;", "g = h % G;"),
     "skip_on_scaled_x": ("yt[p] = acc + Dh * xt[p];", "yt[p] = acc + Dh * xs[p];"),
     "no_reset_at_boundary": ("if (t == 0 || k != cur) {", "if (t == 0) {"),
+    "bias_ignored": ("+ (dt_bias ? dt_bias[h] : 0.0);", "+ 0.0;"),
+    "softplus_wrong_branch": ("dtv + log1p(exp(-dtv))", "dtv + log1p(exp(dtv))"),
+    "softplus_without_log": ("log1p(exp(dtv));", "exp(dtv);"),
+    "zoh_as_euler": ("expm1(dtv * A) / A", "dtv"),
+    "zoh_sign": ("expm1(dtv * A) / A", "expm1(-dtv * A) / -A"),
 }
 
 
@@ -307,7 +402,10 @@ def _pin_suite_passes(lib_path) -> bool:
     try:
         checks = [test_w1_three_steps, test_w1_split_state_handoff, test_w3_one_dimensional_example,
                   test_packed_rows_equal_separate_runs, test_group_mapping_contiguous_heads,
-                  test_linear_in_skip_and_initial_state, test_euler_flag_equals_prescaled_input]
+                  test_linear_in_skip_and_initial_state, test_euler_flag_equals_prescaled_input,
+                  test_softplus_step_size_reproduces_w1, test_softplus_at_zero_is_ln2, test_softplus_tails,
+                  test_zoh_scales_w1_by_the_hold_factor, test_zoh_steps_compose,
+                  test_zoh_tends_to_euler_as_A_vanishes]
         for c in checks:
             c()
         for idx in range(len(CASES)):
