@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 2
+#define SSD_ABI_VERSION 3
 
 /* Element type of x, B and C.  dt, A_log, D, init_state, y and final_state are
  * always fp32.  BF16: bf16 operands, fp32 accumulation; F32: fp32 throughout. */
@@ -51,7 +51,19 @@ enum {
     /* Euler input scaling: the state is written with dt_t * x_t instead of x_t
      * (B-bar = Delta B).  D still multiplies the unscaled x_t.  Off by default:
      * the recurrence above has no Delta on x. */
-    SSD_FLAG_DT_SCALES_X = 1u << 0
+    SSD_FLAG_DT_SCALES_X = 1u << 0,
+    /* Step size Delta = softplus(dt + dt_bias[h]) instead of dt + dt_bias[h]
+     * (the Mamba block maps its step-size projection plus a learned per-head
+     * bias through softplus: the simplified Mamba block pseudocode of the
+     * "Mamba" paper story).  softplus(v) = log(1 + e^v), evaluated in fp32. */
+    SSD_FLAG_DT_SOFTPLUS = 1u << 1,
+    /* Exact zero-order-hold input scaling: the state is written with
+     * (exp(Delta A) - 1) / A * x_t, the solution over one step of
+     * h' = A h + B x with x and B held constant (the pages name the
+     * zero-order hold in section 2 of "Mamba and state space models" without
+     * giving B-bar).  D multiplies the unscaled x_t.  Exclusive with
+     * SSD_FLAG_DT_SCALES_X (both set: SSD_ERR_UNSUPPORTED). */
+    SSD_FLAG_ZOH = 1u << 2
 };
 
 enum {
@@ -106,7 +118,9 @@ size_t ssd_workspace_size(const ssd_problem_t* p);
 /* Full forward on `stream`: one kernel launch, or three when rows are split
  * into segments (see ssd_workspace_size).
  *   x          (batch, seqlen, nheads, headdim)   dtype
- *   dt         (batch, seqlen, nheads)            fp32, the step sizes (> 0 after softplus)
+ *   dt         (batch, seqlen, nheads)            fp32: the step sizes, or with SSD_FLAG_DT_SOFTPLUS
+ *                                                 their pre-activation (any real value)
+ *   dt_bias    (nheads)                           fp32 added to dt before the step-size map, or NULL (= 0)
  *   A_log      (nheads)                           fp32; A_h = -exp(A_log[h])
  *   B, C       (batch, seqlen, ngroups, dstate)   dtype
  *   D          (nheads)                           fp32, or NULL for no skip term
@@ -130,7 +144,7 @@ size_t ssd_workspace_size(const ssd_problem_t* p);
  * is rejected with SSD_ERR_ALIAS.
  * A row of seqlen 0 leaves its final state equal to its initial state. */
 int ssd_forward(const ssd_problem_t* p,
-                const void* x, const float* dt, const float* A_log,
+                const void* x, const float* dt, const float* dt_bias, const float* A_log,
                 const void* B, const void* C, const float* D,
                 const float* init_state, const int32_t* seq_idx,
                 float* y, float* final_state,
@@ -145,16 +159,18 @@ int ssd_forward(const ssd_problem_t* p,
  *   p          problem with seqlen == 1 and nseqs == batch (chunk_len any valid value)
  *   x          (batch, 1, nheads, headdim)   dtype
  *   dt         (batch, 1, nheads)            fp32
+ *   dt_bias    (nheads) fp32, or NULL
  *   A_log      (nheads)                      fp32
  *   B, C       (batch, 1, ngroups, dstate)   dtype
  *   D          (nheads) fp32, or NULL
  *   state      (batch, nheads, headdim, dstate) fp32, read and written (required)
  *   y          (batch, 1, nheads, headdim)   fp32 output
- * SSD_FLAG_DT_SCALES_X applies as in ssd_forward.  One kernel launch; bound by
+ * The flags (Euler or zero-order-hold input scaling, softplus step size) and
+ * dt_bias apply as in ssd_forward.  One kernel launch; bound by
  * reading and writing the state once.  y and state must not overlap each other
  * or any input (SSD_ERR_ALIAS). */
 int ssd_step(const ssd_problem_t* p,
-             const void* x, const float* dt, const float* A_log,
+             const void* x, const float* dt, const float* dt_bias, const float* A_log,
              const void* B, const void* C, const float* D,
              float* state, float* y, void* stream);
 

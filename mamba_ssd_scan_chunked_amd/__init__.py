@@ -7,10 +7,12 @@ the library's HIP kernels.  There is no CPU fallback: if the library is not
 built, or no GPU is present, the calls raise.
 
     y, final = forward(x, dt, A_log, B, C, D=None, chunk_len=256,
-                       init_state=None, seq_idx=None, nseqs=None)
+                       init_state=None, seq_idx=None, nseqs=None,
+                       dt_bias=None, dt_softplus=False, zoh=False)
 
 Layouts: x (b,T,H,P) bf16|f32, dt (b,T,H) f32, A_log (H) f32, B/C (b,T,G,N) same
-dtype as x, D (H) f32, init_state (nseqs,H,P,N) f32, seq_idx (b,T) int32.
+dtype as x, D (H) f32, init_state (nseqs,H,P,N) f32, seq_idx (b,T) int32,
+dt_bias (H) f32.
 Outputs: y (b,T,H,P) f32 and final_state (nseqs,H,P,N) f32.
 """
 from __future__ import annotations
@@ -20,7 +22,8 @@ import os
 from typing import Optional
 
 __all__ = ["forward", "forward_into", "step", "workspace_size", "validate", "problem", "SSDError",
-           "version", "library_path", "load_library", "DTYPE_F32", "DTYPE_BF16", "FLAG_DT_SCALES_X"]
+           "version", "library_path", "load_library", "DTYPE_F32", "DTYPE_BF16", "FLAG_DT_SCALES_X",
+           "FLAG_DT_SOFTPLUS", "FLAG_ZOH"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libssd_mi355x.so"
@@ -28,6 +31,9 @@ _LIB_NAME = "libssd_mi355x.so"
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
 FLAG_DT_SCALES_X = 1
+FLAG_DT_SOFTPLUS = 2
+FLAG_ZOH = 4
+ABI_VERSION = 3
 
 SSD_OK = 0
 ERROR_NAMES = {1: "NULL_POINTER", 2: "BAD_SHAPE", 3: "UNSUPPORTED", 4: "ALIGNMENT", 5: "WORKSPACE",
@@ -67,15 +73,17 @@ def load_library():
     vp, sz = ctypes.c_void_p, ctypes.c_size_t
     lib.ssd_validate.argtypes = [P]
     lib.ssd_validate.restype = ctypes.c_int
-    lib.ssd_step.argtypes = [P] + [vp] * 9
+    lib.ssd_step.argtypes = [P] + [vp] * 10
     lib.ssd_step.restype = ctypes.c_int
     lib.ssd_workspace_size.argtypes = [P]
     lib.ssd_workspace_size.restype = sz
-    lib.ssd_forward.argtypes = [P] + [vp] * 10 + [vp, sz, vp]
+    lib.ssd_forward.argtypes = [P] + [vp] * 11 + [vp, sz, vp]
     lib.ssd_forward.restype = ctypes.c_int
     lib.ssd_strerror.argtypes = [ctypes.c_int]
     lib.ssd_strerror.restype = ctypes.c_char_p
     lib.ssd_version.restype = ctypes.c_int
+    if lib.ssd_version() != ABI_VERSION:
+        raise ImportError("%s has ABI %d, this binding needs %d: rebuild it" % (path, lib.ssd_version(), ABI_VERSION))
     _lib = lib
     return lib
 
@@ -114,7 +122,7 @@ def _stream_of(device, stream):
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def _describe(x, B, dt, A_log, chunk_len, seq_idx, nseqs, dt_scales_x):
+def _describe(x, B, dt, A_log, chunk_len, seq_idx, nseqs, dt_scales_x, dt_softplus=False, zoh=False):
     import torch
     if x.dim() != 4 or B.dim() != 4:
         raise ValueError("x must be (b,T,H,P) and B, C (b,T,G,N)")
@@ -132,16 +140,18 @@ def _describe(x, B, dt, A_log, chunk_len, seq_idx, nseqs, dt_scales_x):
         if nseqs is None:
             raise ValueError("nseqs is required with seq_idx (it sizes final_state)")
         ns = int(nseqs)
-    flags = FLAG_DT_SCALES_X if dt_scales_x else 0
+    flags = (FLAG_DT_SCALES_X if dt_scales_x else 0) | (FLAG_DT_SOFTPLUS if dt_softplus else 0) | \
+        (FLAG_ZOH if zoh else 0)
     return problem(b, T, H, Pd, N, G, chunk_len, ns, dtype, flags)
 
 
-def _check_tensors(x, dt, A_log, B, C, D, init_state, seq_idx):
+def _check_tensors(x, dt, A_log, B, C, D, init_state, seq_idx, dt_bias=None):
     import torch
     dev = x.device
     if dev.type != "cuda":
         raise ValueError("tensors must be on a GPU device")
     for name, t, dt_ in (("dt", dt, torch.float32), ("A_log", A_log, torch.float32), ("D", D, torch.float32),
+                         ("dt_bias", dt_bias, torch.float32),
                          ("init_state", init_state, torch.float32), ("seq_idx", seq_idx, torch.int32),
                          ("B", B, x.dtype), ("C", C, x.dtype)):
         if t is None:
@@ -158,21 +168,30 @@ def _check_tensors(x, dt, A_log, B, C, D, init_state, seq_idx):
         raise ValueError("B and C must be (b,T,G,N)")
     if D is not None and tuple(D.shape) != (H,):
         raise ValueError("D must be (H,)")
+    if dt_bias is not None and tuple(dt_bias.shape) != (H,):
+        raise ValueError("dt_bias must be (H,)")
     if seq_idx is not None and tuple(seq_idx.shape) != (b, T):
         raise ValueError("seq_idx must be (b,T)")
 
 
 def forward(x, dt, A_log, B, C, D=None, chunk_len: int = 256, init_state=None, seq_idx=None,
             nseqs: Optional[int] = None, dt_scales_x: bool = False, y=None, final_state=None,
-            workspace=None, return_final: bool = True, stream=None):
-    """SSD forward through ``ssd_forward``.  Returns (y, final_state or None)."""
+            workspace=None, return_final: bool = True, stream=None, dt_bias=None, dt_softplus: bool = False,
+            zoh: bool = False):
+    """SSD forward through ``ssd_forward``.  Returns (y, final_state or None).
+
+    The step size is dt + dt_bias (dt_bias None = 0), through softplus when
+    ``dt_softplus``; x is written to the state unscaled, times the step size
+    (``dt_scales_x``) or times the exact zero-order hold (exp(step A) - 1) / A
+    (``zoh``)."""
     import torch
-    _check_tensors(x, dt, A_log, B, C, D, init_state, seq_idx)
+    _check_tensors(x, dt, A_log, B, C, D, init_state, seq_idx, dt_bias)
     x, dt, A_log, B, C = (t.contiguous() for t in (x, dt, A_log, B, C))
     D = D.contiguous() if D is not None else None
+    dt_bias = dt_bias.contiguous() if dt_bias is not None else None
     init_state = init_state.contiguous() if init_state is not None else None
     seq_idx = seq_idx.contiguous() if seq_idx is not None else None
-    p = _describe(x, B, dt, A_log, chunk_len, seq_idx, nseqs, dt_scales_x)
+    p = _describe(x, B, dt, A_log, chunk_len, seq_idx, nseqs, dt_scales_x, dt_softplus, zoh)
     lib = load_library()
     _check(lib.ssd_validate(ctypes.byref(p)))
     dev = x.device
@@ -187,22 +206,23 @@ def forward(x, dt, A_log, B, C, D=None, chunk_len: int = 256, init_state=None, s
     wsb = int(lib.ssd_workspace_size(ctypes.byref(p)))
     if workspace is None and wsb > 0:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
-    forward_into(p, x, dt, A_log, B, C, D, init_state, seq_idx, y, final_state, workspace, stream)
+    forward_into(p, x, dt, A_log, B, C, D, init_state, seq_idx, y, final_state, workspace, stream, dt_bias)
     return y, final_state
 
 
 def forward_into(p: Problem, x, dt, A_log, B, C, D, init_state, seq_idx, y, final_state, workspace=None,
-                 stream=None):
+                 stream=None, dt_bias=None):
     """``ssd_forward`` on caller-provided contiguous tensors and problem description
     (no checks beyond the library's own; ``workspace`` may be None when
     :func:`workspace_size` is 0)."""
     wsn = workspace.numel() if workspace is not None else 0
-    _check(load_library().ssd_forward(ctypes.byref(p), _ptr(x), _ptr(dt), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D),
+    _check(load_library().ssd_forward(ctypes.byref(p), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D),
                                       _ptr(init_state), _ptr(seq_idx), _ptr(y), _ptr(final_state),
                                       _ptr(workspace), wsn, _stream_of(x.device, stream)))
 
 
-def step(x, dt, A_log, B, C, D, state, y=None, dt_scales_x: bool = False, stream=None):
+def step(x, dt, A_log, B, C, D, state, y=None, dt_scales_x: bool = False, stream=None, dt_bias=None,
+         dt_softplus: bool = False, zoh: bool = False):
     """``ssd_step``: one token per (row, head).  x (b,1,H,P) or (b,H,P), dt (b,1,H) or
     (b,H), B/C (b,1,G,N) or (b,G,N); ``state`` (b,H,P,N) fp32 is updated in place.
     Returns y (b,1,H,P) fp32."""
@@ -214,13 +234,14 @@ def step(x, dt, A_log, B, C, D, state, y=None, dt_scales_x: bool = False, stream
     dt = dt.reshape(b, 1, H).contiguous()
     B = B.reshape(b, 1, G, N).contiguous()
     C = C.reshape(b, 1, G, N).contiguous()
-    _check_tensors(x, dt, A_log, B, C, D, state, None)
+    _check_tensors(x, dt, A_log, B, C, D, state, None, dt_bias)
     if not state.is_contiguous() or tuple(state.shape) != (b, H, P, N) or state.dtype != torch.float32:
         raise ValueError("state must be a contiguous fp32 (b,H,P,N) tensor")
-    p = _describe(x, B, dt, A_log, 64, None, None, dt_scales_x)
+    p = _describe(x, B, dt, A_log, 64, None, None, dt_scales_x, dt_softplus, zoh)
     if y is None:
         y = torch.empty((b, 1, H, P), dtype=torch.float32, device=x.device)
-    _check(load_library().ssd_step(ctypes.byref(p), _ptr(x), _ptr(dt), _ptr(A_log.contiguous()), _ptr(B), _ptr(C),
+    _check(load_library().ssd_step(ctypes.byref(p), _ptr(x), _ptr(dt),
+                                   _ptr(dt_bias.contiguous() if dt_bias is not None else None), _ptr(A_log.contiguous()), _ptr(B), _ptr(C),
                                    _ptr(D.contiguous() if D is not None else None), _ptr(state), _ptr(y),
                                    _stream_of(x.device, stream)))
     return y

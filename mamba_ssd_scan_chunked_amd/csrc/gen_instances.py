@@ -1,13 +1,13 @@
-"""Write the kernel-instantiation sources (ssd_<dtype>.hip, ssd_<dtype>_s<seq>_e<euler>_l<local>.hip).
+"""Write the kernel-instantiation sources (ssd_<dtype>.hip, ssd_<dtype>_s<seq>_e<xscale>_l<local>.hip).
 
-Each file instantiates the scan kernel for one (dtype, sequence ids, Euler scaling,
+Each file instantiates the scan kernel for one (dtype, sequence ids, input scaling (Euler or zero-order hold),
 local pass or scan) combination over the supported (headdim, dstate, block) shapes, so the build compiles
 them in parallel.  Run it after changing the shape lists below; the outputs are
 committed sources.
 """
 import itertools
 def gen(tag, TI, Ps, Ns, QBs, seq, eul, loc):
-    out = ['// Kernel instantiations: %s inputs, %s sequence ids, %s Euler input scaling, %s.\n#include "ssd_kernels.hpp"\n#include "ssd_launch.hpp"\n\nnamespace ssd {\n' % (tag, "with" if seq else "without", "with" if eul else "without", "local pass" if loc else "scan")]
+    out = ['// Kernel instantiations: %s inputs, %s sequence ids, %s input scaling, %s.\n#include "ssd_kernels.hpp"\n#include "ssd_launch.hpp"\n\nnamespace ssd {\n' % (tag, "with" if seq else "without", "with" if eul else "without", "local pass" if loc else "scan")]
     fn = "launch_scan_%s_s%d_e%d_l%d" % (tag, seq, eul, loc)
     out.append("hipError_t %s(int P, int N, int QB, int spw, const ScanParams& prm, int64_t grid, hipStream_t s) {\n" % fn)
     b = lambda v: "true" if v else "false"
@@ -30,10 +30,10 @@ def gen_common(tag, TI, Ps, Ns, QBs):
     out.append("    const bool n = %s;\n" % " || ".join("N == %d" % v for v in Ns))
     out.append("    const bool q = %s;\n" % " || ".join("QB == %d" % v for v in QBs))
     out.append("    return p && n && q;\n}\n\n")
-    out.append("hipError_t launch_scan_%s(int P, int N, int QB, bool seq, bool euler, bool local, int spw, const ScanParams& prm, int64_t grid, hipStream_t s) {\n" % tag)
+    out.append("hipError_t launch_scan_%s(int P, int N, int QB, bool seq, bool xscale, bool local, int spw, const ScanParams& prm, int64_t grid, hipStream_t s) {\n" % tag)
     out.append("    if (grid <= 0) return hipSuccess;\n")
     for sq, eu, lo in itertools.product((0, 1), (0, 1), (0, 1)):
-        out.append("    if (seq == %s && euler == %s && local == %s) return launch_scan_%s_s%d_e%d_l%d(P, N, QB, spw, prm, grid, s);\n" % ("true" if sq else "false", "true" if eu else "false", "true" if lo else "false", tag, sq, eu, lo))
+        out.append("    if (seq == %s && xscale == %s && local == %s) return launch_scan_%s_s%d_e%d_l%d(P, N, QB, spw, prm, grid, s);\n" % ("true" if sq else "false", "true" if eu else "false", "true" if lo else "false", tag, sq, eu, lo))
     out.append("    return hipErrorInvalidValue;\n}\n\n")
     out.append("hipError_t launch_step_%s(int P, int N, const StepParams& prm, int64_t grid, hipStream_t s) {\n" % tag)
     out.append("    if (grid <= 0) return hipSuccess;\n")

@@ -135,6 +135,13 @@ int slices_per_workgroup(const ssd_problem_t* p, bool seq, int nseg) {
     return npt;
 }
 
+// Factor on x in the state write: 0 none, 1 the step size (Euler), 2 the exact
+// zero-order hold (exp(Delta A) - 1) / A.
+int x_scale_of(const ssd_problem_t* p) {
+    if (p->flags & SSD_FLAG_ZOH) return 2;
+    return (p->flags & SSD_FLAG_DT_SCALES_X) ? 1 : 0;
+}
+
 bool misaligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) != 0; }
 
 bool overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
@@ -173,7 +180,8 @@ Sizes sizes(const ssd_problem_t* p) {
     return s;
 }
 
-int check_args(const ssd_problem_t* p, const void* x, const float* dt, const float* A_log, const void* B,
+int check_args(const ssd_problem_t* p, const void* x, const float* dt, const float* dt_bias, const float* A_log,
+               const void* B,
                const void* C, const float* D, const float* init, const int32_t* seq_idx, const float* y,
                const float* fin, const void* ws, size_t ws_bytes) {
     const int v = ssd_validate(p);
@@ -185,7 +193,7 @@ int check_args(const ssd_problem_t* p, const void* x, const float* dt, const flo
     if (wsb > 0 && !ws) return SSD_ERR_WORKSPACE;
     if (!seq_idx && p->nseqs != p->batch) return SSD_ERR_BAD_SHAPE;
     if (misaligned(x, 16) || misaligned(B, 16) || misaligned(C, 16) || misaligned(y, 16) || misaligned(dt, 4) ||
-        misaligned(A_log, 4) ||
+        misaligned(A_log, 4) || misaligned(dt_bias, 4) ||
         misaligned(D, 4) || misaligned(init, 16) || misaligned(fin, 16) || misaligned(seq_idx, 4) ||
         misaligned(ws, 256))
         return SSD_ERR_ALIGNMENT;
@@ -193,9 +201,9 @@ int check_args(const ssd_problem_t* p, const void* x, const float* dt, const flo
     const Sizes s = sizes(p);
     const int64_t hb = p->nheads * 4;
     // outputs must not overlap any input, the workspace or each other
-    const void* in_ptr[] = {x, dt, A_log, B, C, D, seq_idx, ws};
-    const int64_t in_sz[] = {s.x, s.dt, hb, s.bc, s.bc, hb, s.seq, wsb};
-    for (int i = 0; i < 8; ++i) {
+    const void* in_ptr[] = {x, dt, A_log, B, C, D, seq_idx, ws, dt_bias};
+    const int64_t in_sz[] = {s.x, s.dt, hb, s.bc, s.bc, hb, s.seq, wsb, hb};
+    for (int i = 0; i < 9; ++i) {
         if (overlap(y, s.y, in_ptr[i], in_sz[i])) return SSD_ERR_ALIAS;
         if (overlap(fin, s.state, in_ptr[i], in_sz[i])) return SSD_ERR_ALIAS;
     }
@@ -205,7 +213,8 @@ int check_args(const ssd_problem_t* p, const void* x, const float* dt, const flo
     return SSD_OK;
 }
 
-int launch_scan(const ssd_problem_t* p, const void* x, const float* dt, const float* A_log, const void* B,
+int launch_scan(const ssd_problem_t* p, const void* x, const float* dt, const float* dt_bias, const float* A_log,
+                const void* B,
                 const void* C, const float* D, const float* init, const int32_t* seq_idx, float* y, float* fin,
                 void* ws, hipStream_t stream) {
     const int q = block_len(p);
@@ -228,7 +237,9 @@ int launch_scan(const ssd_problem_t* p, const void* x, const float* dt, const fl
     prm.G = p->ngroups;
     prm.nseqs = p->nseqs;
     prm.nblk = static_cast<int>(nblocks(p));
-    prm.dt_scales_x = (p->flags & SSD_FLAG_DT_SCALES_X) ? 1 : 0;
+    prm.dt_bias = dt_bias;
+    prm.dt_softplus = (p->flags & SSD_FLAG_DT_SOFTPLUS) ? 1 : 0;
+    prm.x_scale = x_scale_of(p);
     prm.seg_blocks = sg.seg_blocks;
     prm.nseg = sg.nseg;
     prm.seg_state = sg.nseg > 1 ? static_cast<float*>(ws) : nullptr;
@@ -236,13 +247,13 @@ int launch_scan(const ssd_problem_t* p, const void* x, const float* dt, const fl
     const int64_t rows = p->batch * p->nheads;
     if (rows == 0) return SSD_OK;
     if (p->seqlen == 0 && (seq_idx || !fin)) return SSD_OK;   // no token, no sequence to hand out
-    const bool seq = seq_idx != nullptr, euler = prm.dt_scales_x != 0;
+    const bool seq = seq_idx != nullptr, xscale = prm.x_scale != 0;
     const int P = (int)p->headdim, N = (int)p->dstate;
     const int npt = P / 16;
     const int spw = slices_per_workgroup(p, seq, sg.nseg);
     auto scan = [&](bool local, int spw, int64_t grid) {
-        return p->dtype == SSD_DTYPE_BF16 ? ssd::launch_scan_bf16(P, N, q, seq, euler, local, spw, prm, grid, stream)
-                                          : ssd::launch_scan_f32(P, N, q, seq, euler, local, spw, prm, grid, stream);
+        return p->dtype == SSD_DTYPE_BF16 ? ssd::launch_scan_bf16(P, N, q, seq, xscale, local, spw, prm, grid, stream)
+                                          : ssd::launch_scan_f32(P, N, q, seq, xscale, local, spw, prm, grid, stream);
     };
 
     hipError_t e = hipSuccess;
@@ -285,7 +296,8 @@ int ssd_validate(const ssd_problem_t* p) {
     if (p->nheads % p->ngroups != 0) return SSD_ERR_BAD_SHAPE;
     if (p->chunk_len <= 0) return SSD_ERR_BAD_SHAPE;
     if (p->dtype != SSD_DTYPE_BF16 && p->dtype != SSD_DTYPE_F32) return SSD_ERR_UNSUPPORTED;
-    if (p->flags & ~uint32_t(SSD_FLAG_DT_SCALES_X)) return SSD_ERR_UNSUPPORTED;
+    if (p->flags & ~uint32_t(SSD_FLAG_DT_SCALES_X | SSD_FLAG_DT_SOFTPLUS | SSD_FLAG_ZOH)) return SSD_ERR_UNSUPPORTED;
+    if ((p->flags & SSD_FLAG_DT_SCALES_X) && (p->flags & SSD_FLAG_ZOH)) return SSD_ERR_UNSUPPORTED;
     const int q = block_len(p);
     if (!q) return SSD_ERR_UNSUPPORTED;
     if (p->headdim > 4096 || p->dstate > 4096) return SSD_ERR_UNSUPPORTED;
@@ -309,19 +321,21 @@ size_t ssd_workspace_size(const ssd_problem_t* p) {
     return static_cast<size_t>(workspace_bytes(p));
 }
 
-int ssd_forward(const ssd_problem_t* p, const void* x, const float* dt, const float* A_log, const void* B,
+int ssd_forward(const ssd_problem_t* p, const void* x, const float* dt, const float* dt_bias, const float* A_log,
+                const void* B,
                 const void* C, const float* D, const float* init_state, const int32_t* seq_idx, float* y,
                 float* final_state, void* workspace, size_t workspace_bytes, void* stream) {
-    const int v = check_args(p, x, dt, A_log, B, C, D, init_state, seq_idx, y, final_state, workspace,
+    const int v = check_args(p, x, dt, dt_bias, A_log, B, C, D, init_state, seq_idx, y, final_state, workspace,
                              workspace_bytes);
     if (v != SSD_OK) return v;
     const int d = check_device();
     if (d != SSD_OK) return d;
-    return launch_scan(p, x, dt, A_log, B, C, D, init_state, seq_idx, y, final_state, workspace,
+    return launch_scan(p, x, dt, dt_bias, A_log, B, C, D, init_state, seq_idx, y, final_state, workspace,
                        static_cast<hipStream_t>(stream));
 }
 
-int ssd_step(const ssd_problem_t* p, const void* x, const float* dt, const float* A_log, const void* B,
+int ssd_step(const ssd_problem_t* p, const void* x, const float* dt, const float* dt_bias, const float* A_log,
+             const void* B,
              const void* C, const float* D, float* state, float* y, void* stream) {
     if (!p) return SSD_ERR_NULL_POINTER;
     if (p->seqlen != 1 || p->nseqs != p->batch) return SSD_ERR_BAD_SHAPE;
@@ -330,13 +344,13 @@ int ssd_step(const ssd_problem_t* p, const void* x, const float* dt, const float
     if (!A_log) return SSD_ERR_NULL_POINTER;
     if (p->batch > 0 && (!x || !dt || !B || !C || !state || !y)) return SSD_ERR_NULL_POINTER;
     if (misaligned(x, 16) || misaligned(B, 16) || misaligned(C, 16) || misaligned(state, 16) ||
-        misaligned(y, 4) || misaligned(dt, 4) || misaligned(A_log, 4) || misaligned(D, 4))
+        misaligned(y, 4) || misaligned(dt, 4) || misaligned(A_log, 4) || misaligned(D, 4) || misaligned(dt_bias, 4))
         return SSD_ERR_ALIGNMENT;
     const Sizes s = sizes(p);
     const int64_t hb = p->nheads * 4;
-    const void* in_ptr[] = {x, dt, A_log, B, C, D};
-    const int64_t in_sz[] = {s.x, s.dt, hb, s.bc, s.bc, hb};
-    for (int i = 0; i < 6; ++i)
+    const void* in_ptr[] = {x, dt, A_log, B, C, D, dt_bias};
+    const int64_t in_sz[] = {s.x, s.dt, hb, s.bc, s.bc, hb, hb};
+    for (int i = 0; i < 7; ++i)
         if (overlap(y, s.y, in_ptr[i], in_sz[i]) || overlap(state, s.state, in_ptr[i], in_sz[i])) return SSD_ERR_ALIAS;
     if (overlap(y, s.y, state, s.state)) return SSD_ERR_ALIAS;
     const int d = check_device();
@@ -353,7 +367,9 @@ int ssd_step(const ssd_problem_t* p, const void* x, const float* dt, const float
     prm.batch = p->batch;
     prm.H = p->nheads;
     prm.G = p->ngroups;
-    prm.dt_scales_x = (p->flags & SSD_FLAG_DT_SCALES_X) ? 1 : 0;
+    prm.dt_bias = dt_bias;
+    prm.dt_softplus = (p->flags & SSD_FLAG_DT_SOFTPLUS) ? 1 : 0;
+    prm.x_scale = x_scale_of(p);
     const int64_t grid = p->batch * p->nheads;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const hipError_t e = p->dtype == SSD_DTYPE_BF16

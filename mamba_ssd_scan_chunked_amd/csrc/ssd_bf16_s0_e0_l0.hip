@@ -1,4 +1,4 @@
-// Kernel instantiations: bf16 inputs, without sequence ids, without Euler input scaling, scan.
+// Kernel instantiations: bf16 inputs, without sequence ids, without input scaling, scan.
 #include "ssd_kernels.hpp"
 #include "ssd_launch.hpp"
 

@@ -1,4 +1,4 @@
-// Kernel instantiations: bf16 inputs, with sequence ids, without Euler input scaling, local pass.
+// Kernel instantiations: bf16 inputs, with sequence ids, without input scaling, local pass.
 #include "ssd_kernels.hpp"
 #include "ssd_launch.hpp"
 

@@ -10,16 +10,16 @@ bool supported_f32(int P, int N, int QB) {
     return p && n && q;
 }
 
-hipError_t launch_scan_f32(int P, int N, int QB, bool seq, bool euler, bool local, int spw, const ScanParams& prm, int64_t grid, hipStream_t s) {
+hipError_t launch_scan_f32(int P, int N, int QB, bool seq, bool xscale, bool local, int spw, const ScanParams& prm, int64_t grid, hipStream_t s) {
     if (grid <= 0) return hipSuccess;
-    if (seq == false && euler == false && local == false) return launch_scan_f32_s0_e0_l0(P, N, QB, spw, prm, grid, s);
-    if (seq == false && euler == false && local == true) return launch_scan_f32_s0_e0_l1(P, N, QB, spw, prm, grid, s);
-    if (seq == false && euler == true && local == false) return launch_scan_f32_s0_e1_l0(P, N, QB, spw, prm, grid, s);
-    if (seq == false && euler == true && local == true) return launch_scan_f32_s0_e1_l1(P, N, QB, spw, prm, grid, s);
-    if (seq == true && euler == false && local == false) return launch_scan_f32_s1_e0_l0(P, N, QB, spw, prm, grid, s);
-    if (seq == true && euler == false && local == true) return launch_scan_f32_s1_e0_l1(P, N, QB, spw, prm, grid, s);
-    if (seq == true && euler == true && local == false) return launch_scan_f32_s1_e1_l0(P, N, QB, spw, prm, grid, s);
-    if (seq == true && euler == true && local == true) return launch_scan_f32_s1_e1_l1(P, N, QB, spw, prm, grid, s);
+    if (seq == false && xscale == false && local == false) return launch_scan_f32_s0_e0_l0(P, N, QB, spw, prm, grid, s);
+    if (seq == false && xscale == false && local == true) return launch_scan_f32_s0_e0_l1(P, N, QB, spw, prm, grid, s);
+    if (seq == false && xscale == true && local == false) return launch_scan_f32_s0_e1_l0(P, N, QB, spw, prm, grid, s);
+    if (seq == false && xscale == true && local == true) return launch_scan_f32_s0_e1_l1(P, N, QB, spw, prm, grid, s);
+    if (seq == true && xscale == false && local == false) return launch_scan_f32_s1_e0_l0(P, N, QB, spw, prm, grid, s);
+    if (seq == true && xscale == false && local == true) return launch_scan_f32_s1_e0_l1(P, N, QB, spw, prm, grid, s);
+    if (seq == true && xscale == true && local == false) return launch_scan_f32_s1_e1_l0(P, N, QB, spw, prm, grid, s);
+    if (seq == true && xscale == true && local == true) return launch_scan_f32_s1_e1_l1(P, N, QB, spw, prm, grid, s);
     return hipErrorInvalidValue;
 }
 

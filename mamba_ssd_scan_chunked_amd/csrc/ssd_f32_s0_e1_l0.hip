@@ -1,4 +1,4 @@
-// Kernel instantiations: f32 inputs, without sequence ids, with Euler input scaling, scan.
+// Kernel instantiations: f32 inputs, without sequence ids, with input scaling, scan.
 #include "ssd_kernels.hpp"
 #include "ssd_launch.hpp"
 

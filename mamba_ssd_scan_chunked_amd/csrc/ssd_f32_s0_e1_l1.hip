@@ -1,4 +1,4 @@
-// Kernel instantiations: f32 inputs, without sequence ids, with Euler input scaling, local pass.
+// Kernel instantiations: f32 inputs, without sequence ids, with input scaling, local pass.
 #include "ssd_kernels.hpp"
 #include "ssd_launch.hpp"
 

@@ -1,4 +1,4 @@
-// Kernel instantiations: f32 inputs, with sequence ids, without Euler input scaling, scan.
+// Kernel instantiations: f32 inputs, with sequence ids, without input scaling, scan.
 #include "ssd_kernels.hpp"
 #include "ssd_launch.hpp"
 

@@ -77,6 +77,22 @@ template <> __device__ inline float lds_frag<float>(const float* p) { return *p;
 
 __device__ inline float fast_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
 
+// Step size from the dt input: dt + bias, optionally through softplus(v) =
+// log(1 + e^v) (the Mamba block's step-size map, simplified block pseudocode
+// of the "Mamba" paper story), in a form where neither branch overflows.
+__device__ inline float step_size(float v, int softplus) {
+    if (!softplus) return v;
+    return v > 0.f ? v + log1pf(expf(-v)) : log1pf(expf(v));
+}
+
+// Factor on x_t in the state write: 1, the step size (Euler), or the exact
+// zero-order hold (exp(Delta A) - 1) / A of h' = A h + B x over one step with
+// x and B held (the hold named in section 2 of "Mamba and state space
+// models").  A < 0 always (A = -exp(A_log)).
+__device__ inline float x_factor(float dtv, float A, int mode) {
+    return mode == 2 ? expm1f(dtv * A) / A : (mode == 1 ? dtv : 1.f);
+}
+
 // Rows of the state tiles.  The state S (P x N) is held transposed, S^T[n][p],
 // as N/16 accumulator tiles per wave; accumulator row rho = 4*(l/16) + i of
 // tile m holds state row n = nrow(m, rho).  For N % 32 == 0 the rows of tile
@@ -295,7 +311,9 @@ struct ScanParams {
     const void* C;
     int64_t batch, T, H, G, nseqs;
     int nblk;
-    int dt_scales_x;
+    const float* dt_bias;   // (H) added to dt before the step-size map, or null
+    int dt_softplus;        // step size softplus(dt + dt_bias) instead of dt + dt_bias
+    int x_scale;            // factor on x in the state write: 0 none, 1 step size, 2 zero-order hold
     // A row may be split into nseg segments of seg_blocks blocks that run in
     // parallel: a local pass gives each segment but the last its end state from
     // a zero incoming state and the decay it carries across, a combine step
@@ -332,7 +350,9 @@ struct StepParams {
     float* state;           // (batch, H, P, N), updated in place
     float* y;               // (batch, H, P)
     int64_t batch, H, G;
-    int dt_scales_x;
+    const float* dt_bias;   // (H) or null
+    int dt_softplus;        // as in ScanParams
+    int x_scale;            // as in ScanParams
 };
 
 // One workgroup of 256 threads per (row, head).  Thread t owns state row
@@ -348,9 +368,10 @@ __global__ __launch_bounds__(256) void ssd_step_kernel(StepParams prm) {
     const int64_t g = h / (prm.H / prm.G);
     const int tid = threadIdx.x, p = tid / R, q = tid % R;
     const float xv = to_f32(((const TI*)prm.x)[bh * P + p]);
-    const float dtv = prm.dt[bh];
-    const float a = expf(dtv * -expf(prm.A_log[h]));
-    const float xs = prm.dt_scales_x ? dtv * xv : xv;        // Euler input scaling (D uses x)
+    const float A = -expf(prm.A_log[h]);
+    const float dtv = step_size(prm.dt[bh] + (prm.dt_bias ? prm.dt_bias[h] : 0.f), prm.dt_softplus);
+    const float a = expf(dtv * A);
+    const float xs = x_factor(dtv, A, prm.x_scale) * xv;         // input scaling (D uses the unscaled x)
     const TI* Bg = (const TI*)prm.B + (b * prm.G + g) * N + q * NPT;
     const TI* Cg = (const TI*)prm.C + (b * prm.G + g) * N + q * NPT;
     float* srow = prm.state + (bh * P + p) * N + q * NPT;
@@ -478,7 +499,7 @@ struct ScanCfg {
 
 // LOCAL: the local pass over segments 0 .. nseg-2 (end state from a zero incoming
 // state and the carried decay, no outputs); otherwise the scan proper.
-template <typename TI, int P, int N, int QB, bool SEQ, bool EULER, bool LOCAL, int SPW = P / 16>
+template <typename TI, int P, int N, int QB, bool SEQ, bool XSCALE, bool LOCAL, int SPW = P / 16>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, ScanCfg<TI, P, N, QB, SPW>::NT),
                           amdgpu_waves_per_eu(SEQ && SPW == P / 16 ? 2 : ScanCfg<TI, P, N, QB, SPW>::WPE)))
 void ssd_scan_kernel(ScanParams prm) {
@@ -496,12 +517,12 @@ void ssd_scan_kernel(ScanParams prm) {
 
     __shared__ __attribute__((aligned(16))) TI smem[K::BUF_ELEMS];
     // per-token scalars of the block, shared by all waves (written by wave 0)
-    constexpr int SQ = SEQ ? 1 : 0, EU = EULER ? 1 : 0;
+    constexpr int SQ = SEQ ? 1 : 0, EU = XSCALE ? 1 : 0;
     // (one copy per head of the workgroup, written by that head's first wave)
     __shared__ __attribute__((aligned(16))) cum_t sCumH[MLH][64];      // cumulative log2 decay
     __shared__ __attribute__((aligned(16))) float sRowH[MLH][64];      // read-out row scale
     __shared__ __attribute__((aligned(16))) float sWxH[MLH][64];       // end-state weight exp2(cum_end - cum) (dt)
-    __shared__ __attribute__((aligned(16))) float sDtfH[MLH][64 * EU + 4];   // dt (Euler input scaling)
+    __shared__ __attribute__((aligned(16))) float sDtfH[MLH][64 * EU + 4];   // factor on x_t (input scaling)
     __shared__ __attribute__((aligned(16))) int sSeg[64 * SQ + 4];     // segment of each token
     __shared__ int sStart[65 * SQ + 1];
     __shared__ int sSeqOf[65 * SQ + 1];
@@ -556,6 +577,8 @@ void ssd_scan_kernel(ScanParams prm) {
     if constexpr (sizeof(cum_t) == 8) A2 = -exp((double)prm.A_log[h]) * 1.4426950408889634;
     else A2 = -expf(prm.A_log[h]) * 1.4426950408889634f;
     const float Dh = prm.D ? prm.D[h] : 0.f;
+    const float dtb = prm.dt_bias ? prm.dt_bias[h] : 0.f;
+    const float Anat = -expf(prm.A_log[h]);                      // A_h for the zero-order-hold factor
     const int32_t* seqg = SEQ ? prm.seq_idx + b * T : nullptr;
     auto clamp_seq = [&](int s) { return s < 0 ? 0 : (s >= prm.nseqs ? (int)prm.nseqs - 1 : s); };
 
@@ -695,6 +718,8 @@ void ssd_scan_kernel(ScanParams prm) {
                 }
             }
         }
+        if (prm.dt_bias || prm.dt_softplus)                        // step size; 0 past the row's end
+            dtv = lane < rows ? step_size(dtv + dtb, prm.dt_softplus) : 0.f;
         const cum_t cum = wave_incl_scan((cum_t)dtv * A2);        // dt = 0 past the row's end
         const cum_t cend = __shfl(cum, QB - 1);
         int nstart = 0;
@@ -731,12 +756,12 @@ void ssd_scan_kernel(ScanParams prm) {
         cend_f = (float)cend;
         seg_total += cend;
         seg_reset |= nstart > 0;
-        const float dtf = EULER ? dtv : 1.f;
+        const float dtf = XSCALE ? x_factor(dtv, Anat, prm.x_scale) : 1.f;
         if (head_leader && lane < QB) {
             sCum[lane] = cum;
             sRow[lane] = fast_exp2((float)(cum - before));
             sWx[lane] = fast_exp2((float)(cend - cum)) * dtf;  // end-state weight of token lane
-            if constexpr (EULER) sDtf[lane] = dtv;
+            if constexpr (XSCALE) sDtf[lane] = dtf;
         }
 
         // X (row-major; each thread holds VE channels of one token)
@@ -750,7 +775,7 @@ void ssd_scan_kernel(ScanParams prm) {
     // ---- this wave's causal tiles of L o CB: C B^T on MFMA (as (C B^T)^T, rows s,
     //      columns t, so that each lane holds 4 consecutive s of one token t), then
     //      the masked decay exp2(cum_t - cum_s) for s <= t (else 0) in registers
-    //      (times dt_s with Euler input scaling; zero across sequence segments).
+    //      (times the input factor of token s when x is scaled; zero across sequence segments).
     //      Surplus slots recompute a tile another wave owns and write the same values.
     //      The values are held in registers and written after the state update, so
     //      that no LDS write separates the operand reads of the MFMA phase (the
@@ -792,7 +817,7 @@ void ssd_scan_kernel(ScanParams prm) {
                     const float lv = fast_exp2((float)(ct - csv[e])) * acc[e];
                     val[e] = (s0 + e <= t) ? lv : 0.f;
                 }
-                if constexpr (EULER) {
+                if constexpr (XSCALE) {
                     const float4 d4 = *(const float4*)(&sDtfH[l][s0]);
                     val[0] *= d4.x; val[1] *= d4.y; val[2] *= d4.z; val[3] *= d4.w;
                 }
@@ -910,7 +935,7 @@ void ssd_scan_kernel(ScanParams prm) {
                 const cum_t ce = sCum[e];
                 auto wseg = [&](int t) {
                     float df = 1.f;
-                    if constexpr (EULER) df = sDtf[t];
+                    if constexpr (XSCALE) df = sDtf[t];
                     return (sSeg[t] == j) ? fast_exp2((float)(ce - sCum[t])) * df : 0.f;
                 };
                 const cum_t before = (a == 0) ? (cum_t)0 : sCum[a - 1];

@@ -11,12 +11,12 @@ struct StepParams;
 
 // Return hipSuccess, hipErrorInvalidValue for a shape with no instantiation,
 // or the launch error.
-// seq: sequence ids present (segment handling compiled in); euler: dt scales x;
+// seq: sequence ids present (segment handling compiled in); xscale: x scaled per token (Euler or zero-order hold);
 // local: the local pass of a row split into segments (else the scan proper);
 // spw: 16-channel slices per workgroup (P / 16: one head per workgroup)
-hipError_t launch_scan_bf16(int P, int N, int QB, bool seq, bool euler, bool local, int spw, const ScanParams& prm,
+hipError_t launch_scan_bf16(int P, int N, int QB, bool seq, bool xscale, bool local, int spw, const ScanParams& prm,
                             int64_t grid, hipStream_t s);
-hipError_t launch_scan_f32(int P, int N, int QB, bool seq, bool euler, bool local, int spw, const ScanParams& prm,
+hipError_t launch_scan_f32(int P, int N, int QB, bool seq, bool xscale, bool local, int spw, const ScanParams& prm,
                            int64_t grid, hipStream_t s);
 hipError_t launch_combine(const CombineParams& prm, hipStream_t s);
 hipError_t launch_step_bf16(int P, int N, const StepParams& prm, int64_t grid, hipStream_t s);

@@ -37,10 +37,10 @@ def run_gpu(prob, chunk_len=256, dt_scales_x=False, **kw):
     return y.cpu().double().numpy(), (f.cpu().double().numpy() if f is not None else None)
 
 
-def run_oracle(prob, dt_scales_x=False, nthreads=0):
+def run_oracle(prob, dt_scales_x=False, nthreads=0, **kw):
     return oracle.recurrence(prob["x"], prob["dt"], prob["A_log"], prob["B"], prob["C"], prob["D"],
                              prob["init"], prob["seq_idx"], prob["nseqs"] if prob["seq_idx"] is not None else None,
-                             dt_scales_x=dt_scales_x, nthreads=nthreads)
+                             dt_scales_x=dt_scales_x, nthreads=nthreads, **kw)
 
 
 def sub_problem(prob, b, h):

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_strerror():
-    assert ssd.version() == 2
+    assert ssd.version() == 3
     lib = ssd.load_library()
     for code in range(0, 9):
         assert lib.ssd_strerror(code)
@@ -59,7 +59,8 @@ def test_validate_accepts_the_measured_shapes():
     (dict(batch=-1), 2), (dict(seqlen=-5), 2), (dict(nheads=0), 2), (dict(headdim=0), 2),
     (dict(ngroups=3), 2), (dict(chunk_len=0), 2), (dict(nseqs=-1), 2),
     (dict(chunk_len=48), 3), (dict(chunk_len=16), 3), (dict(chunk_len=100), 3),
-    (dict(headdim=48), 3), (dict(dstate=96), 3), (dict(dstate=16), 3), (dict(dtype=7), 3), (dict(flags=2), 3),
+    (dict(headdim=48), 3), (dict(dstate=96), 3), (dict(dstate=16), 3), (dict(dtype=7), 3), (dict(flags=8), 3),
+    (dict(flags=ssd.FLAG_DT_SCALES_X | ssd.FLAG_ZOH), 3),
     (dict(dtype=ssd.DTYPE_F32, dstate=256), 3),
 ])
 def test_validate_rejects(kw, code):
@@ -91,11 +92,12 @@ def _forward(p, **ptrs):
     lib = ssd.load_library()
     names = ["x", "dt", "A_log", "B", "C", "D", "init", "seq", "y", "fin"]
     vals = {n: A + 0x1000000 * (i + 1) for i, n in enumerate(names)}
-    vals.update({"D": None, "init": None, "seq": None})
+    vals.update({"D": None, "init": None, "seq": None, "dt_bias": None})
     ws = ptrs.pop("ws", A + 0x40000000)
     wsb = ptrs.pop("wsb", ssd.workspace_size(p))
     vals.update(ptrs)
-    return lib.ssd_forward(ctypes.byref(p), *[vals[n] for n in names], ws, wsb, None)
+    order = ["x", "dt", "dt_bias"] + names[2:]
+    return lib.ssd_forward(ctypes.byref(p), *[vals[n] for n in order], ws, wsb, None)
 
 
 def small():
@@ -118,6 +120,17 @@ def test_forward_rejects_aliasing():
     assert _forward(small(), y=A + 0x4000000) == 6          # y on top of B
     assert _forward(small(), fin=A + 0x3000000) == 6        # final on top of A_log
     assert _forward(small(), fin=A + 0x5000000) == 6        # final on top of C
+
+
+def test_forward_checks_dt_bias():
+    assert _forward(small(), dt_bias=A + 0x30000000 + 2) == 4            # misaligned
+    assert _forward(small(), dt_bias=A + 0x9000000) == 6                 # y on top of dt_bias
+    assert _forward(small(), dt_bias=A + 0xA000000) == 6                 # final on top of dt_bias
+
+
+@pytest.mark.parametrize("flags", [0, 1, 2, 4, 1 | 2, 2 | 4])
+def test_validate_accepts_step_size_and_scaling_flags(flags):
+    assert ssd.validate(prob(flags=flags)) == 0
 
 
 def test_forward_requires_seq_idx_for_packed_nseqs():
@@ -145,9 +158,10 @@ def _step(p, **ptrs):
     lib = ssd.load_library()
     names = ["x", "dt", "A_log", "B", "C", "D", "state", "y"]
     vals = {n: A + 0x1000000 * (i + 1) for i, n in enumerate(names)}
-    vals.update({"D": None})
+    vals.update({"D": None, "dt_bias": None})
     vals.update(ptrs)
-    return lib.ssd_step(ctypes.byref(p), *[vals[n] for n in names], None)
+    order = ["x", "dt", "dt_bias"] + names[2:]
+    return lib.ssd_step(ctypes.byref(p), *[vals[n] for n in order], None)
 
 
 def test_step_rejects_bad_arguments():
@@ -161,6 +175,9 @@ def test_step_rejects_bad_arguments():
     assert _step(one, y=A + 0x1000000) == 6                               # y on top of x
     assert _step(one, state=A + 0x4000000) == 6                           # state on top of B
     assert _step(one, y=A + 0x7000000) == 6                               # y on top of the state
+    assert _step(one, y=A + 0x30000000, dt_bias=A + 0x30000000) == 6      # y on top of dt_bias
+    assert _step(one, dt_bias=A + 0x30000000 + 1) == 4                    # misaligned dt_bias
+    assert _step(prob(batch=2, seqlen=1, nheads=4, flags=1 | 4)) == 3      # Euler and hold together
 
 
 def test_step_without_device_reports_no_device():
