@@ -145,12 +145,12 @@ def make_problem(batch: int, seqlen: int, nheads: int, headdim: int, dstate: int
 
 
 def raw_step_sizes(batch: int, seqlen: int, nheads: int, *, seed: int = 0, lo: float = -4.0,
-                   hi: float = 1.0) -> dict:
+                   hi: float = 1.0, bias_range=(-0.5, 0.5)) -> dict:
     """Pre-activation step sizes for the fused step-size map: dt_raw (b,T,H) f32 and a
-    per-head bias (H) f32, with dt_raw + bias ~ U(lo, hi) (bias ~ U(-0.5, 0.5)).
+    per-head bias (H) f32, with dt_raw + bias ~ U(lo, hi) and bias ~ U(bias_range).
     Both sides take these values as given."""
     rng = np.random.default_rng(seed)
-    bias = rng.uniform(-0.5, 0.5, size=(nheads,))
+    bias = rng.uniform(bias_range[0], bias_range[1], size=(nheads,))
     u = rng.uniform(lo, hi, size=(batch, seqlen, nheads))
     f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
     return {"dt": f32(u - bias[None, None, :]), "dt_bias": f32(bias)}

@@ -34,11 +34,16 @@ def announce(msg):
 
 
 def with_raw_dt(prob, seed, softplus):
+    """Pre-activation dt and a bias for the softplus map; without it, the problem's
+    positive step sizes and a small positive bias (a negative step size would make
+    the decay exceed 1 and the state grow without bound)."""
     b, T, H = prob["dt"].shape
-    raw = si.raw_step_sizes(b, T, H, seed=seed)
     q = dict(prob)
     if softplus:
+        raw = si.raw_step_sizes(b, T, H, seed=seed)
         q["dt"] = raw["dt"]
+    else:
+        raw = si.raw_step_sizes(b, T, H, seed=seed, bias_range=(0.0, 0.2))
     q["dt_bias"] = raw["dt_bias"]
     return q
 
