@@ -5,6 +5,8 @@ this package.  The GPU library never calls it and shares no code with it.
 
 * :func:`recurrence` — the plain fp64 step-by-step recurrence (C, OpenMP over
   (row, head) units).  This is the definition the GPU path must match.
+* :func:`gradients` — reverse-mode differentiation of that recurrence, step by
+  step (C): the gradients of <dy, y> + <dfinal, final> with respect to every input.
 * :mod:`oracle.brute` — the dual (masked-attention) matrix form and the
   unrolled closed form in numpy, written independently, for tiny inputs.
 """
@@ -36,6 +38,10 @@ def _load():
     f.argtypes = [i64, i64, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci,
                   vp, vp, ci]
     f.restype = ctypes.c_int
+    b = lib.ssd_oracle_bwd_f64
+    b.argtypes = [i64, i64, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, vp, vp,
+                  vp, vp, vp, vp, vp, vp, vp, vp, ci]
+    b.restype = ctypes.c_int
     lib.ssd_oracle_max_threads.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -97,3 +103,47 @@ def recurrence(x, dt, A_log, B, C, D=None, init=None, seq_idx=None, nseqs: Optio
     if rc != 0:
         raise ValueError("oracle rejected its arguments (code %d)" % rc)
     return y, final
+
+
+def gradients(x, dt, A_log, B, C, dy, D=None, init=None, dfinal=None, seq_idx=None, nseqs: Optional[int] = None,
+              dt_scales_x: bool = False, dt_bias=None, dt_softplus: bool = False, zoh: bool = False,
+              nthreads: int = 0):
+    """Gradients of L = <dy, y> + <dfinal, final_state> for the forward map of
+    :func:`recurrence` (same arguments), by the adjoint recurrence in fp64.
+
+    Returns a dict of float64 arrays: dx (b,T,H,P), ddt (b,T,H) (with respect to
+    the dt input), dA_log (H), dB and dC (b,T,G,N), dD (H), dinit (nseqs,H,P,N),
+    ddt_bias (H).  dD, dinit and ddt_bias are returned whether or not D, init and
+    dt_bias were given (the gradient at zero / no bias).
+    """
+    if dt_scales_x and zoh:
+        raise ValueError("Euler and zero-order-hold input scaling are exclusive")
+    lib = _load()
+    x, dt, A_log, B, C, dy = (_f64(v) for v in (x, dt, A_log, B, C, dy))
+    D, init, dfinal, dt_bias = (_f64(v) for v in (D, init, dfinal, dt_bias))
+    b, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    if seq_idx is not None:
+        if hasattr(seq_idx, "detach"):
+            seq_idx = seq_idx.detach().cpu().numpy()
+        seq_idx = np.ascontiguousarray(seq_idx, dtype=np.int32)
+        if nseqs is None:
+            nseqs = int(seq_idx.max()) + 1 if seq_idx.size else 0
+    else:
+        nseqs = b
+    assert dy.shape == (b, T, H, P)
+    assert dfinal is None or dfinal.shape == (nseqs, H, P, N)
+    out = {"dx": np.empty((b, T, H, P)), "ddt": np.empty((b, T, H)), "dA_log": np.empty(H),
+           "dB": np.empty((b, T, G, N)), "dC": np.empty((b, T, G, N)), "dD": np.empty(H),
+           "dinit": np.empty((nseqs, H, P, N)), "ddt_bias": np.empty(H)}
+
+    def p(a):
+        return a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
+
+    rc = lib.ssd_oracle_bwd_f64(b, T, H, P, N, G, nseqs, p(x), p(dt), p(A_log), p(B), p(C), p(D), p(init),
+                                p(seq_idx), p(dt_bias), int(bool(dt_softplus)), 2 if zoh else int(bool(dt_scales_x)),
+                                p(dy), p(dfinal), p(out["dx"]), p(out["ddt"]), p(out["dA_log"]), p(out["dB"]),
+                                p(out["dC"]), p(out["dD"]), p(out["dinit"]), p(out["ddt_bias"]), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments (code %d)" % rc)
+    return out
