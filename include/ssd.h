@@ -174,6 +174,50 @@ int ssd_step(const ssd_problem_t* p,
              const void* B, const void* C, const float* D,
              float* state, float* y, void* stream);
 
+/* Bytes of device workspace ssd_backward needs (0 if the problem is invalid):
+ * per-token and per-(row, head) scalars, and, when a group holds more than one
+ * head, each head's dB and dC contribution, (batch, seqlen, nheads, dstate)
+ * fp32 each, before the sum over the group.  The contents need no
+ * initialisation. */
+size_t ssd_backward_workspace_size(const ssd_problem_t* p);
+
+/* Gradients of the forward map (training).  For a scalar loss L with
+ * dL/dy = dy and dL/dfinal_state = dfinal (NULL: L does not depend on the
+ * final states), writes dL/d(every input).  The pages give no backward
+ * algorithm: this is the chain rule applied to the recurrence of "088
+ * Mamba-2" (section 2.1), G_t = dL/dS_t = dy_t C_t^T + a_{t+1} G_{t+1},
+ * evaluated with the same block (dual) form as the forward (sections 2.2-3).
+ *   inputs     as ssd_forward (same problem, flags and tensors), plus
+ *   dy         (batch, seqlen, nheads, headdim)   fp32
+ *   dfinal     (batch, nheads, headdim, dstate)   fp32, or NULL
+ *   outputs (fp32):
+ *   dx         (batch, seqlen, nheads, headdim)
+ *   ddt        (batch, seqlen, nheads)     with respect to the dt input (through softplus if flagged)
+ *   dA_log     (nheads)
+ *   dB, dC     (batch, seqlen, ngroups, dstate)   summed over the heads of each group
+ *   dD         (nheads), or NULL
+ *   dinit      (batch, nheads, headdim, dstate), or NULL (the gradient with respect to
+ *              init_state, also when init_state is NULL, i.e. at a zero initial state)
+ *   ddt_bias   (nheads), or NULL
+ *   workspace  >= ssd_backward_workspace_size(p) bytes, 256-byte aligned
+ * seq_idx must be NULL (packed sequences are supported by the forward only:
+ * SSD_ERR_UNSUPPORTED).  Supported shapes: BF16 headdim 32 or 64 with dstate 64,
+ * 128 or 256; F32 headdim 16, 32 or 64 with dstate 16 .. 128.  Outputs must not
+ * overlap any input, the workspace or each other (SSD_ERR_ALIAS).  x, B, C, dy,
+ * dB, dC, init_state, dfinal and dinit need 16-byte alignment, the rest 4.
+ * Two kernel launches walk each (row, head) once forwards and once backwards
+ * with the state on chip; then, with more than one head per group, a sum of the
+ * heads' dB and dC; then the per-head sums over rows.  Per-head sums are taken in
+ * a fixed order, so results are deterministic. */
+int ssd_backward(const ssd_problem_t* p,
+                 const void* x, const float* dt, const float* dt_bias, const float* A_log,
+                 const void* B, const void* C, const float* D,
+                 const float* init_state, const int32_t* seq_idx,
+                 const float* dy, const float* dfinal,
+                 float* dx, float* ddt, float* dA_log, float* dB, float* dC,
+                 float* dD, float* dinit, float* ddt_bias,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static description of an error code. */
 const char* ssd_strerror(int status);
 

@@ -43,6 +43,23 @@ def gen_common(tag, TI, Ps, Ns, QBs):
     out.append("    return hipErrorInvalidValue;\n}\n}  // namespace ssd\n")
     return "".join(out)
 
+def gen_bwd(tag, TI, Ps, Ns, QB):
+    out = ['// Backward kernels (forward and reverse pass) for %s inputs.\n#include "ssd_bwd.hpp"\n#include "ssd_launch.hpp"\n\nnamespace ssd {\n' % tag]
+    out.append("bool supported_bwd_%s(int P, int N) {\n" % tag)
+    out.append("    return (%s) && (%s);\n}\n\n" % (" || ".join("P == %d" % v for v in Ps), " || ".join("N == %d" % v for v in Ns)))
+    out.append("int bwd_block_%s() { return %d; }\n\n" % (tag, QB))
+    out.append("hipError_t launch_bwd_%s(int P, int N, const BwdParams& prm, int64_t grid, hipStream_t s) {\n" % tag)
+    out.append("    if (grid <= 0) return hipSuccess;\n")
+    for P in Ps:
+        for N in Ns:
+            out.append("    if (P == %d && N == %d) {\n" % (P, N))
+            out.append("        hipLaunchKernelGGL((ssd_bwd_fwd_kernel<%s, %d, %d, %d>), dim3((unsigned)grid), dim3(BwdCfg<%s, %d, %d, %d>::NT), 0, s, prm);\n" % (TI, P, N, QB, TI, P, N, QB))
+            out.append("        hipError_t e = hipGetLastError();\n        if (e != hipSuccess) return e;\n")
+            out.append("        hipLaunchKernelGGL((ssd_bwd_rev_kernel<%s, %d, %d, %d>), dim3((unsigned)grid), dim3(BwdCfg<%s, %d, %d, %d>::NT), 0, s, prm);\n" % (TI, P, N, QB, TI, P, N, QB))
+            out.append("        return hipGetLastError();\n    }\n")
+    out.append("    return hipErrorInvalidValue;\n}\n}  // namespace ssd\n")
+    return "".join(out)
+
 import os
 d = os.path.dirname(os.path.abspath(__file__)) + "/"
 cfg = {"bf16": ("__bf16", [32, 64], [64, 128, 256], [32, 64]), "f32": ("float", [16, 32, 64], [16, 32, 64, 128], [32, 64])}
@@ -54,4 +71,9 @@ for tag, (TI, Ps, Ns, QBs) in cfg.items():
         fn = "ssd_%s_s%d_e%d_l%d.hip" % (tag, sq, eu, lo)
         open(d + fn, "w").write(gen(tag, TI, Ps, Ns, QBs, sq, eu, lo))
         files.append(fn)
+bwd = {"bf16": ("__bf16", [32, 64], [64, 128, 256], 64), "f32": ("float", [16, 32, 64], [16, 32, 64, 128], 32)}
+for tag, (TI, Ps, Ns, QB) in bwd.items():
+    fn = "ssd_bwd_%s.hip" % tag
+    open(d + fn, "w").write(gen_bwd(tag, TI, Ps, Ns, QB))
+    files.append(fn)
 print(files)

@@ -1,0 +1,687 @@
+// SSD backward for gfx950 (MI355X): the gradients of L = <dy, y> + <dfinal, final>
+// with respect to x, dt, dt_bias, A_log, B, C, D and the initial states.
+//
+// The pages give the forward map only.  The backward is the chain rule applied
+// to the recurrence of "088 Mamba-2" (section 2.1), H_t = a_t H_{t-1} +
+// f_t x_t B_t^T, y_t = H_t C_t + D x_t, evaluated block by block in the same
+// dual form as the forward (sections 2.2 and 3 of that page: masked
+// attention-like products inside a block, a carried state between blocks).
+// With G_t = dL/dH_t:
+//   G_t  = dy_t C_t^T + a_{t+1} G_{t+1}       (after the last token: dfinal)
+//   dC_t = sum_heads H_t^T dy_t,   dB_t = sum_heads f_t G_t^T x_t
+//   dx_t = f_t G_t B_t + D dy_t
+//   dl_t = q_t - f_t u_t + dl_{t+1},  dl_T = <dfinal, H_{T-1}>   (dl = dL/dlog a)
+//   q_t  = dy_t . (H_t C_t) = C_t . (H_t^T dy_t),   u_t = x_t . (G_t B_t)
+// (dl_t = <G_t, a_t H_{t-1}>; expanding G_t and H_t gives the recursion.)
+//
+// ssd_bwd_fwd_kernel walks each (row, head) forwards with H on chip and
+// produces the head's dC contribution and q; ssd_bwd_rev_kernel walks it
+// backwards with G on chip (as K = a_{t+1} G_{t+1}, the gradient that
+// reaches the block from its right) and produces dx, the head's dB
+// contribution, u, dl by a suffix scan, ddt, the per-row partial sums of
+// dA_log, ddt_bias and dD, and dinit = a_0 G_0.  The contributions of the
+// heads of a group are summed by ssd_bwd_group_sum_kernel (not needed when each
+// group has one head: then the passes write dB and dC directly), the per-row
+// scalars by ssd_bwd_scalars_kernel.
+//
+// Per 64-token block (32 for fp32 inputs) of QB tokens, with cum_t the inclusive
+// cumulative log2 decay inside the block and cend = cum_{QB-1}:
+//   forward pass:  W[t][s] = (s <= t) 2^(cum_t - cum_s) f_s (dy_t . x_s)
+//                  dC^h   = W B + 2^cum_t dy H_in          (QB x N)
+//                  H_out  = 2^cend H_in + X^T diag(f 2^(cend - cum)) B
+//   reverse pass:  E[t][s] = (s >= t) 2^(cum_s - cum_t) (B_t . C_s)
+//                  F[t][s] = (s >= t) 2^(cum_s - cum_t) (x_t . dy_s)
+//                  GB      = E dY + 2^(cend - cum_t) B K^T  (QB x P; = G_t B_t)
+//                  dB^h    = f_t (F C + 2^(cend - cum_t) X K)
+//                  K_prev  = 2^cend K + dY^T diag(2^cum) C
+// All products run on MFMA from tiles staged in LDS (bf16 operands with fp32
+// accumulation for bf16 inputs, fp32 throughout for fp32 inputs); every
+// operand is read either along its rows or, through the LDS transpose read,
+// along its columns, so each tile is stored once.
+
+#pragma once
+#include "ssd_kernels.hpp"
+
+namespace ssd {
+
+struct BwdParams {
+    const void* x;
+    const float* dt;
+    const float* dt_bias;
+    const float* A_log;
+    const void* B;
+    const void* C;
+    const float* D;
+    const float* init;
+    const float* dy;
+    const float* dfinal;
+    float* dx;
+    float* ddt;
+    float* dBh;       // (batch, T, HB, N): per-head dB (HB = H), or dB itself (HB = G = H)
+    float* dCh;       // same for dC
+    float* dinit;     // (batch, H, P, N) or null
+    float* q;         // (batch, T, H) workspace
+    float* phi;       // (batch, H) workspace: <dfinal, final>
+    float* part;      // (batch, H, 3) workspace: per-row sums for dA (natural A), ddt_bias, dD
+    int64_t batch, T, H, G, HB;
+    int nblk;
+    int dt_softplus, x_scale;
+};
+
+// Fragment of an operand stored with K contiguous: row `row`, K values
+// k0 + KPL*(l/16) .. (bf16: one 16-byte read; fp32: one value).
+__device__ inline bf16x8 frag_k(const __bf16* base, int pitch, int row, int k0, int lg) {
+    return *(const bf16x8*)(base + row * pitch + k0 + 8 * lg);
+}
+__device__ inline float frag_k(const float* base, int pitch, int row, int k0, int lg) {
+    return base[row * pitch + k0 + lg];
+}
+// Fragment of an operand stored with its rows contiguous (layout [k][m]):
+// row m0 + l%16, K values k0 + KPL*(l/16) ..  (bf16: two LDS transpose reads).
+__device__ inline bf16x8 frag_t(const __bf16* base, int pitch, int m0, int k0, int lr, int lg) {
+    return x_frag(base, pitch, k0, m0, lr, lg);
+}
+__device__ inline float frag_t(const float* base, int pitch, int m0, int k0, int lr, int lg) {
+    return base[(k0 + lg) * pitch + m0 + lr];
+}
+// The same with K value k scaled by wk[k] (rounded once to the input type).
+__device__ inline bf16x8 frag_t_w(const __bf16* base, int pitch, int m0, int k0, int lr, int lg, const float* wk) {
+    const bf16x8 v = x_frag(base, pitch, k0, m0, lr, lg);
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = (__bf16)(wk[k0 + 8 * lg + e] * (float)v[e]);
+    return r;
+}
+__device__ inline float frag_t_w(const float* base, int pitch, int m0, int k0, int lr, int lg, const float* wk) {
+    return wk[k0 + lg] * base[(k0 + lg) * pitch + m0 + lr];
+}
+
+// Four consecutive values of one row into LDS (8 bytes for bf16, 16 for fp32).
+__device__ inline void lds_store4(__bf16* dst, float a, float b, float c, float d) {
+    *(bf16x4*)dst = bf16x4{(__bf16)a, (__bf16)b, (__bf16)c, (__bf16)d};
+}
+__device__ inline void lds_store4(float* dst, float a, float b, float c, float d) {
+    *(f32x4*)dst = f32x4{a, b, c, d};
+}
+
+__device__ inline void buf_store_f32(float v, rsrc_t r, int off) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, v), r, off, 0, 0);
+}
+
+// Sum over the 16 lanes of each lane group (lanes with equal l/16).
+__device__ inline float group16_sum(float v) {
+    v += __shfl_xor(v, 1);
+    v += __shfl_xor(v, 2);
+    v += __shfl_xor(v, 4);
+    v += __shfl_xor(v, 8);
+    return v;
+}
+
+template <typename TI, int P, int N, int QB>
+struct BwdCfg {
+    static constexpr int NW = 8, NT = 64 * NW;
+    static constexpr int SZ = sizeof(TI);
+    static constexpr int KSTEP = Mfma<TI>::KSTEP;
+    static constexpr int PAD = SZ == 2 ? 8 : 4;                 // keeps 16-byte aligned rows
+    static constexpr int LP = P + PAD, LN = N + PAD, LQ = QB + PAD;
+    static constexpr int QT = QB / 16, PT = P / 16, NTL = N / 16;
+    static constexpr int T_QQ = (QT * QT + NW - 1) / NW;       // token x token tiles per wave
+    static constexpr int T_QN = (QT * NTL + NW - 1) / NW;      // token x state tiles per wave
+    static constexpr int T_QP = (QT * PT + NW - 1) / NW;       // token x channel tiles per wave
+    static constexpr int T_NP = (NTL * PT + NW - 1) / NW;      // state tiles per wave
+    static constexpr int XU = QB * P * SZ / 16;                // 16-byte chunks of x per block
+    static constexpr int YU = QB * P * 4 / 16;                 // of dy (fp32)
+    static constexpr int BU = QB * N * SZ / 16;                // of B or C
+    static constexpr int XPT = (XU + NT - 1) / NT, YPT = (YU + NT - 1) / NT, BPT = (BU + NT - 1) / NT;
+    static_assert(QB == 32 || QB == 64, "block");
+    static_assert(P % 16 == 0 && N % 16 == 0 && P % KSTEP == 0 && N % KSTEP == 0 && QB % KSTEP == 0, "shape");
+};
+
+// Staging of one block: global loads into registers (issued a block ahead),
+// then into LDS.  dy is converted to the input type for the products.
+template <typename TI, int P, int N, int QB>
+struct BwdStage {
+    using K = BwdCfg<TI, P, N, QB>;
+    uint4 xr[K::XPT], yr[K::YPT], br[K::BPT], cr[K::BPT];
+
+    __device__ inline void issue(const char* xrow, int64_t xrec, int xs, const char* yrow, int64_t yrec, int ys,
+                                 const char* brow, const char* crow, int64_t brec, int bs, int64_t t0, int tid) {
+        const rsrc_t rx = make_rsrc(xrow + t0 * xs, xrec - t0 * xs);
+        const rsrc_t ry = make_rsrc(yrow + t0 * ys, yrec - t0 * ys);
+        const rsrc_t rb = make_rsrc(brow + t0 * bs, brec - t0 * bs);
+        const rsrc_t rc = make_rsrc(crow + t0 * bs, brec - t0 * bs);
+        constexpr int XC = P * K::SZ / 16, YC = P / 4, BC = N * K::SZ / 16;
+#pragma unroll
+        for (int j = 0; j < K::XPT; ++j) {
+            const int v = tid + j * K::NT;
+            if (K::XU % K::NT == 0 || v < K::XU) xr[j] = buf_load16(rx, (v / XC) * xs + (v % XC) * 16);
+        }
+#pragma unroll
+        for (int j = 0; j < K::YPT; ++j) {
+            const int v = tid + j * K::NT;
+            if (K::YU % K::NT == 0 || v < K::YU) yr[j] = buf_load16(ry, (v / YC) * ys + (v % YC) * 16);
+        }
+#pragma unroll
+        for (int j = 0; j < K::BPT; ++j) {
+            const int v = tid + j * K::NT;
+            if (K::BU % K::NT == 0 || v < K::BU) {
+                br[j] = buf_load16(rb, (v / BC) * bs + (v % BC) * 16);
+                cr[j] = buf_load16(rc, (v / BC) * bs + (v % BC) * 16);
+            }
+        }
+    }
+    __device__ inline void store(TI* sX, TI* sDY, TI* sB, TI* sC, int tid) const {
+        constexpr int XC = P * K::SZ / 16, YC = P / 4, BC = N * K::SZ / 16, VE = 16 / K::SZ;
+#pragma unroll
+        for (int j = 0; j < K::XPT; ++j) {
+            const int v = tid + j * K::NT;
+            if (K::XU % K::NT == 0 || v < K::XU) *(uint4*)(sX + (v / XC) * K::LP + (v % XC) * VE) = xr[j];
+        }
+#pragma unroll
+        for (int j = 0; j < K::YPT; ++j) {
+            const int v = tid + j * K::NT;
+            if (K::YU % K::NT == 0 || v < K::YU) {
+                const float4 f = __builtin_bit_cast(float4, yr[j]);
+                lds_store4(sDY + (v / YC) * K::LP + (v % YC) * 4, f.x, f.y, f.z, f.w);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < K::BPT; ++j) {
+            const int v = tid + j * K::NT;
+            if (K::BU % K::NT == 0 || v < K::BU) {
+                *(uint4*)(sB + (v / BC) * K::LN + (v % BC) * VE) = br[j];
+                *(uint4*)(sC + (v / BC) * K::LN + (v % BC) * VE) = cr[j];
+            }
+        }
+    }
+};
+
+// ------------------------------------------------------------ forward pass
+template <typename TI, int P, int N, int QB>
+__global__ __launch_bounds__(512) void ssd_bwd_fwd_kernel(BwdParams prm) {
+    using K = BwdCfg<TI, P, N, QB>;
+    using M = Mfma<TI>;
+    typedef typename CumType<TI>::type cum_t;
+    constexpr int NW = K::NW, LP = K::LP, LN = K::LN, LQ = K::LQ, QT = K::QT, PT = K::PT, NTL = K::NTL;
+    constexpr int KS = M::KSTEP;
+    __shared__ __attribute__((aligned(16))) TI sDY[QB * LP];
+    __shared__ __attribute__((aligned(16))) TI sX[QB * LP];
+    __shared__ __attribute__((aligned(16))) TI sB[QB * LN];
+    __shared__ __attribute__((aligned(16))) TI sC[QB * LN];
+    __shared__ __attribute__((aligned(16))) TI sW[QB * LQ];
+    __shared__ __attribute__((aligned(16))) TI sS[P * LN];    // carried state H[p][n], operand copy
+    __shared__ __attribute__((aligned(16))) cum_t sCum[64];
+    __shared__ __attribute__((aligned(16))) float sF[64];      // input factor f_s
+    __shared__ __attribute__((aligned(16))) float sWx[64];     // f_s 2^(cend - cum_s)
+    __shared__ __attribute__((aligned(16))) float sDin[64];    // 2^cum_t
+    __shared__ float sQp[NTL][QB];
+    __shared__ float sRed[NW];
+    __shared__ float sCend;
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
+    const int64_t bh = blockIdx.x, b = bh / prm.H, h = bh % prm.H;
+    const int64_t H = prm.H, G = prm.G, T = prm.T, HB = prm.HB;
+    const int64_t g = h / (H / G), hb = HB == H ? h : g;
+    constexpr int SZ = K::SZ;
+    const int xs = (int)(H * P * SZ), ys = (int)(H * P * 4), bs = (int)(G * N * SZ);
+    const char* xrow = (const char*)prm.x + (b * T * H + h) * P * SZ;
+    const char* yrow = (const char*)prm.dy + (b * T * H + h) * P * 4;
+    const char* brow = (const char*)prm.B + (b * T * G + g) * N * SZ;
+    const char* crow = (const char*)prm.C + (b * T * G + g) * N * SZ;
+    const int64_t xrec = T * xs, yrec = T * ys, brec = T * bs;
+    const float Anat = -expf(prm.A_log[h]);
+    cum_t A2;
+    if constexpr (sizeof(cum_t) == 8) A2 = -exp((double)prm.A_log[h]) * 1.4426950408889634;
+    else A2 = Anat * 1.4426950408889634f;
+    const float dtb = prm.dt_bias ? prm.dt_bias[h] : 0.f;
+
+    BwdStage<TI, P, N, QB> stg;
+    float dtn = 0.f;                      // wave 0: the next block's dt (lane = token)
+    auto issue = [&](int blk) {
+        const int64_t t0 = (int64_t)blk * QB;
+        stg.issue(xrow, xrec, xs, yrow, yrec, ys, brow, crow, brec, bs, t0, tid);
+        if (w == 0) dtn = buf_load_f32(make_rsrc(prm.dt + (b * T + t0) * H + h, (T - t0) * H * 4), lane * (int)(H * 4));
+    };
+    // per-token scalars of a block (wave 0, lane = token)
+    auto scalars = [&](int blk) {
+        const int rows = (int)min((int64_t)QB, T - (int64_t)blk * QB);
+        const float d = lane < rows ? step_size(dtn + dtb, prm.dt_softplus) : 0.f;
+        const cum_t cum = wave_incl_scan((cum_t)d * A2);
+        const cum_t cend = __shfl(cum, QB - 1);
+        const float f = x_factor(d, Anat, prm.x_scale);
+        if (lane < QB) {
+            sCum[lane] = cum;
+            sF[lane] = f;
+            sWx[lane] = f * fast_exp2((float)(cend - cum));
+            sDin[lane] = fast_exp2((float)cum);
+        }
+        if (lane == 0) sCend = fast_exp2((float)cend);
+    };
+
+    // carried state H^T as accumulator tiles (rows n, columns p), and its operand copy
+    f32x4 st[K::T_NP];
+#pragma unroll
+    for (int j = 0; j < K::T_NP; ++j) {
+        const int tile = w + NW * j;
+        st[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (tile < NTL * PT) {
+            const int n0 = 16 * (tile / PT) + 4 * lg, p = 16 * (tile % PT) + lr;
+            if (prm.init) {
+                const float4 v = *(const float4*)(prm.init + (bh * P + p) * N + n0);
+                st[j] = f32x4{v.x, v.y, v.z, v.w};
+            }
+            lds_store4(sS + p * LN + n0, st[j][0], st[j][1], st[j][2], st[j][3]);
+        }
+    }
+
+    issue(0);
+    stg.store(sX, sDY, sB, sC, tid);
+    if (w == 0) scalars(0);
+    block_sync_lds();
+
+    for (int blk = 0; blk < prm.nblk; ++blk) {
+        const int64_t t0 = (int64_t)blk * QB;
+        if (blk + 1 < prm.nblk) issue(blk + 1);
+
+        // ---- phase A: W^T tiles (rows s, columns t), and dy H_in
+#pragma unroll
+        for (int j = 0; j < K::T_QQ; ++j) {
+            const int tile = w + NW * j;
+            if (tile < QT * QT) {
+                const int si = tile / QT, ti = tile % QT;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int k0 = 0; k0 < P; k0 += KS)
+                    acc = M::mma(frag_k(sX, LP, 16 * si + lr, k0, lg), frag_k(sDY, LP, 16 * ti + lr, k0, lg), acc);
+                const int t = 16 * ti + lr, s0 = 16 * si + 4 * lg;
+                const cum_t ct = sCum[t];
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int s = s0 + e;
+                    v[e] = s <= t ? fast_exp2((float)(ct - sCum[s])) * sF[s] * acc[e] : 0.f;
+                }
+                lds_store4(sW + t * LQ + s0, v[0], v[1], v[2], v[3]);
+            }
+        }
+        f32x4 a3[K::T_QN];
+#pragma unroll
+        for (int j = 0; j < K::T_QN; ++j) {
+            const int tile = w + NW * j;
+            a3[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (tile < QT * NTL) {
+                const int ti = tile / NTL, ni = tile % NTL;
+#pragma unroll
+                for (int k0 = 0; k0 < P; k0 += KS)
+                    a3[j] = M::mma(frag_k(sDY, LP, 16 * ti + lr, k0, lg), frag_t(sS, LN, 16 * ni, k0, lr, lg), a3[j]);
+            }
+        }
+        block_sync_lds();
+
+        // ---- phase B: dC^h = W B + 2^cum dy H_in, q partial sums; state update
+        {
+            const rsrc_t rdc = make_rsrc(prm.dCh + ((b * T + t0) * HB + hb) * N, (T - t0) * HB * N * 4);
+#pragma unroll
+            for (int j = 0; j < K::T_QN; ++j) {
+                const int tile = w + NW * j;
+                if (tile < QT * NTL) {
+                    const int ti = tile / NTL, ni = tile % NTL;
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int k0 = 0; k0 < QB; k0 += KS)
+                        acc = M::mma(frag_k(sW, LQ, 16 * ti + lr, k0, lg), frag_t(sB, LN, 16 * ni, k0, lr, lg), acc);
+                    const int n = 16 * ni + lr;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int t = 16 * ti + 4 * lg + e;
+                        const float v = acc[e] + sDin[t] * a3[j][e];
+                        buf_store_f32(v, rdc, (int)((t * HB * N + n) * 4));
+                        const float qs = group16_sum(v * to_f32(sC[t * LN + n]));
+                        if (lr == 0) sQp[ni][t] = qs;
+                    }
+                }
+            }
+            const float dec = sCend;
+#pragma unroll
+            for (int j = 0; j < K::T_NP; ++j) {
+                const int tile = w + NW * j;
+                if (tile < NTL * PT) {
+                    const int ni = tile / PT, pj = tile % PT;
+                    f32x4 acc = st[j] * dec;
+#pragma unroll
+                    for (int k0 = 0; k0 < QB; k0 += KS)
+                        acc = M::mma(frag_t(sB, LN, 16 * ni, k0, lr, lg), frag_t_w(sX, LP, 16 * pj, k0, lr, lg, sWx),
+                                     acc);
+                    st[j] = acc;
+                    lds_store4(sS + (16 * pj + lr) * LN + 16 * ni + 4 * lg, acc[0], acc[1], acc[2], acc[3]);
+                }
+            }
+        }
+        block_sync_lds();
+
+        // ---- phase C: q, then the next block into LDS
+        if (w == 0 && lane < QB) {
+            float qv = 0.f;
+#pragma unroll
+            for (int ni = 0; ni < NTL; ++ni) qv += sQp[ni][lane];
+            if (t0 + lane < T) prm.q[(b * T + t0 + lane) * H + h] = qv;
+        }
+        if (blk + 1 < prm.nblk) {
+            stg.store(sX, sDY, sB, sC, tid);
+            if (w == 0) scalars(blk + 1);
+        }
+        block_sync_lds();
+    }
+
+    // <dfinal, final>
+    float ph = 0.f;
+    if (prm.dfinal) {
+#pragma unroll
+        for (int j = 0; j < K::T_NP; ++j) {
+            const int tile = w + NW * j;
+            if (tile < NTL * PT) {
+                const int n0 = 16 * (tile / PT) + 4 * lg, p = 16 * (tile % PT) + lr;
+                const float4 v = *(const float4*)(prm.dfinal + (bh * P + p) * N + n0);
+                ph += v.x * st[j][0] + v.y * st[j][1] + v.z * st[j][2] + v.w * st[j][3];
+            }
+        }
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) ph += __shfl_xor(ph, d);
+    if (lane == 0) sRed[w] = ph;
+    block_sync_lds();
+    if (tid == 0) {
+        float s = 0.f;
+        for (int i = 0; i < NW; ++i) s += sRed[i];
+        prm.phi[bh] = s;
+    }
+}
+
+// ------------------------------------------------------------ reverse pass
+template <typename TI, int P, int N, int QB>
+__global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
+    using K = BwdCfg<TI, P, N, QB>;
+    using M = Mfma<TI>;
+    typedef typename CumType<TI>::type cum_t;
+    constexpr int NW = K::NW, LP = K::LP, LN = K::LN, LQ = K::LQ, QT = K::QT, PT = K::PT, NTL = K::NTL;
+    constexpr int KS = M::KSTEP;
+    __shared__ __attribute__((aligned(16))) TI sDY[QB * LP];
+    __shared__ __attribute__((aligned(16))) TI sX[QB * LP];
+    __shared__ __attribute__((aligned(16))) TI sB[QB * LN];
+    __shared__ __attribute__((aligned(16))) TI sC[QB * LN];
+    __shared__ __attribute__((aligned(16))) TI sE[QB * LQ];
+    __shared__ __attribute__((aligned(16))) TI sFm[QB * LQ];
+    __shared__ __attribute__((aligned(16))) TI sK[P * LN];    // K[p][n], operand copy
+    __shared__ __attribute__((aligned(16))) cum_t sCum[64];
+    __shared__ __attribute__((aligned(16))) float sF[64];      // f_t
+    __shared__ __attribute__((aligned(16))) float sDin[64];    // 2^cum_t
+    __shared__ __attribute__((aligned(16))) float sDout[64];   // 2^(cend - cum_t)
+    __shared__ __attribute__((aligned(16))) float sDel[64];    // step size Delta_t
+    __shared__ __attribute__((aligned(16))) float sPre[64];    // dt + bias (softplus argument)
+    __shared__ float sUp[PT][QB];
+    __shared__ float sDDp[PT][QB];
+    __shared__ float sCend;
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
+    const int64_t bh = blockIdx.x, b = bh / prm.H, h = bh % prm.H;
+    const int64_t H = prm.H, G = prm.G, T = prm.T, HB = prm.HB;
+    const int64_t g = h / (H / G), hb = HB == H ? h : g;
+    constexpr int SZ = K::SZ;
+    const int xs = (int)(H * P * SZ), ys = (int)(H * P * 4), bs = (int)(G * N * SZ);
+    const char* xrow = (const char*)prm.x + (b * T * H + h) * P * SZ;
+    const char* yrow = (const char*)prm.dy + (b * T * H + h) * P * 4;
+    const char* brow = (const char*)prm.B + (b * T * G + g) * N * SZ;
+    const char* crow = (const char*)prm.C + (b * T * G + g) * N * SZ;
+    const int64_t xrec = T * xs, yrec = T * ys, brec = T * bs;
+    const float Anat = -expf(prm.A_log[h]);
+    cum_t A2;
+    if constexpr (sizeof(cum_t) == 8) A2 = -exp((double)prm.A_log[h]) * 1.4426950408889634;
+    else A2 = Anat * 1.4426950408889634f;
+    const float dtb = prm.dt_bias ? prm.dt_bias[h] : 0.f;
+    const float Dh = prm.D ? prm.D[h] : 0.f;
+
+    BwdStage<TI, P, N, QB> stg;
+    float dtn = 0.f, qn = 0.f;            // wave 0: the next block's dt and q (lane = token)
+    auto issue = [&](int blk) {
+        const int64_t t0 = (int64_t)blk * QB;
+        stg.issue(xrow, xrec, xs, yrow, yrec, ys, brow, crow, brec, bs, t0, tid);
+        if (w == 0) {
+            dtn = buf_load_f32(make_rsrc(prm.dt + (b * T + t0) * H + h, (T - t0) * H * 4), lane * (int)(H * 4));
+            qn = buf_load_f32(make_rsrc(prm.q + (b * T + t0) * H + h, (T - t0) * H * 4), lane * (int)(H * 4));
+        }
+    };
+    float qcur = 0.f;
+    auto scalars = [&](int blk) {
+        const int rows = (int)min((int64_t)QB, T - (int64_t)blk * QB);
+        const float pre = dtn + dtb;
+        const float d = lane < rows ? step_size(pre, prm.dt_softplus) : 0.f;
+        const cum_t cum = wave_incl_scan((cum_t)d * A2);
+        const cum_t cend = __shfl(cum, QB - 1);
+        if (lane < QB) {
+            sCum[lane] = cum;
+            sF[lane] = x_factor(d, Anat, prm.x_scale);
+            sDin[lane] = fast_exp2((float)cum);
+            sDout[lane] = fast_exp2((float)(cend - cum));
+            sDel[lane] = d;
+            sPre[lane] = pre;
+        }
+        if (lane == 0) sCend = fast_exp2((float)cend);
+        qcur = qn;
+    };
+
+    // carried K^T = (a_{t+1} G_{t+1})^T as accumulator tiles (rows n, columns p)
+    f32x4 kst[K::T_NP];
+#pragma unroll
+    for (int j = 0; j < K::T_NP; ++j) {
+        const int tile = w + NW * j;
+        kst[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (tile < NTL * PT) {
+            const int n0 = 16 * (tile / PT) + 4 * lg, p = 16 * (tile % PT) + lr;
+            if (prm.dfinal) {
+                const float4 v = *(const float4*)(prm.dfinal + (bh * P + p) * N + n0);
+                kst[j] = f32x4{v.x, v.y, v.z, v.w};
+            }
+            lds_store4(sK + p * LN + n0, kst[j][0], kst[j][1], kst[j][2], kst[j][3]);
+        }
+    }
+
+    // wave 0: the running dl (starting from <dfinal, final>) and per-row sums
+    typedef cum_t acc_t;
+    acc_t dl_carry = (acc_t)prm.phi[bh];
+    acc_t sum_dA = 0, sum_bias = 0, sum_D = 0;
+    const int fdmode = prm.x_scale;
+
+    issue(prm.nblk - 1);
+    stg.store(sX, sDY, sB, sC, tid);
+    if (w == 0) scalars(prm.nblk - 1);
+    block_sync_lds();
+
+    for (int blk = prm.nblk - 1; blk >= 0; --blk) {
+        const int64_t t0 = (int64_t)blk * QB;
+        if (blk > 0) issue(blk - 1);
+
+        // ---- phase A: E and F (from E^T, F^T tiles: rows s, columns t), B K^T, X K
+#pragma unroll
+        for (int j = 0; j < K::T_QQ; ++j) {
+            const int tile = w + NW * j;
+            if (tile < QT * QT) {
+                const int si = tile / QT, ti = tile % QT;
+                f32x4 ae = {0.f, 0.f, 0.f, 0.f}, af = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int k0 = 0; k0 < N; k0 += KS)
+                    ae = M::mma(frag_k(sC, LN, 16 * si + lr, k0, lg), frag_k(sB, LN, 16 * ti + lr, k0, lg), ae);
+#pragma unroll
+                for (int k0 = 0; k0 < P; k0 += KS)
+                    af = M::mma(frag_k(sDY, LP, 16 * si + lr, k0, lg), frag_k(sX, LP, 16 * ti + lr, k0, lg), af);
+                const int t = 16 * ti + lr, s0 = 16 * si + 4 * lg;
+                const cum_t ct = sCum[t];
+                float ve[4], vf[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int s = s0 + e;
+                    const float m = s >= t ? fast_exp2((float)(sCum[s] - ct)) : 0.f;
+                    ve[e] = s >= t ? m * ae[e] : 0.f;
+                    vf[e] = s >= t ? m * af[e] : 0.f;
+                }
+                lds_store4(sE + t * LQ + s0, ve[0], ve[1], ve[2], ve[3]);
+                lds_store4(sFm + t * LQ + s0, vf[0], vf[1], vf[2], vf[3]);
+            }
+        }
+        f32x4 a3[K::T_QP];
+#pragma unroll
+        for (int j = 0; j < K::T_QP; ++j) {
+            const int tile = w + NW * j;
+            a3[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (tile < QT * PT) {
+                const int ti = tile / PT, pj = tile % PT;
+#pragma unroll
+                for (int k0 = 0; k0 < N; k0 += KS)
+                    a3[j] = M::mma(frag_k(sB, LN, 16 * ti + lr, k0, lg), frag_k(sK, LN, 16 * pj + lr, k0, lg), a3[j]);
+            }
+        }
+        f32x4 a5[K::T_QN];
+#pragma unroll
+        for (int j = 0; j < K::T_QN; ++j) {
+            const int tile = w + NW * j;
+            a5[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (tile < QT * NTL) {
+                const int ti = tile / NTL, ni = tile % NTL;
+#pragma unroll
+                for (int k0 = 0; k0 < P; k0 += KS)
+                    a5[j] = M::mma(frag_k(sX, LP, 16 * ti + lr, k0, lg), frag_t(sK, LN, 16 * ni, k0, lr, lg), a5[j]);
+            }
+        }
+        block_sync_lds();
+
+        // ---- phase B: G B (-> dx, u, dy.x), dB^h, K update
+        {
+            const rsrc_t rdy = make_rsrc(prm.dy + ((b * T + t0) * H + h) * P, (T - t0) * H * P * 4);
+            const rsrc_t rdx = make_rsrc(prm.dx + ((b * T + t0) * H + h) * P, (T - t0) * H * P * 4);
+#pragma unroll
+            for (int j = 0; j < K::T_QP; ++j) {
+                const int tile = w + NW * j;
+                if (tile < QT * PT) {
+                    const int ti = tile / PT, pj = tile % PT;
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int k0 = 0; k0 < QB; k0 += KS)
+                        acc = M::mma(frag_k(sE, LQ, 16 * ti + lr, k0, lg), frag_t(sDY, LP, 16 * pj, k0, lr, lg), acc);
+                    const int p = 16 * pj + lr;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int t = 16 * ti + 4 * lg + e;
+                        const float gb = acc[e] + sDout[t] * a3[j][e];
+                        const int off = (int)((t * H * P + p) * 4);
+                        const float dyv = buf_load_f32(rdy, off);
+                        const float xv = to_f32(sX[t * LP + p]);
+                        buf_store_f32(sF[t] * gb + Dh * dyv, rdx, off);
+                        const float us = group16_sum(xv * gb);
+                        const float ds = group16_sum(xv * dyv);
+                        if (lr == 0) {
+                            sUp[pj][t] = us;
+                            sDDp[pj][t] = ds;
+                        }
+                    }
+                }
+            }
+            const rsrc_t rdb = make_rsrc(prm.dBh + ((b * T + t0) * HB + hb) * N, (T - t0) * HB * N * 4);
+#pragma unroll
+            for (int j = 0; j < K::T_QN; ++j) {
+                const int tile = w + NW * j;
+                if (tile < QT * NTL) {
+                    const int ti = tile / NTL, ni = tile % NTL;
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int k0 = 0; k0 < QB; k0 += KS)
+                        acc = M::mma(frag_k(sFm, LQ, 16 * ti + lr, k0, lg), frag_t(sC, LN, 16 * ni, k0, lr, lg), acc);
+                    const int n = 16 * ni + lr;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int t = 16 * ti + 4 * lg + e;
+                        buf_store_f32(sF[t] * (acc[e] + sDout[t] * a5[j][e]), rdb, (int)((t * HB * N + n) * 4));
+                    }
+                }
+            }
+            const float dec = sCend;
+#pragma unroll
+            for (int j = 0; j < K::T_NP; ++j) {
+                const int tile = w + NW * j;
+                if (tile < NTL * PT) {
+                    const int ni = tile / PT, pj = tile % PT;
+                    f32x4 acc = kst[j] * dec;
+#pragma unroll
+                    for (int k0 = 0; k0 < QB; k0 += KS)
+                        acc = M::mma(frag_t(sC, LN, 16 * ni, k0, lr, lg), frag_t_w(sDY, LP, 16 * pj, k0, lr, lg, sDin),
+                                     acc);
+                    kst[j] = acc;
+                    lds_store4(sK + (16 * pj + lr) * LN + 16 * ni + 4 * lg, acc[0], acc[1], acc[2], acc[3]);
+                }
+            }
+        }
+        block_sync_lds();
+
+        // ---- phase C (wave 0): dl by a suffix scan, ddt, per-row sums; then the next block
+        if (w == 0) {
+            const int rows = (int)min((int64_t)QB, T - t0);
+            float u = 0.f, dd = 0.f;
+            if (lane < QB) {
+#pragma unroll
+                for (int pj = 0; pj < PT; ++pj) {
+                    u += sUp[pj][lane];
+                    dd += sDDp[pj][lane];
+                }
+            }
+            const bool valid = lane < rows;
+            const float f = lane < QB ? sF[lane] : 0.f;
+            const acc_t sv = valid ? (acc_t)qcur - (acc_t)f * (acc_t)u : (acc_t)0;
+            const acc_t incl = wave_incl_scan(sv);
+            const acc_t total = __shfl(incl, 63);
+            const acc_t dl = dl_carry + (total - incl + sv);     // sum over k >= t of the block, plus what follows
+            dl_carry += total;
+            if (valid) {
+                const float d = sDel[lane];
+                const float a = expf(d * Anat);                   // a_t
+                const float fD = fdmode == 1 ? 1.f : (fdmode == 2 ? a : 0.f);
+                const float fA = fdmode == 2 ? (d * Anat * a - a + 1.f) / (Anat * Anat) : 0.f;
+                float gdt = (float)dl * Anat + u * fD;
+                if (prm.dt_softplus) gdt *= 1.f / (1.f + expf(-sPre[lane]));
+                prm.ddt[(b * T + t0 + lane) * H + h] = gdt;
+                sum_dA += dl * (acc_t)d + (acc_t)(u * fA);
+                sum_bias += (acc_t)gdt;
+                sum_D += (acc_t)dd;
+            }
+        }
+        if (blk > 0) {
+            stg.store(sX, sDY, sB, sC, tid);
+            if (w == 0) scalars(blk - 1);
+        }
+        block_sync_lds();
+    }
+
+    // dinit = a_0 G_0 = the K that leaves the first block
+    if (prm.dinit) {
+#pragma unroll
+        for (int j = 0; j < K::T_NP; ++j) {
+            const int tile = w + NW * j;
+            if (tile < NTL * PT) {
+                const int n0 = 16 * (tile / PT) + 4 * lg, p = 16 * (tile % PT) + lr;
+                *(float4*)(prm.dinit + (bh * P + p) * N + n0) = make_float4(kst[j][0], kst[j][1], kst[j][2], kst[j][3]);
+            }
+        }
+    }
+    if (w == 0) {
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) {
+            sum_dA += __shfl_xor(sum_dA, d);
+            sum_bias += __shfl_xor(sum_bias, d);
+            sum_D += __shfl_xor(sum_D, d);
+        }
+        if (lane == 0) {
+            prm.part[bh * 3 + 0] = (float)sum_dA;
+            prm.part[bh * 3 + 1] = (float)sum_bias;
+            prm.part[bh * 3 + 2] = (float)sum_D;
+        }
+    }
+}
+
+}  // namespace ssd

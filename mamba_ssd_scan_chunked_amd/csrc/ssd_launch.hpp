@@ -8,6 +8,7 @@ namespace ssd {
 struct ScanParams;
 struct CombineParams;
 struct StepParams;
+struct BwdParams;
 
 // Return hipSuccess, hipErrorInvalidValue for a shape with no instantiation,
 // or the launch error.
@@ -37,4 +38,12 @@ SSD_DECLARE_SCAN2(f32, 1, 1)
 
 bool supported_bf16(int P, int N, int QB);
 bool supported_f32(int P, int N, int QB);
+
+// Backward: the forward pass then the reverse pass, one workgroup per (row, head).
+hipError_t launch_bwd_bf16(int P, int N, const BwdParams& prm, int64_t grid, hipStream_t s);
+hipError_t launch_bwd_f32(int P, int N, const BwdParams& prm, int64_t grid, hipStream_t s);
+bool supported_bwd_bf16(int P, int N);
+bool supported_bwd_f32(int P, int N);
+int bwd_block_bf16();   // tokens per block of the backward kernels
+int bwd_block_f32();
 }  // namespace ssd

@@ -185,3 +185,54 @@ def test_step_without_device_reports_no_device():
     if torch.cuda.is_available():
         pytest.skip("a GPU is present: this call would launch on fake pointers")
     assert _step(prob(batch=2, seqlen=1, nheads=4, headdim=64, dstate=128)) == 8
+
+
+def _backward(p, **ptrs):
+    lib = ssd.load_library()
+    names = ["x", "dt", "dt_bias", "A_log", "B", "C", "D", "init", "seq", "dy", "dfinal",
+             "dx", "ddt", "dA_log", "dB", "dC", "dD", "dinit", "ddt_bias"]
+    vals = {n: A + 0x2000000 * (i + 1) for i, n in enumerate(names)}
+    vals.update({"dt_bias": None, "D": None, "init": None, "seq": None, "dfinal": None, "dD": None, "dinit": None,
+                 "ddt_bias": None})
+    ws = ptrs.pop("ws", A + 0x60000000)
+    wsb = ptrs.pop("wsb", ssd.backward_workspace_size(p))
+    vals.update(ptrs)
+    return lib.ssd_backward(ctypes.byref(p), *[vals[n] for n in names], ws, wsb, None)
+
+
+def small_bwd(**kw):
+    base = dict(batch=1, seqlen=64, nheads=2, headdim=32, dstate=64, chunk_len=64)
+    base.update(kw)
+    return prob(**base)
+
+
+def test_backward_workspace_sizes():
+    p = prob(ngroups=1)                           # 80 heads share one group: per-head dB, dC kept
+    bth, bh = 4 * 4096 * 80, 4 * 80
+    r = lambda v: (v + 255) // 256 * 256
+    assert ssd.backward_workspace_size(p) == r(bth * 4) + r(bh * 4) + r(bh * 12) + 2 * r(bth * 128 * 4)
+    p = prob(nheads=8, ngroups=8)                 # one head per group: written directly
+    assert ssd.backward_workspace_size(p) == r(4 * 4096 * 8 * 4) + r(32 * 4) + r(32 * 12)
+    assert ssd.backward_workspace_size(prob(headdim=48)) == 0
+
+
+def test_backward_rejects_bad_arguments():
+    assert _backward(small_bwd(), seq=A + 0x7000000) == 3               # packed sequences: forward only
+    assert _backward(small_bwd(dtype=ssd.DTYPE_F32, dstate=256)) == 3    # no fp32 N = 256 build
+    for n in ("x", "dt", "A_log", "B", "C", "dy", "dx", "ddt", "dA_log", "dB", "dC"):
+        assert _backward(small_bwd(), **{n: None}) == 1, n
+    assert _backward(small_bwd(), ws=None) == 5
+    assert _backward(small_bwd(), wsb=16) == 5
+    assert _backward(small_bwd(), dy=A + 0x14000000 + 4) == 4            # misaligned dy
+    assert _backward(small_bwd(), dB=A + 0x1E000000 + 8) == 4            # misaligned dB
+    assert _backward(small_bwd(), dx=A + 0x2000000) == 6                 # dx on top of x
+    assert _backward(small_bwd(), dB=A + 0x1A000000) == 6                # dB on top of ddt
+    assert _backward(small_bwd(), dinit=A + 0x14000000) == 6             # dinit on top of dy
+    assert _backward(small_bwd(), dA_log=A + 0x60000000) == 6            # dA_log in the workspace
+
+
+def test_backward_without_device_reports_no_device():
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present: this call would launch on fake pointers")
+    assert _backward(small_bwd()) == 8

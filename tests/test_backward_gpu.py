@@ -1,0 +1,150 @@
+"""Parity of the backward pass (ssd_backward, through the C ABI) with the CPU
+oracle's adjoint recurrence (oracle.gradients, fp64, pinned by finite
+differences in test_oracle_grad_pins.py).
+
+Every output is compared element by element: max |got - ref| <= tol * max |ref|
+per tensor, with tol = 2e-2 for bf16 inputs (bf16 MFMA operands, fp32
+accumulation) and 1e-5 for fp32 inputs.  The loss is L = <dy, y> + <dfinal, final>
+with seeded random dy and dfinal.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ssd_inputs as si
+from ssd_testlib import TOL, assert_parity, dtype_name, to_device
+
+pytestmark = pytest.mark.gpu
+
+OUTS = ("dx", "ddt", "dA_log", "dB", "dC", "dD", "dinit", "ddt_bias")
+
+
+def announce(msg):
+    print("[case] " + msg, flush=True)
+    sys.stdout.flush()
+
+
+def cotangents(prob, seed):
+    b, T, H, P = prob["x"].shape
+    N = prob["B"].shape[3]
+    rng = np.random.default_rng(seed)
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return f32(rng.standard_normal((b, T, H, P))), f32(rng.standard_normal((b, H, P, N)))
+
+
+def run_both(prob, dy, dfinal, *, dt_bias=None, dt_softplus=False, zoh=False, dt_scales_x=False, workers=0):
+    import mamba_ssd_scan_chunked_amd as ssd
+    d = to_device(prob)
+    g = ssd.backward(d["x"], d["dt"], d["A_log"], d["B"], d["C"], dy.cuda(), D=d["D"], init_state=d["init"],
+                     dfinal=dfinal.cuda() if dfinal is not None else None, dt_scales_x=dt_scales_x,
+                     dt_bias=dt_bias.cuda() if dt_bias is not None else None, dt_softplus=dt_softplus, zoh=zoh)
+    torch.cuda.synchronize()
+    got = {k: v.cpu().double().numpy() for k, v in g.items()}
+    ref = oracle.gradients(prob["x"], prob["dt"], prob["A_log"], prob["B"], prob["C"], dy, prob["D"], prob["init"],
+                           dfinal, dt_scales_x=dt_scales_x, dt_bias=dt_bias, dt_softplus=dt_softplus, zoh=zoh,
+                           nthreads=workers)
+    return got, ref
+
+
+def check(got, ref, tol, outs=OUTS):
+    errs = {}
+    for k in outs:
+        errs[k] = assert_parity(got[k], ref[k], tol, k)
+    print("[errors] " + " ".join("%s=%.2e" % kv for kv in errs.items()), flush=True)
+
+
+SHAPES = [
+    # dtype, b, T, H, P, N, G   (ragged last blocks; G < H exercises the sum over a group's heads)
+    ("bf16", 2, 200, 4, 64, 128, 2),
+    ("bf16", 1, 130, 2, 32, 64, 2),
+    ("bf16", 1, 100, 2, 64, 256, 1),
+    ("bf16", 2, 64, 3, 32, 128, 1),
+    ("f32", 2, 150, 2, 64, 128, 1),
+    ("f32", 1, 77, 4, 16, 16, 2),
+    ("f32", 1, 65, 2, 32, 64, 2),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "%s-b%d-T%d-H%d-P%d-N%d-G%d" % s)
+def test_backward_matches_oracle(shape):
+    dt, b, T, H, P, N, G = shape
+    prob = si.make_problem(b, T, H, P, N, G, dtype=dt, seed=T + N + 5, d_skip=True, init_std=0.5)
+    dy, dfinal = cotangents(prob, T + 1)
+    announce("backward %s" % (shape,))
+    got, ref = run_both(prob, dy, dfinal)
+    check(got, ref, TOL[dt])
+
+
+MODES = {
+    "euler": dict(dt_scales_x=True),
+    "zoh": dict(zoh=True),
+    "softplus_bias": dict(dt_softplus=True, bias=True),
+    "softplus_zoh": dict(dt_softplus=True, zoh=True, bias=True),
+}
+
+
+@pytest.mark.parametrize("mode", sorted(MODES))
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_backward_step_size_map_and_scaling(dt, mode):
+    kw = dict(MODES[mode])
+    bias = kw.pop("bias", False)
+    b, T, H, P, N, G = 2, 140, 4, 64, 128 if dt == "bf16" else 64, 2
+    prob = si.make_problem(b, T, H, P, N, G, dtype=dt, seed=11, d_skip=True, init_std=0.5)
+    if kw.get("dt_softplus"):
+        raw = si.raw_step_sizes(b, T, H, seed=12)
+        prob = dict(prob, dt=raw["dt"])
+        dtb = raw["dt_bias"]
+    else:
+        dtb = si.raw_step_sizes(b, T, H, seed=12, bias_range=(0.0, 0.2))["dt_bias"] if bias else None
+    dy, dfinal = cotangents(prob, 13)
+    announce("backward mode=%s dtype=%s" % (mode, dt))
+    got, ref = run_both(prob, dy, dfinal, dt_bias=dtb, **kw)
+    check(got, ref, TOL[dt])
+
+
+def test_backward_without_init_dfinal_and_skip():
+    prob = si.make_problem(1, 96, 2, 64, 128, 1, dtype="bf16", seed=17)
+    dy, _ = cotangents(prob, 18)
+    announce("backward without init/dfinal/D")
+    got, ref = run_both(prob, dy, None)
+    check(got, ref, TOL["bf16"], outs=("dx", "ddt", "dA_log", "dB", "dC", "dinit", "dD"))
+
+
+def test_backward_no_tokens():
+    import mamba_ssd_scan_chunked_amd as ssd
+    prob = si.make_problem(2, 0, 2, 64, 128, 1, dtype="bf16", seed=19, d_skip=True, init_std=0.5)
+    _, dfinal = cotangents(prob, 20)
+    d = to_device(prob)
+    announce("backward T=0")
+    g = ssd.backward(d["x"], d["dt"], d["A_log"], d["B"], d["C"], torch.zeros(2, 0, 2, 64, device="cuda"), D=d["D"],
+                     init_state=d["init"], dfinal=dfinal.cuda())
+    torch.cuda.synchronize()
+    assert torch.equal(g["dinit"].cpu(), dfinal)
+    assert not g["dA_log"].any() and not g["dD"].any() and not g["ddt_bias"].any()
+
+
+def test_backward_is_deterministic():
+    import mamba_ssd_scan_chunked_amd as ssd
+    prob = si.make_problem(2, 300, 4, 64, 128, 2, dtype="bf16", seed=23, d_skip=True, init_std=0.5)
+    dy, dfinal = cotangents(prob, 24)
+    d = to_device(prob)
+    announce("backward determinism")
+    runs = [ssd.backward(d["x"], d["dt"], d["A_log"], d["B"], d["C"], dy.cuda(), D=d["D"], init_state=d["init"],
+                         dfinal=dfinal.cuda()) for _ in range(2)]
+    torch.cuda.synchronize()
+    for k in OUTS:
+        assert torch.equal(runs[0][k], runs[1][k]), k
+
+
+def test_backward_headline_shape():
+    """The 2.7B-layer shape (b=4, T=4096, H=80, P=64, N=128, bf16), every output
+    against the oracle over the whole problem."""
+    w = si.WORKLOADS["m2p7_bf16"]
+    prob = si.make_workload(w)
+    dy, dfinal = cotangents(prob, 29)
+    announce("backward 2.7B-layer shape")
+    got, ref = run_both(prob, dy, dfinal)
+    check(got, ref, TOL["bf16"])
