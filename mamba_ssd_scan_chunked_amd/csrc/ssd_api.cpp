@@ -179,26 +179,32 @@ int slices_per_workgroup(const ssd_problem_t* p, bool seq, int nseg) {
     return npt;
 }
 
-// Workspace of the backward pass: per-token q (b, T, H), <dfinal, final> per
-// (row, head), the per-row scalar sums (b, H, 3), and, when a group has more
-// than one head, each head's dB and dC contribution (b, T, H, N) before the
-// sum over the group.
+// Workspace of the backward pass: a per-token scalar (b, T, H), each block's
+// incoming state (b, H, blocks, P, N) in the input type, the per-row scalar
+// sums (b, H, 3), and, when a group has more than one head, each head's dB and
+// dC contribution (b, T, H, N) before the sum over the group.
+int bwd_block(const ssd_problem_t* p);
 struct BwdWs {
-    int64_t q_off, phi_off, part_off, dbh_off, dch_off, total;
+    int64_t q_off, hin_off, part_off, dbh_off, dch_off, total;
 };
 BwdWs bwd_ws_layout(const ssd_problem_t* p) {
     BwdWs l;
     const int64_t bth = p->batch * p->seqlen * p->nheads, bh = p->batch * p->nheads;
     const bool per_head = p->ngroups != p->nheads;
+    const int qb = bwd_block(p);
+    const int64_t nblk = (p->seqlen + qb - 1) / qb;
     l.q_off = 0;
-    l.phi_off = align256(bth * 4);
-    l.part_off = l.phi_off + align256(bh * 4);
+    l.hin_off = align256(bth * 4);
+    l.part_off = l.hin_off + align256(bh * nblk * p->headdim * p->dstate * elem_size(p->dtype));
     l.dbh_off = l.part_off + align256(bh * 12);
     const int64_t hn = per_head ? align256(bth * p->dstate * 4) : 0;
     l.dch_off = l.dbh_off + hn;
     l.total = l.dch_off + hn;
     return l;
 }
+
+// Tokens per block of the backward kernels.
+int bwd_block(const ssd_problem_t* p) { return p->dtype == SSD_DTYPE_BF16 ? ssd::bwd_block_bf16() : ssd::bwd_block_f32(); }
 
 // Factor on x in the state write: 0 none, 1 the step size (Euler), 2 the exact
 // zero-order hold (exp(Delta A) - 1) / A.
@@ -475,7 +481,7 @@ int ssd_backward(const ssd_problem_t* p, const void* x, const float* dt, const f
         misaligned(dD, 4) || misaligned(workspace, 256))
         return SSD_ERR_ALIGNMENT;
     // one block of tokens is addressed with 32-bit byte offsets
-    const int qb = bf ? ssd::bwd_block_bf16() : ssd::bwd_block_f32();
+    const int qb = bwd_block(p);
     if (double(qb) * double(p->nheads) * double(std::max(p->headdim, p->dstate)) * 4.0 >= 2147483647.0)
         return SSD_ERR_BAD_SHAPE;
     const Sizes s = sizes(p);
@@ -527,7 +533,7 @@ int ssd_backward(const ssd_problem_t* p, const void* x, const float* dt, const f
     prm.dCh = per_head ? reinterpret_cast<float*>(ws + wl.dch_off) : dC;
     prm.dinit = dinit;
     prm.q = reinterpret_cast<float*>(ws + wl.q_off);
-    prm.phi = reinterpret_cast<float*>(ws + wl.phi_off);
+    prm.hin = ws + wl.hin_off;
     prm.part = reinterpret_cast<float*>(ws + wl.part_off);
     prm.batch = p->batch;
     prm.T = p->seqlen;

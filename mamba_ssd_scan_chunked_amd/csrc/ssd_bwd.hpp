@@ -10,16 +10,23 @@
 //   G_t  = dy_t C_t^T + a_{t+1} G_{t+1}       (after the last token: dfinal)
 //   dC_t = sum_heads H_t^T dy_t,   dB_t = sum_heads f_t G_t^T x_t
 //   dx_t = f_t G_t B_t + D dy_t
-//   dl_t = q_t - f_t u_t + dl_{t+1},  dl_T = <dfinal, H_{T-1}>   (dl = dL/dlog a)
-//   q_t  = dy_t . (H_t C_t) = C_t . (H_t^T dy_t),   u_t = x_t . (G_t B_t)
-// (dl_t = <G_t, a_t H_{t-1}>; expanding G_t and H_t gives the recursion.)
+//   dl_t = dL/dlog a_t = <G_t, a_t H_{t-1}>,   u_t = x_t . (G_t B_t) = dL/df_t
+// Inside a block of tokens with incoming state H_in and incoming gradient
+// K (= a G of the first token after the block), dl_t splits exactly into
+//   sum over s >= t > r of Z[s][r]  +  sum over s >= t of qoff_s
+//   + sum over r < t of roff_r  +  2^cend <K, H_in>,
+// Z[s][r] = 2^(cum_s - cum_r) f_r (dy_s . x_r)(C_s . B_r),
+// qoff_s = 2^cum_s dy_s . (H_in C_s),  roff_r = 2^(cend - cum_r) f_r x_r . (K B_r),
+// so that no rounding error is carried from block to block (a running sum of
+// per-token terms over the whole row would accumulate it).
 //
 // ssd_bwd_fwd_kernel walks each (row, head) forwards with H on chip and
-// produces the head's dC contribution and q; ssd_bwd_rev_kernel walks it
-// backwards with G on chip (as K = a_{t+1} G_{t+1}, the gradient that
-// reaches the block from its right) and produces dx, the head's dB
-// contribution, u, dl by a suffix scan, ddt, the per-row partial sums of
-// dA_log, ddt_bias and dD, and dinit = a_0 G_0.  The contributions of the
+// produces the head's dC contribution, qoff and each block's incoming state
+// (kept for the inner product above); ssd_bwd_rev_kernel walks it backwards
+// with G on chip (as K, the gradient that reaches the block from its right)
+// and produces dx, the head's dB contribution, Z (from the C B^T and dy x^T
+// tiles it forms anyway), roff, dl, ddt, the per-row partial sums of dA_log,
+// ddt_bias and dD, and dinit = a_0 G_0.  The contributions of the
 // heads of a group are summed by ssd_bwd_group_sum_kernel (not needed when each
 // group has one head: then the passes write dB and dC directly), the per-row
 // scalars by ssd_bwd_scalars_kernel.
@@ -60,8 +67,8 @@ struct BwdParams {
     float* dBh;       // (batch, T, HB, N): per-head dB (HB = H), or dB itself (HB = G = H)
     float* dCh;       // same for dC
     float* dinit;     // (batch, H, P, N) or null
-    float* q;         // (batch, T, H) workspace
-    float* phi;       // (batch, H) workspace: <dfinal, final>
+    float* q;         // (batch, T, H) workspace: qoff
+    void* hin;        // (batch, H, nblk, P, N) workspace: each block's incoming state (input type)
     float* part;      // (batch, H, 3) workspace: per-row sums for dA (natural A), ddt_bias, dD
     int64_t batch, T, H, G, HB;
     int nblk;
@@ -215,7 +222,6 @@ __global__ __launch_bounds__(512) void ssd_bwd_fwd_kernel(BwdParams prm) {
     __shared__ __attribute__((aligned(16))) float sWx[64];     // f_s 2^(cend - cum_s)
     __shared__ __attribute__((aligned(16))) float sDin[64];    // 2^cum_t
     __shared__ float sQp[NTL][QB];
-    __shared__ float sRed[NW];
     __shared__ float sCend;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
@@ -283,7 +289,12 @@ __global__ __launch_bounds__(512) void ssd_bwd_fwd_kernel(BwdParams prm) {
         const int64_t t0 = (int64_t)blk * QB;
         if (blk + 1 < prm.nblk) issue(blk + 1);
 
-        // ---- phase A: W^T tiles (rows s, columns t), and dy H_in
+        // ---- phase A: the incoming state to the workspace; W^T tiles (rows s, columns t), and dy H_in
+        {
+            constexpr int HU = P * N * SZ / 16, HC = N * SZ / 16, VE = 16 / SZ;
+            uint4* dst = (uint4*)((TI*)prm.hin + (bh * prm.nblk + blk) * (int64_t)(P * N));
+            for (int v = tid; v < HU; v += K::NT) dst[v] = *(const uint4*)(sS + (v / HC) * LN + (v % HC) * VE);
+        }
 #pragma unroll
         for (int j = 0; j < K::T_QQ; ++j) {
             const int tile = w + NW * j;
@@ -334,9 +345,9 @@ __global__ __launch_bounds__(512) void ssd_bwd_fwd_kernel(BwdParams prm) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int t = 16 * ti + 4 * lg + e;
-                        const float v = acc[e] + sDin[t] * a3[j][e];
-                        buf_store_f32(v, rdc, (int)((t * HB * N + n) * 4));
-                        const float qs = group16_sum(v * to_f32(sC[t * LN + n]));
+                        const float off = sDin[t] * a3[j][e];
+                        buf_store_f32(acc[e] + off, rdc, (int)((t * HB * N + n) * 4));
+                        const float qs = group16_sum(off * to_f32(sC[t * LN + n]));
                         if (lr == 0) sQp[ni][t] = qs;
                     }
                 }
@@ -373,28 +384,6 @@ __global__ __launch_bounds__(512) void ssd_bwd_fwd_kernel(BwdParams prm) {
         block_sync_lds();
     }
 
-    // <dfinal, final>
-    float ph = 0.f;
-    if (prm.dfinal) {
-#pragma unroll
-        for (int j = 0; j < K::T_NP; ++j) {
-            const int tile = w + NW * j;
-            if (tile < NTL * PT) {
-                const int n0 = 16 * (tile / PT) + 4 * lg, p = 16 * (tile % PT) + lr;
-                const float4 v = *(const float4*)(prm.dfinal + (bh * P + p) * N + n0);
-                ph += v.x * st[j][0] + v.y * st[j][1] + v.z * st[j][2] + v.w * st[j][3];
-            }
-        }
-    }
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) ph += __shfl_xor(ph, d);
-    if (lane == 0) sRed[w] = ph;
-    block_sync_lds();
-    if (tid == 0) {
-        float s = 0.f;
-        for (int i = 0; i < NW; ++i) s += sRed[i];
-        prm.phi[bh] = s;
-    }
 }
 
 // ------------------------------------------------------------ reverse pass
@@ -418,8 +407,12 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
     __shared__ __attribute__((aligned(16))) float sDout[64];   // 2^(cend - cum_t)
     __shared__ __attribute__((aligned(16))) float sDel[64];    // step size Delta_t
     __shared__ __attribute__((aligned(16))) float sPre[64];    // dt + bias (softplus argument)
-    __shared__ float sUp[PT][QB];
-    __shared__ float sDDp[PT][QB];
+    __shared__ float sUp[PT][QB];      // x . (G B) over each 16-channel tile
+    __shared__ float sUop[PT][QB];     // x . (2^(cend - cum) K B) over each tile
+    __shared__ float sDDp[PT][QB];     // x . dy over each tile
+    __shared__ float sCz[QT][QB];      // column sums of Z below the diagonal, per row tile
+    __shared__ float sRz[QT][QB];      // row sums of Z left of the diagonal, per column tile
+    __shared__ float sKap[NW];         // <K, H_in> over each wave's state tiles
     __shared__ float sCend;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
@@ -441,7 +434,20 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
     const float Dh = prm.D ? prm.D[h] : 0.f;
 
     BwdStage<TI, P, N, QB> stg;
-    float dtn = 0.f, qn = 0.f;            // wave 0: the next block's dt and q (lane = token)
+    float dtn = 0.f, qn = 0.f;            // wave 0: the next block's dt and qoff (lane = token)
+    // the block's incoming state at this lane's state-tile positions (4 values per tile)
+    typedef typename std::conditional<K::SZ == 2, uint2, uint4>::type h4_t;
+    auto load_hin = [&](int blk, h4_t (&hv)[K::T_NP]) {
+        const TI* hb0 = (const TI*)prm.hin + (bh * prm.nblk + blk) * (int64_t)(P * N);
+#pragma unroll
+        for (int j = 0; j < K::T_NP; ++j) {
+            const int tile = w + NW * j;
+            if (tile < NTL * PT) {
+                const int n0 = 16 * (tile / PT) + 4 * lg, p = 16 * (tile % PT) + lr;
+                hv[j] = *(const h4_t*)(hb0 + p * N + n0);
+            }
+        }
+    };
     auto issue = [&](int blk) {
         const int64_t t0 = (int64_t)blk * QB;
         stg.issue(xrow, xrec, xs, yrow, yrec, ys, brow, crow, brec, bs, t0, tid);
@@ -485,9 +491,8 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
         }
     }
 
-    // wave 0: the running dl (starting from <dfinal, final>) and per-row sums
+    // wave 0: per-row sums
     typedef cum_t acc_t;
-    acc_t dl_carry = (acc_t)prm.phi[bh];
     acc_t sum_dA = 0, sum_bias = 0, sum_D = 0;
     const int fdmode = prm.x_scale;
 
@@ -498,6 +503,8 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
 
     for (int blk = prm.nblk - 1; blk >= 0; --blk) {
         const int64_t t0 = (int64_t)blk * QB;
+        h4_t hcur[K::T_NP];
+        load_hin(blk, hcur);              // used after this block's first products
         if (blk > 0) issue(blk - 1);
 
         // ---- phase A: E and F (from E^T, F^T tiles: rows s, columns t), B K^T, X K
@@ -515,14 +522,23 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
                     af = M::mma(frag_k(sDY, LP, 16 * si + lr, k0, lg), frag_k(sX, LP, 16 * ti + lr, k0, lg), af);
                 const int t = 16 * ti + lr, s0 = 16 * si + 4 * lg;
                 const cum_t ct = sCum[t];
-                float ve[4], vf[4];
+                const float ft = sF[t];
+                float ve[4], vf[4], zc = 0.f;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int s = s0 + e;
                     const float m = s >= t ? fast_exp2((float)(sCum[s] - ct)) : 0.f;
                     ve[e] = s >= t ? m * ae[e] : 0.f;
                     vf[e] = s >= t ? m * af[e] : 0.f;
+                    // Z[s][t] below the diagonal: its column sum (over s) and row sum (over t)
+                    const float z = s > t ? m * ft * ae[e] * af[e] : 0.f;
+                    zc += z;
+                    const float zr = group16_sum(z);
+                    if (lr == 0) sRz[ti][s] = zr;
                 }
+                zc += __shfl_xor(zc, 16);
+                zc += __shfl_xor(zc, 32);
+                if (lg == 0) sCz[si][t] = zc;
                 lds_store4(sE + t * LQ + s0, ve[0], ve[1], ve[2], ve[3]);
                 lds_store4(sFm + t * LQ + s0, vf[0], vf[1], vf[2], vf[3]);
             }
@@ -538,6 +554,21 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
                 for (int k0 = 0; k0 < N; k0 += KS)
                     a3[j] = M::mma(frag_k(sB, LN, 16 * ti + lr, k0, lg), frag_k(sK, LN, 16 * pj + lr, k0, lg), a3[j]);
             }
+        }
+        {   // <K, H_in> over this wave's state tiles (K as it enters the block)
+            float kp = 0.f;
+#pragma unroll
+            for (int j = 0; j < K::T_NP; ++j) {
+                const int tile = w + NW * j;
+                if (tile < NTL * PT) {
+                    const TI* hv = (const TI*)&hcur[j];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) kp += kst[j][e] * to_f32(hv[e]);
+                }
+            }
+#pragma unroll
+            for (int d = 32; d >= 1; d >>= 1) kp += __shfl_xor(kp, d);
+            if (lane == 0) sKap[w] = kp;
         }
         f32x4 a5[K::T_QN];
 #pragma unroll
@@ -570,15 +601,18 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int t = 16 * ti + 4 * lg + e;
-                        const float gb = acc[e] + sDout[t] * a3[j][e];
+                        const float gof = sDout[t] * a3[j][e];
+                        const float gb = acc[e] + gof;
                         const int off = (int)((t * H * P + p) * 4);
                         const float dyv = buf_load_f32(rdy, off);
                         const float xv = to_f32(sX[t * LP + p]);
                         buf_store_f32(sF[t] * gb + Dh * dyv, rdx, off);
                         const float us = group16_sum(xv * gb);
+                        const float uo = group16_sum(xv * gof);
                         const float ds = group16_sum(xv * dyv);
                         if (lr == 0) {
                             sUp[pj][t] = us;
+                            sUop[pj][t] = uo;
                             sDDp[pj][t] = ds;
                         }
                     }
@@ -623,21 +657,32 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
         // ---- phase C (wave 0): dl by a suffix scan, ddt, per-row sums; then the next block
         if (w == 0) {
             const int rows = (int)min((int64_t)QB, T - t0);
-            float u = 0.f, dd = 0.f;
+            float u = 0.f, uo = 0.f, dd = 0.f, cz = 0.f, rz = 0.f;
             if (lane < QB) {
 #pragma unroll
                 for (int pj = 0; pj < PT; ++pj) {
                     u += sUp[pj][lane];
+                    uo += sUop[pj][lane];
                     dd += sDDp[pj][lane];
                 }
+#pragma unroll
+                for (int i = 0; i < QT; ++i) {
+                    cz += sCz[i][lane];
+                    rz += sRz[i][lane];
+                }
             }
+            float kap = 0.f;
+#pragma unroll
+            for (int i = 0; i < NW; ++i) kap += sKap[i];
             const bool valid = lane < rows;
             const float f = lane < QB ? sF[lane] : 0.f;
-            const acc_t sv = valid ? (acc_t)qcur - (acc_t)f * (acc_t)u : (acc_t)0;
-            const acc_t incl = wave_incl_scan(sv);
-            const acc_t total = __shfl(incl, 63);
-            const acc_t dl = dl_carry + (total - incl + sv);     // sum over k >= t of the block, plus what follows
-            dl_carry += total;
+            // dl_t = [sum_{k<t} (c_k - rho_k)] + [sum_{s>=t} qoff_s] + [sum_{r<t} roff_r] + 2^cend <K, H_in>
+            const acc_t zv = lane < QB ? (acc_t)cz - (acc_t)rz : (acc_t)0;
+            const acc_t qv = valid ? (acc_t)qcur : (acc_t)0;
+            const acc_t rv = lane < QB ? (acc_t)f * (acc_t)uo : (acc_t)0;
+            const acc_t zi = wave_incl_scan(zv), qi = wave_incl_scan(qv), ri = wave_incl_scan(rv);
+            const acc_t qtot = __shfl(qi, 63);
+            const acc_t dl = (zi - zv) + (qtot - qi + qv) + (ri - rv) + (acc_t)sCend * (acc_t)kap;
             if (valid) {
                 const float d = sDel[lane];
                 const float a = expf(d * Anat);                   // a_t
