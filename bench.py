@@ -6,7 +6,9 @@ A step is one full forward (ssd_forward: one launch of the scan kernel) over
 the workload's batch, with inputs and outputs already resident in HBM.
 Prints one JSON line: tokens/s over K timed steps, the roofline of the scan
 kernel measured with HIP events on the stream it is launched on, and the CPU
-oracle timed on the same workload.
+oracle timed on the same workload.  The line also carries a "backward" object:
+the time of one ssd_backward call (every gradient) on the same workload and its
+fraction of the HBM roofline (skipped with --no-backward).
 """
 from __future__ import annotations
 
@@ -44,6 +46,65 @@ def algorithmic_flops(w) -> int:
     b, T, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk_len
     nc = -(-T // Q)
     return 2 * (b * H * nc * (Q * (Q + 1) // 2 * P + 2 * Q * N * P) + b * G * nc * Q * (Q + 1) // 2 * N)
+
+
+def backward_algorithmic_bytes(w, init_nonzero: bool) -> int:
+    """Bytes the gradients must move: the forward's inputs, dy and dfinal read once;
+    dx, ddt, dB, dC, dinit and the per-head gradients written once."""
+    sx = 2 if w.dtype == "bf16" else 4
+    b, T, H, P, N, G = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups
+    reads = sx * (b * T * H * P + 2 * b * T * G * N) + 4 * b * T * H + 8 * H + 4 * b * T * H * P + 4 * b * H * P * N
+    if init_nonzero:
+        reads += 4 * b * H * P * N
+    writes = 4 * b * T * H * P + 4 * b * T * H + 2 * 4 * b * T * G * N + 4 * b * H * P * N + 12 * H
+    return reads + writes
+
+
+def backward_leg(w, prob, d, steps: int, warmup: int):
+    """Time ssd_backward (every gradient of <dy, y> + <dfinal, final>) on the workload."""
+    import numpy as np
+    import torch
+
+    import mamba_ssd_scan_chunked_amd as ssd
+    if w.nseqs_packed:
+        return None                   # the backward takes no packed sequences
+    dev = d["x"].device
+    rng = np.random.default_rng(1234)
+    b, T, H, P, N, G = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups
+    dy = torch.from_numpy(rng.standard_normal((b, T, H, P), dtype=np.float32)).to(dev)
+    dfinal = torch.from_numpy(rng.standard_normal((b, H, P, N), dtype=np.float32)).to(dev)
+    dtype = ssd.DTYPE_BF16 if w.dtype == "bf16" else ssd.DTYPE_F32
+    p = ssd.problem(b, T, H, P, N, G, w.chunk_len, b, dtype, 0)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = {"dx": torch.empty((b, T, H, P), **f32), "ddt": torch.empty((b, T, H), **f32),
+           "dA_log": torch.empty((H,), **f32), "dB": torch.empty((b, T, G, N), **f32),
+           "dC": torch.empty((b, T, G, N), **f32), "dD": torch.empty((H,), **f32),
+           "dinit": torch.empty((b, H, P, N), **f32), "ddt_bias": torch.empty((H,), **f32)}
+    ws = torch.empty(max(1, ssd.backward_workspace_size(p)), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def run():
+        ssd.backward_into(p, d["x"], d["dt"], None, d["A_log"], d["B"], d["C"], d["D"], d["init"], dy, dfinal, out,
+                          ws, stream=stream)
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for e in evs:
+        e[0].record(stream)
+        run()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
+    mean = sum(ms) / len(ms)
+    balg = backward_algorithmic_bytes(w, prob["init"] is not None)
+    return {"what": "ssd_backward: dx, ddt, dA_log, dB, dC, dD, dinit, ddt_bias of <dy, y> + <dfinal, final>",
+            "ms_per_step": round(mean, 5), "ms_median": round(ms[len(ms) // 2], 5),
+            "tokens_per_s": round(b * T / (mean / 1000.0), 1),
+            "roofline": {"bound": "hbm", "achieved": round(balg / (mean / 1000.0) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(balg / (mean / 1000.0) / 1e9 / HBM_PEAK_GBS, 4),
+                         "alg_bytes_per_step": balg, "kernels": "all launches of one ssd_backward call"}}
 
 
 def kernel_source_hash() -> str:
@@ -102,6 +163,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="m2p7_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of known size (reference for the HBM traffic counters)")
     args = ap.parse_args()
@@ -178,6 +240,10 @@ def main():
                 "alg_bytes_per_launch": balg, "alg_flops_per_step": falg,
                 "step_frac_of_hbm_roofline": round(balg / (ms_per_step / 1000.0) / 1e9 / HBM_PEAK_GBS, 4)}
 
+    bwd = None
+    if not args.no_backward:
+        bwd = backward_leg(w, prob, d, steps=max(5, min(args.steps, 20)), warmup=2)
+
     base = None
     if not args.no_cpu_baseline:
         base = cpu_baseline(prob, w)
@@ -190,7 +256,7 @@ def main():
                       "headdim": w.headdim, "dstate": w.dstate, "ngroups": w.ngroups, "chunk_len": w.chunk_len,
                       "kernel_block": 64 if w.chunk_len >= 64 else w.chunk_len, "outputs": "y fp32 + final fp32",
                       "parallelism": "single GPU"},
-           "roofline": roofline, "cpu_baseline": base}
+           "roofline": roofline, "cpu_baseline": base, "backward": bwd}
     print(json.dumps(out), flush=True)
 
 
