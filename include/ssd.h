@@ -177,7 +177,9 @@ int ssd_step(const ssd_problem_t* p,
 /* Bytes of device workspace ssd_backward needs (0 if the problem is invalid):
  * per-token and per-(row, head) scalars, and, when a group holds more than one
  * head, each head's dB and dC contribution, (batch, seqlen, nheads, dstate)
- * fp32 each, before the sum over the group.  The contents need no
+ * each in the input type (bf16 or fp32), before the fp32 sum over the group;
+ * and each 64-token (bf16) or 32-token (fp32) block's incoming state,
+ * (batch, nheads, blocks, headdim, dstate) in the input type.  The contents need no
  * initialisation. */
 size_t ssd_backward_workspace_size(const ssd_problem_t* p);
 

@@ -46,8 +46,15 @@ __global__ __launch_bounds__(256) void ssd_combine_kernel(CombineParams prm) {
     }
 }
 
-// dB or dC of a group = the sum of its heads' contributions, in head order.
-__global__ __launch_bounds__(256) void ssd_bwd_group_sum_kernel(const float* __restrict__ src, float* __restrict__ dst,
+// dB or dC of a group = the sum of its heads' contributions (fp32 or bf16), in
+// head order, in fp32.  One thread per 4 consecutive outputs.
+__device__ inline float4 load4(const float* p) { return *(const float4*)p; }
+__device__ inline float4 load4(const __bf16* p) {
+    const bf16x4 v = *(const bf16x4*)p;
+    return make_float4((float)v[0], (float)v[1], (float)v[2], (float)v[3]);
+}
+template <typename S>
+__global__ __launch_bounds__(256) void ssd_bwd_group_sum_kernel(const S* __restrict__ src, float* __restrict__ dst,
                                                                 int64_t rows, int H, int G, int N) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;        // float4 index of dst
     const int n4 = N / 4;
@@ -56,10 +63,10 @@ __global__ __launch_bounds__(256) void ssd_bwd_group_sum_kernel(const float* __r
     const int64_t bt = i / (G * n4);
     const int g = (int)((i / n4) % G), c = (int)(i % n4);
     const int hpg = H / G;
-    const float4* s = (const float4*)(src + ((bt * H + (int64_t)g * hpg) * N)) + c;
-    float4 acc = s[0];
+    const S* s = src + (bt * H + (int64_t)g * hpg) * N + 4 * c;
+    float4 acc = load4(s);
     for (int j = 1; j < hpg; ++j) {
-        const float4 v = s[(int64_t)j * n4];
+        const float4 v = load4(s + (int64_t)j * N);
         acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
     }
     ((float4*)dst)[i] = acc;
@@ -182,7 +189,7 @@ int slices_per_workgroup(const ssd_problem_t* p, bool seq, int nseg) {
 // Workspace of the backward pass: a per-token scalar (b, T, H), each block's
 // incoming state (b, H, blocks, P, N) in the input type, the per-row scalar
 // sums (b, H, 3), and, when a group has more than one head, each head's dB and
-// dC contribution (b, T, H, N) before the sum over the group.
+// dC contribution (b, T, H, N) in the input type before the sum over the group.
 int bwd_block(const ssd_problem_t* p);
 struct BwdWs {
     int64_t q_off, hin_off, part_off, dbh_off, dch_off, total;
@@ -197,7 +204,7 @@ BwdWs bwd_ws_layout(const ssd_problem_t* p) {
     l.hin_off = align256(bth * 4);
     l.part_off = l.hin_off + align256(bh * nblk * p->headdim * p->dstate * elem_size(p->dtype));
     l.dbh_off = l.part_off + align256(bh * 12);
-    const int64_t hn = per_head ? align256(bth * p->dstate * 4) : 0;
+    const int64_t hn = per_head ? align256(bth * p->dstate * elem_size(p->dtype)) : 0;
     l.dch_off = l.dbh_off + hn;
     l.total = l.dch_off + hn;
     return l;
@@ -529,8 +536,9 @@ int ssd_backward(const ssd_problem_t* p, const void* x, const float* dt, const f
     prm.dfinal = dfinal;
     prm.dx = dx;
     prm.ddt = ddt;
-    prm.dBh = per_head ? reinterpret_cast<float*>(ws + wl.dbh_off) : dB;
-    prm.dCh = per_head ? reinterpret_cast<float*>(ws + wl.dch_off) : dC;
+    prm.dBh = per_head ? static_cast<void*>(ws + wl.dbh_off) : static_cast<void*>(dB);
+    prm.dCh = per_head ? static_cast<void*>(ws + wl.dch_off) : static_cast<void*>(dC);
+    prm.h_bf16 = per_head && bf ? 1 : 0;
     prm.dinit = dinit;
     prm.q = reinterpret_cast<float*>(ws + wl.q_off);
     prm.hin = ws + wl.hin_off;
@@ -549,10 +557,17 @@ int ssd_backward(const ssd_problem_t* p, const void* x, const float* dt, const f
         const int64_t rows = p->batch * p->seqlen;
         const int64_t n4 = rows * p->ngroups * N / 4;
         const unsigned blocks = (unsigned)((n4 + 255) / 256);
-        hipLaunchKernelGGL(ssd::ssd_bwd_group_sum_kernel, dim3(blocks), dim3(256), 0, st, prm.dBh, dB, rows,
-                           (int)p->nheads, (int)p->ngroups, N);
-        hipLaunchKernelGGL(ssd::ssd_bwd_group_sum_kernel, dim3(blocks), dim3(256), 0, st, prm.dCh, dC, rows,
-                           (int)p->nheads, (int)p->ngroups, N);
+        if (prm.h_bf16) {
+            hipLaunchKernelGGL(ssd::ssd_bwd_group_sum_kernel<__bf16>, dim3(blocks), dim3(256), 0, st,
+                               (const __bf16*)prm.dBh, dB, rows, (int)p->nheads, (int)p->ngroups, N);
+            hipLaunchKernelGGL(ssd::ssd_bwd_group_sum_kernel<__bf16>, dim3(blocks), dim3(256), 0, st,
+                               (const __bf16*)prm.dCh, dC, rows, (int)p->nheads, (int)p->ngroups, N);
+        } else {
+            hipLaunchKernelGGL(ssd::ssd_bwd_group_sum_kernel<float>, dim3(blocks), dim3(256), 0, st,
+                               (const float*)prm.dBh, dB, rows, (int)p->nheads, (int)p->ngroups, N);
+            hipLaunchKernelGGL(ssd::ssd_bwd_group_sum_kernel<float>, dim3(blocks), dim3(256), 0, st,
+                               (const float*)prm.dCh, dC, rows, (int)p->nheads, (int)p->ngroups, N);
+        }
         e = hipGetLastError();
     }
     if (e == hipSuccess) {

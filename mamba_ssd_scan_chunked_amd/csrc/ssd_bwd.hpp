@@ -64,8 +64,9 @@ struct BwdParams {
     const float* dfinal;
     float* dx;
     float* ddt;
-    float* dBh;       // (batch, T, HB, N): per-head dB (HB = H), or dB itself (HB = G = H)
-    float* dCh;       // same for dC
+    void* dBh;        // (batch, T, HB, N): per-head dB (HB = H), or dB itself (HB = G = H)
+    void* dCh;        // same for dC
+    int h_bf16;       // per-head contributions stored as bf16 (bf16 inputs, HB = H > G), else fp32
     float* dinit;     // (batch, H, P, N) or null
     float* q;         // (batch, T, H) workspace: qoff
     void* hin;        // (batch, H, nblk, P, N) workspace: each block's incoming state (input type)
@@ -114,6 +115,14 @@ __device__ inline void lds_store4(float* dst, float a, float b, float c, float d
 __device__ inline void buf_store_f32(float v, rsrc_t r, int off) {
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, v), r, off, 0, 0);
 }
+__device__ inline void buf_store_bf16(float v, rsrc_t r, int off) {
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (__bf16)v), r, off, 0, 0);
+}
+// One value of a dB / dC output: fp32, or bf16 for per-head contributions of bf16 inputs.
+__device__ inline void store_grad(float v, rsrc_t r, int64_t elem, int as_bf16) {
+    if (as_bf16) buf_store_bf16(v, r, (int)(elem * 2));
+    else buf_store_f32(v, r, (int)(elem * 4));
+}
 
 // Sum over the 16 lanes of each lane group (lanes with equal l/16).
 __device__ inline float group16_sum(float v) {
@@ -136,6 +145,9 @@ struct BwdCfg {
     static constexpr int T_QN = (QT * NTL + NW - 1) / NW;      // token x state tiles per wave
     static constexpr int T_QP = (QT * PT + NW - 1) / NW;       // token x channel tiles per wave
     static constexpr int T_NP = (NTL * PT + NW - 1) / NW;      // state tiles per wave
+    // every wave has a full set of tiles (no bounds test needed)
+    static constexpr bool QQ_FULL = (QT * QT) % NW == 0, QN_FULL = (QT * NTL) % NW == 0;
+    static constexpr bool QP_FULL = (QT * PT) % NW == 0, NP_FULL = (NTL * PT) % NW == 0;
     static constexpr int XU = QB * P * SZ / 16;                // 16-byte chunks of x per block
     static constexpr int YU = QB * P * 4 / 16;                 // of dy (fp32)
     static constexpr int BU = QB * N * SZ / 16;                // of B or C
@@ -270,7 +282,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_fwd_kernel(BwdParams prm) {
     for (int j = 0; j < K::T_NP; ++j) {
         const int tile = w + NW * j;
         st[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (tile < NTL * PT) {
+        if (K::NP_FULL || tile < NTL * PT) {
             const int n0 = 16 * (tile / PT) + 4 * lg, p = 16 * (tile % PT) + lr;
             if (prm.init) {
                 const float4 v = *(const float4*)(prm.init + (bh * P + p) * N + n0);
@@ -298,7 +310,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_fwd_kernel(BwdParams prm) {
 #pragma unroll
         for (int j = 0; j < K::T_QQ; ++j) {
             const int tile = w + NW * j;
-            if (tile < QT * QT) {
+            if (K::QQ_FULL || tile < QT * QT) {
                 const int si = tile / QT, ti = tile % QT;
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -320,7 +332,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_fwd_kernel(BwdParams prm) {
         for (int j = 0; j < K::T_QN; ++j) {
             const int tile = w + NW * j;
             a3[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (tile < QT * NTL) {
+            if (K::QN_FULL || tile < QT * NTL) {
                 const int ti = tile / NTL, ni = tile % NTL;
 #pragma unroll
                 for (int k0 = 0; k0 < P; k0 += KS)
@@ -331,11 +343,12 @@ __global__ __launch_bounds__(512) void ssd_bwd_fwd_kernel(BwdParams prm) {
 
         // ---- phase B: dC^h = W B + 2^cum dy H_in, q partial sums; state update
         {
-            const rsrc_t rdc = make_rsrc(prm.dCh + ((b * T + t0) * HB + hb) * N, (T - t0) * HB * N * 4);
+            const int es = prm.h_bf16 ? 2 : 4;
+            const rsrc_t rdc = make_rsrc((char*)prm.dCh + ((b * T + t0) * HB + hb) * N * es, (T - t0) * HB * N * es);
 #pragma unroll
             for (int j = 0; j < K::T_QN; ++j) {
                 const int tile = w + NW * j;
-                if (tile < QT * NTL) {
+                if (K::QN_FULL || tile < QT * NTL) {
                     const int ti = tile / NTL, ni = tile % NTL;
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -346,7 +359,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_fwd_kernel(BwdParams prm) {
                     for (int e = 0; e < 4; ++e) {
                         const int t = 16 * ti + 4 * lg + e;
                         const float off = sDin[t] * a3[j][e];
-                        buf_store_f32(acc[e] + off, rdc, (int)((t * HB * N + n) * 4));
+                        store_grad(acc[e] + off, rdc, t * HB * N + n, prm.h_bf16);
                         const float qs = group16_sum(off * to_f32(sC[t * LN + n]));
                         if (lr == 0) sQp[ni][t] = qs;
                     }
@@ -356,7 +369,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_fwd_kernel(BwdParams prm) {
 #pragma unroll
             for (int j = 0; j < K::T_NP; ++j) {
                 const int tile = w + NW * j;
-                if (tile < NTL * PT) {
+                if (K::NP_FULL || tile < NTL * PT) {
                     const int ni = tile / PT, pj = tile % PT;
                     f32x4 acc = st[j] * dec;
 #pragma unroll
@@ -442,7 +455,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
 #pragma unroll
         for (int j = 0; j < K::T_NP; ++j) {
             const int tile = w + NW * j;
-            if (tile < NTL * PT) {
+            if (K::NP_FULL || tile < NTL * PT) {
                 const int n0 = 16 * (tile / PT) + 4 * lg, p = 16 * (tile % PT) + lr;
                 hv[j] = *(const h4_t*)(hb0 + p * N + n0);
             }
@@ -481,7 +494,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
     for (int j = 0; j < K::T_NP; ++j) {
         const int tile = w + NW * j;
         kst[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (tile < NTL * PT) {
+        if (K::NP_FULL || tile < NTL * PT) {
             const int n0 = 16 * (tile / PT) + 4 * lg, p = 16 * (tile % PT) + lr;
             if (prm.dfinal) {
                 const float4 v = *(const float4*)(prm.dfinal + (bh * P + p) * N + n0);
@@ -511,7 +524,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
 #pragma unroll
         for (int j = 0; j < K::T_QQ; ++j) {
             const int tile = w + NW * j;
-            if (tile < QT * QT) {
+            if (K::QQ_FULL || tile < QT * QT) {
                 const int si = tile / QT, ti = tile % QT;
                 f32x4 ae = {0.f, 0.f, 0.f, 0.f}, af = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -548,7 +561,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
         for (int j = 0; j < K::T_QP; ++j) {
             const int tile = w + NW * j;
             a3[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (tile < QT * PT) {
+            if (K::QP_FULL || tile < QT * PT) {
                 const int ti = tile / PT, pj = tile % PT;
 #pragma unroll
                 for (int k0 = 0; k0 < N; k0 += KS)
@@ -560,7 +573,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
 #pragma unroll
             for (int j = 0; j < K::T_NP; ++j) {
                 const int tile = w + NW * j;
-                if (tile < NTL * PT) {
+                if (K::NP_FULL || tile < NTL * PT) {
                     const TI* hv = (const TI*)&hcur[j];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) kp += kst[j][e] * to_f32(hv[e]);
@@ -575,7 +588,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
         for (int j = 0; j < K::T_QN; ++j) {
             const int tile = w + NW * j;
             a5[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (tile < QT * NTL) {
+            if (K::QN_FULL || tile < QT * NTL) {
                 const int ti = tile / NTL, ni = tile % NTL;
 #pragma unroll
                 for (int k0 = 0; k0 < P; k0 += KS)
@@ -586,12 +599,11 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
 
         // ---- phase B: G B (-> dx, u, dy.x), dB^h, K update
         {
-            const rsrc_t rdy = make_rsrc(prm.dy + ((b * T + t0) * H + h) * P, (T - t0) * H * P * 4);
             const rsrc_t rdx = make_rsrc(prm.dx + ((b * T + t0) * H + h) * P, (T - t0) * H * P * 4);
 #pragma unroll
             for (int j = 0; j < K::T_QP; ++j) {
                 const int tile = w + NW * j;
-                if (tile < QT * PT) {
+                if (K::QP_FULL || tile < QT * PT) {
                     const int ti = tile / PT, pj = tile % PT;
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -604,7 +616,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
                         const float gof = sDout[t] * a3[j][e];
                         const float gb = acc[e] + gof;
                         const int off = (int)((t * H * P + p) * 4);
-                        const float dyv = buf_load_f32(rdy, off);
+                        const float dyv = to_f32(sDY[t * LP + p]);
                         const float xv = to_f32(sX[t * LP + p]);
                         buf_store_f32(sF[t] * gb + Dh * dyv, rdx, off);
                         const float us = group16_sum(xv * gb);
@@ -618,11 +630,12 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
                     }
                 }
             }
-            const rsrc_t rdb = make_rsrc(prm.dBh + ((b * T + t0) * HB + hb) * N, (T - t0) * HB * N * 4);
+            const int es = prm.h_bf16 ? 2 : 4;
+            const rsrc_t rdb = make_rsrc((char*)prm.dBh + ((b * T + t0) * HB + hb) * N * es, (T - t0) * HB * N * es);
 #pragma unroll
             for (int j = 0; j < K::T_QN; ++j) {
                 const int tile = w + NW * j;
-                if (tile < QT * NTL) {
+                if (K::QN_FULL || tile < QT * NTL) {
                     const int ti = tile / NTL, ni = tile % NTL;
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -632,7 +645,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int t = 16 * ti + 4 * lg + e;
-                        buf_store_f32(sF[t] * (acc[e] + sDout[t] * a5[j][e]), rdb, (int)((t * HB * N + n) * 4));
+                        store_grad(sF[t] * (acc[e] + sDout[t] * a5[j][e]), rdb, t * HB * N + n, prm.h_bf16);
                     }
                 }
             }
@@ -640,7 +653,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
 #pragma unroll
             for (int j = 0; j < K::T_NP; ++j) {
                 const int tile = w + NW * j;
-                if (tile < NTL * PT) {
+                if (K::NP_FULL || tile < NTL * PT) {
                     const int ni = tile / PT, pj = tile % PT;
                     f32x4 acc = kst[j] * dec;
 #pragma unroll
@@ -708,7 +721,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
 #pragma unroll
         for (int j = 0; j < K::T_NP; ++j) {
             const int tile = w + NW * j;
-            if (tile < NTL * PT) {
+            if (K::NP_FULL || tile < NTL * PT) {
                 const int n0 = 16 * (tile / PT) + 4 * lg, p = 16 * (tile % PT) + lr;
                 *(float4*)(prm.dinit + (bh * P + p) * N + n0) = make_float4(kst[j][0], kst[j][1], kst[j][2], kst[j][3]);
             }
