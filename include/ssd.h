@@ -206,7 +206,7 @@ size_t ssd_backward_workspace_size(const ssd_problem_t* p);
  * SSD_ERR_UNSUPPORTED).  Supported shapes: BF16 headdim 32 or 64 with dstate 64,
  * 128 or 256; F32 headdim 16, 32 or 64 with dstate 16 .. 128.  Outputs must not
  * overlap any input, the workspace or each other (SSD_ERR_ALIAS).  x, B, C, dy,
- * dB, dC, init_state, dfinal and dinit need 16-byte alignment, the rest 4.
+ * dx, dB, dC, init_state, dfinal and dinit need 16-byte alignment, the rest 4.
  * Two kernel launches walk each (row, head) once forwards and once backwards
  * with the state on chip; then, with more than one head per group, a sum of the
  * heads' dB and dC; then the per-head sums over rows.  Per-head sums are taken in

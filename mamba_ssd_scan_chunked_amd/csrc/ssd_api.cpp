@@ -483,7 +483,7 @@ int ssd_backward(const ssd_problem_t* p, const void* x, const float* dt, const f
     if (tokens && static_cast<int64_t>(workspace_bytes) < wl.total) return SSD_ERR_WORKSPACE;
     if (misaligned(x, 16) || misaligned(B, 16) || misaligned(C, 16) || misaligned(dy, 16) || misaligned(dB, 16) ||
         misaligned(dC, 16) || misaligned(init_state, 16) || misaligned(dfinal, 16) || misaligned(dinit, 16) ||
-        misaligned(dx, 4) || misaligned(dt, 4) || misaligned(ddt, 4) || misaligned(A_log, 4) ||
+        misaligned(dx, 16) || misaligned(dt, 4) || misaligned(ddt, 4) || misaligned(A_log, 4) ||
         misaligned(dA_log, 4) || misaligned(dt_bias, 4) || misaligned(ddt_bias, 4) || misaligned(D, 4) ||
         misaligned(dD, 4) || misaligned(workspace, 256))
         return SSD_ERR_ALIGNMENT;

@@ -118,10 +118,28 @@ __device__ inline void buf_store_f32(float v, rsrc_t r, int off) {
 __device__ inline void buf_store_bf16(float v, rsrc_t r, int off) {
     __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (__bf16)v), r, off, 0, 0);
 }
-// One value of a dB / dC output: fp32, or bf16 for per-head contributions of bf16 inputs.
-__device__ inline void store_grad(float v, rsrc_t r, int64_t elem, int as_bf16) {
-    if (as_bf16) buf_store_bf16(v, r, (int)(elem * 2));
-    else buf_store_f32(v, r, (int)(elem * 4));
+// Four consecutive values of a dB / dC output: fp32, or bf16 for per-head
+// contributions of bf16 inputs.
+__device__ inline void store_grad4(f32x4 v, rsrc_t r, int64_t elem, int as_bf16) {
+    if (as_bf16) {
+        const bf16x4 h = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+        typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2, h), r, (int)(elem * 2), 0, 0);
+    } else {
+        buf_store16(v, r, (int)(elem * 4));
+    }
+}
+// Four consecutive values of one LDS row as fp32.
+__device__ inline f32x4 lds_load4(const __bf16* p) {
+    const bf16x4 v = *(const bf16x4*)p;
+    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+__device__ inline f32x4 lds_load4(const float* p) { return *(const f32x4*)p; }
+// Sum over the four lane groups (lanes with equal l % 16).
+__device__ inline float group4_sum(float v) {
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    return v;
 }
 
 // Sum over the 16 lanes of each lane group (lanes with equal l/16).
@@ -145,9 +163,6 @@ struct BwdCfg {
     static constexpr int T_QN = (QT * NTL + NW - 1) / NW;      // token x state tiles per wave
     static constexpr int T_QP = (QT * PT + NW - 1) / NW;       // token x channel tiles per wave
     static constexpr int T_NP = (NTL * PT + NW - 1) / NW;      // state tiles per wave
-    // every wave has a full set of tiles (no bounds test needed)
-    static constexpr bool QQ_FULL = (QT * QT) % NW == 0, QN_FULL = (QT * NTL) % NW == 0;
-    static constexpr bool QP_FULL = (QT * PT) % NW == 0, NP_FULL = (NTL * PT) % NW == 0;
     static constexpr int XU = QB * P * SZ / 16;                // 16-byte chunks of x per block
     static constexpr int YU = QB * P * 4 / 16;                 // of dy (fp32)
     static constexpr int BU = QB * N * SZ / 16;                // of B or C
@@ -282,7 +297,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_fwd_kernel(BwdParams prm) {
     for (int j = 0; j < K::T_NP; ++j) {
         const int tile = w + NW * j;
         st[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (K::NP_FULL || tile < NTL * PT) {
+        if (tile < NTL * PT) {
             const int n0 = 16 * (tile / PT) + 4 * lg, p = 16 * (tile % PT) + lr;
             if (prm.init) {
                 const float4 v = *(const float4*)(prm.init + (bh * P + p) * N + n0);
@@ -310,7 +325,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_fwd_kernel(BwdParams prm) {
 #pragma unroll
         for (int j = 0; j < K::T_QQ; ++j) {
             const int tile = w + NW * j;
-            if (K::QQ_FULL || tile < QT * QT) {
+            if (tile < QT * QT) {
                 const int si = tile / QT, ti = tile % QT;
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -332,11 +347,11 @@ __global__ __launch_bounds__(512) void ssd_bwd_fwd_kernel(BwdParams prm) {
         for (int j = 0; j < K::T_QN; ++j) {
             const int tile = w + NW * j;
             a3[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (K::QN_FULL || tile < QT * NTL) {
+            if (tile < QT * NTL) {
                 const int ti = tile / NTL, ni = tile % NTL;
 #pragma unroll
                 for (int k0 = 0; k0 < P; k0 += KS)
-                    a3[j] = M::mma(frag_k(sDY, LP, 16 * ti + lr, k0, lg), frag_t(sS, LN, 16 * ni, k0, lr, lg), a3[j]);
+                    a3[j] = M::mma(frag_t(sS, LN, 16 * ni, k0, lr, lg), frag_k(sDY, LP, 16 * ti + lr, k0, lg), a3[j]);
             }
         }
         block_sync_lds();
@@ -348,28 +363,26 @@ __global__ __launch_bounds__(512) void ssd_bwd_fwd_kernel(BwdParams prm) {
 #pragma unroll
             for (int j = 0; j < K::T_QN; ++j) {
                 const int tile = w + NW * j;
-                if (K::QN_FULL || tile < QT * NTL) {
+                if (tile < QT * NTL) {
                     const int ti = tile / NTL, ni = tile % NTL;
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int k0 = 0; k0 < QB; k0 += KS)
-                        acc = M::mma(frag_k(sW, LQ, 16 * ti + lr, k0, lg), frag_t(sB, LN, 16 * ni, k0, lr, lg), acc);
-                    const int n = 16 * ni + lr;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int t = 16 * ti + 4 * lg + e;
-                        const float off = sDin[t] * a3[j][e];
-                        store_grad(acc[e] + off, rdc, t * HB * N + n, prm.h_bf16);
-                        const float qs = group16_sum(off * to_f32(sC[t * LN + n]));
-                        if (lr == 0) sQp[ni][t] = qs;
-                    }
+                        acc = M::mma(frag_t(sB, LN, 16 * ni, k0, lr, lg), frag_k(sW, LQ, 16 * ti + lr, k0, lg), acc);
+                    // this lane: state rows n0 .. n0+3 of token t
+                    const int t = 16 * ti + lr, n0 = 16 * ni + 4 * lg;
+                    const f32x4 off = a3[j] * sDin[t];
+                    store_grad4(acc + off, rdc, t * HB * N + n0, prm.h_bf16);
+                    const f32x4 c4 = lds_load4(sC + t * LN + n0);
+                    const float qs = group4_sum(off[0] * c4[0] + off[1] * c4[1] + off[2] * c4[2] + off[3] * c4[3]);
+                    if (lg == 0) sQp[ni][t] = qs;
                 }
             }
             const float dec = sCend;
 #pragma unroll
             for (int j = 0; j < K::T_NP; ++j) {
                 const int tile = w + NW * j;
-                if (K::NP_FULL || tile < NTL * PT) {
+                if (tile < NTL * PT) {
                     const int ni = tile / PT, pj = tile % PT;
                     f32x4 acc = st[j] * dec;
 #pragma unroll
@@ -455,7 +468,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
 #pragma unroll
         for (int j = 0; j < K::T_NP; ++j) {
             const int tile = w + NW * j;
-            if (K::NP_FULL || tile < NTL * PT) {
+            if (tile < NTL * PT) {
                 const int n0 = 16 * (tile / PT) + 4 * lg, p = 16 * (tile % PT) + lr;
                 hv[j] = *(const h4_t*)(hb0 + p * N + n0);
             }
@@ -494,7 +507,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
     for (int j = 0; j < K::T_NP; ++j) {
         const int tile = w + NW * j;
         kst[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (K::NP_FULL || tile < NTL * PT) {
+        if (tile < NTL * PT) {
             const int n0 = 16 * (tile / PT) + 4 * lg, p = 16 * (tile % PT) + lr;
             if (prm.dfinal) {
                 const float4 v = *(const float4*)(prm.dfinal + (bh * P + p) * N + n0);
@@ -524,7 +537,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
 #pragma unroll
         for (int j = 0; j < K::T_QQ; ++j) {
             const int tile = w + NW * j;
-            if (K::QQ_FULL || tile < QT * QT) {
+            if (tile < QT * QT) {
                 const int si = tile / QT, ti = tile % QT;
                 f32x4 ae = {0.f, 0.f, 0.f, 0.f}, af = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -561,11 +574,11 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
         for (int j = 0; j < K::T_QP; ++j) {
             const int tile = w + NW * j;
             a3[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (K::QP_FULL || tile < QT * PT) {
+            if (tile < QT * PT) {
                 const int ti = tile / PT, pj = tile % PT;
 #pragma unroll
                 for (int k0 = 0; k0 < N; k0 += KS)
-                    a3[j] = M::mma(frag_k(sB, LN, 16 * ti + lr, k0, lg), frag_k(sK, LN, 16 * pj + lr, k0, lg), a3[j]);
+                    a3[j] = M::mma(frag_k(sK, LN, 16 * pj + lr, k0, lg), frag_k(sB, LN, 16 * ti + lr, k0, lg), a3[j]);
             }
         }
         {   // <K, H_in> over this wave's state tiles (K as it enters the block)
@@ -573,7 +586,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
 #pragma unroll
             for (int j = 0; j < K::T_NP; ++j) {
                 const int tile = w + NW * j;
-                if (K::NP_FULL || tile < NTL * PT) {
+                if (tile < NTL * PT) {
                     const TI* hv = (const TI*)&hcur[j];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) kp += kst[j][e] * to_f32(hv[e]);
@@ -588,11 +601,11 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
         for (int j = 0; j < K::T_QN; ++j) {
             const int tile = w + NW * j;
             a5[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (K::QN_FULL || tile < QT * NTL) {
+            if (tile < QT * NTL) {
                 const int ti = tile / NTL, ni = tile % NTL;
 #pragma unroll
                 for (int k0 = 0; k0 < P; k0 += KS)
-                    a5[j] = M::mma(frag_k(sX, LP, 16 * ti + lr, k0, lg), frag_t(sK, LN, 16 * ni, k0, lr, lg), a5[j]);
+                    a5[j] = M::mma(frag_t(sK, LN, 16 * ni, k0, lr, lg), frag_k(sX, LP, 16 * ti + lr, k0, lg), a5[j]);
             }
         }
         block_sync_lds();
@@ -603,30 +616,25 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
 #pragma unroll
             for (int j = 0; j < K::T_QP; ++j) {
                 const int tile = w + NW * j;
-                if (K::QP_FULL || tile < QT * PT) {
+                if (tile < QT * PT) {
                     const int ti = tile / PT, pj = tile % PT;
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int k0 = 0; k0 < QB; k0 += KS)
-                        acc = M::mma(frag_k(sE, LQ, 16 * ti + lr, k0, lg), frag_t(sDY, LP, 16 * pj, k0, lr, lg), acc);
-                    const int p = 16 * pj + lr;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int t = 16 * ti + 4 * lg + e;
-                        const float gof = sDout[t] * a3[j][e];
-                        const float gb = acc[e] + gof;
-                        const int off = (int)((t * H * P + p) * 4);
-                        const float dyv = to_f32(sDY[t * LP + p]);
-                        const float xv = to_f32(sX[t * LP + p]);
-                        buf_store_f32(sF[t] * gb + Dh * dyv, rdx, off);
-                        const float us = group16_sum(xv * gb);
-                        const float uo = group16_sum(xv * gof);
-                        const float ds = group16_sum(xv * dyv);
-                        if (lr == 0) {
-                            sUp[pj][t] = us;
-                            sUop[pj][t] = uo;
-                            sDDp[pj][t] = ds;
-                        }
+                        acc = M::mma(frag_t(sDY, LP, 16 * pj, k0, lr, lg), frag_k(sE, LQ, 16 * ti + lr, k0, lg), acc);
+                    // this lane: channels p0 .. p0+3 of token t
+                    const int t = 16 * ti + lr, p0 = 16 * pj + 4 * lg;
+                    const f32x4 gof = a3[j] * sDout[t];
+                    const f32x4 gb = acc + gof;
+                    const f32x4 dy4 = lds_load4(sDY + t * LP + p0), x4 = lds_load4(sX + t * LP + p0);
+                    buf_store16(gb * sF[t] + dy4 * Dh, rdx, (int)((t * H * P + p0) * 4));
+                    const float us = group4_sum(x4[0] * gb[0] + x4[1] * gb[1] + x4[2] * gb[2] + x4[3] * gb[3]);
+                    const float uo = group4_sum(x4[0] * gof[0] + x4[1] * gof[1] + x4[2] * gof[2] + x4[3] * gof[3]);
+                    const float ds = group4_sum(x4[0] * dy4[0] + x4[1] * dy4[1] + x4[2] * dy4[2] + x4[3] * dy4[3]);
+                    if (lg == 0) {
+                        sUp[pj][t] = us;
+                        sUop[pj][t] = uo;
+                        sDDp[pj][t] = ds;
                     }
                 }
             }
@@ -635,25 +643,21 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
 #pragma unroll
             for (int j = 0; j < K::T_QN; ++j) {
                 const int tile = w + NW * j;
-                if (K::QN_FULL || tile < QT * NTL) {
+                if (tile < QT * NTL) {
                     const int ti = tile / NTL, ni = tile % NTL;
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int k0 = 0; k0 < QB; k0 += KS)
-                        acc = M::mma(frag_k(sFm, LQ, 16 * ti + lr, k0, lg), frag_t(sC, LN, 16 * ni, k0, lr, lg), acc);
-                    const int n = 16 * ni + lr;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int t = 16 * ti + 4 * lg + e;
-                        store_grad(sF[t] * (acc[e] + sDout[t] * a5[j][e]), rdb, t * HB * N + n, prm.h_bf16);
-                    }
+                        acc = M::mma(frag_t(sC, LN, 16 * ni, k0, lr, lg), frag_k(sFm, LQ, 16 * ti + lr, k0, lg), acc);
+                    const int t = 16 * ti + lr, n0 = 16 * ni + 4 * lg;
+                    store_grad4((acc + a5[j] * sDout[t]) * sF[t], rdb, t * HB * N + n0, prm.h_bf16);
                 }
             }
             const float dec = sCend;
 #pragma unroll
             for (int j = 0; j < K::T_NP; ++j) {
                 const int tile = w + NW * j;
-                if (K::NP_FULL || tile < NTL * PT) {
+                if (tile < NTL * PT) {
                     const int ni = tile / PT, pj = tile % PT;
                     f32x4 acc = kst[j] * dec;
 #pragma unroll
@@ -721,7 +725,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
 #pragma unroll
         for (int j = 0; j < K::T_NP; ++j) {
             const int tile = w + NW * j;
-            if (K::NP_FULL || tile < NTL * PT) {
+            if (tile < NTL * PT) {
                 const int n0 = 16 * (tile / PT) + 4 * lg, p = 16 * (tile % PT) + lr;
                 *(float4*)(prm.dinit + (bh * P + p) * N + n0) = make_float4(kst[j][0], kst[j][1], kst[j][2], kst[j][3]);
             }
