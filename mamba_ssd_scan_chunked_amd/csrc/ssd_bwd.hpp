@@ -142,12 +142,13 @@ __device__ inline float group4_sum(float v) {
     return v;
 }
 
-// Sum over the 16 lanes of each lane group (lanes with equal l/16).
-__device__ inline float group16_sum(float v) {
-    v += __shfl_xor(v, 1);
-    v += __shfl_xor(v, 2);
-    v += __shfl_xor(v, 4);
-    v += __shfl_xor(v, 8);
+// Sum over the 16 lanes of each lane group (lanes with equal l/16), left in the
+// group's last lane (DPP row shifts, as in the wavefront scan).
+__device__ inline float row16_sum(float v) {
+    v = dpp_add<0x111, 0xf>(v);   // row_shr:1
+    v = dpp_add<0x112, 0xf>(v);   // row_shr:2
+    v = dpp_add<0x114, 0xf>(v);   // row_shr:4
+    v = dpp_add<0x118, 0xf>(v);   // row_shr:8
     return v;
 }
 
@@ -269,13 +270,13 @@ __global__ __launch_bounds__(512) void ssd_bwd_fwd_kernel(BwdParams prm) {
     const float dtb = prm.dt_bias ? prm.dt_bias[h] : 0.f;
 
     BwdStage<TI, P, N, QB> stg;
-    float dtn = 0.f;                      // wave 0: the next block's dt (lane = token)
+    float dtn = 0.f;                      // wave 1: the next block's dt (lane = token)
     auto issue = [&](int blk) {
         const int64_t t0 = (int64_t)blk * QB;
         stg.issue(xrow, xrec, xs, yrow, yrec, ys, brow, crow, brec, bs, t0, tid);
-        if (w == 0) dtn = buf_load_f32(make_rsrc(prm.dt + (b * T + t0) * H + h, (T - t0) * H * 4), lane * (int)(H * 4));
+        if (w == 1) dtn = buf_load_f32(make_rsrc(prm.dt + (b * T + t0) * H + h, (T - t0) * H * 4), lane * (int)(H * 4));
     };
-    // per-token scalars of a block (wave 0, lane = token)
+    // per-token scalars of a block (wave 1, lane = token)
     auto scalars = [&](int blk) {
         const int rows = (int)min((int64_t)QB, T - (int64_t)blk * QB);
         const float d = lane < rows ? step_size(dtn + dtb, prm.dt_softplus) : 0.f;
@@ -309,7 +310,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_fwd_kernel(BwdParams prm) {
 
     issue(0);
     stg.store(sX, sDY, sB, sC, tid);
-    if (w == 0) scalars(0);
+    if (w == 1) scalars(0);
     block_sync_lds();
 
     for (int blk = 0; blk < prm.nblk; ++blk) {
@@ -396,7 +397,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_fwd_kernel(BwdParams prm) {
         }
         block_sync_lds();
 
-        // ---- phase C: q, then the next block into LDS
+        // ---- phase C: q (wave 0), then the next block into LDS and its scalars (wave 1)
         if (w == 0 && lane < QB) {
             float qv = 0.f;
 #pragma unroll
@@ -405,7 +406,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_fwd_kernel(BwdParams prm) {
         }
         if (blk + 1 < prm.nblk) {
             stg.store(sX, sDY, sB, sC, tid);
-            if (w == 0) scalars(blk + 1);
+            if (w == 1) scalars(blk + 1);
         }
         block_sync_lds();
     }
@@ -460,7 +461,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
     const float Dh = prm.D ? prm.D[h] : 0.f;
 
     BwdStage<TI, P, N, QB> stg;
-    float dtn = 0.f, qn = 0.f;            // wave 0: the next block's dt and qoff (lane = token)
+    float dtn = 0.f, qn = 0.f;            // the next block's dt (wave 1) and qoff (wave 0), lane = token
     // the block's incoming state at this lane's state-tile positions (4 values per tile)
     typedef typename std::conditional<K::SZ == 2, uint2, uint4>::type h4_t;
     auto load_hin = [&](int blk, h4_t (&hv)[K::T_NP]) {
@@ -477,10 +478,8 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
     auto issue = [&](int blk) {
         const int64_t t0 = (int64_t)blk * QB;
         stg.issue(xrow, xrec, xs, yrow, yrec, ys, brow, crow, brec, bs, t0, tid);
-        if (w == 0) {
-            dtn = buf_load_f32(make_rsrc(prm.dt + (b * T + t0) * H + h, (T - t0) * H * 4), lane * (int)(H * 4));
-            qn = buf_load_f32(make_rsrc(prm.q + (b * T + t0) * H + h, (T - t0) * H * 4), lane * (int)(H * 4));
-        }
+        if (w == 1) dtn = buf_load_f32(make_rsrc(prm.dt + (b * T + t0) * H + h, (T - t0) * H * 4), lane * (int)(H * 4));
+        if (w == 0) qn = buf_load_f32(make_rsrc(prm.q + (b * T + t0) * H + h, (T - t0) * H * 4), lane * (int)(H * 4));
     };
     float qcur = 0.f;
     auto scalars = [&](int blk) {
@@ -498,7 +497,6 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
             sPre[lane] = pre;
         }
         if (lane == 0) sCend = fast_exp2((float)cend);
-        qcur = qn;
     };
 
     // carried K^T = (a_{t+1} G_{t+1})^T as accumulator tiles (rows n, columns p)
@@ -524,7 +522,8 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
 
     issue(prm.nblk - 1);
     stg.store(sX, sDY, sB, sC, tid);
-    if (w == 0) scalars(prm.nblk - 1);
+    if (w == 1) scalars(prm.nblk - 1);
+    qcur = qn;
     block_sync_lds();
 
     for (int blk = prm.nblk - 1; blk >= 0; --blk) {
@@ -559,8 +558,8 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
                     // Z[s][t] below the diagonal: its column sum (over s) and row sum (over t)
                     const float z = s > t ? m * ft * ae[e] * af[e] : 0.f;
                     zc += z;
-                    const float zr = group16_sum(z);
-                    if (lr == 0) sRz[ti][s] = zr;
+                    const float zr = row16_sum(z);
+                    if (lr == 15) sRz[ti][s] = zr;
                 }
                 zc += __shfl_xor(zc, 16);
                 zc += __shfl_xor(zc, 32);
@@ -669,9 +668,16 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
                 }
             }
         }
+        float f_r = 0.f, d_r = 0.f, pre_r = 0.f, cend_r = 0.f;   // wave 0: this block's scalars
+        if (w == 0) {
+            f_r = sF[lane];
+            d_r = sDel[lane];
+            pre_r = sPre[lane];
+            cend_r = sCend;
+        }
         block_sync_lds();
 
-        // ---- phase C (wave 0): dl by a suffix scan, ddt, per-row sums; then the next block
+        // ---- phase C: dl, ddt and the per-row sums (wave 0); the next block into LDS and its scalars (wave 1)
         if (w == 0) {
             const int rows = (int)min((int64_t)QB, T - t0);
             float u = 0.f, uo = 0.f, dd = 0.f, cz = 0.f, rz = 0.f;
@@ -692,21 +698,21 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
 #pragma unroll
             for (int i = 0; i < NW; ++i) kap += sKap[i];
             const bool valid = lane < rows;
-            const float f = lane < QB ? sF[lane] : 0.f;
+            const float f = lane < QB ? f_r : 0.f;
             // dl_t = [sum_{k<t} (c_k - rho_k)] + [sum_{s>=t} qoff_s] + [sum_{r<t} roff_r] + 2^cend <K, H_in>
             const acc_t zv = lane < QB ? (acc_t)cz - (acc_t)rz : (acc_t)0;
             const acc_t qv = valid ? (acc_t)qcur : (acc_t)0;
             const acc_t rv = lane < QB ? (acc_t)f * (acc_t)uo : (acc_t)0;
             const acc_t zi = wave_incl_scan(zv), qi = wave_incl_scan(qv), ri = wave_incl_scan(rv);
             const acc_t qtot = __shfl(qi, 63);
-            const acc_t dl = (zi - zv) + (qtot - qi + qv) + (ri - rv) + (acc_t)sCend * (acc_t)kap;
+            const acc_t dl = (zi - zv) + (qtot - qi + qv) + (ri - rv) + (acc_t)cend_r * (acc_t)kap;
             if (valid) {
-                const float d = sDel[lane];
+                const float d = d_r;
                 const float a = expf(d * Anat);                   // a_t
                 const float fD = fdmode == 1 ? 1.f : (fdmode == 2 ? a : 0.f);
                 const float fA = fdmode == 2 ? (d * Anat * a - a + 1.f) / (Anat * Anat) : 0.f;
                 float gdt = (float)dl * Anat + u * fD;
-                if (prm.dt_softplus) gdt *= 1.f / (1.f + expf(-sPre[lane]));
+                if (prm.dt_softplus) gdt *= 1.f / (1.f + expf(-pre_r));
                 prm.ddt[(b * T + t0 + lane) * H + h] = gdt;
                 sum_dA += dl * (acc_t)d + (acc_t)(u * fA);
                 sum_bias += (acc_t)gdt;
@@ -715,7 +721,8 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
         }
         if (blk > 0) {
             stg.store(sX, sDY, sB, sC, tid);
-            if (w == 0) scalars(blk - 1);
+            if (w == 1) scalars(blk - 1);
+            qcur = qn;
         }
         block_sync_lds();
     }
