@@ -175,7 +175,8 @@ int ssd_step(const ssd_problem_t* p,
              float* state, float* y, void* stream);
 
 /* Bytes of device workspace ssd_backward needs (0 if the problem is invalid):
- * per-token and per-(row, head) scalars, and, when a group holds more than one
+ * per-token scalars and dt transposed to (batch, nheads, seqlen), per-(row, head)
+ * scalars, and, when a group holds more than one
  * head, each head's dB and dC contribution, (batch, seqlen, nheads, dstate)
  * each in the input type (bf16 or fp32), before the fp32 sum over the group;
  * and each 64-token (bf16) or 32-token (fp32) block's incoming state,

@@ -72,6 +72,16 @@ __global__ __launch_bounds__(256) void ssd_bwd_group_sum_kernel(const S* __restr
     ((float4*)dst)[i] = acc;
 }
 
+// dt (b, T, H) -> (b, H, T): the backward kernels read each (row, head)'s step
+// sizes as one contiguous run per block.
+__global__ __launch_bounds__(256) void ssd_transpose_dt_kernel(const float* __restrict__ dt, float* __restrict__ dtT,
+                                                               int64_t batch, int64_t T, int64_t H) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // index into dtT
+    if (i >= batch * H * T) return;
+    const int64_t t = i % T, bh = i / T;
+    dtT[i] = dt[((bh / H) * T + t) * H + bh % H];
+}
+
 // Per-head scalars: sums over rows (in row order) of the reverse pass's partial sums.
 __global__ __launch_bounds__(256) void ssd_bwd_scalars_kernel(const float* __restrict__ part,
                                                               const float* __restrict__ A_log, int64_t batch, int H,
@@ -186,13 +196,13 @@ int slices_per_workgroup(const ssd_problem_t* p, bool seq, int nseg) {
     return npt;
 }
 
-// Workspace of the backward pass: a per-token scalar (b, T, H), each block's
+// Workspace of the backward pass: a per-token scalar and dt, both (b, H, T), each block's
 // incoming state (b, H, blocks, P, N) in the input type, the per-row scalar
 // sums (b, H, 3), and, when a group has more than one head, each head's dB and
 // dC contribution (b, T, H, N) in the input type before the sum over the group.
 int bwd_block(const ssd_problem_t* p);
 struct BwdWs {
-    int64_t q_off, hin_off, part_off, dbh_off, dch_off, total;
+    int64_t q_off, dt_off, hin_off, part_off, dbh_off, dch_off, total;
 };
 BwdWs bwd_ws_layout(const ssd_problem_t* p) {
     BwdWs l;
@@ -201,7 +211,8 @@ BwdWs bwd_ws_layout(const ssd_problem_t* p) {
     const int qb = bwd_block(p);
     const int64_t nblk = (p->seqlen + qb - 1) / qb;
     l.q_off = 0;
-    l.hin_off = align256(bth * 4);
+    l.dt_off = align256(bth * 4);
+    l.hin_off = l.dt_off + align256(bth * 4);
     l.part_off = l.hin_off + align256(bh * nblk * p->headdim * p->dstate * elem_size(p->dtype));
     l.dbh_off = l.part_off + align256(bh * 12);
     const int64_t hn = per_head ? align256(bth * p->dstate * elem_size(p->dtype)) : 0;
@@ -525,7 +536,7 @@ int ssd_backward(const ssd_problem_t* p, const void* x, const float* dt, const f
     const bool per_head = p->ngroups != p->nheads;
     ssd::BwdParams prm;
     prm.x = x;
-    prm.dt = dt;
+    prm.dt = reinterpret_cast<float*>(ws + wl.dt_off);
     prm.dt_bias = dt_bias;
     prm.A_log = A_log;
     prm.B = B;
@@ -552,7 +563,14 @@ int ssd_backward(const ssd_problem_t* p, const void* x, const float* dt, const f
     prm.dt_softplus = (p->flags & SSD_FLAG_DT_SOFTPLUS) ? 1 : 0;
     prm.x_scale = x_scale_of(p);
     const int64_t grid = p->batch * p->nheads;
-    e = bf ? ssd::launch_bwd_bf16(P, N, prm, grid, st) : ssd::launch_bwd_f32(P, N, prm, grid, st);
+    {
+        const int64_t n = p->batch * p->nheads * p->seqlen;
+        hipLaunchKernelGGL(ssd::ssd_transpose_dt_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, dt,
+                           const_cast<float*>(prm.dt), p->batch, p->seqlen, p->nheads);
+        e = hipGetLastError();
+    }
+    if (e == hipSuccess)
+        e = bf ? ssd::launch_bwd_bf16(P, N, prm, grid, st) : ssd::launch_bwd_f32(P, N, prm, grid, st);
     if (e == hipSuccess && per_head) {
         const int64_t rows = p->batch * p->seqlen;
         const int64_t n4 = rows * p->ngroups * N / 4;

@@ -53,7 +53,7 @@ namespace ssd {
 
 struct BwdParams {
     const void* x;
-    const float* dt;
+    const float* dt;        // (batch, H, T): the dt input transposed, token-contiguous per (row, head)
     const float* dt_bias;
     const float* A_log;
     const void* B;
@@ -68,8 +68,9 @@ struct BwdParams {
     void* dCh;        // same for dC
     int h_bf16;       // per-head contributions stored as bf16 (bf16 inputs, HB = H > G), else fp32
     float* dinit;     // (batch, H, P, N) or null
-    float* q;         // (batch, T, H) workspace: qoff
-    void* hin;        // (batch, H, nblk, P, N) workspace: each block's incoming state (input type)
+    float* q;         // (batch, H, T) workspace: qoff
+    void* hin;        // (batch, H, nblk, P * N) workspace: each block's incoming state (input type), in
+                      // the order the state tiles are held: tile, lane, 4 values
     float* part;      // (batch, H, 3) workspace: per-row sums for dA (natural A), ddt_bias, dD
     int64_t batch, T, H, G, HB;
     int nblk;
@@ -104,11 +105,11 @@ __device__ inline float frag_t_w(const float* base, int pitch, int m0, int k0, i
     return wk[k0 + lg] * base[(k0 + lg) * pitch + m0 + lr];
 }
 
-// Four consecutive values of one row into LDS (8 bytes for bf16, 16 for fp32).
-__device__ inline void lds_store4(__bf16* dst, float a, float b, float c, float d) {
+// Four consecutive values of one row (8 bytes for bf16, 16 for fp32), LDS or global.
+__device__ inline void store4(__bf16* dst, float a, float b, float c, float d) {
     *(bf16x4*)dst = bf16x4{(__bf16)a, (__bf16)b, (__bf16)c, (__bf16)d};
 }
-__device__ inline void lds_store4(float* dst, float a, float b, float c, float d) {
+__device__ inline void store4(float* dst, float a, float b, float c, float d) {
     *(f32x4*)dst = f32x4{a, b, c, d};
 }
 
@@ -217,7 +218,7 @@ struct BwdStage {
             const int v = tid + j * K::NT;
             if (K::YU % K::NT == 0 || v < K::YU) {
                 const float4 f = __builtin_bit_cast(float4, yr[j]);
-                lds_store4(sDY + (v / YC) * K::LP + (v % YC) * 4, f.x, f.y, f.z, f.w);
+                store4(sDY + (v / YC) * K::LP + (v % YC) * 4, f.x, f.y, f.z, f.w);
             }
         }
 #pragma unroll
@@ -274,7 +275,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_fwd_kernel(BwdParams prm) {
     auto issue = [&](int blk) {
         const int64_t t0 = (int64_t)blk * QB;
         stg.issue(xrow, xrec, xs, yrow, yrec, ys, brow, crow, brec, bs, t0, tid);
-        if (w == 1) dtn = buf_load_f32(make_rsrc(prm.dt + (b * T + t0) * H + h, (T - t0) * H * 4), lane * (int)(H * 4));
+        if (w == 1) dtn = buf_load_f32(make_rsrc(prm.dt + bh * T + t0, (T - t0) * 4), lane * 4);
     };
     // per-token scalars of a block (wave 1, lane = token)
     auto scalars = [&](int blk) {
@@ -304,7 +305,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_fwd_kernel(BwdParams prm) {
                 const float4 v = *(const float4*)(prm.init + (bh * P + p) * N + n0);
                 st[j] = f32x4{v.x, v.y, v.z, v.w};
             }
-            lds_store4(sS + p * LN + n0, st[j][0], st[j][1], st[j][2], st[j][3]);
+            store4(sS + p * LN + n0, st[j][0], st[j][1], st[j][2], st[j][3]);
         }
     }
 
@@ -319,9 +320,12 @@ __global__ __launch_bounds__(512) void ssd_bwd_fwd_kernel(BwdParams prm) {
 
         // ---- phase A: the incoming state to the workspace; W^T tiles (rows s, columns t), and dy H_in
         {
-            constexpr int HU = P * N * SZ / 16, HC = N * SZ / 16, VE = 16 / SZ;
-            uint4* dst = (uint4*)((TI*)prm.hin + (bh * prm.nblk + blk) * (int64_t)(P * N));
-            for (int v = tid; v < HU; v += K::NT) dst[v] = *(const uint4*)(sS + (v / HC) * LN + (v % HC) * VE);
+            TI* hb0 = (TI*)prm.hin + (bh * prm.nblk + blk) * (int64_t)(P * N);
+#pragma unroll
+            for (int j = 0; j < K::T_NP; ++j) {
+                const int tile = w + NW * j;
+                if (tile < NTL * PT) store4(hb0 + (tile * 64 + lane) * 4, st[j][0], st[j][1], st[j][2], st[j][3]);
+            }
         }
 #pragma unroll
         for (int j = 0; j < K::T_QQ; ++j) {
@@ -340,7 +344,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_fwd_kernel(BwdParams prm) {
                     const int s = s0 + e;
                     v[e] = s <= t ? fast_exp2((float)(ct - sCum[s])) * sF[s] * acc[e] : 0.f;
                 }
-                lds_store4(sW + t * LQ + s0, v[0], v[1], v[2], v[3]);
+                store4(sW + t * LQ + s0, v[0], v[1], v[2], v[3]);
             }
         }
         f32x4 a3[K::T_QN];
@@ -391,7 +395,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_fwd_kernel(BwdParams prm) {
                         acc = M::mma(frag_t(sB, LN, 16 * ni, k0, lr, lg), frag_t_w(sX, LP, 16 * pj, k0, lr, lg, sWx),
                                      acc);
                     st[j] = acc;
-                    lds_store4(sS + (16 * pj + lr) * LN + 16 * ni + 4 * lg, acc[0], acc[1], acc[2], acc[3]);
+                    store4(sS + (16 * pj + lr) * LN + 16 * ni + 4 * lg, acc[0], acc[1], acc[2], acc[3]);
                 }
             }
         }
@@ -402,7 +406,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_fwd_kernel(BwdParams prm) {
             float qv = 0.f;
 #pragma unroll
             for (int ni = 0; ni < NTL; ++ni) qv += sQp[ni][lane];
-            if (t0 + lane < T) prm.q[(b * T + t0 + lane) * H + h] = qv;
+            if (t0 + lane < T) prm.q[bh * T + t0 + lane] = qv;
         }
         if (blk + 1 < prm.nblk) {
             stg.store(sX, sDY, sB, sC, tid);
@@ -470,16 +474,15 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
         for (int j = 0; j < K::T_NP; ++j) {
             const int tile = w + NW * j;
             if (tile < NTL * PT) {
-                const int n0 = 16 * (tile / PT) + 4 * lg, p = 16 * (tile % PT) + lr;
-                hv[j] = *(const h4_t*)(hb0 + p * N + n0);
+                hv[j] = *(const h4_t*)(hb0 + (tile * 64 + lane) * 4);
             }
         }
     };
     auto issue = [&](int blk) {
         const int64_t t0 = (int64_t)blk * QB;
         stg.issue(xrow, xrec, xs, yrow, yrec, ys, brow, crow, brec, bs, t0, tid);
-        if (w == 1) dtn = buf_load_f32(make_rsrc(prm.dt + (b * T + t0) * H + h, (T - t0) * H * 4), lane * (int)(H * 4));
-        if (w == 0) qn = buf_load_f32(make_rsrc(prm.q + (b * T + t0) * H + h, (T - t0) * H * 4), lane * (int)(H * 4));
+        if (w == 1) dtn = buf_load_f32(make_rsrc(prm.dt + bh * T + t0, (T - t0) * 4), lane * 4);
+        if (w == 0) qn = buf_load_f32(make_rsrc(prm.q + bh * T + t0, (T - t0) * 4), lane * 4);
     };
     float qcur = 0.f;
     auto scalars = [&](int blk) {
@@ -511,7 +514,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
                 const float4 v = *(const float4*)(prm.dfinal + (bh * P + p) * N + n0);
                 kst[j] = f32x4{v.x, v.y, v.z, v.w};
             }
-            lds_store4(sK + p * LN + n0, kst[j][0], kst[j][1], kst[j][2], kst[j][3]);
+            store4(sK + p * LN + n0, kst[j][0], kst[j][1], kst[j][2], kst[j][3]);
         }
     }
 
@@ -564,8 +567,8 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
                 zc += __shfl_xor(zc, 16);
                 zc += __shfl_xor(zc, 32);
                 if (lg == 0) sCz[si][t] = zc;
-                lds_store4(sE + t * LQ + s0, ve[0], ve[1], ve[2], ve[3]);
-                lds_store4(sFm + t * LQ + s0, vf[0], vf[1], vf[2], vf[3]);
+                store4(sE + t * LQ + s0, ve[0], ve[1], ve[2], ve[3]);
+                store4(sFm + t * LQ + s0, vf[0], vf[1], vf[2], vf[3]);
             }
         }
         f32x4 a3[K::T_QP];
@@ -664,7 +667,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
                         acc = M::mma(frag_t(sC, LN, 16 * ni, k0, lr, lg), frag_t_w(sDY, LP, 16 * pj, k0, lr, lg, sDin),
                                      acc);
                     kst[j] = acc;
-                    lds_store4(sK + (16 * pj + lr) * LN + 16 * ni + 4 * lg, acc[0], acc[1], acc[2], acc[3]);
+                    store4(sK + (16 * pj + lr) * LN + 16 * ni + 4 * lg, acc[0], acc[1], acc[2], acc[3]);
                 }
             }
         }

@@ -207,15 +207,15 @@ def small_bwd(**kw):
 
 
 def test_backward_workspace_sizes():
-    # per-token scalars, each 64-token block's incoming state (bf16), per-row sums, and
+    # a per-token scalar and dt, each 64-token block's incoming state (bf16), per-row sums, and
     # per-head dB, dC when 80 heads share one group
     p = prob(ngroups=1)
     bth, bh = 4 * 4096 * 80, 4 * 80
     r = lambda v: (v + 255) // 256 * 256
     hin = bh * 64 * 64 * 128 * 2
-    assert ssd.backward_workspace_size(p) == r(bth * 4) + r(hin) + r(bh * 12) + 2 * r(bth * 128 * 2)
+    assert ssd.backward_workspace_size(p) == 2 * r(bth * 4) + r(hin) + r(bh * 12) + 2 * r(bth * 128 * 2)
     p = prob(nheads=8, ngroups=8)                 # one head per group: dB, dC written directly
-    assert ssd.backward_workspace_size(p) == r(4 * 4096 * 8 * 4) + r(32 * 64 * 64 * 128 * 2) + r(32 * 12)
+    assert ssd.backward_workspace_size(p) == 2 * r(4 * 4096 * 8 * 4) + r(32 * 64 * 64 * 128 * 2) + r(32 * 12)
     assert ssd.backward_workspace_size(prob(headdim=48)) == 0
 
 
