@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libssd_mi355x.so")
-SOURCES = ["ssd_api.cpp", "ssd_bf16.hip", "ssd_f32.hip"] + [
+SOURCES = ["ssd_api.cpp", "ssd_bwd_api.cpp", "ssd_bf16.hip", "ssd_f32.hip"] + [
     "ssd_%s_s%d_e%d_l%d.hip" % (t, sq, eu, lo) for t in ("bf16", "f32") for sq in (0, 1) for eu in (0, 1)
     for lo in (0, 1)] + ["ssd_bwd_bf16.hip", "ssd_bwd_f32.hip"]
 

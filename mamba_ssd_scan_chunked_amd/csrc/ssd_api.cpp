@@ -9,7 +9,7 @@
 #include <cstdlib>
 #include <cstdio>
 
-#include "ssd_bwd.hpp"
+#include "ssd_host.hpp"
 #include "ssd_kernels.hpp"
 #include "ssd_launch.hpp"
 
@@ -46,66 +46,6 @@ __global__ __launch_bounds__(256) void ssd_combine_kernel(CombineParams prm) {
     }
 }
 
-// dB or dC of a group = the sum of its heads' contributions (fp32 or bf16), in
-// head order, in fp32.  One thread per 4 consecutive outputs.
-__device__ inline float4 load4(const float* p) { return *(const float4*)p; }
-__device__ inline float4 load4(const __bf16* p) {
-    const bf16x4 v = *(const bf16x4*)p;
-    return make_float4((float)v[0], (float)v[1], (float)v[2], (float)v[3]);
-}
-template <typename S>
-__global__ __launch_bounds__(256) void ssd_bwd_group_sum_kernel(const S* __restrict__ src, float* __restrict__ dst,
-                                                                int64_t rows, int H, int G, int N) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;        // float4 index of dst
-    const int n4 = N / 4;
-    const int64_t total = rows * G * n4;
-    if (i >= total) return;
-    const int64_t bt = i / (G * n4);
-    const int g = (int)((i / n4) % G), c = (int)(i % n4);
-    const int hpg = H / G;
-    const S* s = src + (bt * H + (int64_t)g * hpg) * N + 4 * c;
-    float4 acc = load4(s);
-    for (int j = 1; j < hpg; ++j) {
-        const float4 v = load4(s + (int64_t)j * N);
-        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-    }
-    ((float4*)dst)[i] = acc;
-}
-
-// dt (b, T, H) -> (b, H, T): the backward kernels read each (row, head)'s step
-// sizes as one contiguous run per block.
-__global__ __launch_bounds__(256) void ssd_transpose_dt_kernel(const float* __restrict__ dt, float* __restrict__ dtT,
-                                                               int64_t batch, int64_t T, int64_t H) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // index into dtT
-    if (i >= batch * H * T) return;
-    const int64_t t = i % T, bh = i / T;
-    dtT[i] = dt[((bh / H) * T + t) * H + bh % H];
-}
-
-// Per-head scalars: sums over rows (in row order) of the reverse pass's partial sums.
-__global__ __launch_bounds__(256) void ssd_bwd_scalars_kernel(const float* __restrict__ part,
-                                                              const float* __restrict__ A_log, int64_t batch, int H,
-                                                              float* dA_log, float* ddt_bias, float* dD) {
-    const int h = blockIdx.x * 256 + threadIdx.x;
-    if (h >= H) return;
-    float a = 0.f, bb = 0.f, d = 0.f;
-    for (int64_t r = 0; r < batch; ++r) {
-        const float* q = part + (r * H + h) * 3;
-        a += q[0];
-        bb += q[1];
-        d += q[2];
-    }
-    dA_log[h] = a * -expf(A_log[h]);      // dA/dA_log = A
-    if (ddt_bias) ddt_bias[h] = bb;
-    if (dD) dD[h] = d;
-}
-
-// Fill / copy for the degenerate cases (no token): dinit = dfinal or 0, scalars 0.
-__global__ __launch_bounds__(256) void ssd_fill_kernel(float* dst, const float* src, int64_t n) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i < n) dst[i] = src ? src[i] : 0.f;
-}
-
 hipError_t launch_combine(const CombineParams& prm, hipStream_t s) {
     const int64_t threads = prm.batch * prm.H * (int64_t)prm.P * prm.N / 4;
     if (threads <= 0) return hipSuccess;
@@ -116,6 +56,8 @@ hipError_t launch_combine(const CombineParams& prm, hipStream_t s) {
 
 namespace {
 
+using namespace ssd_host;
+
 constexpr int64_t kMaxDim = int64_t(1) << 31;
 
 int block_len(const ssd_problem_t* p) {
@@ -124,14 +66,10 @@ int block_len(const ssd_problem_t* p) {
     return 0;
 }
 
-int64_t elem_size(int32_t dtype) { return dtype == SSD_DTYPE_BF16 ? 2 : 4; }
-
 int64_t nblocks(const ssd_problem_t* p) {
     const int q = block_len(p);
     return q ? (p->seqlen + q - 1) / q : 0;
 }
-
-int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
 
 // Segments per row.  With at most 128 (row, head) items, rows are split into
 // up to 512 / items segments that run in parallel (a local pass, a combine
@@ -194,79 +132,6 @@ int slices_per_workgroup(const ssd_problem_t* p, bool seq, int nseg) {
         ((p->nheads / p->ngroups) * npt) % (npt + 1) == 0)
         return npt + 1;
     return npt;
-}
-
-// Workspace of the backward pass: a per-token scalar and dt, both (b, H, T), each block's
-// incoming state (b, H, blocks, P, N) in the input type, the per-row scalar
-// sums (b, H, 3), and, when a group has more than one head, each head's dB and
-// dC contribution (b, T, H, N) in the input type before the sum over the group.
-int bwd_block(const ssd_problem_t* p);
-struct BwdWs {
-    int64_t q_off, dt_off, hin_off, part_off, dbh_off, dch_off, total;
-};
-BwdWs bwd_ws_layout(const ssd_problem_t* p) {
-    BwdWs l;
-    const int64_t bth = p->batch * p->seqlen * p->nheads, bh = p->batch * p->nheads;
-    const bool per_head = p->ngroups != p->nheads;
-    const int qb = bwd_block(p);
-    const int64_t nblk = (p->seqlen + qb - 1) / qb;
-    l.q_off = 0;
-    l.dt_off = align256(bth * 4);
-    l.hin_off = l.dt_off + align256(bth * 4);
-    l.part_off = l.hin_off + align256(bh * nblk * p->headdim * p->dstate * elem_size(p->dtype));
-    l.dbh_off = l.part_off + align256(bh * 12);
-    const int64_t hn = per_head ? align256(bth * p->dstate * elem_size(p->dtype)) : 0;
-    l.dch_off = l.dbh_off + hn;
-    l.total = l.dch_off + hn;
-    return l;
-}
-
-// Tokens per block of the backward kernels.
-int bwd_block(const ssd_problem_t* p) { return p->dtype == SSD_DTYPE_BF16 ? ssd::bwd_block_bf16() : ssd::bwd_block_f32(); }
-
-// Factor on x in the state write: 0 none, 1 the step size (Euler), 2 the exact
-// zero-order hold (exp(Delta A) - 1) / A.
-int x_scale_of(const ssd_problem_t* p) {
-    if (p->flags & SSD_FLAG_ZOH) return 2;
-    return (p->flags & SSD_FLAG_DT_SCALES_X) ? 1 : 0;
-}
-
-bool misaligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) != 0; }
-
-bool overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
-    if (!a || !b || abytes <= 0 || bbytes <= 0) return false;
-    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
-    return a0 < b0 + static_cast<uintptr_t>(bbytes) && b0 < a0 + static_cast<uintptr_t>(abytes);
-}
-
-bool log_enabled() {
-    static const bool on = [] {
-        const char* v = std::getenv("SSD_LOG");
-        return v && v[0] == '1';
-    }();
-    return on;
-}
-
-int check_device() {
-    int n = 0;
-    if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) return SSD_ERR_NO_DEVICE;
-    return SSD_OK;
-}
-
-// Byte sizes of the tensors of a problem.
-struct Sizes {
-    int64_t x, dt, bc, y, state, seq;
-};
-Sizes sizes(const ssd_problem_t* p) {
-    Sizes s;
-    const int64_t bt = p->batch * p->seqlen;
-    s.x = bt * p->nheads * p->headdim * elem_size(p->dtype);
-    s.dt = bt * p->nheads * 4;
-    s.bc = bt * p->ngroups * p->dstate * elem_size(p->dtype);
-    s.y = bt * p->nheads * p->headdim * 4;
-    s.state = p->nseqs * p->nheads * p->headdim * p->dstate * 4;
-    s.seq = bt * 4;
-    return s;
 }
 
 int check_args(const ssd_problem_t* p, const void* x, const float* dt, const float* dt_bias, const float* A_log,
@@ -467,135 +332,6 @@ int ssd_step(const ssd_problem_t* p, const void* x, const float* dt, const float
     if (log_enabled())
         std::fprintf(stderr, "[ssd] step dtype=%d P=%lld N=%lld grid=%lld -> %s\n", p->dtype, (long long)p->headdim,
                      (long long)p->dstate, (long long)grid, hipGetErrorString(e));
-    return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
-}
-
-size_t ssd_backward_workspace_size(const ssd_problem_t* p) {
-    if (ssd_validate(p) != SSD_OK) return 0;
-    return (size_t)bwd_ws_layout(p).total;
-}
-
-int ssd_backward(const ssd_problem_t* p, const void* x, const float* dt, const float* dt_bias, const float* A_log,
-                 const void* B, const void* C, const float* D, const float* init_state, const int32_t* seq_idx,
-                 const float* dy, const float* dfinal, float* dx, float* ddt, float* dA_log, float* dB, float* dC,
-                 float* dD, float* dinit, float* ddt_bias, void* workspace, size_t workspace_bytes, void* stream) {
-    const int v = ssd_validate(p);
-    if (v != SSD_OK) return v;
-    if (seq_idx) return SSD_ERR_UNSUPPORTED;                   // packed sequences: forward only
-    if (p->nseqs != p->batch) return SSD_ERR_BAD_SHAPE;
-    const int P = (int)p->headdim, N = (int)p->dstate;
-    const bool bf = p->dtype == SSD_DTYPE_BF16;
-    if (!(bf ? ssd::supported_bwd_bf16(P, N) : ssd::supported_bwd_f32(P, N))) return SSD_ERR_UNSUPPORTED;
-    const bool tokens = p->batch > 0 && p->seqlen > 0;
-    if (!A_log || !dA_log) return SSD_ERR_NULL_POINTER;
-    if (tokens && (!x || !dt || !B || !C || !dy || !dx || !ddt || !dB || !dC)) return SSD_ERR_NULL_POINTER;
-    const BwdWs wl = bwd_ws_layout(p);
-    if (wl.total > 0 && tokens && !workspace) return SSD_ERR_WORKSPACE;
-    if (tokens && static_cast<int64_t>(workspace_bytes) < wl.total) return SSD_ERR_WORKSPACE;
-    if (misaligned(x, 16) || misaligned(B, 16) || misaligned(C, 16) || misaligned(dy, 16) || misaligned(dB, 16) ||
-        misaligned(dC, 16) || misaligned(init_state, 16) || misaligned(dfinal, 16) || misaligned(dinit, 16) ||
-        misaligned(dx, 16) || misaligned(dt, 4) || misaligned(ddt, 4) || misaligned(A_log, 4) ||
-        misaligned(dA_log, 4) || misaligned(dt_bias, 4) || misaligned(ddt_bias, 4) || misaligned(D, 4) ||
-        misaligned(dD, 4) || misaligned(workspace, 256))
-        return SSD_ERR_ALIGNMENT;
-    // one block of tokens is addressed with 32-bit byte offsets
-    const int qb = bwd_block(p);
-    if (double(qb) * double(p->nheads) * double(std::max(p->headdim, p->dstate)) * 4.0 >= 2147483647.0)
-        return SSD_ERR_BAD_SHAPE;
-    const Sizes s = sizes(p);
-    const int64_t hb = p->nheads * 4;
-    const int64_t gbc = p->batch * p->seqlen * p->ngroups * p->dstate * 4;
-    const void* in_ptr[] = {x, dt, dt_bias, A_log, B, C, D, init_state, dy, dfinal, workspace};
-    const int64_t in_sz[] = {s.x, s.dt, hb, hb, s.bc, s.bc, hb, s.state, s.y, s.state, wl.total};
-    const void* out_ptr[] = {dx, ddt, dA_log, dB, dC, dD, dinit, ddt_bias};
-    const int64_t out_sz[] = {s.y, s.dt, hb, gbc, gbc, hb, s.state, hb};
-    for (int o = 0; o < 8; ++o) {
-        for (int i = 0; i < 11; ++i)
-            if (overlap(out_ptr[o], out_sz[o], in_ptr[i], in_sz[i])) return SSD_ERR_ALIAS;
-        for (int o2 = o + 1; o2 < 8; ++o2)
-            if (overlap(out_ptr[o], out_sz[o], out_ptr[o2], out_sz[o2])) return SSD_ERR_ALIAS;
-    }
-    const int d = check_device();
-    if (d != SSD_OK) return d;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    auto fill = [&](float* dst, const float* src, int64_t n) {
-        if (!dst || n <= 0) return hipSuccess;
-        hipLaunchKernelGGL(ssd::ssd_fill_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, dst, src, n);
-        return hipGetLastError();
-    };
-    hipError_t e = hipSuccess;
-    if (!tokens) {
-        // no token: final = init, so dinit = dfinal; every per-head sum is empty
-        e = fill(dA_log, nullptr, p->nheads);
-        if (e == hipSuccess) e = fill(dD, nullptr, p->nheads);
-        if (e == hipSuccess) e = fill(ddt_bias, nullptr, p->nheads);
-        if (e == hipSuccess) e = fill(dinit, dfinal, p->batch * p->nheads * p->headdim * p->dstate);
-        return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
-    }
-    char* ws = static_cast<char*>(workspace);
-    const bool per_head = p->ngroups != p->nheads;
-    ssd::BwdParams prm;
-    prm.x = x;
-    prm.dt = reinterpret_cast<float*>(ws + wl.dt_off);
-    prm.dt_bias = dt_bias;
-    prm.A_log = A_log;
-    prm.B = B;
-    prm.C = C;
-    prm.D = D;
-    prm.init = init_state;
-    prm.dy = dy;
-    prm.dfinal = dfinal;
-    prm.dx = dx;
-    prm.ddt = ddt;
-    prm.dBh = per_head ? static_cast<void*>(ws + wl.dbh_off) : static_cast<void*>(dB);
-    prm.dCh = per_head ? static_cast<void*>(ws + wl.dch_off) : static_cast<void*>(dC);
-    prm.h_bf16 = per_head && bf ? 1 : 0;
-    prm.dinit = dinit;
-    prm.q = reinterpret_cast<float*>(ws + wl.q_off);
-    prm.hin = ws + wl.hin_off;
-    prm.part = reinterpret_cast<float*>(ws + wl.part_off);
-    prm.batch = p->batch;
-    prm.T = p->seqlen;
-    prm.H = p->nheads;
-    prm.G = p->ngroups;
-    prm.HB = per_head ? p->nheads : p->ngroups;
-    prm.nblk = (int)((p->seqlen + qb - 1) / qb);
-    prm.dt_softplus = (p->flags & SSD_FLAG_DT_SOFTPLUS) ? 1 : 0;
-    prm.x_scale = x_scale_of(p);
-    const int64_t grid = p->batch * p->nheads;
-    {
-        const int64_t n = p->batch * p->nheads * p->seqlen;
-        hipLaunchKernelGGL(ssd::ssd_transpose_dt_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, dt,
-                           const_cast<float*>(prm.dt), p->batch, p->seqlen, p->nheads);
-        e = hipGetLastError();
-    }
-    if (e == hipSuccess)
-        e = bf ? ssd::launch_bwd_bf16(P, N, prm, grid, st) : ssd::launch_bwd_f32(P, N, prm, grid, st);
-    if (e == hipSuccess && per_head) {
-        const int64_t rows = p->batch * p->seqlen;
-        const int64_t n4 = rows * p->ngroups * N / 4;
-        const unsigned blocks = (unsigned)((n4 + 255) / 256);
-        if (prm.h_bf16) {
-            hipLaunchKernelGGL(ssd::ssd_bwd_group_sum_kernel<__bf16>, dim3(blocks), dim3(256), 0, st,
-                               (const __bf16*)prm.dBh, dB, rows, (int)p->nheads, (int)p->ngroups, N);
-            hipLaunchKernelGGL(ssd::ssd_bwd_group_sum_kernel<__bf16>, dim3(blocks), dim3(256), 0, st,
-                               (const __bf16*)prm.dCh, dC, rows, (int)p->nheads, (int)p->ngroups, N);
-        } else {
-            hipLaunchKernelGGL(ssd::ssd_bwd_group_sum_kernel<float>, dim3(blocks), dim3(256), 0, st,
-                               (const float*)prm.dBh, dB, rows, (int)p->nheads, (int)p->ngroups, N);
-            hipLaunchKernelGGL(ssd::ssd_bwd_group_sum_kernel<float>, dim3(blocks), dim3(256), 0, st,
-                               (const float*)prm.dCh, dC, rows, (int)p->nheads, (int)p->ngroups, N);
-        }
-        e = hipGetLastError();
-    }
-    if (e == hipSuccess) {
-        hipLaunchKernelGGL(ssd::ssd_bwd_scalars_kernel, dim3((unsigned)((p->nheads + 255) / 256)), dim3(256), 0, st,
-                           prm.part, A_log, p->batch, (int)p->nheads, dA_log, ddt_bias, dD);
-        e = hipGetLastError();
-    }
-    if (log_enabled())
-        std::fprintf(stderr, "[ssd] backward dtype=%d P=%d N=%d QB=%d grid=%lld per-head sums=%d -> %s\n", p->dtype, P, N,
-                     qb, (long long)grid, (int)per_head, hipGetErrorString(e));
     return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
 }
 
