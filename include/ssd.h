@@ -175,8 +175,8 @@ int ssd_step(const ssd_problem_t* p,
              float* state, float* y, void* stream);
 
 /* Bytes of device workspace ssd_backward needs (0 if the problem is invalid):
- * per-token scalars and dt transposed to (batch, nheads, seqlen), per-(row, head)
- * scalars, and, when a group holds more than one
+ * per-token scalars and dt transposed to (batch, nheads, seqlen), per-(sequence,
+ * head) scalars, a table of the packed sequences, and, when a group holds more than one
  * head, each head's dB and dC contribution, (batch, seqlen, nheads, dstate)
  * each in the input type (bf16 or fp32), before the fp32 sum over the group;
  * and each 64-token (bf16) or 32-token (fp32) block's incoming state,
@@ -192,19 +192,22 @@ size_t ssd_backward_workspace_size(const ssd_problem_t* p);
  * evaluated with the same block (dual) form as the forward (sections 2.2-3).
  *   inputs     as ssd_forward (same problem, flags and tensors), plus
  *   dy         (batch, seqlen, nheads, headdim)   fp32
- *   dfinal     (batch, nheads, headdim, dstate)   fp32, or NULL
+ *   dfinal     (nseqs, nheads, headdim, dstate)   fp32, or NULL
  *   outputs (fp32):
  *   dx         (batch, seqlen, nheads, headdim)
  *   ddt        (batch, seqlen, nheads)     with respect to the dt input (through softplus if flagged)
  *   dA_log     (nheads)
  *   dB, dC     (batch, seqlen, ngroups, dstate)   summed over the heads of each group
  *   dD         (nheads), or NULL
- *   dinit      (batch, nheads, headdim, dstate), or NULL (the gradient with respect to
+ *   dinit      (nseqs, nheads, headdim, dstate), or NULL (the gradient with respect to
  *              init_state, also when init_state is NULL, i.e. at a zero initial state)
  *   ddt_bias   (nheads), or NULL
  *   workspace  >= ssd_backward_workspace_size(p) bytes, 256-byte aligned
- * seq_idx must be NULL (packed sequences are supported by the forward only:
- * SSD_ERR_UNSUPPORTED).  Supported shapes: BF16 headdim 32 or 64 with dstate 64,
+ * With seq_idx (packed sequences, as in ssd_forward) dfinal and dinit are per
+ * sequence; a sequence id that does not occur gets dinit = 0.  Each (sequence,
+ * head) is walked on its own, in blocks aligned to the sequence's first token;
+ * a device-side table of the sequences is built from seq_idx first (the host
+ * never reads it).  Supported shapes: BF16 headdim 32 or 64 with dstate 64,
  * 128 or 256; F32 headdim 16, 32 or 64 with dstate 16 .. 128.  Outputs must not
  * overlap any input, the workspace or each other (SSD_ERR_ALIAS).  x, B, C, dy,
  * dx, dB, dC, init_state, dfinal and dinit need 16-byte alignment, the rest 4.

@@ -257,53 +257,56 @@ def backward_workspace_size(p: Problem) -> int:
 
 def backward(x, dt, A_log, B, C, dy, D=None, init_state=None, dfinal=None, chunk_len: int = 256,
              dt_scales_x: bool = False, dt_bias=None, dt_softplus: bool = False, zoh: bool = False,
-             workspace=None, stream=None):
+             workspace=None, stream=None, seq_idx=None, nseqs: Optional[int] = None):
     """Gradients through ``ssd_backward`` of L = <dy, y> + <dfinal, final_state> for the
     forward map of :func:`forward` with the same arguments.  Returns a dict of fp32
     tensors: dx, ddt, dA_log, dB, dC, dD, dinit, ddt_bias (dD, dinit and ddt_bias are
     the gradients at D = 0, a zero initial state and a zero bias when those were not
-    given)."""
+    given).  With ``seq_idx`` (and ``nseqs``) the rows are packed sequences as in
+    :func:`forward`; dfinal and dinit are then per sequence."""
     import torch
-    _check_tensors(x, dt, A_log, B, C, D, init_state, None, dt_bias)
+    _check_tensors(x, dt, A_log, B, C, D, init_state, seq_idx, dt_bias)
     x, dt, A_log, B, C = (t.contiguous() for t in (x, dt, A_log, B, C))
     D = D.contiguous() if D is not None else None
     dt_bias = dt_bias.contiguous() if dt_bias is not None else None
     init_state = init_state.contiguous() if init_state is not None else None
-    p = _describe(x, B, dt, A_log, chunk_len, None, None, dt_scales_x, dt_softplus, zoh)
+    seq_idx = seq_idx.contiguous() if seq_idx is not None else None
+    p = _describe(x, B, dt, A_log, chunk_len, seq_idx, nseqs, dt_scales_x, dt_softplus, zoh)
     lib = load_library()
     _check(lib.ssd_validate(ctypes.byref(p)))
     b, T, H, P = x.shape
+    ns = p.nseqs
     G, N = B.shape[2], B.shape[3]
     dev = x.device
     if tuple(dy.shape) != (b, T, H, P) or dy.dtype != torch.float32 or dy.device != dev:
         raise ValueError("dy must be an fp32 (b,T,H,P) tensor on the device of x")
     dy = dy.contiguous()
     if dfinal is not None:
-        if tuple(dfinal.shape) != (b, H, P, N) or dfinal.dtype != torch.float32 or dfinal.device != dev:
-            raise ValueError("dfinal must be an fp32 (b,H,P,N) tensor on the device of x")
+        if tuple(dfinal.shape) != (ns, H, P, N) or dfinal.dtype != torch.float32 or dfinal.device != dev:
+            raise ValueError("dfinal must be an fp32 (nseqs,H,P,N) tensor on the device of x")
         dfinal = dfinal.contiguous()
-    if init_state is not None and tuple(init_state.shape) != (b, H, P, N):
-        raise ValueError("init_state must be (b,H,P,N)")
+    if init_state is not None and tuple(init_state.shape) != (ns, H, P, N):
+        raise ValueError("init_state must be (nseqs,H,P,N)")
     f32 = dict(dtype=torch.float32, device=dev)
     out = {"dx": torch.empty((b, T, H, P), **f32), "ddt": torch.empty((b, T, H), **f32),
            "dA_log": torch.empty((H,), **f32), "dB": torch.empty((b, T, G, N), **f32),
            "dC": torch.empty((b, T, G, N), **f32), "dD": torch.empty((H,), **f32),
-           "dinit": torch.empty((b, H, P, N), **f32), "ddt_bias": torch.empty((H,), **f32)}
+           "dinit": torch.empty((ns, H, P, N), **f32), "ddt_bias": torch.empty((H,), **f32)}
     wsb = backward_workspace_size(p)
     if workspace is None and wsb > 0:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
-    backward_into(p, x, dt, dt_bias, A_log, B, C, D, init_state, dy, dfinal, out, workspace, stream)
+    backward_into(p, x, dt, dt_bias, A_log, B, C, D, init_state, dy, dfinal, out, workspace, stream, seq_idx)
     return out
 
 
 def backward_into(p: Problem, x, dt, dt_bias, A_log, B, C, D, init_state, dy, dfinal, out: dict, workspace=None,
-                  stream=None):
+                  stream=None, seq_idx=None):
     """``ssd_backward`` on caller-provided contiguous tensors; ``out`` maps dx, ddt,
     dA_log, dB, dC (required) and dD, dinit, ddt_bias (optional) to output tensors."""
     wsn = workspace.numel() if workspace is not None else 0
     g = out.get
     _check(load_library().ssd_backward(ctypes.byref(p), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A_log), _ptr(B),
-                                       _ptr(C), _ptr(D), _ptr(init_state), None, _ptr(dy), _ptr(dfinal),
+                                       _ptr(C), _ptr(D), _ptr(init_state), _ptr(seq_idx), _ptr(dy), _ptr(dfinal),
                                        _ptr(g("dx")), _ptr(g("ddt")), _ptr(g("dA_log")), _ptr(g("dB")), _ptr(g("dC")),
                                        _ptr(g("dD")), _ptr(g("dinit")), _ptr(g("ddt_bias")), _ptr(workspace), wsn,
                                        _stream_of(x.device, stream)))

@@ -146,6 +146,7 @@ int check_args(const ssd_problem_t* p, const void* x, const float* dt, const flo
     if (!empty_tokens && (!x || !dt || !B || !C || !y)) return SSD_ERR_NULL_POINTER;
     if (wsb > 0 && !ws) return SSD_ERR_WORKSPACE;
     if (!seq_idx && p->nseqs != p->batch) return SSD_ERR_BAD_SHAPE;
+    if (seq_idx && !empty_tokens && p->nseqs < 1) return SSD_ERR_BAD_SHAPE;   // ids need a sequence to name
     if (misaligned(x, 16) || misaligned(B, 16) || misaligned(C, 16) || misaligned(y, 16) || misaligned(dt, 4) ||
         misaligned(A_log, 4) || misaligned(dt_bias, 4) ||
         misaligned(D, 4) || misaligned(init, 16) || misaligned(fin, 16) || misaligned(seq_idx, 4) ||

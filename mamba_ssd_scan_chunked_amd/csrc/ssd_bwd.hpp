@@ -69,13 +69,42 @@ struct BwdParams {
     int h_bf16;       // per-head contributions stored as bf16 (bf16 inputs, HB = H > G), else fp32
     float* dinit;     // (batch, H, P, N) or null
     float* q;         // (batch, H, T) workspace: qoff
-    void* hin;        // (batch, H, nblk, P * N) workspace: each block's incoming state (input type), in
+    void* hin;        // (H, hin_blocks, P * N) workspace: each block's incoming state (input type), in
                       // the order the state tiles are held: tile, lane, 4 values
     float* part;      // (batch, H, 3) workspace: per-row sums for dA (natural A), ddt_bias, dD
     int64_t batch, T, H, G, HB;
-    int nblk;
+    int nblk;                 // blocks per row
+    int64_t hin_blocks;       // block slots per head in hin
+    // Packed sequences: (row, first token, end token, first hin slot) of each
+    // sequence, or null when every row is one sequence.  A workgroup walks one
+    // (sequence, head), with its blocks aligned to the sequence's first token.
+    const int64_t* seqtab;
     int dt_softplus, x_scale;
 };
+
+// The token range a workgroup walks: sequence kq of the packed rows, or row kq.
+// Values are clamped, so inconsistent sequence ids stay memory-safe.
+struct ItemRange {
+    int64_t b, s0, len, hslot;
+};
+template <int QB>
+__device__ inline ItemRange item_range(const BwdParams& prm, int64_t kq) {
+    ItemRange r;
+    if (!prm.seqtab) {
+        r.b = kq;
+        r.s0 = 0;
+        r.len = prm.T;
+        r.hslot = kq * prm.nblk;
+    } else {
+        const int64_t* e = prm.seqtab + 4 * kq;
+        r.b = min(max(e[0], (int64_t)0), prm.batch - 1);
+        r.s0 = min(max(e[1], (int64_t)0), prm.T);
+        r.len = min(max(e[2] - r.s0, (int64_t)0), prm.T - r.s0);
+        r.hslot = max(e[3], (int64_t)0);
+        if (r.hslot + (r.len + QB - 1) / QB > prm.hin_blocks) r.len = 0;
+    }
+    return r;
+}
 
 // Fragment of an operand stored with K contiguous: row `row`, K values
 // k0 + KPL*(l/16) .. (bf16: one 16-byte read; fp32: one value).
@@ -254,15 +283,21 @@ __global__ __launch_bounds__(512) void ssd_bwd_fwd_kernel(BwdParams prm) {
     __shared__ float sCend;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
-    const int64_t bh = blockIdx.x, b = bh / prm.H, h = bh % prm.H;
-    const int64_t H = prm.H, G = prm.G, T = prm.T, HB = prm.HB;
+    // item: (sequence or row kq, head h); tokens s0 .. s0+len-1 of row b
+    const int64_t H = prm.H, G = prm.G, HB = prm.HB;
+    const int64_t kq = blockIdx.x / H, h = blockIdx.x % H;
+    const ItemRange ir = item_range<QB>(prm, kq);
+    const int64_t b = ir.b, T = ir.len, tb = b * prm.T + ir.s0;   // T: this item's tokens; tb: its first token
+    const int64_t bh = kq * H + h;          // (sequence, head): init, dfinal, dinit, per-item sums
+    const int64_t rh = b * H + h;           // (row, head): the token-contiguous dt and qoff runs
+    const int nblk = (int)((T + QB - 1) / QB);
     const int64_t g = h / (H / G), hb = HB == H ? h : g;
     constexpr int SZ = K::SZ;
     const int xs = (int)(H * P * SZ), ys = (int)(H * P * 4), bs = (int)(G * N * SZ);
-    const char* xrow = (const char*)prm.x + (b * T * H + h) * P * SZ;
-    const char* yrow = (const char*)prm.dy + (b * T * H + h) * P * 4;
-    const char* brow = (const char*)prm.B + (b * T * G + g) * N * SZ;
-    const char* crow = (const char*)prm.C + (b * T * G + g) * N * SZ;
+    const char* xrow = (const char*)prm.x + (tb * H + h) * P * SZ;
+    const char* yrow = (const char*)prm.dy + (tb * H + h) * P * 4;
+    const char* brow = (const char*)prm.B + (tb * G + g) * N * SZ;
+    const char* crow = (const char*)prm.C + (tb * G + g) * N * SZ;
     const int64_t xrec = T * xs, yrec = T * ys, brec = T * bs;
     const float Anat = -expf(prm.A_log[h]);
     cum_t A2;
@@ -275,7 +310,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_fwd_kernel(BwdParams prm) {
     auto issue = [&](int blk) {
         const int64_t t0 = (int64_t)blk * QB;
         stg.issue(xrow, xrec, xs, yrow, yrec, ys, brow, crow, brec, bs, t0, tid);
-        if (w == 1) dtn = buf_load_f32(make_rsrc(prm.dt + bh * T + t0, (T - t0) * 4), lane * 4);
+        if (w == 1) dtn = buf_load_f32(make_rsrc(prm.dt + rh * prm.T + ir.s0 + t0, (T - t0) * 4), lane * 4);
     };
     // per-token scalars of a block (wave 1, lane = token)
     auto scalars = [&](int blk) {
@@ -309,18 +344,20 @@ __global__ __launch_bounds__(512) void ssd_bwd_fwd_kernel(BwdParams prm) {
         }
     }
 
-    issue(0);
-    stg.store(sX, sDY, sB, sC, tid);
-    if (w == 1) scalars(0);
-    block_sync_lds();
+    if (nblk > 0) {                       // (uniform over the workgroup)
+        issue(0);
+        stg.store(sX, sDY, sB, sC, tid);
+        if (w == 1) scalars(0);
+        block_sync_lds();
+    }
 
-    for (int blk = 0; blk < prm.nblk; ++blk) {
+    for (int blk = 0; blk < nblk; ++blk) {
         const int64_t t0 = (int64_t)blk * QB;
-        if (blk + 1 < prm.nblk) issue(blk + 1);
+        if (blk + 1 < nblk) issue(blk + 1);
 
         // ---- phase A: the incoming state to the workspace; W^T tiles (rows s, columns t), and dy H_in
         {
-            TI* hb0 = (TI*)prm.hin + (bh * prm.nblk + blk) * (int64_t)(P * N);
+            TI* hb0 = (TI*)prm.hin + (h * prm.hin_blocks + ir.hslot + blk) * (int64_t)(P * N);
 #pragma unroll
             for (int j = 0; j < K::T_NP; ++j) {
                 const int tile = w + NW * j;
@@ -364,7 +401,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_fwd_kernel(BwdParams prm) {
         // ---- phase B: dC^h = W B + 2^cum dy H_in, q partial sums; state update
         {
             const int es = prm.h_bf16 ? 2 : 4;
-            const rsrc_t rdc = make_rsrc((char*)prm.dCh + ((b * T + t0) * HB + hb) * N * es, (T - t0) * HB * N * es);
+            const rsrc_t rdc = make_rsrc((char*)prm.dCh + ((tb + t0) * HB + hb) * N * es, (T - t0) * HB * N * es);
 #pragma unroll
             for (int j = 0; j < K::T_QN; ++j) {
                 const int tile = w + NW * j;
@@ -406,9 +443,9 @@ __global__ __launch_bounds__(512) void ssd_bwd_fwd_kernel(BwdParams prm) {
             float qv = 0.f;
 #pragma unroll
             for (int ni = 0; ni < NTL; ++ni) qv += sQp[ni][lane];
-            if (t0 + lane < T) prm.q[bh * T + t0 + lane] = qv;
+            if (t0 + lane < T) prm.q[rh * prm.T + ir.s0 + t0 + lane] = qv;
         }
-        if (blk + 1 < prm.nblk) {
+        if (blk + 1 < nblk) {
             stg.store(sX, sDY, sB, sC, tid);
             if (w == 1) scalars(blk + 1);
         }
@@ -447,15 +484,21 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
     __shared__ float sCend;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
-    const int64_t bh = blockIdx.x, b = bh / prm.H, h = bh % prm.H;
-    const int64_t H = prm.H, G = prm.G, T = prm.T, HB = prm.HB;
+    // item: (sequence or row kq, head h); tokens s0 .. s0+len-1 of row b
+    const int64_t H = prm.H, G = prm.G, HB = prm.HB;
+    const int64_t kq = blockIdx.x / H, h = blockIdx.x % H;
+    const ItemRange ir = item_range<QB>(prm, kq);
+    const int64_t b = ir.b, T = ir.len, tb = b * prm.T + ir.s0;   // T: this item's tokens; tb: its first token
+    const int64_t bh = kq * H + h;          // (sequence, head): init, dfinal, dinit, per-item sums
+    const int64_t rh = b * H + h;           // (row, head): the token-contiguous dt and qoff runs
+    const int nblk = (int)((T + QB - 1) / QB);
     const int64_t g = h / (H / G), hb = HB == H ? h : g;
     constexpr int SZ = K::SZ;
     const int xs = (int)(H * P * SZ), ys = (int)(H * P * 4), bs = (int)(G * N * SZ);
-    const char* xrow = (const char*)prm.x + (b * T * H + h) * P * SZ;
-    const char* yrow = (const char*)prm.dy + (b * T * H + h) * P * 4;
-    const char* brow = (const char*)prm.B + (b * T * G + g) * N * SZ;
-    const char* crow = (const char*)prm.C + (b * T * G + g) * N * SZ;
+    const char* xrow = (const char*)prm.x + (tb * H + h) * P * SZ;
+    const char* yrow = (const char*)prm.dy + (tb * H + h) * P * 4;
+    const char* brow = (const char*)prm.B + (tb * G + g) * N * SZ;
+    const char* crow = (const char*)prm.C + (tb * G + g) * N * SZ;
     const int64_t xrec = T * xs, yrec = T * ys, brec = T * bs;
     const float Anat = -expf(prm.A_log[h]);
     cum_t A2;
@@ -469,7 +512,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
     // the block's incoming state at this lane's state-tile positions (4 values per tile)
     typedef typename std::conditional<K::SZ == 2, uint2, uint4>::type h4_t;
     auto load_hin = [&](int blk, h4_t (&hv)[K::T_NP]) {
-        const TI* hb0 = (const TI*)prm.hin + (bh * prm.nblk + blk) * (int64_t)(P * N);
+        const TI* hb0 = (const TI*)prm.hin + (h * prm.hin_blocks + ir.hslot + blk) * (int64_t)(P * N);
 #pragma unroll
         for (int j = 0; j < K::T_NP; ++j) {
             const int tile = w + NW * j;
@@ -481,8 +524,8 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
     auto issue = [&](int blk) {
         const int64_t t0 = (int64_t)blk * QB;
         stg.issue(xrow, xrec, xs, yrow, yrec, ys, brow, crow, brec, bs, t0, tid);
-        if (w == 1) dtn = buf_load_f32(make_rsrc(prm.dt + bh * T + t0, (T - t0) * 4), lane * 4);
-        if (w == 0) qn = buf_load_f32(make_rsrc(prm.q + bh * T + t0, (T - t0) * 4), lane * 4);
+        if (w == 1) dtn = buf_load_f32(make_rsrc(prm.dt + rh * prm.T + ir.s0 + t0, (T - t0) * 4), lane * 4);
+        if (w == 0) qn = buf_load_f32(make_rsrc(prm.q + rh * prm.T + ir.s0 + t0, (T - t0) * 4), lane * 4);
     };
     float qcur = 0.f;
     auto scalars = [&](int blk) {
@@ -523,13 +566,15 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
     acc_t sum_dA = 0, sum_bias = 0, sum_D = 0;
     const int fdmode = prm.x_scale;
 
-    issue(prm.nblk - 1);
-    stg.store(sX, sDY, sB, sC, tid);
-    if (w == 1) scalars(prm.nblk - 1);
-    qcur = qn;
-    block_sync_lds();
+    if (nblk > 0) {                       // (uniform over the workgroup)
+        issue(nblk - 1);
+        stg.store(sX, sDY, sB, sC, tid);
+        if (w == 1) scalars(nblk - 1);
+        qcur = qn;
+        block_sync_lds();
+    }
 
-    for (int blk = prm.nblk - 1; blk >= 0; --blk) {
+    for (int blk = nblk - 1; blk >= 0; --blk) {
         const int64_t t0 = (int64_t)blk * QB;
         h4_t hcur[K::T_NP];
         load_hin(blk, hcur);              // used after this block's first products
@@ -614,7 +659,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
 
         // ---- phase B: G B (-> dx, u, dy.x), dB^h, K update
         {
-            const rsrc_t rdx = make_rsrc(prm.dx + ((b * T + t0) * H + h) * P, (T - t0) * H * P * 4);
+            const rsrc_t rdx = make_rsrc(prm.dx + ((tb + t0) * H + h) * P, (T - t0) * H * P * 4);
 #pragma unroll
             for (int j = 0; j < K::T_QP; ++j) {
                 const int tile = w + NW * j;
@@ -641,7 +686,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
                 }
             }
             const int es = prm.h_bf16 ? 2 : 4;
-            const rsrc_t rdb = make_rsrc((char*)prm.dBh + ((b * T + t0) * HB + hb) * N * es, (T - t0) * HB * N * es);
+            const rsrc_t rdb = make_rsrc((char*)prm.dBh + ((tb + t0) * HB + hb) * N * es, (T - t0) * HB * N * es);
 #pragma unroll
             for (int j = 0; j < K::T_QN; ++j) {
                 const int tile = w + NW * j;
@@ -716,7 +761,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
                 const float fA = fdmode == 2 ? (d * Anat * a - a + 1.f) / (Anat * Anat) : 0.f;
                 float gdt = (float)dl * Anat + u * fD;
                 if (prm.dt_softplus) gdt *= 1.f / (1.f + expf(-pre_r));
-                prm.ddt[(b * T + t0 + lane) * H + h] = gdt;
+                prm.ddt[(tb + t0 + lane) * H + h] = gdt;
                 sum_dA += dl * (acc_t)d + (acc_t)(u * fA);
                 sum_bias += (acc_t)gdt;
                 sum_D += (acc_t)dd;
@@ -730,7 +775,12 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
         block_sync_lds();
     }
 
-    // dinit = a_0 G_0 = the K that leaves the first block
+    // dinit = a_0 G_0 = the K that leaves the first block (with no token: dfinal for a
+    // row, whose final state is its initial state; 0 for a sequence that does not occur)
+    if (prm.seqtab && nblk == 0) {
+#pragma unroll
+        for (int j = 0; j < K::T_NP; ++j) kst[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     if (prm.dinit) {
 #pragma unroll
         for (int j = 0; j < K::T_NP; ++j) {

@@ -50,7 +50,7 @@ __global__ __launch_bounds__(256) void ssd_transpose_dt_kernel(const float* __re
     dtT[i] = dt[((bh / H) * T + t) * H + bh % H];
 }
 
-// Per-head scalars: sums over rows (in row order) of the reverse pass's partial sums.
+// Per-head scalars: sums over rows or packed sequences (in order) of the reverse pass's partial sums.
 __global__ __launch_bounds__(256) void ssd_bwd_scalars_kernel(const float* __restrict__ part,
                                                               const float* __restrict__ A_log, int64_t batch, int H,
                                                               float* dA_log, float* ddt_bias, float* dD) {
@@ -68,6 +68,45 @@ __global__ __launch_bounds__(256) void ssd_bwd_scalars_kernel(const float* __res
     if (dD) dD[h] = d;
 }
 
+// The table of packed sequences: each token that starts or ends its sequence
+// writes the sequence's row and first or end token (ids clamped to 0..nseqs-1;
+// ids that are not nondecreasing or repeat across rows give meaningless but
+// in-range entries).  Entries are (row, first token, end token, first hin slot).
+__global__ __launch_bounds__(256) void ssd_seq_table_kernel(const int32_t* __restrict__ seq, int64_t batch, int64_t T,
+                                                            int64_t nseqs, int64_t* __restrict__ tab) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= batch * T) return;
+    const int64_t r = i / T, t = i % T;
+    auto id = [&](int64_t u) {
+        const int64_t v = seq[r * T + u];
+        return v < 0 ? (int64_t)0 : (v >= nseqs ? nseqs - 1 : v);
+    };
+    const int64_t k = id(t);
+    if (t == 0 || id(t - 1) != k) {
+        tab[4 * k + 0] = r;
+        tab[4 * k + 1] = t;
+    }
+    if (t == T - 1 || id(t + 1) != k) tab[4 * k + 2] = t + 1;
+}
+// First hin slot of each sequence: the running count of blocks of the sequences
+// before it (a sequence that would not fit the slots is given no tokens).
+__global__ __launch_bounds__(64) void ssd_seq_slots_kernel(int64_t* tab, int64_t nseqs, int64_t qb, int64_t cap) {
+    if (threadIdx.x != 0) return;
+    int64_t off = 0;
+    for (int64_t k = 0; k < nseqs; ++k) {
+        int64_t* e = tab + 4 * k;
+        const int64_t len = e[2] > e[1] ? e[2] - e[1] : 0;
+        const int64_t nb = (len + qb - 1) / qb;
+        if (off + nb > cap) {
+            e[2] = e[1];
+            e[3] = 0;
+            continue;
+        }
+        e[3] = off;
+        off += nb;
+    }
+}
+
 // Fill / copy for the degenerate cases (no token): dinit = dfinal or 0, scalars 0.
 __global__ __launch_bounds__(256) void ssd_fill_kernel(float* dst, const float* src, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -83,24 +122,30 @@ using namespace ssd_host;
 // Tokens per block of the backward kernels.
 int bwd_block(const ssd_problem_t* p) { return p->dtype == SSD_DTYPE_BF16 ? ssd::bwd_block_bf16() : ssd::bwd_block_f32(); }
 
-// Workspace of the backward pass: a per-token scalar and dt, both (b, H, T), each block's
-// incoming state (b, H, blocks, P, N) in the input type, the per-row scalar
-// sums (b, H, 3), and, when a group has more than one head, each head's dB and
-// dC contribution (b, T, H, N) in the input type before the sum over the group.
+// Workspace of the backward pass: a per-token scalar and dt, both (b, H, T); each
+// block's incoming state in the input type, (H, slots, P, N) with
+// slots = b * blocks per row + nseqs (enough for any split of the rows into
+// sequences, each sequence starting a new block); the per-sequence scalar sums
+// (nseqs, H, 3); the table of packed sequences (nseqs x 4 int64); and, when a
+// group has more than one head, each head's dB and dC contribution (b, T, H, N)
+// in the input type before the sum over the group.
 struct BwdWs {
-    int64_t q_off, dt_off, hin_off, part_off, dbh_off, dch_off, total;
+    int64_t q_off, dt_off, hin_off, part_off, tab_off, dbh_off, dch_off, total, hin_slots;
 };
 BwdWs bwd_ws_layout(const ssd_problem_t* p) {
     BwdWs l;
-    const int64_t bth = p->batch * p->seqlen * p->nheads, bh = p->batch * p->nheads;
+    const int64_t bth = p->batch * p->seqlen * p->nheads;
+    const int64_t items = std::max(p->nseqs, p->batch);
     const bool per_head = p->ngroups != p->nheads;
     const int qb = bwd_block(p);
     const int64_t nblk = (p->seqlen + qb - 1) / qb;
+    l.hin_slots = p->batch * nblk + p->nseqs;
     l.q_off = 0;
     l.dt_off = align256(bth * 4);
     l.hin_off = l.dt_off + align256(bth * 4);
-    l.part_off = l.hin_off + align256(bh * nblk * p->headdim * p->dstate * elem_size(p->dtype));
-    l.dbh_off = l.part_off + align256(bh * 12);
+    l.part_off = l.hin_off + align256(p->nheads * l.hin_slots * p->headdim * p->dstate * elem_size(p->dtype));
+    l.tab_off = l.part_off + align256(items * p->nheads * 12);
+    l.dbh_off = l.tab_off + align256(p->nseqs * 32);
     const int64_t hn = per_head ? align256(bth * p->dstate * elem_size(p->dtype)) : 0;
     l.dch_off = l.dbh_off + hn;
     l.total = l.dch_off + hn;
@@ -122,8 +167,8 @@ int ssd_backward(const ssd_problem_t* p, const void* x, const float* dt, const f
                  float* dD, float* dinit, float* ddt_bias, void* workspace, size_t workspace_bytes, void* stream) {
     const int v = ssd_validate(p);
     if (v != SSD_OK) return v;
-    if (seq_idx) return SSD_ERR_UNSUPPORTED;                   // packed sequences: forward only
-    if (p->nseqs != p->batch) return SSD_ERR_BAD_SHAPE;
+    if (!seq_idx && p->nseqs != p->batch) return SSD_ERR_BAD_SHAPE;
+    if (seq_idx && p->batch > 0 && p->seqlen > 0 && p->nseqs < 1) return SSD_ERR_BAD_SHAPE;
     const int P = (int)p->headdim, N = (int)p->dstate;
     const bool bf = p->dtype == SSD_DTYPE_BF16;
     if (!(bf ? ssd::supported_bwd_bf16(P, N) : ssd::supported_bwd_f32(P, N))) return SSD_ERR_UNSUPPORTED;
@@ -137,7 +182,7 @@ int ssd_backward(const ssd_problem_t* p, const void* x, const float* dt, const f
         misaligned(dC, 16) || misaligned(init_state, 16) || misaligned(dfinal, 16) || misaligned(dinit, 16) ||
         misaligned(dx, 16) || misaligned(dt, 4) || misaligned(ddt, 4) || misaligned(A_log, 4) ||
         misaligned(dA_log, 4) || misaligned(dt_bias, 4) || misaligned(ddt_bias, 4) || misaligned(D, 4) ||
-        misaligned(dD, 4) || misaligned(workspace, 256))
+        misaligned(dD, 4) || misaligned(seq_idx, 4) || misaligned(workspace, 256))
         return SSD_ERR_ALIGNMENT;
     // one block of tokens is addressed with 32-bit byte offsets
     const int qb = bwd_block(p);
@@ -146,12 +191,12 @@ int ssd_backward(const ssd_problem_t* p, const void* x, const float* dt, const f
     const Sizes s = sizes(p);
     const int64_t hb = p->nheads * 4;
     const int64_t gbc = p->batch * p->seqlen * p->ngroups * p->dstate * 4;
-    const void* in_ptr[] = {x, dt, dt_bias, A_log, B, C, D, init_state, dy, dfinal, workspace};
-    const int64_t in_sz[] = {s.x, s.dt, hb, hb, s.bc, s.bc, hb, s.state, s.y, s.state, wl.total};
+    const void* in_ptr[] = {x, dt, dt_bias, A_log, B, C, D, init_state, dy, dfinal, workspace, seq_idx};
+    const int64_t in_sz[] = {s.x, s.dt, hb, hb, s.bc, s.bc, hb, s.state, s.y, s.state, wl.total, s.seq};
     const void* out_ptr[] = {dx, ddt, dA_log, dB, dC, dD, dinit, ddt_bias};
     const int64_t out_sz[] = {s.y, s.dt, hb, gbc, gbc, hb, s.state, hb};
     for (int o = 0; o < 8; ++o) {
-        for (int i = 0; i < 11; ++i)
+        for (int i = 0; i < 12; ++i)
             if (overlap(out_ptr[o], out_sz[o], in_ptr[i], in_sz[i])) return SSD_ERR_ALIAS;
         for (int o2 = o + 1; o2 < 8; ++o2)
             if (overlap(out_ptr[o], out_sz[o], out_ptr[o2], out_sz[o2])) return SSD_ERR_ALIAS;
@@ -170,7 +215,8 @@ int ssd_backward(const ssd_problem_t* p, const void* x, const float* dt, const f
         e = fill(dA_log, nullptr, p->nheads);
         if (e == hipSuccess) e = fill(dD, nullptr, p->nheads);
         if (e == hipSuccess) e = fill(ddt_bias, nullptr, p->nheads);
-        if (e == hipSuccess) e = fill(dinit, dfinal, p->batch * p->nheads * p->headdim * p->dstate);
+        // (a packed sequence that does not occur has no influence: dinit = 0)
+        if (e == hipSuccess) e = fill(dinit, seq_idx ? nullptr : dfinal, p->nseqs * p->nheads * p->headdim * p->dstate);
         return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
     }
     char* ws = static_cast<char*>(workspace);
@@ -201,10 +247,25 @@ int ssd_backward(const ssd_problem_t* p, const void* x, const float* dt, const f
     prm.G = p->ngroups;
     prm.HB = per_head ? p->nheads : p->ngroups;
     prm.nblk = (int)((p->seqlen + qb - 1) / qb);
+    prm.hin_blocks = wl.hin_slots;
+    prm.seqtab = seq_idx ? reinterpret_cast<const int64_t*>(ws + wl.tab_off) : nullptr;
     prm.dt_softplus = (p->flags & SSD_FLAG_DT_SOFTPLUS) ? 1 : 0;
     prm.x_scale = x_scale_of(p);
-    const int64_t grid = p->batch * p->nheads;
-    {
+    const int64_t items = seq_idx ? p->nseqs : p->batch;     // sequences, or rows
+    const int64_t grid = items * p->nheads;
+    if (seq_idx) {
+        int64_t* tab = reinterpret_cast<int64_t*>(ws + wl.tab_off);
+        e = fill(reinterpret_cast<float*>(tab), nullptr, p->nseqs * 8);
+        const int64_t n = p->batch * p->seqlen;
+        if (e == hipSuccess) {
+            hipLaunchKernelGGL(ssd::ssd_seq_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, seq_idx,
+                               p->batch, p->seqlen, p->nseqs, tab);
+            hipLaunchKernelGGL(ssd::ssd_seq_slots_kernel, dim3(1), dim3(64), 0, st, tab, p->nseqs, (int64_t)qb,
+                               wl.hin_slots);
+            e = hipGetLastError();
+        }
+    }
+    if (e == hipSuccess) {
         const int64_t n = p->batch * p->nheads * p->seqlen;
         hipLaunchKernelGGL(ssd::ssd_transpose_dt_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, dt,
                            const_cast<float*>(prm.dt), p->batch, p->seqlen, p->nheads);
@@ -231,7 +292,7 @@ int ssd_backward(const ssd_problem_t* p, const void* x, const float* dt, const f
     }
     if (e == hipSuccess) {
         hipLaunchKernelGGL(ssd::ssd_bwd_scalars_kernel, dim3((unsigned)((p->nheads + 255) / 256)), dim3(256), 0, st,
-                           prm.part, A_log, p->batch, (int)p->nheads, dA_log, ddt_bias, dD);
+                           prm.part, A_log, items, (int)p->nheads, dA_log, ddt_bias, dD);
         e = hipGetLastError();
     }
     if (log_enabled())

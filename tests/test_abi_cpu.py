@@ -207,20 +207,21 @@ def small_bwd(**kw):
 
 
 def test_backward_workspace_sizes():
-    # a per-token scalar and dt, each 64-token block's incoming state (bf16), per-row sums, and
-    # per-head dB, dC when 80 heads share one group
+    # a per-token scalar and dt, each 64-token block's incoming state (bf16), per-row sums, the
+    # sequence table, and per-head dB, dC when 80 heads share one group
     p = prob(ngroups=1)
     bth, bh = 4 * 4096 * 80, 4 * 80
     r = lambda v: (v + 255) // 256 * 256
-    hin = bh * 64 * 64 * 128 * 2
-    assert ssd.backward_workspace_size(p) == 2 * r(bth * 4) + r(hin) + r(bh * 12) + 2 * r(bth * 128 * 2)
+    hin = 80 * (4 * 64 + 4) * 64 * 128 * 2      # (H, b * blocks + nseqs slots, P, N)
+    assert ssd.backward_workspace_size(p) == (2 * r(bth * 4) + r(hin) + r(bh * 12) + r(4 * 32)
+                                              + 2 * r(bth * 128 * 2))
     p = prob(nheads=8, ngroups=8)                 # one head per group: dB, dC written directly
-    assert ssd.backward_workspace_size(p) == 2 * r(4 * 4096 * 8 * 4) + r(32 * 64 * 64 * 128 * 2) + r(32 * 12)
+    assert ssd.backward_workspace_size(p) == (2 * r(4 * 4096 * 8 * 4) + r(8 * 260 * 64 * 128 * 2) + r(32 * 12)
+                                              + r(4 * 32))
     assert ssd.backward_workspace_size(prob(headdim=48)) == 0
 
 
 def test_backward_rejects_bad_arguments():
-    assert _backward(small_bwd(), seq=A + 0x7000000) == 3               # packed sequences: forward only
     assert _backward(small_bwd(dtype=ssd.DTYPE_F32, dstate=256)) == 3    # no fp32 N = 256 build
     for n in ("x", "dt", "A_log", "B", "C", "dy", "dx", "ddt", "dA_log", "dB", "dC"):
         assert _backward(small_bwd(), **{n: None}) == 1, n
@@ -232,6 +233,14 @@ def test_backward_rejects_bad_arguments():
     assert _backward(small_bwd(), dB=A + 0x1A000000) == 6                # dB on top of ddt
     assert _backward(small_bwd(), dinit=A + 0x14000000) == 6             # dinit on top of dy
     assert _backward(small_bwd(), dA_log=A + 0x60000000) == 6            # dA_log in the workspace
+
+
+def test_packed_sequences_need_at_least_one_sequence():
+    # seq_idx with tokens but nseqs = 0: no sequence to clamp the ids to
+    p = small_bwd(nseqs=0)
+    assert _backward(p, seq=A + 0x8000000) == 2
+    q = prob(batch=1, seqlen=64, nheads=2, headdim=32, dstate=64, chunk_len=64, nseqs=0)
+    assert _forward(q, seq=A + 0x8000000) == 2
 
 
 def test_backward_without_device_reports_no_device():

@@ -30,22 +30,25 @@ def announce(msg):
 def cotangents(prob, seed):
     b, T, H, P = prob["x"].shape
     N = prob["B"].shape[3]
+    ns = prob["nseqs"]
     rng = np.random.default_rng(seed)
     f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
-    return f32(rng.standard_normal((b, T, H, P))), f32(rng.standard_normal((b, H, P, N)))
+    return f32(rng.standard_normal((b, T, H, P))), f32(rng.standard_normal((ns, H, P, N)))
 
 
 def run_both(prob, dy, dfinal, *, dt_bias=None, dt_softplus=False, zoh=False, dt_scales_x=False, workers=0):
     import mamba_ssd_scan_chunked_amd as ssd
     d = to_device(prob)
+    packed = prob["seq_idx"] is not None
     g = ssd.backward(d["x"], d["dt"], d["A_log"], d["B"], d["C"], dy.cuda(), D=d["D"], init_state=d["init"],
                      dfinal=dfinal.cuda() if dfinal is not None else None, dt_scales_x=dt_scales_x,
-                     dt_bias=dt_bias.cuda() if dt_bias is not None else None, dt_softplus=dt_softplus, zoh=zoh)
+                     dt_bias=dt_bias.cuda() if dt_bias is not None else None, dt_softplus=dt_softplus, zoh=zoh,
+                     seq_idx=d["seq_idx"], nseqs=prob["nseqs"] if packed else None)
     torch.cuda.synchronize()
     got = {k: v.cpu().double().numpy() for k, v in g.items()}
     ref = oracle.gradients(prob["x"], prob["dt"], prob["A_log"], prob["B"], prob["C"], dy, prob["D"], prob["init"],
-                           dfinal, dt_scales_x=dt_scales_x, dt_bias=dt_bias, dt_softplus=dt_softplus, zoh=zoh,
-                           nthreads=workers)
+                           dfinal, prob["seq_idx"], prob["nseqs"] if packed else None, dt_scales_x=dt_scales_x,
+                           dt_bias=dt_bias, dt_softplus=dt_softplus, zoh=zoh, nthreads=workers)
     return got, ref
 
 
@@ -137,6 +140,51 @@ def test_backward_is_deterministic():
     torch.cuda.synchronize()
     for k in OUTS:
         assert torch.equal(runs[0][k], runs[1][k]), k
+
+
+PACKED = [
+    # dtype, b, T, H, P, N, G, sequence lengths per row (starts at, inside and across block edges; length 1)
+    ("bf16", 2, 300, 4, 64, 128, 2, [[100, 1, 199], [64, 236]]),
+    ("bf16", 1, 257, 2, 32, 64, 1, [[1, 63, 64, 128, 1]]),
+    ("f32", 1, 200, 2, 64, 64, 1, [[37, 64, 99]]),
+    ("f32", 2, 96, 3, 16, 32, 3, [[32, 32, 32], [95, 1]]),
+]
+
+
+@pytest.mark.parametrize("case", PACKED, ids=lambda c: "%s-b%d-T%d-H%d-P%d-N%d-G%d" % c[:7])
+def test_backward_packed_sequences(case):
+    dt, b, T, H, P, N, G, lens = case
+    prob = si.make_problem(b, T, H, P, N, G, dtype=dt, seed=T + 3, d_skip=True, init_std=0.5, seqlens=lens)
+    dy, dfinal = cotangents(prob, T + 4)
+    announce("backward packed %s" % (case[:7],))
+    got, ref = run_both(prob, dy, dfinal)
+    check(got, ref, TOL[dt])
+
+
+def test_backward_packed_with_absent_sequence_ids():
+    """Ids 1, 2 and 3 of 0..4 never occur: their dinit is 0; the others as the oracle."""
+    prob = si.make_problem(1, 200, 2, 64, 128, 1, dtype="bf16", seed=33, d_skip=True, init_std=0.5,
+                           seqlens=[[80, 120]])
+    seq = prob["seq_idx"].clone()
+    seq[seq == 1] = 4                          # sequences 0 and 4; 1, 2, 3 absent
+    prob = dict(prob, seq_idx=seq, nseqs=5,
+                init=torch.from_numpy(np.random.default_rng(34).normal(0, 0.5, (5, 2, 64, 128)).astype(np.float32)))
+    dy, dfinal = cotangents(prob, 35)
+    announce("backward packed, absent ids")
+    got, ref = run_both(prob, dy, dfinal)
+    check(got, ref, TOL["bf16"])
+    assert not got["dinit"][1:4].any()
+
+
+def test_backward_packed_workload():
+    """The packed workload at full size: 16 sequences (minimum length 64) in one row of
+    8192 tokens, 48 heads in 8 groups, init states, every output against the oracle."""
+    w = si.WORKLOADS["packed_bf16"]
+    prob = si.make_workload(w)
+    dy, dfinal = cotangents(prob, 37)
+    announce("backward packed workload")
+    got, ref = run_both(prob, dy, dfinal)
+    check(got, ref, TOL["bf16"])
 
 
 def test_backward_headline_shape():
