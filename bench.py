@@ -53,10 +53,13 @@ def backward_algorithmic_bytes(w, init_nonzero: bool) -> int:
     dx, ddt, dB, dC, dinit and the per-head gradients written once."""
     sx = 2 if w.dtype == "bf16" else 4
     b, T, H, P, N, G = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups
-    reads = sx * (b * T * H * P + 2 * b * T * G * N) + 4 * b * T * H + 8 * H + 4 * b * T * H * P + 4 * b * H * P * N
+    ns = w.nseqs_packed * b if w.nseqs_packed else b
+    reads = sx * (b * T * H * P + 2 * b * T * G * N) + 4 * b * T * H + 8 * H + 4 * b * T * H * P + 4 * ns * H * P * N
     if init_nonzero:
-        reads += 4 * b * H * P * N
-    writes = 4 * b * T * H * P + 4 * b * T * H + 2 * 4 * b * T * G * N + 4 * b * H * P * N + 12 * H
+        reads += 4 * ns * H * P * N
+    if w.nseqs_packed:
+        reads += 4 * b * T      # seq_idx
+    writes = 4 * b * T * H * P + 4 * b * T * H + 2 * 4 * b * T * G * N + 4 * ns * H * P * N + 12 * H
     return reads + writes
 
 
@@ -66,26 +69,25 @@ def backward_leg(w, prob, d, steps: int, warmup: int):
     import torch
 
     import mamba_ssd_scan_chunked_amd as ssd
-    if w.nseqs_packed:
-        return None                   # the backward takes no packed sequences
     dev = d["x"].device
     rng = np.random.default_rng(1234)
     b, T, H, P, N, G = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups
+    ns = prob["nseqs"]
     dy = torch.from_numpy(rng.standard_normal((b, T, H, P), dtype=np.float32)).to(dev)
-    dfinal = torch.from_numpy(rng.standard_normal((b, H, P, N), dtype=np.float32)).to(dev)
+    dfinal = torch.from_numpy(rng.standard_normal((ns, H, P, N), dtype=np.float32)).to(dev)
     dtype = ssd.DTYPE_BF16 if w.dtype == "bf16" else ssd.DTYPE_F32
-    p = ssd.problem(b, T, H, P, N, G, w.chunk_len, b, dtype, 0)
+    p = ssd.problem(b, T, H, P, N, G, w.chunk_len, ns, dtype, 0)
     f32 = dict(dtype=torch.float32, device=dev)
     out = {"dx": torch.empty((b, T, H, P), **f32), "ddt": torch.empty((b, T, H), **f32),
            "dA_log": torch.empty((H,), **f32), "dB": torch.empty((b, T, G, N), **f32),
            "dC": torch.empty((b, T, G, N), **f32), "dD": torch.empty((H,), **f32),
-           "dinit": torch.empty((b, H, P, N), **f32), "ddt_bias": torch.empty((H,), **f32)}
+           "dinit": torch.empty((ns, H, P, N), **f32), "ddt_bias": torch.empty((H,), **f32)}
     ws = torch.empty(max(1, ssd.backward_workspace_size(p)), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def run():
         ssd.backward_into(p, d["x"], d["dt"], None, d["A_log"], d["B"], d["C"], d["D"], d["init"], dy, dfinal, out,
-                          ws, stream=stream)
+                          ws, stream=stream, seq_idx=d["seq_idx"])
 
     for _ in range(warmup):
         run()
