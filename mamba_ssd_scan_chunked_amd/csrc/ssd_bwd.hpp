@@ -96,11 +96,18 @@ __device__ inline ItemRange item_range(const BwdParams& prm, int64_t kq) {
         r.len = prm.T;
         r.hslot = kq * prm.nblk;
     } else {
+        // one entry per workgroup: kept in scalar registers, so that the buffer
+        // resources built from it are uniform
         const int64_t* e = prm.seqtab + 4 * kq;
-        r.b = min(max(e[0], (int64_t)0), prm.batch - 1);
-        r.s0 = min(max(e[1], (int64_t)0), prm.T);
-        r.len = min(max(e[2] - r.s0, (int64_t)0), prm.T - r.s0);
-        r.hslot = max(e[3], (int64_t)0);
+        auto uni = [](int64_t v) {
+            const int lo = __builtin_amdgcn_readfirstlane((int)(v & 0xffffffff));
+            const int hi = __builtin_amdgcn_readfirstlane((int)(v >> 32));
+            return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+        };
+        r.b = min(max(uni(e[0]), (int64_t)0), prm.batch - 1);
+        r.s0 = min(max(uni(e[1]), (int64_t)0), prm.T);
+        r.len = min(max(uni(e[2]) - r.s0, (int64_t)0), prm.T - r.s0);
+        r.hslot = max(uni(e[3]), (int64_t)0);
         if (r.hslot + (r.len + QB - 1) / QB > prm.hin_blocks) r.len = 0;
     }
     return r;
@@ -282,7 +289,8 @@ __global__ __launch_bounds__(512) void ssd_bwd_fwd_kernel(BwdParams prm) {
     __shared__ float sQp[NTL][QB];
     __shared__ float sCend;
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
+    const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: per-wave branches stay scalar
     // item: (sequence or row kq, head h); tokens s0 .. s0+len-1 of row b
     const int64_t H = prm.H, G = prm.G, HB = prm.HB;
     const int64_t kq = blockIdx.x / H, h = blockIdx.x % H;
@@ -483,7 +491,8 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
     __shared__ float sKap[NW];         // <K, H_in> over each wave's state tiles
     __shared__ float sCend;
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
+    const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: per-wave branches stay scalar
     // item: (sequence or row kq, head h); tokens s0 .. s0+len-1 of row b
     const int64_t H = prm.H, G = prm.G, HB = prm.HB;
     const int64_t kq = blockIdx.x / H, h = blockIdx.x % H;
@@ -511,14 +520,13 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
     float dtn = 0.f, qn = 0.f;            // the next block's dt (wave 1) and qoff (wave 0), lane = token
     // the block's incoming state at this lane's state-tile positions (4 values per tile)
     typedef typename std::conditional<K::SZ == 2, uint2, uint4>::type h4_t;
+    // (no branch around the loads, so that nothing waits for them before their use)
     auto load_hin = [&](int blk, h4_t (&hv)[K::T_NP]) {
         const TI* hb0 = (const TI*)prm.hin + (h * prm.hin_blocks + ir.hslot + blk) * (int64_t)(P * N);
 #pragma unroll
         for (int j = 0; j < K::T_NP; ++j) {
-            const int tile = w + NW * j;
-            if (tile < NTL * PT) {
-                hv[j] = *(const h4_t*)(hb0 + (tile * 64 + lane) * 4);
-            }
+            const int tile = min(w + NW * j, NTL * PT - 1);      // surplus slots reload a valid tile
+            hv[j] = *(const h4_t*)(hb0 + (tile * 64 + lane) * 4);
         }
     };
     auto issue = [&](int blk) {
