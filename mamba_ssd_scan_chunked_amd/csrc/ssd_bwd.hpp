@@ -289,8 +289,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_fwd_kernel(BwdParams prm) {
     __shared__ float sQp[NTL][QB];
     __shared__ float sCend;
 
-    const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: per-wave branches stay scalar
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 15, lg = lane >> 4;
     // item: (sequence or row kq, head h); tokens s0 .. s0+len-1 of row b
     const int64_t H = prm.H, G = prm.G, HB = prm.HB;
     const int64_t kq = blockIdx.x / H, h = blockIdx.x % H;
