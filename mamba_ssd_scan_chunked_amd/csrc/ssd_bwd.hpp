@@ -79,18 +79,36 @@ struct BwdParams {
     // sequence, or null when every row is one sequence.  A workgroup walks one
     // (sequence, head), with its blocks aligned to the sequence's first token.
     const int64_t* seqtab;
+    // Rows split into nseg segments of seg_tokens tokens (nseg = 1: whole rows).
+    // Segment s > 0 starts from seg_state[(row, head, s - 1)] (the forward state
+    // entering it) instead of init; segment s < nseg - 1 takes seg_grad[(row,
+    // head, s)] (the gradient with respect to its end state) instead of dfinal;
+    // only segment 0 writes dinit.
+    int nseg;
+    int64_t seg_tokens;
+    const float* seg_state;   // (batch, H, nseg - 1, P, N)
+    const float* seg_grad;    // (batch, H, nseg - 1, P, N)
     int dt_softplus, x_scale;
 };
 
-// The token range a workgroup walks: sequence kq of the packed rows, or row kq.
-// Values are clamped, so inconsistent sequence ids stay memory-safe.
+// The token range a workgroup walks: sequence kq of the packed rows, segment kq
+// of the split rows, or row kq.  Values are clamped, so inconsistent sequence
+// ids stay memory-safe.  seg: the segment's index in its row (0 without split rows).
 struct ItemRange {
     int64_t b, s0, len, hslot;
+    int seg;
 };
 template <int QB>
 __device__ inline ItemRange item_range(const BwdParams& prm, int64_t kq) {
     ItemRange r;
-    if (!prm.seqtab) {
+    r.seg = 0;
+    if (!prm.seqtab && prm.nseg > 1) {
+        r.b = kq / prm.nseg;
+        r.seg = (int)(kq % prm.nseg);
+        r.s0 = min((int64_t)r.seg * prm.seg_tokens, prm.T);
+        r.len = min(prm.seg_tokens, prm.T - r.s0);
+        r.hslot = kq * (prm.seg_tokens / QB);
+    } else if (!prm.seqtab) {
         r.b = kq;
         r.s0 = 0;
         r.len = prm.T;
@@ -295,10 +313,20 @@ __global__ __launch_bounds__(512) void ssd_bwd_fwd_kernel(BwdParams prm) {
     const int64_t kq = blockIdx.x / H, h = blockIdx.x % H;
     const ItemRange ir = item_range<QB>(prm, kq);
     const int64_t b = ir.b, T = ir.len, tb = b * prm.T + ir.s0;   // T: this item's tokens; tb: its first token
-    const int64_t bh = kq * H + h;          // (sequence, head): init, dfinal, dinit, per-item sums
+    const int64_t bh = kq * H + h;          // (item, head): per-item sums
+    const int64_t sh = prm.seqtab ? bh : b * H + h;   // (sequence or row, head): init, dfinal, dinit
     const int64_t rh = b * H + h;           // (row, head): the token-contiguous dt and qoff runs
     const int nblk = (int)((T + QB - 1) / QB);
     const int64_t g = h / (H / G), hb = HB == H ? h : g;
+    // the state entering the item (forward pass), the gradient leaving its end (reverse
+    // pass) and where dinit goes (null: none), each P x N fp32 or null for zero
+    const int64_t PN = (int64_t)P * N;
+    const int64_t slot = (b * H + h) * (prm.nseg - 1) + ir.seg;     // split rows: this segment's slot
+    const float* item_init = ir.seg > 0 ? prm.seg_state + (slot - 1) * PN : (prm.init ? prm.init + sh * PN : nullptr);
+    const float* item_dfinal = ir.seg < prm.nseg - 1 ? prm.seg_grad + slot * PN
+                                                     : (prm.dfinal ? prm.dfinal + sh * PN : nullptr);
+    float* item_dinit = ir.seg == 0 && prm.dinit ? prm.dinit + sh * PN : nullptr;
+    (void)item_init; (void)item_dfinal; (void)item_dinit;
     constexpr int SZ = K::SZ;
     const int xs = (int)(H * P * SZ), ys = (int)(H * P * 4), bs = (int)(G * N * SZ);
     const char* xrow = (const char*)prm.x + (tb * H + h) * P * SZ;
@@ -343,8 +371,8 @@ __global__ __launch_bounds__(512) void ssd_bwd_fwd_kernel(BwdParams prm) {
         st[j] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (tile < NTL * PT) {
             const int n0 = 16 * (tile / PT) + 4 * lg, p = 16 * (tile % PT) + lr;
-            if (prm.init) {
-                const float4 v = *(const float4*)(prm.init + (bh * P + p) * N + n0);
+            if (item_init) {
+                const float4 v = *(const float4*)(item_init + p * N + n0);
                 st[j] = f32x4{v.x, v.y, v.z, v.w};
             }
             store4(sS + p * LN + n0, st[j][0], st[j][1], st[j][2], st[j][3]);
@@ -497,10 +525,20 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
     const int64_t kq = blockIdx.x / H, h = blockIdx.x % H;
     const ItemRange ir = item_range<QB>(prm, kq);
     const int64_t b = ir.b, T = ir.len, tb = b * prm.T + ir.s0;   // T: this item's tokens; tb: its first token
-    const int64_t bh = kq * H + h;          // (sequence, head): init, dfinal, dinit, per-item sums
+    const int64_t bh = kq * H + h;          // (item, head): per-item sums
+    const int64_t sh = prm.seqtab ? bh : b * H + h;   // (sequence or row, head): init, dfinal, dinit
     const int64_t rh = b * H + h;           // (row, head): the token-contiguous dt and qoff runs
     const int nblk = (int)((T + QB - 1) / QB);
     const int64_t g = h / (H / G), hb = HB == H ? h : g;
+    // the state entering the item (forward pass), the gradient leaving its end (reverse
+    // pass) and where dinit goes (null: none), each P x N fp32 or null for zero
+    const int64_t PN = (int64_t)P * N;
+    const int64_t slot = (b * H + h) * (prm.nseg - 1) + ir.seg;     // split rows: this segment's slot
+    const float* item_init = ir.seg > 0 ? prm.seg_state + (slot - 1) * PN : (prm.init ? prm.init + sh * PN : nullptr);
+    const float* item_dfinal = ir.seg < prm.nseg - 1 ? prm.seg_grad + slot * PN
+                                                     : (prm.dfinal ? prm.dfinal + sh * PN : nullptr);
+    float* item_dinit = ir.seg == 0 && prm.dinit ? prm.dinit + sh * PN : nullptr;
+    (void)item_init; (void)item_dfinal; (void)item_dinit;
     constexpr int SZ = K::SZ;
     const int xs = (int)(H * P * SZ), ys = (int)(H * P * 4), bs = (int)(G * N * SZ);
     const char* xrow = (const char*)prm.x + (tb * H + h) * P * SZ;
@@ -560,8 +598,8 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
         kst[j] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (tile < NTL * PT) {
             const int n0 = 16 * (tile / PT) + 4 * lg, p = 16 * (tile % PT) + lr;
-            if (prm.dfinal) {
-                const float4 v = *(const float4*)(prm.dfinal + (bh * P + p) * N + n0);
+            if (item_dfinal) {
+                const float4 v = *(const float4*)(item_dfinal + p * N + n0);
                 kst[j] = f32x4{v.x, v.y, v.z, v.w};
             }
             store4(sK + p * LN + n0, kst[j][0], kst[j][1], kst[j][2], kst[j][3]);
@@ -788,13 +826,13 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
 #pragma unroll
         for (int j = 0; j < K::T_NP; ++j) kst[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    if (prm.dinit) {
+    if (item_dinit) {
 #pragma unroll
         for (int j = 0; j < K::T_NP; ++j) {
             const int tile = w + NW * j;
             if (tile < NTL * PT) {
                 const int n0 = 16 * (tile / PT) + 4 * lg, p = 16 * (tile % PT) + lr;
-                *(float4*)(prm.dinit + (bh * P + p) * N + n0) = make_float4(kst[j][0], kst[j][1], kst[j][2], kst[j][3]);
+                *(float4*)(item_dinit + p * N + n0) = make_float4(kst[j][0], kst[j][1], kst[j][2], kst[j][3]);
             }
         }
     }
@@ -811,6 +849,96 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
             prm.part[bh * 3 + 2] = (float)sum_D;
         }
     }
+}
+
+// ------------------------------------------------------------ reverse local pass
+// For rows split into segments: the gradient that segment j > 0 alone sends to
+// the state before it (zero gradient entering its end), K <- 2^cend K +
+// dY^T diag(2^cum) C block by block from its last block, and the decay across
+// the segment.  The reverse counterpart of the forward's local pass; a combine
+// step then chains the segments from the row's end.  One workgroup per (row,
+// head, segment j > 0); results at (row, head, j - 1).
+template <typename TI, int P, int N, int QB>
+__global__ __launch_bounds__(512) void ssd_bwd_klocal_kernel(BwdParams prm, float* kloc, float* kcarry) {
+    using K = BwdCfg<TI, P, N, QB>;
+    using M = Mfma<TI>;
+    typedef typename CumType<TI>::type cum_t;
+    constexpr int NW = K::NW, NT = K::NT, LP = K::LP, LN = K::LN, PT = K::PT, NTL = K::NTL, SZ = K::SZ;
+    constexpr int KS = M::KSTEP;
+    __shared__ __attribute__((aligned(16))) TI sDY[QB * LP];
+    __shared__ __attribute__((aligned(16))) TI sC[QB * LN];
+    __shared__ __attribute__((aligned(16))) float sDin[64];
+    __shared__ float sCend;
+
+    const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t H = prm.H, G = prm.G, S1 = prm.nseg - 1;
+    const int64_t item = blockIdx.x;                   // (row * H + head) * S1 + j - 1
+    const int64_t bh = item / S1, j = item % S1 + 1;
+    const int64_t b = bh / H, h = bh % H, g = h / (H / G);
+    const int64_t s0 = min(j * prm.seg_tokens, prm.T), T = min(prm.seg_tokens, prm.T - s0), tb = b * prm.T + s0;
+    const int nblk = (int)((T + QB - 1) / QB);
+    const int ys = (int)(H * P * 4), bs = (int)(G * N * SZ);
+    const char* yrow = (const char*)prm.dy + (tb * H + h) * P * 4;
+    const char* crow = (const char*)prm.C + (tb * G + g) * N * SZ;
+    cum_t A2;
+    if constexpr (sizeof(cum_t) == 8) A2 = -exp((double)prm.A_log[h]) * 1.4426950408889634;
+    else A2 = -expf(prm.A_log[h]) * 1.4426950408889634f;
+    const float dtb = prm.dt_bias ? prm.dt_bias[h] : 0.f;
+
+    f32x4 kst[K::T_NP];
+#pragma unroll
+    for (int q = 0; q < K::T_NP; ++q) kst[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    cum_t total = 0;                                   // wave 0: log2 decay across the segment
+    for (int blk = nblk - 1; blk >= 0; --blk) {
+        const int64_t t0 = (int64_t)blk * QB;
+        {   // dy (to the input type) and C of the block into LDS
+            constexpr int YC = P / 4, CC = N * SZ / 16, VE = 16 / SZ;
+            const rsrc_t ry = make_rsrc(yrow + t0 * ys, (T - t0) * ys);
+            const rsrc_t rc = make_rsrc(crow + t0 * bs, (T - t0) * bs);
+            for (int v = tid; v < QB * YC; v += NT) {
+                const float4 f = __builtin_bit_cast(float4, buf_load16(ry, (v / YC) * ys + (v % YC) * 16));
+                store4(sDY + (v / YC) * LP + (v % YC) * 4, f.x, f.y, f.z, f.w);
+            }
+            for (int v = tid; v < QB * CC; v += NT)
+                *(uint4*)(sC + (v / CC) * LN + (v % CC) * VE) = buf_load16(rc, (v / CC) * bs + (v % CC) * 16);
+        }
+        if (w == 0) {
+            const int rows = (int)min((int64_t)QB, T - t0);
+            const float dtv = buf_load_f32(make_rsrc(prm.dt + (b * H + h) * prm.T + s0 + t0, (T - t0) * 4), lane * 4);
+            const float d = lane < rows ? step_size(dtv + dtb, prm.dt_softplus) : 0.f;
+            const cum_t cum = wave_incl_scan((cum_t)d * A2);
+            const cum_t cend = __shfl(cum, QB - 1);
+            if (lane < QB) sDin[lane] = fast_exp2((float)cum);
+            if (lane == 0) sCend = fast_exp2((float)cend);
+            total += cend;
+        }
+        block_sync_lds();
+        const float dec = sCend;
+#pragma unroll
+        for (int q = 0; q < K::T_NP; ++q) {
+            const int tile = w + NW * q;
+            if (tile < NTL * PT) {
+                const int ni = tile / PT, pj = tile % PT;
+                f32x4 acc = kst[q] * dec;
+#pragma unroll
+                for (int k0 = 0; k0 < QB; k0 += KS)
+                    acc = M::mma(frag_t(sC, LN, 16 * ni, k0, lr, lg), frag_t_w(sDY, LP, 16 * pj, k0, lr, lg, sDin), acc);
+                kst[q] = acc;
+            }
+        }
+        block_sync_lds();
+    }
+    float* dst = kloc + item * (int64_t)(P * N);
+#pragma unroll
+    for (int q = 0; q < K::T_NP; ++q) {
+        const int tile = w + NW * q;
+        if (tile < NTL * PT) {
+            const int n0 = 16 * (tile / PT) + 4 * lg, p = 16 * (tile % PT) + lr;
+            *(float4*)(dst + p * N + n0) = make_float4(kst[q][0], kst[q][1], kst[q][2], kst[q][3]);
+        }
+    }
+    if (w == 0 && lane == 0) kcarry[item] = fast_exp2((float)total);
 }
 
 }  // namespace ssd

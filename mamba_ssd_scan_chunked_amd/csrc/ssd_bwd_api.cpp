@@ -8,6 +8,7 @@
 #include <algorithm>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 
 #include "ssd_bwd.hpp"
 #include "ssd_host.hpp"
@@ -107,6 +108,28 @@ __global__ __launch_bounds__(64) void ssd_seq_slots_kernel(int64_t* tab, int64_t
     }
 }
 
+// Gradient with respect to the end state of every row segment but the last,
+// written over the reverse local pass's results: G(S-1) = dfinal and
+// G(j) = carry(j+1) G(j+1) + local(j+1), where slot j holds segment j+1's local
+// gradient and decay.  One thread per 4 consecutive state elements.
+__global__ __launch_bounds__(256) void ssd_bwd_kcombine_kernel(const float* __restrict__ dfinal, float* seg_grad,
+                                                               const float* __restrict__ kcarry, int64_t rows_heads,
+                                                               int64_t pn, int nseg) {
+    const int64_t pn4 = pn / 4;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t bh = idx / pn4, e = idx % pn4;
+    if (bh >= rows_heads) return;
+    const int s1 = nseg - 1;
+    float4 st = dfinal ? *(const float4*)(dfinal + bh * pn + 4 * e) : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = s1 - 1; j >= 0; --j) {
+        const float c = kcarry[bh * s1 + j];
+        float4* slot = (float4*)(seg_grad + (bh * s1 + j) * pn) + e;
+        const float4 l = *slot;
+        st = make_float4(c * st.x + l.x, c * st.y + l.y, c * st.z + l.z, c * st.w + l.w);
+        *slot = st;
+    }
+}
+
 // Fill / copy for the degenerate cases (no token): dinit = dfinal or 0, scalars 0.
 __global__ __launch_bounds__(256) void ssd_fill_kernel(float* dst, const float* src, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -122,6 +145,34 @@ using namespace ssd_host;
 // Tokens per block of the backward kernels.
 int bwd_block(const ssd_problem_t* p) { return p->dtype == SSD_DTYPE_BF16 ? ssd::bwd_block_bf16() : ssd::bwd_block_f32(); }
 
+// Segments per row (rows without sequence ids).  With at most 128 (row, head)
+// items, rows are cut into up to 512 / items segments of whole 64-token blocks,
+// down to 4 blocks per segment, as the forward does; SSD_BWD_SEGMENTS=<n> forces n.
+// A function of the problem alone, so the workspace size is known on the host.
+struct BwdSegs {
+    int nseg;
+    int64_t seg_tokens;
+};
+BwdSegs bwd_segments(const ssd_problem_t* p) {
+    const int64_t nb64 = (p->seqlen + 63) / 64;
+    BwdSegs r{1, std::max<int64_t>(p->seqlen, 1)};
+    if (nb64 <= 1 || p->batch == 0) return r;
+    int64_t S = 1;
+    const char* env = std::getenv("SSD_BWD_SEGMENTS");
+    if (env && std::atoi(env) > 0) {
+        S = std::atoi(env);
+    } else {
+        const int64_t units = p->batch * p->nheads;
+        if (units <= 128) S = std::min<int64_t>(512 / units, nb64 / 4);
+    }
+    S = std::max<int64_t>(1, std::min<int64_t>(S, nb64));
+    if (S == 1) return r;
+    r.seg_tokens = (nb64 + S - 1) / S * 64;
+    r.nseg = (int)((p->seqlen + r.seg_tokens - 1) / r.seg_tokens);
+    if (r.nseg == 1) r.seg_tokens = p->seqlen;
+    return r;
+}
+
 // Workspace of the backward pass: a per-token scalar and dt, both (b, H, T); each
 // block's incoming state in the input type, (H, slots, P, N) with
 // slots = b * blocks per row + nseqs (enough for any split of the rows into
@@ -130,22 +181,31 @@ int bwd_block(const ssd_problem_t* p) { return p->dtype == SSD_DTYPE_BF16 ? ssd:
 // group has more than one head, each head's dB and dC contribution (b, T, H, N)
 // in the input type before the sum over the group.
 struct BwdWs {
-    int64_t q_off, dt_off, hin_off, part_off, tab_off, dbh_off, dch_off, total, hin_slots;
+    int64_t q_off, dt_off, hin_off, part_off, tab_off, seg_off, segc_off, grad_off, gradc_off, dbh_off, dch_off, total,
+        hin_slots;
 };
 BwdWs bwd_ws_layout(const ssd_problem_t* p) {
     BwdWs l;
+    const BwdSegs sg = bwd_segments(p);
     const int64_t bth = p->batch * p->seqlen * p->nheads;
-    const int64_t items = std::max(p->nseqs, p->batch);
+    const int64_t items = std::max(std::max(p->nseqs, p->batch), p->batch * sg.nseg);
     const bool per_head = p->ngroups != p->nheads;
     const int qb = bwd_block(p);
     const int64_t nblk = (p->seqlen + qb - 1) / qb;
-    l.hin_slots = p->batch * nblk + p->nseqs;
+    l.hin_slots = std::max(p->batch * nblk + p->nseqs, p->batch * sg.nseg * ((sg.seg_tokens + qb - 1) / qb));
     l.q_off = 0;
     l.dt_off = align256(bth * 4);
     l.hin_off = l.dt_off + align256(bth * 4);
     l.part_off = l.hin_off + align256(p->nheads * l.hin_slots * p->headdim * p->dstate * elem_size(p->dtype));
     l.tab_off = l.part_off + align256(items * p->nheads * 12);
-    l.dbh_off = l.tab_off + align256(p->nseqs * 32);
+    // split rows: incoming states and their decays (forward local pass), then the
+    // gradients at segment ends and their decays (reverse local pass)
+    const int64_t nsl = p->batch * p->nheads * (sg.nseg - 1);
+    l.seg_off = l.tab_off + align256(p->nseqs * 32);
+    l.segc_off = l.seg_off + align256(nsl * p->headdim * p->dstate * 4);
+    l.grad_off = l.segc_off + align256(nsl * 4);
+    l.gradc_off = l.grad_off + align256(nsl * p->headdim * p->dstate * 4);
+    l.dbh_off = l.gradc_off + align256(nsl * 4);
     const int64_t hn = per_head ? align256(bth * p->dstate * elem_size(p->dtype)) : 0;
     l.dch_off = l.dbh_off + hn;
     l.total = l.dch_off + hn;
@@ -251,7 +311,12 @@ int ssd_backward(const ssd_problem_t* p, const void* x, const float* dt, const f
     prm.seqtab = seq_idx ? reinterpret_cast<const int64_t*>(ws + wl.tab_off) : nullptr;
     prm.dt_softplus = (p->flags & SSD_FLAG_DT_SOFTPLUS) ? 1 : 0;
     prm.x_scale = x_scale_of(p);
-    const int64_t items = seq_idx ? p->nseqs : p->batch;     // sequences, or rows
+    const BwdSegs sg = seq_idx ? BwdSegs{1, p->seqlen} : bwd_segments(p);
+    prm.nseg = sg.nseg;
+    prm.seg_tokens = sg.seg_tokens;
+    prm.seg_state = reinterpret_cast<const float*>(ws + wl.seg_off);
+    prm.seg_grad = reinterpret_cast<const float*>(ws + wl.grad_off);
+    const int64_t items = seq_idx ? p->nseqs : p->batch * sg.nseg;     // sequences, row segments or rows
     const int64_t grid = items * p->nheads;
     if (seq_idx) {
         int64_t* tab = reinterpret_cast<int64_t*>(ws + wl.tab_off);
@@ -270,6 +335,64 @@ int ssd_backward(const ssd_problem_t* p, const void* x, const float* dt, const f
         hipLaunchKernelGGL(ssd::ssd_transpose_dt_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, dt,
                            const_cast<float*>(prm.dt), p->batch, p->seqlen, p->nheads);
         e = hipGetLastError();
+    }
+    if (e == hipSuccess && sg.nseg > 1) {
+        // forward state entering each segment: the forward's local pass and combine step
+        ssd::ScanParams sp;
+        sp.x = x;
+        sp.dt = dt;
+        sp.A_log = A_log;
+        sp.D = D;
+        sp.init = init_state;
+        sp.seq_idx = nullptr;
+        sp.y = nullptr;
+        sp.fin = nullptr;
+        sp.B = B;
+        sp.C = C;
+        sp.batch = p->batch;
+        sp.T = p->seqlen;
+        sp.H = p->nheads;
+        sp.G = p->ngroups;
+        sp.nseqs = p->batch;
+        sp.nblk = (int)((p->seqlen + 63) / 64);
+        sp.dt_bias = dt_bias;
+        sp.dt_softplus = prm.dt_softplus;
+        sp.x_scale = prm.x_scale;
+        sp.seg_blocks = (int)(sg.seg_tokens / 64);
+        sp.nseg = sg.nseg;
+        sp.seg_state = reinterpret_cast<float*>(ws + wl.seg_off);
+        sp.seg_carry = reinterpret_cast<float*>(ws + wl.segc_off);
+        const int64_t lgrid = p->batch * p->nheads * (sg.nseg - 1);
+        e = bf ? ssd::launch_scan_bf16(P, N, 64, false, prm.x_scale != 0, true, P / 16, sp, lgrid, st)
+               : ssd::launch_scan_f32(P, N, 64, false, prm.x_scale != 0, true, P / 16, sp, lgrid, st);
+        if (e == hipSuccess) {
+            ssd::CombineParams cp;
+            cp.init = init_state;
+            cp.seq_idx = nullptr;
+            cp.seg_state = sp.seg_state;
+            cp.seg_carry = sp.seg_carry;
+            cp.batch = p->batch;
+            cp.T = p->seqlen;
+            cp.H = p->nheads;
+            cp.nseqs = p->batch;
+            cp.P = P;
+            cp.N = N;
+            cp.nseg = sg.nseg;
+            e = ssd::launch_combine(cp, st);
+        }
+        // gradient leaving each segment's end: the reverse local pass and combine step
+        float* kloc = reinterpret_cast<float*>(ws + wl.grad_off);
+        float* kcar = reinterpret_cast<float*>(ws + wl.gradc_off);
+        if (e == hipSuccess)
+            e = bf ? ssd::launch_bwd_klocal_bf16(P, N, prm, kloc, kcar, lgrid, st)
+                   : ssd::launch_bwd_klocal_f32(P, N, prm, kloc, kcar, lgrid, st);
+        if (e == hipSuccess) {
+            const int64_t rh = p->batch * p->nheads, pn = (int64_t)P * N;
+            const int64_t n = rh * pn / 4;
+            hipLaunchKernelGGL(ssd::ssd_bwd_kcombine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                               dfinal, kloc, kcar, rh, pn, sg.nseg);
+            e = hipGetLastError();
+        }
     }
     if (e == hipSuccess)
         e = bf ? ssd::launch_bwd_bf16(P, N, prm, grid, st) : ssd::launch_bwd_f32(P, N, prm, grid, st);
@@ -296,8 +419,9 @@ int ssd_backward(const ssd_problem_t* p, const void* x, const float* dt, const f
         e = hipGetLastError();
     }
     if (log_enabled())
-        std::fprintf(stderr, "[ssd] backward dtype=%d P=%d N=%d QB=%d grid=%lld per-head sums=%d -> %s\n", p->dtype, P, N,
-                     qb, (long long)grid, (int)per_head, hipGetErrorString(e));
+        std::fprintf(stderr, "[ssd] backward dtype=%d P=%d N=%d QB=%d grid=%lld segments=%d x %lld tokens per-head sums=%d -> %s\n",
+                     p->dtype, P, N, qb, (long long)grid, sg.nseg, (long long)sg.seg_tokens, (int)per_head,
+                     hipGetErrorString(e));
     return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
 }
 

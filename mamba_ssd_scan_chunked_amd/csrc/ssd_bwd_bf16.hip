@@ -55,4 +55,15 @@ hipError_t launch_bwd_bf16(int P, int N, const BwdParams& prm, int64_t grid, hip
     }
     return hipErrorInvalidValue;
 }
+
+hipError_t launch_bwd_klocal_bf16(int P, int N, const BwdParams& prm, float* kloc, float* kcarry, int64_t grid, hipStream_t s) {
+    if (grid <= 0) return hipSuccess;
+    if (P == 32 && N == 64) { hipLaunchKernelGGL((ssd_bwd_klocal_kernel<__bf16, 32, 64, 64>), dim3((unsigned)grid), dim3(BwdCfg<__bf16, 32, 64, 64>::NT), 0, s, prm, kloc, kcarry); return hipGetLastError(); }
+    if (P == 32 && N == 128) { hipLaunchKernelGGL((ssd_bwd_klocal_kernel<__bf16, 32, 128, 64>), dim3((unsigned)grid), dim3(BwdCfg<__bf16, 32, 128, 64>::NT), 0, s, prm, kloc, kcarry); return hipGetLastError(); }
+    if (P == 32 && N == 256) { hipLaunchKernelGGL((ssd_bwd_klocal_kernel<__bf16, 32, 256, 64>), dim3((unsigned)grid), dim3(BwdCfg<__bf16, 32, 256, 64>::NT), 0, s, prm, kloc, kcarry); return hipGetLastError(); }
+    if (P == 64 && N == 64) { hipLaunchKernelGGL((ssd_bwd_klocal_kernel<__bf16, 64, 64, 64>), dim3((unsigned)grid), dim3(BwdCfg<__bf16, 64, 64, 64>::NT), 0, s, prm, kloc, kcarry); return hipGetLastError(); }
+    if (P == 64 && N == 128) { hipLaunchKernelGGL((ssd_bwd_klocal_kernel<__bf16, 64, 128, 64>), dim3((unsigned)grid), dim3(BwdCfg<__bf16, 64, 128, 64>::NT), 0, s, prm, kloc, kcarry); return hipGetLastError(); }
+    if (P == 64 && N == 256) { hipLaunchKernelGGL((ssd_bwd_klocal_kernel<__bf16, 64, 256, 64>), dim3((unsigned)grid), dim3(BwdCfg<__bf16, 64, 256, 64>::NT), 0, s, prm, kloc, kcarry); return hipGetLastError(); }
+    return hipErrorInvalidValue;
+}
 }  // namespace ssd

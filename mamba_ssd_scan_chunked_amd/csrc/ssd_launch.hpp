@@ -46,4 +46,9 @@ bool supported_bwd_bf16(int P, int N);
 bool supported_bwd_f32(int P, int N);
 int bwd_block_bf16();   // tokens per block of the backward kernels
 int bwd_block_f32();
+// Reverse local pass of rows split into segments (one workgroup per (row, head, segment > 0)).
+hipError_t launch_bwd_klocal_bf16(int P, int N, const BwdParams& prm, float* kloc, float* kcarry, int64_t grid,
+                                  hipStream_t s);
+hipError_t launch_bwd_klocal_f32(int P, int N, const BwdParams& prm, float* kloc, float* kcarry, int64_t grid,
+                                 hipStream_t s);
 }  // namespace ssd

@@ -196,3 +196,63 @@ def test_backward_headline_shape():
     announce("backward 2.7B-layer shape")
     got, ref = run_both(prob, dy, dfinal)
     check(got, ref, TOL["bf16"])
+
+
+SPLIT = [
+    # dtype, b, T, H, P, N, G, forced segments (0: the automatic choice)
+    ("bf16", 1, 1000, 2, 64, 128, 1, 0),       # 2 items: split automatically
+    ("bf16", 2, 700, 2, 64, 128, 2, 3),        # ragged last segment
+    ("bf16", 1, 640, 3, 32, 64, 3, 5),
+    ("f32", 1, 500, 2, 64, 64, 1, 2),
+    ("f32", 2, 300, 2, 16, 32, 2, 0),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT, ids=lambda c: "%s-b%d-T%d-H%d-P%d-N%d-G%d-S%d" % c)
+def test_backward_split_rows(case, monkeypatch):
+    """Rows cut into segments (the state entering each segment from the forward's local
+    pass and combine step, the gradient leaving each from the reverse local pass and
+    combine step): every output against the oracle."""
+    dt, b, T, H, P, N, G, S = case
+    if S:
+        monkeypatch.setenv("SSD_BWD_SEGMENTS", str(S))
+    prob = si.make_problem(b, T, H, P, N, G, dtype=dt, seed=T + 7, d_skip=True, init_std=0.5)
+    dy, dfinal = cotangents(prob, T + 8)
+    announce("backward split rows %s" % (case,))
+    got, ref = run_both(prob, dy, dfinal)
+    check(got, ref, TOL[dt])
+
+
+@pytest.mark.parametrize("mode", ["softplus_zoh", "euler"])
+def test_backward_split_rows_step_size_modes(mode, monkeypatch):
+    monkeypatch.setenv("SSD_BWD_SEGMENTS", "4")
+    kw = dict(MODES[mode])
+    kw.pop("bias", None)
+    b, T, H = 1, 600, 2
+    prob = si.make_problem(b, T, H, 64, 128, 1, dtype="bf16", seed=41, d_skip=True, init_std=0.5)
+    dtb = None
+    if kw.get("dt_softplus"):
+        raw = si.raw_step_sizes(b, T, H, seed=42)
+        prob = dict(prob, dt=raw["dt"])
+        dtb = raw["dt_bias"]
+    dy, dfinal = cotangents(prob, 43)
+    announce("backward split rows mode=%s" % mode)
+    got, ref = run_both(prob, dy, dfinal, dt_bias=dtb, **kw)
+    check(got, ref, TOL["bf16"])
+
+
+def test_backward_split_equals_unsplit(monkeypatch):
+    """The same problem with 1 and 4 segments: equal within the tolerance."""
+    import mamba_ssd_scan_chunked_amd as ssd
+    prob = si.make_problem(1, 512, 2, 64, 128, 1, dtype="bf16", seed=47, d_skip=True, init_std=0.5)
+    dy, dfinal = cotangents(prob, 48)
+    d = to_device(prob)
+    outs = []
+    for S in ("1", "4"):
+        monkeypatch.setenv("SSD_BWD_SEGMENTS", S)
+        g = ssd.backward(d["x"], d["dt"], d["A_log"], d["B"], d["C"], dy.cuda(), D=d["D"], init_state=d["init"],
+                         dfinal=dfinal.cuda())
+        torch.cuda.synchronize()
+        outs.append({k: v.cpu().double().numpy() for k, v in g.items()})
+    for k in OUTS:
+        assert_parity(outs[1][k], outs[0][k], TOL["bf16"], k)
