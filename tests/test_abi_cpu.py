@@ -215,9 +215,12 @@ def test_backward_workspace_sizes():
     hin = 80 * (4 * 64 + 4) * 64 * 128 * 2      # (H, b * blocks + nseqs slots, P, N)
     assert ssd.backward_workspace_size(p) == (2 * r(bth * 4) + r(hin) + r(bh * 12) + r(4 * 32)
                                               + 2 * r(bth * 128 * 2))
-    p = prob(nheads=8, ngroups=8)                 # one head per group: dB, dC written directly
-    assert ssd.backward_workspace_size(p) == (2 * r(4 * 4096 * 8 * 4) + r(8 * 260 * 64 * 128 * 2) + r(32 * 12)
-                                              + r(4 * 32))
+    # one head per group (dB, dC written directly); 32 (row, head) items: rows cut into
+    # 16 segments of 256 tokens, with the states and gradients at 15 segment edges
+    p = prob(nheads=8, ngroups=8)
+    edges = 4 * 8 * 15
+    assert ssd.backward_workspace_size(p) == (2 * r(4 * 4096 * 8 * 4) + r(8 * 260 * 64 * 128 * 2) + r(64 * 8 * 12)
+                                              + r(4 * 32) + 2 * (r(edges * 64 * 128 * 4) + r(edges * 4)))
     assert ssd.backward_workspace_size(prob(headdim=48)) == 0
 
 
