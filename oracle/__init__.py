@@ -40,7 +40,7 @@ def _load():
     f.restype = ctypes.c_int
     b = lib.ssd_oracle_bwd_f64
     b.argtypes = [i64, i64, i64, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, vp, vp,
-                  vp, vp, vp, vp, vp, vp, vp, vp, ci]
+                  vp, vp, vp, vp, vp, vp, vp, vp, vp, ci]
     b.restype = ctypes.c_int
     lib.ssd_oracle_max_threads.restype = ctypes.c_int
     _lib = lib
@@ -113,7 +113,8 @@ def gradients(x, dt, A_log, B, C, dy, D=None, init=None, dfinal=None, seq_idx=No
 
     Returns a dict of float64 arrays: dx (b,T,H,P), ddt (b,T,H) (with respect to
     the dt input), dA_log (H), dB and dC (b,T,G,N), dD (H), dinit (nseqs,H,P,N),
-    ddt_bias (H).  dD, dinit and ddt_bias are returned whether or not D, init and
+    ddt_bias (H), and under "abs_terms" the per-head sums of the absolute
+    per-token terms of dA_log, ddt_bias and dD.  dD, dinit and ddt_bias are returned whether or not D, init and
     dt_bias were given (the gradient at zero / no bias).
     """
     if dt_scales_x and zoh:
@@ -136,6 +137,7 @@ def gradients(x, dt, A_log, B, C, dy, D=None, init=None, dfinal=None, seq_idx=No
     out = {"dx": np.empty((b, T, H, P)), "ddt": np.empty((b, T, H)), "dA_log": np.empty(H),
            "dB": np.empty((b, T, G, N)), "dC": np.empty((b, T, G, N)), "dD": np.empty(H),
            "dinit": np.empty((nseqs, H, P, N)), "ddt_bias": np.empty(H)}
+    abs_sums = np.empty((H, 3))
 
     def p(a):
         return a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
@@ -143,7 +145,10 @@ def gradients(x, dt, A_log, B, C, dy, D=None, init=None, dfinal=None, seq_idx=No
     rc = lib.ssd_oracle_bwd_f64(b, T, H, P, N, G, nseqs, p(x), p(dt), p(A_log), p(B), p(C), p(D), p(init),
                                 p(seq_idx), p(dt_bias), int(bool(dt_softplus)), 2 if zoh else int(bool(dt_scales_x)),
                                 p(dy), p(dfinal), p(out["dx"]), p(out["ddt"]), p(out["dA_log"]), p(out["dB"]),
-                                p(out["dC"]), p(out["dD"]), p(out["dinit"]), p(out["ddt_bias"]), int(nthreads))
+                                p(out["dC"]), p(out["dD"]), p(out["dinit"]), p(out["ddt_bias"]), p(abs_sums),
+                                int(nthreads))
     if rc != 0:
         raise ValueError("oracle rejected its arguments (code %d)" % rc)
+    # per head: sums over rows and tokens of the absolute per-token terms of each reduced gradient
+    out["abs_terms"] = {"dA_log": abs_sums[:, 0].copy(), "ddt_bias": abs_sums[:, 1].copy(), "dD": abs_sums[:, 2].copy()}
     return out

@@ -172,7 +172,9 @@ int ssd_oracle_max_threads(void)
  * with f = 1, Delta or (e^{Delta A} - 1)/A, so df/dDelta = 0, 1 or e^{Delta A}
  * and df/dA = 0, 0 or (Delta A e^{Delta A} - e^{Delta A} + 1) / A^2.
  * Every state S_t of a (row, head) is kept (T * P * N doubles): meant for test
- * sizes.  dB and dC are summed over the heads of a group in increasing head
+ * sizes.  abs_sums (H x 3, or NULL) receives, per head, the sums over rows and
+ * tokens of the absolute per-token terms of dA_log, ddt_bias and dD (the scale
+ * against which the rounding error of those sums is judged).  dB and dC are summed over the heads of a group in increasing head
  * order, the per-head scalars over rows in increasing row order.
  */
 int ssd_oracle_bwd_f64(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
@@ -183,7 +185,7 @@ int ssd_oracle_bwd_f64(int64_t batch, int64_t seqlen, int64_t nheads, int64_t he
                        const double* dt_bias, int dt_softplus, int input_scaling,
                        const double* dy, const double* dfinal,
                        double* dx, double* ddt, double* dA_log, double* dB, double* dC,
-                       double* dD, double* dinit, double* ddt_bias, int nthreads)
+                       double* dD, double* dinit, double* ddt_bias, double* abs_sums, int nthreads)
 {
     const int64_t T = seqlen, H = nheads, P = headdim, N = dstate, G = ngroups;
     if (batch < 0 || T < 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0 || H % G != 0)
@@ -200,8 +202,9 @@ int ssd_oracle_bwd_f64(int64_t batch, int64_t seqlen, int64_t nheads, int64_t he
     double* sA = (double*)calloc((size_t)units, sizeof(double));
     double* sD = (double*)calloc((size_t)units, sizeof(double));
     double* sBias = (double*)calloc((size_t)units, sizeof(double));
-    if (!dBu || !dCu || !sA || !sD || !sBias) {
-        free(dBu); free(dCu); free(sA); free(sD); free(sBias);
+    double* sAbs = (double*)calloc((size_t)units * 3, sizeof(double));
+    if (!dBu || !dCu || !sA || !sD || !sBias || !sAbs) {
+        free(dBu); free(dCu); free(sA); free(sD); free(sBias); free(sAbs);
         return 2;
     }
     memset(dinit, 0, (size_t)(nseqs * H * P * N) * sizeof(double));
@@ -252,7 +255,7 @@ int ssd_oracle_bwd_f64(int64_t batch, int64_t seqlen, int64_t nheads, int64_t he
         }
         if (bad) { free(S); free(Gs); free(gb); free(v); free(seq); continue; }
         /* backward, from the last token */
-        double dA = 0.0, dDs = 0.0, dbs = 0.0;
+        double dA = 0.0, dDs = 0.0, dbs = 0.0, aA = 0.0, aD = 0.0, ab = 0.0;
         for (int64_t t = T - 1; t >= 0; --t) {
             const int64_t k = seq[t];
             const int last = (t == T - 1 || seq[t + 1] != k);
@@ -308,12 +311,15 @@ int ssd_oracle_bwd_f64(int64_t batch, int64_t seqlen, int64_t nheads, int64_t he
             }
             const double dDelta = da * a * A + df * dfdD;
             dA += da * a * Dv + df * dfdA;
+            aA += fabs((da * a * Dv + df * dfdA) * A);
             double g_dt = dDelta;
             if (dt_softplus)
                 g_dt *= 1.0 / (1.0 + exp(-pre[t]));
             ddt[(r * T + t) * H + h] = g_dt;
             dbs += g_dt;
             dDs += dDt;
+            ab += fabs(g_dt);
+            aD += fabs(dDt);
             if (start) {
                 double* di = dinit + (k * H + h) * P * N;
                 for (size_t i = 0; i < PN; ++i)
@@ -329,6 +335,9 @@ int ssd_oracle_bwd_f64(int64_t batch, int64_t seqlen, int64_t nheads, int64_t he
         sA[u] = dA * A;
         sD[u] = dDs;
         sBias[u] = dbs;
+        sAbs[3 * u + 0] = aA;
+        sAbs[3 * u + 1] = ab;
+        sAbs[3 * u + 2] = aD;
         free(S); free(Gs); free(gb); free(v); free(seq);
     }
     if (!bad) {
@@ -353,8 +362,19 @@ int ssd_oracle_bwd_f64(int64_t batch, int64_t seqlen, int64_t nheads, int64_t he
             dA_log[h] = a;
             if (dD) dD[h] = d;
             if (ddt_bias) ddt_bias[h] = bb;
+            if (abs_sums) {
+                double s0 = 0.0, s1 = 0.0, s2 = 0.0;
+                for (int64_t r = 0; r < batch; ++r) {
+                    s0 += sAbs[3 * (r * H + h) + 0];
+                    s1 += sAbs[3 * (r * H + h) + 1];
+                    s2 += sAbs[3 * (r * H + h) + 2];
+                }
+                abs_sums[3 * h + 0] = s0;
+                abs_sums[3 * h + 1] = s1;
+                abs_sums[3 * h + 2] = s2;
+            }
         }
     }
-    free(dBu); free(dCu); free(sA); free(sD); free(sBias);
+    free(dBu); free(dCu); free(sA); free(sD); free(sBias); free(sAbs);
     return bad ? 2 : 0;
 }

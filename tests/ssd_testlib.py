@@ -101,6 +101,24 @@ def assert_parity(got, ref, tol, what="y"):
     return e
 
 
+# Per-head sums over every token (dA_log, ddt_bias, dD of the backward): their
+# rounding error grows with the sum of the absolute per-token terms, not with the
+# sum itself, which cancellation can make small.  Each term carries a relative
+# error of a few units of the operand precision, so the error of the sum is
+# bounded by about that times the absolute sum; the test allows tol * max(max|ref|,
+# SUM_FRACTION * max_h sum_t |term|), i.e. 2e-3 (bf16) or 1e-6 (fp32) of the
+# absolute sum.
+SUM_FRACTION = 0.1
+
+
+def assert_parity_sum(got, ref, abs_terms, tol, what):
+    assert np.isfinite(got).all(), "%s has non-finite values" % what
+    scale = max(float(np.abs(ref).max()), SUM_FRACTION * float(np.abs(abs_terms).max()))
+    e = float(np.abs(got - ref).max()) / scale if scale > 0 else float(np.abs(got).max())
+    assert e <= tol, "%s: max|err| / scale = %.3e > %.1e (scale %.3e)" % (what, e, tol, scale)
+    return e
+
+
 def sample_pairs(b, H, k, seed=0):
     rng = np.random.default_rng(seed)
     allp = [(i, j) for i in range(b) for j in range(H)]

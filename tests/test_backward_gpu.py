@@ -4,8 +4,11 @@ differences in test_oracle_grad_pins.py).
 
 Every output is compared element by element: max |got - ref| <= tol * max |ref|
 per tensor, with tol = 2e-2 for bf16 inputs (bf16 MFMA operands, fp32
-accumulation) and 1e-5 for fp32 inputs.  The loss is L = <dy, y> + <dfinal, final>
-with seeded random dy and dfinal.
+accumulation) and 1e-5 for fp32 inputs.  The per-head sums over all tokens
+(dA_log, ddt_bias, dD) are judged against max(max|ref|, 0.1 * the sum of their
+absolute per-token terms) instead: cancellation can make a sum far smaller than
+the rounding its terms carry.  The loss is L = <dy, y> + <dfinal, final> with
+seeded random dy and dfinal.
 """
 import sys
 
@@ -15,7 +18,7 @@ import torch
 
 import oracle
 import ssd_inputs as si
-from ssd_testlib import TOL, assert_parity, dtype_name, to_device
+from ssd_testlib import TOL, assert_parity, assert_parity_sum, dtype_name, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -52,10 +55,16 @@ def run_both(prob, dy, dfinal, *, dt_bias=None, dt_softplus=False, zoh=False, dt
     return got, ref
 
 
+SUMS = ("dA_log", "ddt_bias", "dD")
+
+
 def check(got, ref, tol, outs=OUTS):
     errs = {}
     for k in outs:
-        errs[k] = assert_parity(got[k], ref[k], tol, k)
+        if k in SUMS:
+            errs[k] = assert_parity_sum(got[k], ref[k], ref["abs_terms"][k], tol, k)
+        else:
+            errs[k] = assert_parity(got[k], ref[k], tol, k)
     print("[errors] " + " ".join("%s=%.2e" % kv for kv in errs.items()), flush=True)
 
 
