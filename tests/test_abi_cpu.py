@@ -212,8 +212,11 @@ def test_backward_workspace_sizes():
     p = prob(ngroups=1)
     bth, bh = 4 * 4096 * 80, 4 * 80
     r = lambda v: (v + 255) // 256 * 256
+    # (320 items: rows cut into 4 segments, states and gradients at 3 edges per row)
     hin = 80 * (4 * 64 + 4) * 64 * 128 * 2      # (H, b * blocks + nseqs slots, P, N)
-    assert ssd.backward_workspace_size(p) == (2 * r(bth * 4) + r(hin) + r(bh * 12) + r(4 * 32)
+    edges = 4 * 80 * 3
+    assert ssd.backward_workspace_size(p) == (2 * r(bth * 4) + r(hin) + r(4 * 4 * 80 * 12) + r(4 * 32)
+                                              + 2 * (r(edges * 64 * 128 * 4) + r(edges * 4))
                                               + 2 * r(bth * 128 * 2))
     # one head per group (dB, dC written directly); 32 (row, head) items: rows cut into
     # 16 segments of 256 tokens, with the states and gradients at 15 segment edges
