@@ -8,7 +8,12 @@ Prints one JSON line: tokens/s over K timed steps, the roofline of the scan
 kernel measured with HIP events on the stream it is launched on, and the CPU
 oracle timed on the same workload.  The line also carries a "backward" object:
 the time of one ssd_backward call (every gradient) on the same workload and its
-fraction of the HBM roofline (skipped with --no-backward).
+fraction of the HBM roofline (skipped with --no-backward); a "step" object: the
+single-token decoding step (ssd_step) at the workload's batch and heads, bound by
+one read and one write of the fp32 state (eager and replayed from a HIP graph of
+16 steps); and a "fused_step_size" object: the same forward fed the raw step
+size and a per-head bias with the softplus map and the Euler input scaling done
+in the kernel (skipped with --no-extra-legs).
 """
 from __future__ import annotations
 
@@ -109,6 +114,106 @@ def backward_leg(w, prob, d, steps: int, warmup: int):
                          "alg_bytes_per_step": balg, "kernels": "all launches of one ssd_backward call"}}
 
 
+def step_leg(w, prob, d, steps: int, warmup: int):
+    """Time ssd_step (one token per (row, head) on the fp32 state, in place) at the
+    workload's batch and heads, on the workload's first token."""
+    import torch
+
+    import mamba_ssd_scan_chunked_amd as ssd
+    if d["seq_idx"] is not None:
+        return None
+    dev = d["x"].device
+    b, H, P, N, G = w.batch, w.nheads, w.headdim, w.dstate, w.ngroups
+    sx = 2 if w.dtype == "bf16" else 4
+    x1, dt1, B1, C1 = (d[k][:, :1].contiguous() for k in ("x", "dt", "B", "C"))
+    state = torch.zeros((b, H, P, N), dtype=torch.float32, device=dev)
+    y1 = torch.empty((b, 1, H, P), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def run():
+        # on torch's current stream: the bench stream here, the capture stream below
+        ssd.step(x1, dt1, d["A_log"], B1, C1, d["D"], state, y=y1)
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for e in evs:
+        e[0].record(stream)
+        run()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
+    kms = sum(ms) / len(ms)
+    # a decoding loop of 16 steps captured once and replayed
+    K, R = 16, max(2, steps // 16)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(K):
+            run()
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(R):
+        g.replay()
+    torch.cuda.synchronize()
+    gms = (time.perf_counter() - t0) * 1000.0 / (R * K)
+    balg = 2 * 4 * b * H * P * N + sx * (b * H * P + 2 * b * G * N) + 4 * b * H + 4 * b * H * P
+    return {"what": "ssd_step: one token per (row, head), fp32 state read and written in place",
+            "batch": b, "kernel_ms": round(kms, 5), "kernel_ms_median": round(ms[len(ms) // 2], 5),
+            "eager_ms_per_token": round(wall * 1000.0, 5), "graph_ms_per_token": round(gms, 5),
+            "tokens_per_s_graph": round(b / (gms / 1000.0), 1),
+            "roofline": {"bound": "hbm", "achieved": round(balg / (kms / 1000.0) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(balg / (kms / 1000.0) / 1e9 / HBM_PEAK_GBS, 4),
+                         "alg_bytes_per_launch": balg, "kernel": "ssd_step_kernel"}}
+
+
+def fused_step_size_leg(w, prob, d, steps: int, warmup: int):
+    """Time the forward fed the raw step size and a per-head bias: softplus(dt + bias)
+    and the Euler input scaling are computed in the scan kernel's per-token preparation."""
+    import torch
+
+    import ssd_inputs as si
+    import mamba_ssd_scan_chunked_amd as ssd
+    dev = d["x"].device
+    b, T, H, P, N, G = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups
+    raw = si.raw_step_sizes(b, T, H, seed=w.seed + 100, lo=w.dt_range[0], hi=w.dt_range[1])
+    dt_raw, bias = raw["dt"].to(dev), raw["dt_bias"].to(dev)
+    dtype = ssd.DTYPE_BF16 if w.dtype == "bf16" else ssd.DTYPE_F32
+    flags = ssd.FLAG_DT_SOFTPLUS | ssd.FLAG_DT_SCALES_X
+    p = ssd.problem(b, T, H, P, N, G, w.chunk_len, prob["nseqs"], dtype, flags)
+    y = torch.empty((b, T, H, P), dtype=torch.float32, device=dev)
+    fin = torch.empty((prob["nseqs"], H, P, N), dtype=torch.float32, device=dev)
+    wsb = ssd.workspace_size(p)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb > 0 else None
+    stream = torch.cuda.current_stream(dev)
+
+    def run():
+        ssd.forward_into(p, d["x"], dt_raw, d["A_log"], d["B"], d["C"], d["D"], d["init"], d["seq_idx"], y, fin,
+                         ws, stream=stream, dt_bias=bias)
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for e in evs:
+        e[0].record(stream)
+        run()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
+    mean = sum(ms) / len(ms)
+    balg = algorithmic_bytes(w, prob["init"] is not None) + 4 * H
+    return {"what": "ssd_forward with the step-size map softplus(dt + dt_bias) and the Euler input scaling "
+                    "fused into the scan kernel",
+            "kernel_ms": round(mean, 5), "kernel_ms_median": round(ms[len(ms) // 2], 5),
+            "roofline": {"bound": "hbm", "achieved": round(balg / (mean / 1000.0) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(balg / (mean / 1000.0) / 1e9 / HBM_PEAK_GBS, 4),
+                         "alg_bytes_per_launch": balg}}
+
+
 def kernel_source_hash() -> str:
     """Hash of the sources of the forward path (kernels, instantiations, host
     launch code); the backward's files and the instance generator are left out."""
@@ -170,6 +275,7 @@ def main():
     ap.add_argument("--workload", default="m2p7_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass leg")
+    ap.add_argument("--no-extra-legs", action="store_true", help="skip the decoding-step and fused step-size legs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of known size (reference for the HBM traffic counters)")
     args = ap.parse_args()
@@ -250,6 +356,11 @@ def main():
     if not args.no_backward:
         bwd = backward_leg(w, prob, d, steps=max(5, min(args.steps, 20)), warmup=2)
 
+    step = fused = None
+    if not args.no_extra_legs:
+        step = step_leg(w, prob, d, steps=max(20, args.steps), warmup=3)
+        fused = fused_step_size_leg(w, prob, d, steps=max(5, min(args.steps, 20)), warmup=2)
+
     base = None
     if not args.no_cpu_baseline:
         base = cpu_baseline(prob, w)
@@ -262,7 +373,8 @@ def main():
                       "headdim": w.headdim, "dstate": w.dstate, "ngroups": w.ngroups, "chunk_len": w.chunk_len,
                       "kernel_block": 64 if w.chunk_len >= 64 else w.chunk_len, "outputs": "y fp32 + final fp32",
                       "parallelism": "single GPU"},
-           "roofline": roofline, "cpu_baseline": base, "backward": bwd}
+           "roofline": roofline, "cpu_baseline": base, "backward": bwd, "step": step,
+           "fused_step_size": fused}
     print(json.dumps(out), flush=True)
 
 
