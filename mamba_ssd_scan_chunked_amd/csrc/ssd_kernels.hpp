@@ -365,55 +365,63 @@ struct StepParams {
     int x_scale;            // as in ScanParams
 };
 
-// One workgroup of 256 threads per (row, head).  Thread t owns state row
-// p = t / R (R = 256 / P threads per row) and the NPT = N / R consecutive
-// values n in [q NPT, (q + 1) NPT), q = t % R; the read-out of row p is summed
-// over its R lanes (consecutive in the wave) in a fixed order.
+// One workgroup of 256 threads per (row, head).  The head's state is P rows of
+// L = N/4 float4s; in pass j thread t handles float4 f = 256 j + t, i.e. row
+// p = f / L and columns n = 4c .. 4c+3 with c = t % L, the same columns in every
+// pass, so B and C are read once per thread.  Each pass reads and writes 4 KB
+// of contiguous state per workgroup (64 lanes x 16 bytes per instruction), and
+// the read-out of row p is summed over its L lanes (consecutive in the wave) by
+// a fixed butterfly, so y is deterministic.
 template <typename TI, int P, int N>
 __global__ __launch_bounds__(256) void ssd_step_kernel(StepParams prm) {
-    constexpr int R = 256 / P, NPT = N / R;
-    static_assert(256 % P == 0 && R <= 64 && N % R == 0, "step shape");
+    constexpr int L = N / 4, F = P * N / 4, J = (F + 255) / 256;
+    static_assert(N % 4 == 0 && L <= 64 && 64 % L == 0 && F >= 64, "step shape");
     const int64_t bh = blockIdx.x;
     const int64_t b = bh / prm.H, h = bh % prm.H;
     const int64_t g = h / (prm.H / prm.G);
-    const int tid = threadIdx.x, p = tid / R, q = tid % R;
-    const float xv = to_f32(((const TI*)prm.x)[bh * P + p]);
+    const int tid = threadIdx.x, c = tid % L;
     const float A = -expf(prm.A_log[h]);
     const float dtv = step_size(prm.dt[bh] + (prm.dt_bias ? prm.dt_bias[h] : 0.f), prm.dt_softplus);
     const float a = expf(dtv * A);
-    const float xs = x_factor(dtv, A, prm.x_scale) * xv;         // input scaling (D uses the unscaled x)
-    const TI* Bg = (const TI*)prm.B + (b * prm.G + g) * N + q * NPT;
-    const TI* Cg = (const TI*)prm.C + (b * prm.G + g) * N + q * NPT;
-    float* srow = prm.state + (bh * P + p) * N + q * NPT;
-    float acc = 0.f;
-    if constexpr (NPT % 4 == 0) {
+    const float xf = x_factor(dtv, A, prm.x_scale);              // input scaling (D uses the unscaled x)
+    const float Dh = prm.D ? prm.D[h] : 0.f;
+    const TI* Bg = (const TI*)prm.B + (b * prm.G + g) * N + 4 * c;
+    const TI* Cg = (const TI*)prm.C + (b * prm.G + g) * N + 4 * c;
+    float bv[4], cv[4];
 #pragma unroll
-        for (int j = 0; j < NPT; j += 4) {
-            float4 sv = *(const float4*)(srow + j);
-            float bv[4], cv[4];
+    for (int e = 0; e < 4; ++e) {
+        bv[e] = to_f32(Bg[e]);
+        cv[e] = to_f32(Cg[e]);
+    }
+    float4* st = (float4*)(prm.state + bh * P * N);
+    const TI* xr = (const TI*)prm.x + bh * P;
+    float4 sv[J];
+    float xv[J];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                bv[e] = to_f32(Bg[j + e]);
-                cv[e] = to_f32(Cg[j + e]);
-            }
-            sv.x = a * sv.x + xs * bv[0];
-            sv.y = a * sv.y + xs * bv[1];
-            sv.z = a * sv.z + xs * bv[2];
-            sv.w = a * sv.w + xs * bv[3];
-            *(float4*)(srow + j) = sv;
-            acc += cv[0] * sv.x + cv[1] * sv.y + cv[2] * sv.z + cv[3] * sv.w;
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < NPT; ++j) {
-            const float sv = a * srow[j] + xs * to_f32(Bg[j]);
-            srow[j] = sv;
-            acc += to_f32(Cg[j]) * sv;
+    for (int j = 0; j < J; ++j) {                                // every load issued before any store
+        const int f = 256 * j + tid;
+        if (F % 256 == 0 || f < F) {
+            sv[j] = st[f];
+            xv[j] = to_f32(xr[f / L]);
         }
     }
 #pragma unroll
-    for (int d = R / 2; d >= 1; d >>= 1) acc += __shfl_xor(acc, d);
-    if (q == 0) prm.y[bh * P + p] = acc + (prm.D ? prm.D[h] : 0.f) * xv;
+    for (int j = 0; j < J; ++j) {
+        const int f = 256 * j + tid;
+        if (F % 256 == 0 || f < F) {                             // whole rows, so whole butterfly groups
+            const float xs = xf * xv[j];
+            float4 v = sv[j];
+            v.x = a * v.x + xs * bv[0];
+            v.y = a * v.y + xs * bv[1];
+            v.z = a * v.z + xs * bv[2];
+            v.w = a * v.w + xs * bv[3];
+            st[f] = v;
+            float acc = cv[0] * v.x + cv[1] * v.y + cv[2] * v.z + cv[3] * v.w;
+#pragma unroll
+            for (int d = L / 2; d >= 1; d >>= 1) acc += __shfl_xor(acc, d);
+            if (c == 0) prm.y[bh * P + f / L] = acc + Dh * xv[j];
+        }
+    }
 }
 
 // ============================================================== scan kernel
