@@ -642,13 +642,15 @@ void ssd_scan_kernel(ScanParams prm) {
         for (int j = 0; j < MTH; ++j)
             *(float4*)(dst + nrow<N>(mb + j, 4 * lg)) = make_float4(s[j][0], s[j][1], s[j][2], s[j][3]);
     };
-    // this wave's half of the state, as read-out operands, for its partner
+    // this wave's half of the state, as read-out operands, for its partner; the
+    // same operands are kept for this wave's own next read-out (the state does
+    // not change in between)
+    frag sfk[NKH];
     auto sx_store = [&]() {
         if constexpr (NH > 1) {
-            frag f[NKH];
-            state_frags<MTH>(st, f);
+            state_frags<MTH>(st, sfk);
 #pragma unroll
-            for (int j = 0; j < NKH; ++j) *(frag*)(sxo + j * 64 * KPL) = f[j];
+            for (int j = 0; j < NKH; ++j) *(frag*)(sxo + j * 64 * KPL) = sfk[j];
         }
     };
 
@@ -873,7 +875,14 @@ void ssd_scan_kernel(ScanParams prm) {
     auto state_phase = [&]() {
         const int nstart = nstart_c;
         frag sfo[NKH], sfp[NKH];
-        if constexpr (!LOCAL) state_frags<MTH>(st, sfo);
+        if constexpr (!LOCAL) {
+            if constexpr (NH > 1) {
+#pragma unroll
+                for (int j = 0; j < NKH; ++j) sfo[j] = sfk[j];
+            } else {
+                state_frags<MTH>(st, sfo);
+            }
+        }
         if constexpr (NH > 1 && !LOCAL) {
 #pragma unroll
             for (int j = 0; j < NKH; ++j) sfp[j] = *(const frag*)(sxp + j * 64 * KPL);
@@ -1001,20 +1010,22 @@ void ssd_scan_kernel(ScanParams prm) {
     constexpr int DKS = (KSTEP == 32 && NH == 2) ? 2 : 0;          // X operands kept across the barrier
     frag xd[DKS > 0 ? DKS : 1];
     auto diag_pre = [&]() {
+        if (prm.D) {                                             // skip term (none without D)
 #pragma unroll
-        for (int i = 0; i < RTH; ++i) {
-            const int t = 16 * K::own_tile(nh, i) + lr;
-            float xv[4];
-            if constexpr (SZ == 2) {
-                const bf16x4 x4 = *(const bf16x4*)(sXr + t * LR + xc + 4 * lg);
+            for (int i = 0; i < RTH; ++i) {
+                const int t = 16 * K::own_tile(nh, i) + lr;
+                float xv[4];
+                if constexpr (SZ == 2) {
+                    const bf16x4 x4 = *(const bf16x4*)(sXr + t * LR + xc + 4 * lg);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) xv[q] = (float)x4[q];
-            } else {
-                const float4 x4 = *(const float4*)(sXr + t * LR + xc + 4 * lg);
-                xv[0] = x4.x; xv[1] = x4.y; xv[2] = x4.z; xv[3] = x4.w;
+                    for (int q = 0; q < 4; ++q) xv[q] = (float)x4[q];
+                } else {
+                    const float4 x4 = *(const float4*)(sXr + t * LR + xc + 4 * lg);
+                    xv[0] = x4.x; xv[1] = x4.y; xv[2] = x4.z; xv[3] = x4.w;
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[i][q] += Dh * xv[q];
             }
-#pragma unroll
-            for (int q = 0; q < 4; ++q) acc[i][q] += Dh * xv[q];
         }
         if constexpr (DKS > 0) {
 #pragma unroll
