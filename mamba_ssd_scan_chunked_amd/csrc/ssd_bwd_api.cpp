@@ -16,29 +16,59 @@
 
 namespace ssd {
 // dB or dC of a group = the sum of its heads' contributions (fp32 or bf16), in
-// head order, in fp32.  One thread per 4 consecutive outputs.
-__device__ inline float4 load4(const float* p) { return *(const float4*)p; }
-__device__ inline float4 load4(const __bf16* p) {
-    const bf16x4 v = *(const bf16x4*)p;
-    return make_float4((float)v[0], (float)v[1], (float)v[2], (float)v[3]);
+// head order, in fp32.  One thread per 8 consecutive outputs; the loads of four
+// heads are issued before their sums, so each thread keeps several in flight.
+struct F8 {
+    float v[8];
+};
+__device__ inline F8 load8(const float* p) {
+    const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+    return F8{{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w}};
+}
+__device__ inline F8 load8(const __bf16* p) {
+    const uint4 u = *(const uint4*)p;
+    F8 r;
+    const unsigned w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        r.v[2 * k] = __uint_as_float(w[k] << 16);
+        r.v[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+    }
+    return r;
 }
 template <typename S>
 __global__ __launch_bounds__(256) void ssd_bwd_group_sum_kernel(const S* __restrict__ src, float* __restrict__ dst,
                                                                 int64_t rows, int H, int G, int N) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;        // float4 index of dst
-    const int n4 = N / 4;
-    const int64_t total = rows * G * n4;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;        // 8-wide chunk of dst
+    const int n8 = N / 8;
+    const int64_t total = rows * G * n8;
     if (i >= total) return;
-    const int64_t bt = i / (G * n4);
-    const int g = (int)((i / n4) % G), c = (int)(i % n4);
+    const int64_t bt = i / (G * n8);
+    const int g = (int)((i / n8) % G), c = (int)(i % n8);
     const int hpg = H / G;
-    const S* s = src + (bt * H + (int64_t)g * hpg) * N + 4 * c;
-    float4 acc = load4(s);
-    for (int j = 1; j < hpg; ++j) {
-        const float4 v = load4(s + (int64_t)j * N);
-        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    const S* s = src + (bt * H + (int64_t)g * hpg) * N + 8 * c;
+    float acc[8];
+    const F8 first = load8(s);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = first.v[k];
+    int j = 1;
+    for (; j + 4 <= hpg; j += 4) {
+        F8 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = load8(s + (int64_t)(j + u) * N);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int k = 0; k < 8; ++k) acc[k] += v[u].v[k];
     }
-    ((float4*)dst)[i] = acc;
+    for (; j < hpg; ++j) {
+        const F8 v = load8(s + (int64_t)j * N);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[k] += v.v[k];
+    }
+    float4* d = (float4*)(dst + 8 * i);
+    d[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    d[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
 }
 
 // dt (b, T, H) -> (b, H, T): the backward kernels read each (row, head)'s step
@@ -413,8 +443,8 @@ int ssd_backward(const ssd_problem_t* p, const void* x, const float* dt, const f
         e = bf ? ssd::launch_bwd_bf16(P, N, prm, grid, st) : ssd::launch_bwd_f32(P, N, prm, grid, st);
     if (e == hipSuccess && per_head) {
         const int64_t rows = p->batch * p->seqlen;
-        const int64_t n4 = rows * p->ngroups * N / 4;
-        const unsigned blocks = (unsigned)((n4 + 255) / 256);
+        const int64_t n8 = rows * p->ngroups * N / 8;
+        const unsigned blocks = (unsigned)((n8 + 255) / 256);
         if (prm.h_bf16) {
             hipLaunchKernelGGL(ssd::ssd_bwd_group_sum_kernel<__bf16>, dim3(blocks), dim3(256), 0, st,
                                (const __bf16*)prm.dBh, dB, rows, (int)p->nheads, (int)p->ngroups, N);
