@@ -179,8 +179,10 @@ def step_leg(w, prob, d, steps: int, warmup: int):
 
 
 def fused_step_size_leg(w, prob, d, steps: int, warmup: int):
-    """Time the forward fed the raw step size and a per-head bias: softplus(dt + bias)
-    and the Euler input scaling are computed in the scan kernel's per-token preparation."""
+    """Time the forward fed the raw step size and a per-head bias (softplus(dt + bias)
+    and the Euler input scaling computed in the scan kernel's per-token preparation)
+    against the plain forward, the two launches alternating so that both see the
+    same clock state."""
     import torch
 
     import ssd_inputs as si
@@ -190,35 +192,43 @@ def fused_step_size_leg(w, prob, d, steps: int, warmup: int):
     raw = si.raw_step_sizes(b, T, H, seed=w.seed + 100, lo=w.dt_range[0], hi=w.dt_range[1])
     dt_raw, bias = raw["dt"].to(dev), raw["dt_bias"].to(dev)
     dtype = ssd.DTYPE_BF16 if w.dtype == "bf16" else ssd.DTYPE_F32
-    flags = ssd.FLAG_DT_SOFTPLUS | ssd.FLAG_DT_SCALES_X
-    p = ssd.problem(b, T, H, P, N, G, w.chunk_len, prob["nseqs"], dtype, flags)
+    pf = ssd.problem(b, T, H, P, N, G, w.chunk_len, prob["nseqs"], dtype, ssd.FLAG_DT_SOFTPLUS | ssd.FLAG_DT_SCALES_X)
+    pp = ssd.problem(b, T, H, P, N, G, w.chunk_len, prob["nseqs"], dtype, 0)
     y = torch.empty((b, T, H, P), dtype=torch.float32, device=dev)
     fin = torch.empty((prob["nseqs"], H, P, N), dtype=torch.float32, device=dev)
-    wsb = ssd.workspace_size(p)
+    wsb = max(ssd.workspace_size(pf), ssd.workspace_size(pp))
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb > 0 else None
     stream = torch.cuda.current_stream(dev)
 
-    def run():
-        ssd.forward_into(p, d["x"], dt_raw, d["A_log"], d["B"], d["C"], d["D"], d["init"], d["seq_idx"], y, fin,
+    def fused():
+        ssd.forward_into(pf, d["x"], dt_raw, d["A_log"], d["B"], d["C"], d["D"], d["init"], d["seq_idx"], y, fin,
                          ws, stream=stream, dt_bias=bias)
 
+    def plain():
+        ssd.forward_into(pp, d["x"], d["dt"], d["A_log"], d["B"], d["C"], d["D"], d["init"], d["seq_idx"], y, fin,
+                         ws, stream=stream)
+
     for _ in range(warmup):
-        run()
+        fused()
+        plain()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     for e in evs:
         e[0].record(stream)
-        run()
+        fused()
         e[1].record(stream)
+        e[2].record(stream)
+        plain()
+        e[3].record(stream)
     torch.cuda.synchronize()
-    ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
-    mean = sum(ms) / len(ms)
+    mf = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    mp = sum(e[2].elapsed_time(e[3]) for e in evs) / steps
     balg = algorithmic_bytes(w, prob["init"] is not None) + 4 * H
     return {"what": "ssd_forward with the step-size map softplus(dt + dt_bias) and the Euler input scaling "
-                    "fused into the scan kernel",
-            "kernel_ms": round(mean, 5), "kernel_ms_median": round(ms[len(ms) // 2], 5),
-            "roofline": {"bound": "hbm", "achieved": round(balg / (mean / 1000.0) / 1e9, 1), "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": round(balg / (mean / 1000.0) / 1e9 / HBM_PEAK_GBS, 4),
+                    "fused into the scan kernel, launches alternating with the plain forward",
+            "kernel_ms": round(mf, 5), "plain_kernel_ms": round(mp, 5), "ratio_to_plain": round(mf / mp, 4),
+            "roofline": {"bound": "hbm", "achieved": round(balg / (mf / 1000.0) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(balg / (mf / 1000.0) / 1e9 / HBM_PEAK_GBS, 4),
                          "alg_bytes_per_launch": balg}}
 
 
