@@ -29,6 +29,9 @@
  *    host before any HIP call, so a rejected call has enqueued nothing.
  *  - The library keeps no per-call state; concurrent calls on different
  *    streams with disjoint outputs and workspaces are safe.
+ *  - A call only launches kernels on `stream` (no allocation, memset, copy or
+ *    synchronisation), so it may be recorded into a HIP graph by stream capture
+ *    and replayed; the captured pointers must stay valid for every replay.
  */
 #ifndef SSD_MI355X_H
 #define SSD_MI355X_H
