@@ -174,6 +174,25 @@ __device__ inline bf16x8 c_frag(const __bf16* row, int k, int lg) { return *(con
 template <int N>
 __device__ inline float c_frag(const float* row, int k, int lg) { return row[nrow<N>(k >> 2, 4 * lg + (k & 3))]; }
 
+// XOR swizzle of the bf16 B and X tiles in LDS.  Row r of a tile keeps its
+// 8-byte units (four bf16), unit u at position u ^ swz(r) (only the low five
+// bits of u change, so a unit stays in its 256-byte span of the row).  swz is
+// linear over GF(2): for row indices with disjoint bits, swz(a + b) = swz(a) ^
+// swz(b), so the part that is a compile-time constant folds away.  The masks
+// were chosen by an exhaustive bank model of the tiles' accesses (the 16-byte
+// row writes, the transposing reads of the state update, the row reads of
+// C B^T and of the skip term): they leave the B tile free of bank conflicts
+// for N = 128 (within 1.25x of it for N = 256) and the X tile within 1.35x for
+// 80-channel workgroups, against 2x (B) and 1.8x (X) for the padded layout.
+__device__ inline int swz(int r) {
+    return (__builtin_popcount(r & 7) & 1) | ((__builtin_popcount(r & 50) & 1) << 1) |
+           ((__builtin_popcount(r & 6) & 1) << 2) | ((__builtin_popcount(r & 28) & 1) << 3) |
+           ((__builtin_popcount(r & 5) & 1) << 4);
+}
+// Element offset of unit u of row r in a tile of pitch lp elements.
+template <bool SW>
+__device__ inline int unit_off(int r, int u, int lp) { return r * lp + 4 * (SW ? (u ^ swz(r)) : u); }
+
 // Operand fragment of X^T (row = channel p0 + l%16, K = tokens ks + KPL*(l/16) ..)
 // read from a row-major tile sX[t][p] (pitch lp elements).  bf16: the LDS
 // transpose read; within each group of 16 lanes, lane j reads 4 channels
@@ -181,35 +200,38 @@ __device__ inline float c_frag(const float* row, int k, int lg) { return row[nro
 // p0 + i of rows R .. R+3; two reads give the 8 tokens of one K step.
 // fp32: one value per lane, no transpose needed.
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+template <bool SW = false>
 __device__ inline bf16x8 x_frag(const __bf16* sX, int lp, int ks, int p0, int lr, int lg) {
-    const __bf16* a = sX + (ks + 8 * lg + (lr >> 2)) * lp + p0 + 4 * (lr & 3);
+    const int rl = 8 * lg + (lr >> 2), u = (p0 >> 2) + (lr & 3);
+    const __bf16* a = SW ? sX + unit_off<SW>(ks + rl, u, lp) : sX + (ks + rl) * lp + p0 + 4 * (lr & 3);
+    const __bf16* a4 = SW ? sX + unit_off<SW>(ks + 4 + rl, u, lp) : a + 4 * lp;
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)a);
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(a + 4 * lp));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)a4);
     const bf16x4 l4 = __builtin_bit_cast(bf16x4, lo), h4 = __builtin_bit_cast(bf16x4, hi);
     return __builtin_shufflevector(l4, h4, 0, 1, 2, 3, 4, 5, 6, 7);
 }
+template <bool SW = false>
 __device__ inline float x_frag(const float* sX, int lp, int ks, int p0, int lr, int lg) {
     return sX[(ks + lg) * lp + p0 + lr];
 }
 
 // The same operand with every token t scaled by wt(t) (and rounded once to the
 // input type): the K values a lane holds are tokens ks + KPL*(l/16) + e.
-template <typename F>
+template <bool SW = false, typename F>
 __device__ inline bf16x8 weighted_x_frag(const __bf16* sX, int lp, int ks, int p0, int lr, int lg, F wt) {
-    const bf16x8 x = x_frag(sX, lp, ks, p0, lr, lg);
+    const bf16x8 x = x_frag<SW>(sX, lp, ks, p0, lr, lg);
     bf16x8 r;
 #pragma unroll
     for (int e = 0; e < 8; ++e) r[e] = (__bf16)(wt(ks + 8 * lg + e) * (float)x[e]);
     return r;
 }
-template <typename F>
+template <bool SW = false, typename F>
 __device__ inline float weighted_x_frag(const float* sX, int lp, int ks, int p0, int lr, int lg, F wt) {
     return wt(ks + lg) * x_frag(sX, lp, ks, p0, lr, lg);
 }
 
-// B tile in LDS: row t holds the N values of token t, pitch LB = N + 4
-// elements (8-byte aligned rows for bf16).  The transposing reads of the state
-// update and the row reads of C B^T see at most 2-way bank conflicts.
+// B tile in LDS: row t holds the N values of token t, pitch LB elements: N + 4
+// (8-byte aligned rows), or N with the swizzle above for bf16 and N >= 128.
 
 // A operand of the state update for state tile m and the K step of tokens
 // ks .. ks+KSTEP-1: row rho = l % 16 is state row n = nrow(m, rho), K values are
@@ -217,28 +239,32 @@ __device__ inline float weighted_x_frag(const float* sX, int lp, int ks, int p0,
 // token-major B tile; lane j of each 16-lane group loads the four values
 // n = nrow(m, 4(j%4)) .. +3 of token ks + 8(l/16) + j/4 (+4 for the second read)
 // and the hardware hands lane i row nrow(m, i) of those four tokens.
-template <int N, int LB>
+template <int N, int LB, bool SW = false>
 __device__ inline bf16x8 bt_frag(const __bf16* sB, int m, int ks, int lr, int lg) {
-    const __bf16* lo = sB + (ks + 8 * lg + (lr >> 2)) * LB + nrow<N>(m, 4 * (lr & 3));
+    const int rl = 8 * lg + (lr >> 2), u = nrow<N>(m, 4 * (lr & 3)) >> 2;
+    const __bf16* lo = SW ? sB + unit_off<SW>(ks + rl, u, LB) : sB + (ks + rl) * LB + nrow<N>(m, 4 * (lr & 3));
+    const __bf16* l4 = SW ? sB + unit_off<SW>(ks + 4 + rl, u, LB) : lo + 4 * LB;
     const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)lo);
-    const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(lo + 4 * LB));
+    const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)l4);
     return __builtin_shufflevector(__builtin_bit_cast(bf16x4, a), __builtin_bit_cast(bf16x4, b), 0, 1, 2, 3, 4, 5, 6, 7);
 }
-template <int N, int LB>
+template <int N, int LB, bool SW = false>
 __device__ inline float bt_frag(const float* sB, int m, int ks, int lr, int lg) {
     return sB[(ks + lg) * LB + nrow<N>(m, lr)];
 }
 
 // Operand of C B^T holding B row s at the K indices n of step k (natural order):
 // bf16 n = 32k + 8(l/16) .. +7 (two 8-byte reads); fp32 n = 4k + l/16.
-template <int N, int LB>
+template <int N, int LB, bool SW = false>
 __device__ inline bf16x8 brow_frag(const __bf16* sB, int s, int k, int lg) {
-    const __bf16* r = sB + s * LB + 32 * k + 8 * lg;
-    const bf16x4 a = *(const bf16x4*)r;
-    const bf16x4 b = *(const bf16x4*)(r + 4);
+    const int u = 8 * k + 2 * lg;
+    const __bf16* r0 = SW ? sB + unit_off<SW>(s, u, LB) : sB + s * LB + 32 * k + 8 * lg;
+    const __bf16* r1 = SW ? sB + unit_off<SW>(s, u + 1, LB) : r0 + 4;
+    const bf16x4 a = *(const bf16x4*)r0;
+    const bf16x4 b = *(const bf16x4*)r1;
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
-template <int N, int LB>
+template <int N, int LB, bool SW = false>
 __device__ inline float brow_frag(const float* sB, int s, int k, int lg) {
     return sB[s * LB + 4 * k + lg];
 }
@@ -481,11 +507,17 @@ struct ScanCfg {
                                                       // needs more registers, are left at two)
     static constexpr int MTH = MT / NH, NKH = NK / NH, RTH = RT / NH;
     static constexpr int LC = N + VE;                 // pitch of C rows (elements)
-    static constexpr int LB = N + 4;                  // pitch of B rows
+    // Swizzled B and X tiles (bf16).  Their addresses cost registers, so they are
+    // used only for five-slice workgroups with N = 128 and 64-token blocks (one
+    // workgroup per CU, three waves per SIMD: 168 VGPRs); elsewhere they spill.
+    static constexpr bool SWB = SZ == 2 && N == 128 && SPW_ == 5 && QB == 64;
+    static constexpr bool SWX = SWB;
+    static constexpr int LB = SWB ? N : N + 4;        // pitch of B rows
     static constexpr int LQ = QB + VE;                // pitch of the rows of L o CB (indexed by token s)
-    static constexpr int LR = XW + 32 / SZ;           // pitch of the row-major X tile (32 bytes of pad:
+    static constexpr int LR = SWX ? 128 : XW + 32 / SZ;  // pitch of the row-major X tile (fp32: 32 bytes of pad:
                                                       // the four rows of a transposed read fall in
                                                       // distinct banks)
+    static_assert(!SWX || XW <= 128, "a swizzled X row holds at most 128 channels");
     static constexpr int NTILE = RT * (RT + 1) / 2;   // causal 16x16 tiles of L o CB
     static constexpr int TPW = (NTILE + NW - 1) / NW; // causal tiles per wave (surplus slots repeat a tile)
     // LDS tiles: C, B (both token-major), masked decay L o CB, X (row-major; the
@@ -729,7 +761,10 @@ void ssd_scan_kernel(ScanParams prm) {
             if (K::CV % NT == 0 || v < K::CV) {
                 const int t = v / (N / VE), c = v % (N / VE);
                 if constexpr (!LOCAL) *(uint4*)(sC + t * LC + c * VE) = cr[j];
-                if constexpr (SZ == 2) {
+                if constexpr (K::SWB) {                        // swizzled 8-byte units
+                    *(uint2*)(sB + unit_off<true>(t, 2 * c, LB)) = make_uint2(br[j].x, br[j].y);
+                    *(uint2*)(sB + unit_off<true>(t, 2 * c + 1, LB)) = make_uint2(br[j].z, br[j].w);
+                } else if constexpr (SZ == 2) {
                     TI* d = sB + t * LB + c * VE;          // 8-byte aligned rows
                     *(uint2*)d = make_uint2(br[j].x, br[j].y);
                     *(uint2*)(d + 4) = make_uint2(br[j].z, br[j].w);
@@ -788,7 +823,15 @@ void ssd_scan_kernel(ScanParams prm) {
 #pragma unroll
         for (int j = 0; j < K::XPT; ++j) {
             const int v = tid + j * NT;
-            if (K::XU % NT == 0 || v < K::XU) *(uint4*)(sXr + (v / (XW / VE)) * LR + (v % (XW / VE)) * VE) = xr[j];
+            if (K::XU % NT == 0 || v < K::XU) {
+                const int t = v / (XW / VE), c = v % (XW / VE);
+                if constexpr (K::SWX) {
+                    *(uint2*)(sXr + unit_off<true>(t, 2 * c, LR)) = make_uint2(xr[j].x, xr[j].y);
+                    *(uint2*)(sXr + unit_off<true>(t, 2 * c + 1, LR)) = make_uint2(xr[j].z, xr[j].w);
+                } else {
+                    *(uint4*)(sXr + t * LR + c * VE) = xr[j];
+                }
+            }
         }
     };
 
@@ -811,7 +854,7 @@ void ssd_scan_kernel(ScanParams prm) {
         for (int k = 0; k < NK; ++k)
 #pragma unroll
             for (int j = 0; j < K::TPW; ++j)
-                cbt[j] = MF::mma(brow_frag<N, LB>(sB, 16 * tJ[j] + lr, k, lg),
+                cbt[j] = MF::mma(brow_frag<N, LB, K::SWB>(sB, 16 * tJ[j] + lr, k, lg),
                                  crow_frag<N>(sC + (16 * tI[j] + lr) * LC, k, lg), cbt[j]);
         // the same C B^T tile under the decay of each head of the workgroup
 #pragma unroll
@@ -913,9 +956,9 @@ void ssd_scan_kernel(ScanParams prm) {
             for (int j = 0; j < MTH; ++j) st[j] *= alpha;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const frag xw = weighted_x_frag(sXr, LR, ks * KSTEP, xc, lr, lg, [&](int t) { return sWx[t]; });
+                const frag xw = weighted_x_frag<K::SWX>(sXr, LR, ks * KSTEP, xc, lr, lg, [&](int t) { return sWx[t]; });
 #pragma unroll
-                for (int j = 0; j < MTH; ++j) st[j] = MF::mma(bt_frag<N, LB>(sB, mb + j, ks * KSTEP, lr, lg), xw, st[j]);
+                for (int j = 0; j < MTH; ++j) st[j] = MF::mma(bt_frag<N, LB, K::SWB>(sB, mb + j, ks * KSTEP, lr, lg), xw, st[j]);
             }
 #pragma unroll
             for (int i = 0; i < (LOCAL ? 0 : RTH); ++i) acc[i] *= sRow[16 * K::own_tile(nh, i) + lr];
@@ -984,9 +1027,9 @@ void ssd_scan_kernel(ScanParams prm) {
                 }
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    const frag xw = weighted_x_frag(sXr, LR, ks * KSTEP, xc, lr, lg, wseg);
+                    const frag xw = weighted_x_frag<K::SWX>(sXr, LR, ks * KSTEP, xc, lr, lg, wseg);
 #pragma unroll
-                    for (int q = 0; q < MTH; ++q) F[q] = MF::mma(bt_frag<N, LB>(sB, mb + q, ks * KSTEP, lr, lg), xw, F[q]);
+                    for (int q = 0; q < MTH; ++q) F[q] = MF::mma(bt_frag<N, LB, K::SWB>(sB, mb + q, ks * KSTEP, lr, lg), xw, F[q]);
                 }
                 if (j < nstart) {
                     if constexpr (!LOCAL) write_state(F, sSeqOf[j]);
@@ -1016,7 +1059,8 @@ void ssd_scan_kernel(ScanParams prm) {
                 const int t = 16 * K::own_tile(nh, i) + lr;
                 float xv[4];
                 if constexpr (SZ == 2) {
-                    const bf16x4 x4 = *(const bf16x4*)(sXr + t * LR + xc + 4 * lg);
+                    const bf16x4 x4 = *(const bf16x4*)(K::SWX ? sXr + unit_off<true>(t, (xc >> 2) + lg, LR)
+                                                               : sXr + t * LR + xc + 4 * lg);
 #pragma unroll
                     for (int q = 0; q < 4; ++q) xv[q] = (float)x4[q];
                 } else {
@@ -1029,7 +1073,7 @@ void ssd_scan_kernel(ScanParams prm) {
         }
         if constexpr (DKS > 0) {
 #pragma unroll
-            for (int q = 0; q < DKS; ++q) xd[q] = x_frag(sXr, LR, 32 * q, xc, lr, lg);
+            for (int q = 0; q < DKS; ++q) xd[q] = x_frag<K::SWX>(sXr, LR, 32 * q, xc, lr, lg);
         }
     };
     auto diag_phase = [&](int blk) {
@@ -1043,7 +1087,7 @@ void ssd_scan_kernel(ScanParams prm) {
                 for (int q = 0; q < (i == 0 ? 1 : 2); ++q) acc[i] = MF::mma(xd[q], lds_frag<TI>(lrow + 32 * q), acc[i]);
             } else {
                 for (int ks = 0; ks < 16 * (r + 1); ks += KSTEP)
-                    acc[i] = MF::mma(x_frag(sXr, LR, ks, xc, lr, lg), lds_frag<TI>(lrow + ks), acc[i]);
+                    acc[i] = MF::mma(x_frag<K::SWX>(sXr, LR, ks, xc, lr, lg), lds_frag<TI>(lrow + ks), acc[i]);
             }
         }
         const int64_t t0 = (int64_t)blk * QB;
