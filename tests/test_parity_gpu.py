@@ -237,6 +237,10 @@ def test_workload_sampled(name, k):
     (2, 70, 150, 128, 1, 64, True),
     (1, 100, 300, 64, 5, 32, False),      # (H/G)*4 = 240 slices per group: still five per workgroup
     (1, 90, 265, 64, 5, 64, False),       # (H/G)*4 = 212: not a multiple of five, one head per workgroup
+    # N = 128 with 64-token blocks: the swizzled B and X tiles
+    (1, 65, 260, 128, 1, 64, False),      # one token past a block
+    (2, 129, 140, 128, 4, 64, False),     # four groups of 35 heads
+    (3, 1, 100, 128, 1, 64, True),        # a single token
 ])
 def test_five_slice_workgroups(case):
     b, T, H, N, G, Q, euler = case
