@@ -72,10 +72,11 @@ int64_t nblocks(const ssd_problem_t* p) {
 }
 
 // Segments per row.  With at most 128 (row, head) items, rows are split into
-// up to 512 / items segments that run in parallel (a local pass, a combine
+// up to 512 / items segments (256 / items where one workgroup fills a CU) that run in parallel (a local pass, a combine
 // step, then the scan of every segment from its incoming state), down to 4
 // blocks per segment.  (Measured on MI355X: 32 items of 256 blocks run best as
-// 16 segments; 192 items of 32 blocks run best unsplit.)  A function of the problem alone (no device query),
+// 16 segments, or 8 with N = 256; 48 packed-sequence items of 128 blocks as 5;
+// 192 items of 32 blocks run best unsplit.)  A function of the problem alone (no device query),
 // so the workspace size is known on the host; SSD_SEGMENTS=<n> overrides it.
 struct Segs {
     int nseg, seg_blocks;
@@ -89,8 +90,14 @@ Segs segments(const ssd_problem_t* p) {
     if (env && std::atoi(env) > 0) {
         S = std::atoi(env);
     } else {
+        // workgroups the scan keeps resident per CU: one where a single
+        // workgroup fills the CU's registers or LDS (bf16 64-channel heads with
+        // sequence ids, or with N = 256), else two
+        const bool one_per_cu = p->dtype == SSD_DTYPE_BF16 && p->headdim == 64 &&
+                                (p->nseqs != p->batch || p->dstate == 256);
+        const int64_t slots = (one_per_cu ? 1 : 2) * 256;
         const int64_t units = p->batch * p->nheads;
-        if (units <= 128) S = std::min<int64_t>(512 / units, nblk / 4);
+        if (units <= 128) S = std::min<int64_t>(slots / units, nblk / 4);
     }
     S = std::max<int64_t>(1, std::min<int64_t>(S, nblk));
     const int64_t sb = (nblk + S - 1) / S;
