@@ -179,7 +179,7 @@ int bwd_block(const ssd_problem_t* p) { return p->dtype == SSD_DTYPE_BF16 ? ssd:
 // items, rows are cut into up to 512 / items segments of whole 64-token blocks,
 // down to 4 blocks per segment, as the forward does.  With more items, the count
 // S <= 8 that minimises the rounds of workgroups over the 256 CUs per unit of
-// row length, ceil(items S / 256) / S, plus a charge of 0.3 (S - 1) / S for the
+// row length, ceil(items S / 256) / S, plus a charge of 0.5 (S - 1) / S for the
 // local passes (measured on MI355X: 320 items run best as 4 segments, 192 unsplit).
 // SSD_BWD_SEGMENTS=<n> forces n.  A function of the problem alone, so the
 // workspace size is known on the host.
@@ -202,7 +202,7 @@ BwdSegs bwd_segments(const ssd_problem_t* p) {
         } else {
             double best = 1e30;
             for (int64_t c = 1; c <= 8 && (c == 1 || nb64 / c >= 4); ++c) {
-                const double cost = double((units * c + 255) / 256) / double(c) + 0.3 * double(c - 1) / double(c);
+                const double cost = double((units * c + 255) / 256) / double(c) + 0.5 * double(c - 1) / double(c);
                 if (cost < best - 1e-9) {
                     best = cost;
                     S = c;
