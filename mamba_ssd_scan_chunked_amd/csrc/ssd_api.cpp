@@ -37,12 +37,27 @@ __global__ __launch_bounds__(256) void ssd_combine_kernel(CombineParams prm) {
         st = *(const float4*)(prm.init + (seq0 * prm.H + h) * prm.P * prm.N + 4 * e);
     }
     const int ns = prm.nseg - 1;
-    for (int sg = 0; sg < ns; ++sg) {
-        const float c = prm.seg_carry[bh * ns + sg];
-        float4* slot = (float4*)(prm.seg_state + ((bh * ns + sg) * prm.P * prm.N)) + e;
-        const float4 l = *slot;
-        st = make_float4(c * st.x + l.x, c * st.y + l.y, c * st.z + l.z, c * st.w + l.w);
-        *slot = st;
+    const int64_t stride = (int64_t)prm.P * prm.N / 4;               // float4s per segment state
+    float4* base = (float4*)(prm.seg_state + bh * ns * prm.P * prm.N) + e;
+    const float* carry = prm.seg_carry + bh * ns;
+    // eight segments' loads in flight before their (sequential) combine
+    for (int s0 = 0; s0 < ns; s0 += 8) {
+        float4 l[8];
+        float c[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            if (s0 + k < ns) {
+                l[k] = base[(s0 + k) * stride];
+                c[k] = carry[s0 + k];
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            if (s0 + k < ns) {
+                st = make_float4(c[k] * st.x + l[k].x, c[k] * st.y + l[k].y, c[k] * st.z + l[k].z, c[k] * st.w + l[k].w);
+                base[(s0 + k) * stride] = st;
+            }
+        }
     }
 }
 

@@ -151,12 +151,26 @@ __global__ __launch_bounds__(256) void ssd_bwd_kcombine_kernel(const float* __re
     if (bh >= rows_heads) return;
     const int s1 = nseg - 1;
     float4 st = dfinal ? *(const float4*)(dfinal + bh * pn + 4 * e) : make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = s1 - 1; j >= 0; --j) {
-        const float c = kcarry[bh * s1 + j];
-        float4* slot = (float4*)(seg_grad + (bh * s1 + j) * pn) + e;
-        const float4 l = *slot;
-        st = make_float4(c * st.x + l.x, c * st.y + l.y, c * st.z + l.z, c * st.w + l.w);
-        *slot = st;
+    float4* base = (float4*)(seg_grad + bh * s1 * pn) + e;
+    const float* carry = kcarry + bh * s1;
+    // eight segments' loads in flight before their (sequential) combine
+    for (int j0 = s1 - 1; j0 >= 0; j0 -= 8) {
+        float4 l[8];
+        float c[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            if (j0 - k >= 0) {
+                l[k] = base[(j0 - k) * (pn / 4)];
+                c[k] = carry[j0 - k];
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            if (j0 - k >= 0) {
+                st = make_float4(c[k] * st.x + l[k].x, c[k] * st.y + l[k].y, c[k] * st.z + l[k].z, c[k] * st.w + l[k].w);
+                base[(j0 - k) * (pn / 4)] = st;
+            }
+        }
     }
 }
 
