@@ -72,13 +72,25 @@ __global__ __launch_bounds__(256) void ssd_bwd_group_sum_kernel(const S* __restr
 }
 
 // dt (b, T, H) -> (b, H, T): the backward kernels read each (row, head)'s step
-// sizes as one contiguous run per block.
+// sizes as one contiguous run per block.  32 x 32 tiles through LDS, so that
+// both the reads (along heads) and the writes (along tokens) are contiguous;
+// workgroup (x, y) = (row and token tile, head tile).
 __global__ __launch_bounds__(256) void ssd_transpose_dt_kernel(const float* __restrict__ dt, float* __restrict__ dtT,
                                                                int64_t batch, int64_t T, int64_t H) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // index into dtT
-    if (i >= batch * H * T) return;
-    const int64_t t = i % T, bh = i / T;
-    dtT[i] = dt[((bh / H) * T + t) * H + bh % H];
+    __shared__ float tile[32][33];
+    const int64_t ntt = (T + 31) / 32;
+    const int64_t b = (int64_t)blockIdx.x / ntt, t0 = ((int64_t)blockIdx.x % ntt) * 32, h0 = (int64_t)blockIdx.y * 32;
+    const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+    if (b >= batch) return;                                       // (uniform over the workgroup)
+    for (int k = ty; k < 32; k += 8) {
+        const int64_t t = t0 + k, h = h0 + tx;
+        tile[k][tx] = (t < T && h < H) ? dt[(b * T + t) * H + h] : 0.f;
+    }
+    __syncthreads();
+    for (int k = ty; k < 32; k += 8) {
+        const int64_t h = h0 + k, t = t0 + tx;
+        if (h < H && t < T) dtT[(b * H + h) * T + t] = tile[tx][k];
+    }
 }
 
 // Per-head scalars: sums over rows or packed sequences (in order) of the reverse pass's partial sums.
@@ -390,8 +402,8 @@ int ssd_backward(const ssd_problem_t* p, const void* x, const float* dt, const f
         }
     }
     if (e == hipSuccess) {
-        const int64_t n = p->batch * p->nheads * p->seqlen;
-        hipLaunchKernelGGL(ssd::ssd_transpose_dt_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, dt,
+        const dim3 grid((unsigned)(p->batch * ((p->seqlen + 31) / 32)), (unsigned)((p->nheads + 31) / 32));
+        hipLaunchKernelGGL(ssd::ssd_transpose_dt_kernel, grid, dim3(256), 0, st, dt,
                            const_cast<float*>(prm.dt), p->batch, p->seqlen, p->nheads);
         e = hipGetLastError();
     }
