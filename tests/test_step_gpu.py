@@ -27,6 +27,7 @@ SHAPES = [
     ("bf16", 3, 8, 64, 128, 1),
     ("bf16", 2, 6, 32, 256, 3),
     ("bf16", 1, 4, 64, 64, 2),
+    ("bf16", 2, 4, 64, 256, 1),     # a state row spans the whole wave (64 float4 per row)
     ("f32", 2, 4, 16, 16, 1),
     ("f32", 1, 6, 32, 64, 2),
     ("f32", 2, 2, 64, 128, 1),
