@@ -48,6 +48,17 @@ def algorithmic_bytes(w, init_nonzero: bool) -> int:
     return total
 
 
+HEADLINE_METRIC = "SSD fwd tokens/sec (2.7B-layer shape, T=4096) and % of MFMA/HBM roofline"
+
+
+def metric_name(w) -> str:
+    """The headline metric for the 2.7B-layer workload; the same measure named for its own shape elsewhere."""
+    if w.name == "m2p7_bf16":
+        return HEADLINE_METRIC
+    return "SSD fwd tokens/sec (%s: b=%d, T=%d, H=%d, P=%d, N=%d, %s) and %% of MFMA/HBM roofline" % (
+        w.name, w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.dtype)
+
+
 def algorithmic_flops(w) -> int:
     b, T, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk_len
     nc = -(-T // Q)
@@ -396,7 +407,7 @@ def main():
     if not args.no_cpu_baseline:
         base = cpu_baseline(prob, w)
 
-    out = {"metric": "SSD fwd tokens/sec (2.7B-layer shape, T=4096) and % of MFMA/HBM roofline",
+    out = {"metric": metric_name(w),
            "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": w.dtype, "data": "synthetic (seeded; random inputs of the layer's shapes)",

@@ -45,3 +45,10 @@ def test_more_than_one_gpu_is_refused_with_a_message():
                        text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in r.stderr
+
+
+def test_metric_names_its_workload():
+    assert bench.metric_name(si.WORKLOADS["m2p7_bf16"]) == \
+        "SSD fwd tokens/sec (2.7B-layer shape, T=4096) and % of MFMA/HBM roofline"
+    m = bench.metric_name(si.WORKLOADS["long_n256"])
+    assert m.startswith("SSD fwd tokens/sec (long_n256: b=1, T=16384, H=32, P=64, N=256, bf16)")
