@@ -456,6 +456,12 @@ __global__ __launch_bounds__(512) void ssd_bwd_fwd_kernel(BwdParams prm) {
                 }
             }
             const float dec = sCend;
+            // every state tile of this wave has channel tile w mod PT: its weighted X
+            // operands are formed once for all of them
+            static_assert(NW % PT == 0, "a wave's state tiles share one channel tile");
+            decltype(frag_t_w(sX, LP, 0, 0, lr, lg, sWx)) xw[QB / KS];
+#pragma unroll
+            for (int k0 = 0; k0 < QB; k0 += KS) xw[k0 / KS] = frag_t_w(sX, LP, 16 * (w % PT), k0, lr, lg, sWx);
 #pragma unroll
             for (int j = 0; j < K::T_NP; ++j) {
                 const int tile = w + NW * j;
@@ -464,8 +470,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_fwd_kernel(BwdParams prm) {
                     f32x4 acc = st[j] * dec;
 #pragma unroll
                     for (int k0 = 0; k0 < QB; k0 += KS)
-                        acc = M::mma(frag_t(sB, LN, 16 * ni, k0, lr, lg), frag_t_w(sX, LP, 16 * pj, k0, lr, lg, sWx),
-                                     acc);
+                        acc = M::mma(frag_t(sB, LN, 16 * ni, k0, lr, lg), xw[k0 / KS], acc);
                     st[j] = acc;
                     store4(sS + (16 * pj + lr) * LN + 16 * ni + 4 * lg, acc[0], acc[1], acc[2], acc[3]);
                 }
@@ -746,6 +751,12 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
                 }
             }
             const float dec = sCend;
+            // every state tile of this wave has channel tile w mod PT: its weighted dY
+            // operands are formed once for all of them
+            static_assert(NW % PT == 0, "a wave's state tiles share one channel tile");
+            decltype(frag_t_w(sDY, LP, 0, 0, lr, lg, sDin)) yw[QB / KS];
+#pragma unroll
+            for (int k0 = 0; k0 < QB; k0 += KS) yw[k0 / KS] = frag_t_w(sDY, LP, 16 * (w % PT), k0, lr, lg, sDin);
 #pragma unroll
             for (int j = 0; j < K::T_NP; ++j) {
                 const int tile = w + NW * j;
@@ -754,8 +765,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
                     f32x4 acc = kst[j] * dec;
 #pragma unroll
                     for (int k0 = 0; k0 < QB; k0 += KS)
-                        acc = M::mma(frag_t(sC, LN, 16 * ni, k0, lr, lg), frag_t_w(sDY, LP, 16 * pj, k0, lr, lg, sDin),
-                                     acc);
+                        acc = M::mma(frag_t(sC, LN, 16 * ni, k0, lr, lg), yw[k0 / KS], acc);
                     kst[j] = acc;
                     store4(sK + (16 * pj + lr) * LN + 16 * ni + 4 * lg, acc[0], acc[1], acc[2], acc[3]);
                 }
