@@ -900,40 +900,72 @@ __global__ __launch_bounds__(512) void ssd_bwd_klocal_kernel(BwdParams prm, floa
 #pragma unroll
     for (int q = 0; q < K::T_NP; ++q) kst[q] = f32x4{0.f, 0.f, 0.f, 0.f};
     cum_t total = 0;                                   // wave 0: log2 decay across the segment
-    for (int blk = nblk - 1; blk >= 0; --blk) {
+    // dy and C of a block are requested one block ahead (registers), then written to
+    // LDS (dy converted to the input type) while the next block's are in flight
+    constexpr int YC = P / 4, CC = N * SZ / 16, VE = 16 / SZ;
+    constexpr int YU = QB * YC, CU = QB * CC, YPT = (YU + NT - 1) / NT, CPT = (CU + NT - 1) / NT;
+    uint4 yv[YPT], cv[CPT];
+    float dtn = 0.f;                                   // wave 0: the block's dt (lane = token)
+    auto issue = [&](int blk) {
         const int64_t t0 = (int64_t)blk * QB;
-        {   // dy (to the input type) and C of the block into LDS
-            constexpr int YC = P / 4, CC = N * SZ / 16, VE = 16 / SZ;
-            const rsrc_t ry = make_rsrc(yrow + t0 * ys, (T - t0) * ys);
-            const rsrc_t rc = make_rsrc(crow + t0 * bs, (T - t0) * bs);
-            for (int v = tid; v < QB * YC; v += NT) {
-                const float4 f = __builtin_bit_cast(float4, buf_load16(ry, (v / YC) * ys + (v % YC) * 16));
+        const rsrc_t ry = make_rsrc(yrow + t0 * ys, (T - t0) * ys);
+        const rsrc_t rc = make_rsrc(crow + t0 * bs, (T - t0) * bs);
+#pragma unroll
+        for (int q = 0; q < YPT; ++q) {
+            const int v = tid + q * NT;
+            if (YU % NT == 0 || v < YU) yv[q] = buf_load16(ry, (v / YC) * ys + (v % YC) * 16);
+        }
+#pragma unroll
+        for (int q = 0; q < CPT; ++q) {
+            const int v = tid + q * NT;
+            if (CU % NT == 0 || v < CU) cv[q] = buf_load16(rc, (v / CC) * bs + (v % CC) * 16);
+        }
+        if (w == 0) dtn = buf_load_f32(make_rsrc(prm.dt + (b * H + h) * prm.T + s0 + t0, (T - t0) * 4), lane * 4);
+    };
+    auto stage = [&](int blk) {
+#pragma unroll
+        for (int q = 0; q < YPT; ++q) {
+            const int v = tid + q * NT;
+            if (YU % NT == 0 || v < YU) {
+                const float4 f = __builtin_bit_cast(float4, yv[q]);
                 store4(sDY + (v / YC) * LP + (v % YC) * 4, f.x, f.y, f.z, f.w);
             }
-            for (int v = tid; v < QB * CC; v += NT)
-                *(uint4*)(sC + (v / CC) * LN + (v % CC) * VE) = buf_load16(rc, (v / CC) * bs + (v % CC) * 16);
+        }
+#pragma unroll
+        for (int q = 0; q < CPT; ++q) {
+            const int v = tid + q * NT;
+            if (CU % NT == 0 || v < CU) *(uint4*)(sC + (v / CC) * LN + (v % CC) * VE) = cv[q];
         }
         if (w == 0) {
-            const int rows = (int)min((int64_t)QB, T - t0);
-            const float dtv = buf_load_f32(make_rsrc(prm.dt + (b * H + h) * prm.T + s0 + t0, (T - t0) * 4), lane * 4);
-            const float d = lane < rows ? step_size(dtv + dtb, prm.dt_softplus) : 0.f;
+            const int rows = (int)min((int64_t)QB, T - (int64_t)blk * QB);
+            const float d = lane < rows ? step_size(dtn + dtb, prm.dt_softplus) : 0.f;
             const cum_t cum = wave_incl_scan((cum_t)d * A2);
             const cum_t cend = __shfl(cum, QB - 1);
             if (lane < QB) sDin[lane] = fast_exp2((float)cum);
             if (lane == 0) sCend = fast_exp2((float)cend);
             total += cend;
         }
+    };
+    if (nblk > 0) issue(nblk - 1);
+    for (int blk = nblk - 1; blk >= 0; --blk) {
+        stage(blk);
+        if (blk > 0) issue(blk - 1);
         block_sync_lds();
         const float dec = sCend;
+        // every state tile of this wave has channel tile w mod PT: its weighted dY
+        // operands are formed once for all of them
+        static_assert(NW % PT == 0, "a wave's state tiles share one channel tile");
+        decltype(frag_t_w(sDY, LP, 0, 0, lr, lg, sDin)) yw[QB / KS];
+#pragma unroll
+        for (int k0 = 0; k0 < QB; k0 += KS) yw[k0 / KS] = frag_t_w(sDY, LP, 16 * (w % PT), k0, lr, lg, sDin);
 #pragma unroll
         for (int q = 0; q < K::T_NP; ++q) {
             const int tile = w + NW * q;
             if (tile < NTL * PT) {
-                const int ni = tile / PT, pj = tile % PT;
+                const int ni = tile / PT;
                 f32x4 acc = kst[q] * dec;
 #pragma unroll
-                for (int k0 = 0; k0 < QB; k0 += KS)
-                    acc = M::mma(frag_t(sC, LN, 16 * ni, k0, lr, lg), frag_t_w(sDY, LP, 16 * pj, k0, lr, lg, sDin), acc);
+                for (int k0 = 0; k0 < QB; k0 += KS) acc = M::mma(frag_t(sC, LN, 16 * ni, k0, lr, lg), yw[k0 / KS], acc);
                 kst[q] = acc;
             }
         }
