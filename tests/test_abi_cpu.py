@@ -62,6 +62,11 @@ def test_validate_accepts_the_measured_shapes():
     (dict(headdim=48), 3), (dict(dstate=96), 3), (dict(dstate=16), 3), (dict(dtype=7), 3), (dict(flags=8), 3),
     (dict(flags=ssd.FLAG_DT_SCALES_X | ssd.FLAG_ZOH), 3),
     (dict(dtype=ssd.DTYPE_F32, dstate=256), 3),
+    # limits: dimensions below 2^31, and one block of tokens addressable with 32-bit byte offsets
+    (dict(batch=1 << 31, nseqs=1 << 31), 2), (dict(seqlen=1 << 31), 2),
+    (dict(nheads=1 << 20), 3),                        # 64 tokens x 2^20 heads x 64 channels x 4 bytes = 2^34
+    (dict(nheads=1 << 16, ngroups=1 << 16), 3),       # 64 tokens x 2^16 groups x 128 x 4 bytes = 2^31
+    (dict(batch=1 << 20, nseqs=1 << 20, seqlen=1, nheads=1 << 11), 2),   # 2^31 (row, head) workgroups
 ])
 def test_validate_rejects(kw, code):
     assert ssd.validate(prob(**kw)) == code
