@@ -118,3 +118,30 @@ def test_random_backward(seed):
         assert_parity(g[k].cpu().double().numpy(), ref[k], tol, k)
     for k in ("dA_log", "ddt_bias", "dD"):
         assert_parity_sum(g[k].cpu().double().numpy(), ref[k], ref["abs_terms"][k], tol, k)
+
+
+def draw_five_slice(seed):
+    """Shapes with 256 < b*H <= 320 heads of 64 channels (bf16, no sequence ids), which the
+    library packs five 16-channel slices per workgroup: the headline layout."""
+    r = random.Random(seed)
+    H = r.choice([65, 70, 75, 80])
+    G = r.choice([g for g in (1, 5, 13, 2, 4) if H % g == 0 and (H // g) % 5 == 0] or [1])
+    T = r.choice([1, 2]) if r.random() < 0.15 else r.randint(3, 300)
+    return dict(dtype="bf16", b=4, T=T, H=H, G=G, P=64, N=r.choice([64, 128, 256]), chunk=r.choice([32, 64, 256]),
+                d_skip=r.random() < 0.5, init_std=0.5 if r.random() < 0.5 else 0.0, packed=0,
+                mode=r.randrange(len(MODES)), seed=seed)
+
+
+@pytest.mark.parametrize("seed", range(300, 312))
+def test_random_five_slice_forward(seed):
+    import mamba_ssd_scan_chunked_amd as ssd
+    c = draw_five_slice(seed)
+    announce("five-slice forward " + describe(c))
+    prob, dt_bias, kw = problem(c)
+    d = to_device(prob)
+    y, f = ssd.forward(d["x"], d["dt"], d["A_log"], d["B"], d["C"], d["D"], chunk_len=c["chunk"],
+                       init_state=d["init"], dt_bias=dt_bias.cuda() if dt_bias is not None else None, **kw)
+    torch.cuda.synchronize()
+    yr, fr = run_oracle(prob, dt_bias=dt_bias, **kw)
+    assert_parity(y.cpu().double().numpy(), yr, TOL["bf16"], "y")
+    assert_parity(f.cpu().double().numpy(), fr, TOL["bf16"], "final")
