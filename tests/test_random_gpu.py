@@ -145,3 +145,35 @@ def test_random_five_slice_forward(seed):
     yr, fr = run_oracle(prob, dt_bias=dt_bias, **kw)
     assert_parity(y.cpu().double().numpy(), yr, TOL["bf16"], "y")
     assert_parity(f.cpu().double().numpy(), fr, TOL["bf16"], "final")
+
+
+def draw_split(seed):
+    """Few (row, head) items on long rows, which the library cuts into segments (a local
+    pass, the combine step, then every segment's scan)."""
+    r = random.Random(seed)
+    c = draw(seed)
+    G = r.choice([1, 2])
+    c.update(b=r.randint(1, 2), G=G, H=G * r.randint(1, 2), T=r.randint(520, 2000),
+             packed=(r.randint(2, 5) if r.random() < 0.3 else 0))
+    return c
+
+
+@pytest.mark.parametrize("seed", range(400, 410))
+def test_random_split_rows_forward(seed):
+    import mamba_ssd_scan_chunked_amd as ssd
+    c = draw_split(seed)
+    announce("split-row forward " + describe(c))
+    prob, dt_bias, kw = problem(c)
+    d = to_device(prob)
+    packed = prob["seq_idx"] is not None
+    p = ssd.problem(c["b"], c["T"], c["H"], c["P"], c["N"], c["G"], c["chunk"], prob["nseqs"],
+                    ssd.DTYPE_BF16 if c["dtype"] == "bf16" else ssd.DTYPE_F32, 0)
+    assert ssd.workspace_size(p) > 0, "rows are split"
+    y, f = ssd.forward(d["x"], d["dt"], d["A_log"], d["B"], d["C"], d["D"], chunk_len=c["chunk"],
+                       init_state=d["init"], seq_idx=d["seq_idx"], nseqs=prob["nseqs"] if packed else None,
+                       dt_bias=dt_bias.cuda() if dt_bias is not None else None, **kw)
+    torch.cuda.synchronize()
+    yr, fr = run_oracle(prob, dt_bias=dt_bias, **kw)
+    tol = TOL[c["dtype"]]
+    assert_parity(y.cpu().double().numpy(), yr, tol, "y")
+    assert_parity(f.cpu().double().numpy(), fr, tol, "final")
