@@ -177,3 +177,33 @@ def test_random_split_rows_forward(seed):
     tol = TOL[c["dtype"]]
     assert_parity(y.cpu().double().numpy(), yr, tol, "y")
     assert_parity(f.cpu().double().numpy(), fr, tol, "final")
+
+
+@pytest.mark.parametrize("seed", range(500, 506))
+def test_random_split_rows_backward(seed):
+    import numpy as np
+
+    import mamba_ssd_scan_chunked_amd as ssd
+    c = draw_split(seed)
+    c["T"] = min(c["T"], 1200)
+    announce("split-row backward " + describe(c))
+    prob, dt_bias, kw = problem(c)
+    d = to_device(prob)
+    packed = prob["seq_idx"] is not None
+    rng = np.random.default_rng(seed)
+    b, T, H, P = prob["x"].shape
+    N = prob["B"].shape[3]
+    dy = torch.from_numpy(rng.standard_normal((b, T, H, P)).astype(np.float32))
+    dfinal = torch.from_numpy(rng.standard_normal((prob["nseqs"], H, P, N)).astype(np.float32))
+    g = ssd.backward(d["x"], d["dt"], d["A_log"], d["B"], d["C"], dy.cuda(), D=d["D"], init_state=d["init"],
+                     dfinal=dfinal.cuda(), chunk_len=c["chunk"], seq_idx=d["seq_idx"],
+                     nseqs=prob["nseqs"] if packed else None,
+                     dt_bias=dt_bias.cuda() if dt_bias is not None else None, **kw)
+    torch.cuda.synchronize()
+    ref = oracle.gradients(prob["x"], prob["dt"], prob["A_log"], prob["B"], prob["C"], dy, prob["D"], prob["init"],
+                           dfinal, prob["seq_idx"], prob["nseqs"] if packed else None, dt_bias=dt_bias, **kw)
+    tol = TOL[c["dtype"]]
+    for k in ("dx", "ddt", "dB", "dC", "dinit"):
+        assert_parity(g[k].cpu().double().numpy(), ref[k], tol, k)
+    for k in ("dA_log", "ddt_bias", "dD"):
+        assert_parity_sum(g[k].cpu().double().numpy(), ref[k], ref["abs_terms"][k], tol, k)
