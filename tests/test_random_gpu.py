@@ -207,3 +207,22 @@ def test_random_split_rows_backward(seed):
         assert_parity(g[k].cpu().double().numpy(), ref[k], tol, k)
     for k in ("dA_log", "ddt_bias", "dD"):
         assert_parity_sum(g[k].cpu().double().numpy(), ref[k], ref["abs_terms"][k], tol, k)
+
+
+@pytest.mark.parametrize("seed", range(600, 616))
+def test_random_step(seed):
+    """One decoding step from a random state: shape, skip term and step-size mode drawn per seed."""
+    import mamba_ssd_scan_chunked_amd as ssd
+    c = draw(seed)
+    c.update(T=1, packed=0, init_std=0.5)
+    announce("step " + describe(c))
+    prob, dt_bias, kw = problem(c)
+    d = to_device(prob)
+    state = d["init"].clone()
+    y = ssd.step(d["x"], d["dt"], d["A_log"], d["B"], d["C"], d["D"], state,
+                 dt_bias=dt_bias.cuda() if dt_bias is not None else None, **kw)
+    torch.cuda.synchronize()
+    yr, fr = run_oracle(prob, dt_bias=dt_bias, **kw)
+    tol = TOL[c["dtype"]]
+    assert_parity(y.cpu().double().numpy(), yr, tol, "y")
+    assert_parity(state.cpu().double().numpy(), fr, tol, "state")
