@@ -143,8 +143,11 @@ size_t ssd_workspace_size(const ssd_problem_t* p);
  * row r is sequence r (nseqs must equal batch).  Ids outside 0..nseqs-1 are
  * clamped (memory-safe, values undefined).  final_state rows of ids that never
  * occur are not written.  final_state may be the same buffer as init_state
- * (in-place state carry); any other overlap between an output and an input
- * is rejected with SSD_ERR_ALIAS.
+ * (in-place state carry) only without seq_idx and when ssd_workspace_size(p)
+ * is 0 (each row scanned in one piece): then every state element is read and
+ * later written by the same wave.  With seq_idx, or with rows split into
+ * segments that run concurrently, an in-place call is rejected with
+ * SSD_ERR_ALIAS, as is any other overlap between an output and an input.
  * A row of seqlen 0 leaves its final state equal to its initial state. */
 int ssd_forward(const ssd_problem_t* p,
                 const void* x, const float* dt, const float* dt_bias, const float* A_log,

@@ -178,6 +178,31 @@ def _check_tensors(x, dt, A_log, B, C, D, init_state, seq_idx, dt_bias=None):
         raise ValueError("seq_idx must be (b,T)")
 
 
+def _check_buffer(name, t, shape, dtype, dev):
+    """A caller-supplied output must be exactly what the kernels write into: the C
+    ABI takes bare pointers and cannot see a short, strided or mistyped buffer."""
+    if t.device != dev:
+        raise ValueError("%s is on %s, x on %s" % (name, t.device, dev))
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _check_workspace(ws, nbytes, dev):
+    if nbytes == 0:
+        return
+    if ws is None:
+        raise ValueError("this problem needs a workspace of %d bytes" % nbytes)
+    import torch
+    if ws.device != dev or not ws.is_contiguous() or ws.dtype != torch.uint8:
+        raise ValueError("workspace must be a contiguous uint8 tensor on %s" % dev)
+    if ws.numel() < nbytes:
+        raise ValueError("workspace holds %d bytes, the problem needs %d" % (ws.numel(), nbytes))
+
+
 def forward(x, dt, A_log, B, C, D=None, chunk_len: int = 256, init_state=None, seq_idx=None,
             nseqs: Optional[int] = None, dt_scales_x: bool = False, y=None, final_state=None,
             workspace=None, return_final: bool = True, stream=None, dt_bias=None, dt_softplus: bool = False,
@@ -190,6 +215,9 @@ def forward(x, dt, A_log, B, C, D=None, chunk_len: int = 256, init_state=None, s
     (``zoh``)."""
     import torch
     _check_tensors(x, dt, A_log, B, C, D, init_state, seq_idx, dt_bias)
+    in_place = final_state is not None and init_state is not None and final_state is init_state
+    if in_place and not init_state.is_contiguous():
+        raise ValueError("an init_state that is also final_state must be contiguous (it is updated in place)")
     x, dt, A_log, B, C = (t.contiguous() for t in (x, dt, A_log, B, C))
     D = D.contiguous() if D is not None else None
     dt_bias = dt_bias.contiguous() if dt_bias is not None else None
@@ -205,11 +233,16 @@ def forward(x, dt, A_log, B, C, D=None, chunk_len: int = 256, init_state=None, s
         raise ValueError("init_state must be (nseqs,H,P,N)")
     if y is None:
         y = torch.empty((b, T, H, P), dtype=torch.float32, device=dev)
+    else:
+        _check_buffer("y", y, (b, T, H, P), torch.float32, dev)
     if final_state is None and return_final:
         final_state = torch.empty((p.nseqs, H, P, N), dtype=torch.float32, device=dev)
+    elif final_state is not None:
+        _check_buffer("final_state", final_state, (p.nseqs, H, P, N), torch.float32, dev)
     wsb = int(lib.ssd_workspace_size(ctypes.byref(p)))
     if workspace is None and wsb > 0:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    _check_workspace(workspace, wsb, dev)
     forward_into(p, x, dt, A_log, B, C, D, init_state, seq_idx, y, final_state, workspace, stream, dt_bias)
     return y, final_state
 
@@ -217,8 +250,15 @@ def forward(x, dt, A_log, B, C, D=None, chunk_len: int = 256, init_state=None, s
 def forward_into(p: Problem, x, dt, A_log, B, C, D, init_state, seq_idx, y, final_state, workspace=None,
                  stream=None, dt_bias=None):
     """``ssd_forward`` on caller-provided contiguous tensors and problem description
-    (no checks beyond the library's own; ``workspace`` may be None when
-    :func:`workspace_size` is 0)."""
+    (``workspace`` may be None when :func:`workspace_size` is 0).  Only the sizes of
+    the outputs and the workspace are checked here, since the library cannot see
+    them; everything else is the library's own validation."""
+    import torch
+    dev = y.device
+    _check_buffer("y", y, (p.batch, p.seqlen, p.nheads, p.headdim), torch.float32, dev)
+    if final_state is not None:
+        _check_buffer("final_state", final_state, (p.nseqs, p.nheads, p.headdim, p.dstate), torch.float32, dev)
+    _check_workspace(workspace, workspace_size(p), dev)
     wsn = workspace.numel() if workspace is not None else 0
     _check(load_library().ssd_forward(ctypes.byref(p), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D),
                                       _ptr(init_state), _ptr(seq_idx), _ptr(y), _ptr(final_state),
@@ -244,6 +284,9 @@ def step(x, dt, A_log, B, C, D, state, y=None, dt_scales_x: bool = False, stream
     p = _describe(x, B, dt, A_log, 64, None, None, dt_scales_x, dt_softplus, zoh)
     if y is None:
         y = torch.empty((b, 1, H, P), dtype=torch.float32, device=x.device)
+    else:
+        _check_buffer("y", y.view(b, 1, H, P) if y.is_contiguous() and y.numel() == b * H * P else y,
+                      (b, 1, H, P), torch.float32, x.device)
     _check(load_library().ssd_step(ctypes.byref(p), _ptr(x), _ptr(dt),
                                    _ptr(dt_bias.contiguous() if dt_bias is not None else None), _ptr(A_log.contiguous()), _ptr(B), _ptr(C),
                                    _ptr(D.contiguous() if D is not None else None), _ptr(state), _ptr(y),
@@ -302,7 +345,18 @@ def backward(x, dt, A_log, B, C, dy, D=None, init_state=None, dfinal=None, chunk
 def backward_into(p: Problem, x, dt, dt_bias, A_log, B, C, D, init_state, dy, dfinal, out: dict, workspace=None,
                   stream=None, seq_idx=None):
     """``ssd_backward`` on caller-provided contiguous tensors; ``out`` maps dx, ddt,
-    dA_log, dB, dC (required) and dD, dinit, ddt_bias (optional) to output tensors."""
+    dA_log, dB, dC (required) and dD, dinit, ddt_bias (optional) to output tensors.
+    The outputs' and the workspace's sizes are checked here (the library cannot
+    see them)."""
+    import torch
+    dev = x.device
+    b, T, H, P, N, G, ns = p.batch, p.seqlen, p.nheads, p.headdim, p.dstate, p.ngroups, p.nseqs
+    shapes = {"dx": (b, T, H, P), "ddt": (b, T, H), "dA_log": (H,), "dB": (b, T, G, N), "dC": (b, T, G, N),
+              "dD": (H,), "dinit": (ns, H, P, N), "ddt_bias": (H,)}
+    for k, shp in shapes.items():
+        if out.get(k) is not None:
+            _check_buffer(k, out[k], shp, torch.float32, dev)
+    _check_workspace(workspace, backward_workspace_size(p), dev)
     wsn = workspace.numel() if workspace is not None else 0
     g = out.get
     _check(load_library().ssd_backward(ctypes.byref(p), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A_log), _ptr(B),

@@ -187,6 +187,14 @@ int check_args(const ssd_problem_t* p, const void* x, const float* dt, const flo
     if (overlap(y, s.y, init, s.state) || overlap(y, s.y, fin, s.state)) return SSD_ERR_ALIAS;
     // final_state may be init_state itself (in-place carry), but not a shifted overlap
     if (fin && init && fin != init && overlap(fin, s.state, init, s.state)) return SSD_ERR_ALIAS;
+    // In-place carry is safe only where every state element is read and then
+    // written by one and the same wave: rows scanned in one piece and without
+    // sequence ids.  With sequence ids, a sequence that starts and ends inside
+    // one block has its initial state read over all N by both waves of a slice
+    // while each writes its half of the final state; with rows split into
+    // segments, a later segment's workgroup writes the final state of a
+    // sequence whose initial state an earlier segment has yet to read.
+    if (fin && fin == init && (seq_idx || segments(p).nseg > 1)) return SSD_ERR_ALIAS;
     return SSD_OK;
 }
 

@@ -127,6 +127,31 @@ def test_forward_rejects_aliasing():
     assert _forward(small(), fin=A + 0x5000000) == 6        # final on top of C
 
 
+def test_in_place_state_carry_only_where_it_is_safe():
+    """final_state == init_state is accepted for rows scanned in one piece without
+    sequence ids, and rejected (ALIAS) where the scan reads an initial state after
+    another wave or workgroup may have written the final one: packed sequences, and
+    rows split into concurrently scanned segments."""
+    st = A + 0x20000000
+    torch = pytest.importorskip("torch")
+    no_dev = not torch.cuda.is_available()
+    if no_dev:
+        assert _forward(small(), init=st, fin=st) == 8                   # passes every check
+    packed = prob(batch=1, seqlen=64, nheads=2, headdim=32, dstate=64, chunk_len=64, nseqs=3)
+    assert _forward(packed, seq=A + 0x8000000, init=st, fin=st) == 6
+    # a long row of few heads: 16 segments per row; buffers 1 GiB apart, so that
+    # only the state buffers can overlap
+    split = prob(batch=1, seqlen=16384, nheads=32)
+    assert ssd.workspace_size(split) > 0
+    far = {n: A + (i + 1) * (1 << 30) for i, n in enumerate(["x", "dt", "A_log", "B", "C", "y"])}
+    st = A + 8 * (1 << 30)
+    ws = A + 9 * (1 << 30)
+    assert _forward(split, ws=ws, init=st, fin=st, **far) == 6
+    assert _forward(split, ws=ws, init=st, fin=st + 256, **far) == 6    # shifted overlap, as before
+    if no_dev:
+        assert _forward(split, ws=ws, init=st, fin=A + 10 * (1 << 30), **far) == 8   # separate buffers
+
+
 def test_forward_checks_dt_bias():
     assert _forward(small(), dt_bias=A + 0x30000000 + 2) == 4            # misaligned
     assert _forward(small(), dt_bias=A + 0x9000000) == 6                 # y on top of dt_bias
@@ -259,3 +284,41 @@ def test_backward_without_device_reports_no_device():
     if torch.cuda.is_available():
         pytest.skip("a GPU is present: this call would launch on fake pointers")
     assert _backward(small_bwd()) == 8
+
+
+def test_binding_checks_caller_outputs_and_workspace():
+    """The raw entry points take caller-owned outputs; the binding checks their
+    shape, dtype and contiguity and the workspace's size before the library is
+    called (a short buffer would be written past its end on the device)."""
+    torch = pytest.importorskip("torch")
+    p = ssd.problem(1, 64, 2, 32, 64, 1, 64, 1, ssd.DTYPE_BF16, 0)
+    x = torch.zeros(1, 64, 2, 32, dtype=torch.bfloat16)
+    B = torch.zeros(1, 64, 1, 64, dtype=torch.bfloat16)
+    dt, A_log = torch.zeros(1, 64, 2), torch.zeros(2)
+    fin = torch.zeros(1, 2, 32, 64)
+    bad_y = [torch.zeros(1, 64, 2, 16),                            # short
+             torch.zeros(1, 64, 2, 32, dtype=torch.bfloat16),      # wrong dtype
+             torch.zeros(1, 64, 2, 64)[..., :32]]                  # strided
+    for y in bad_y:
+        with pytest.raises((ValueError, TypeError)):
+            ssd.forward_into(p, x, dt, A_log, B, B, None, None, None, y, fin)
+    y = torch.zeros(1, 64, 2, 32)
+    with pytest.raises(ValueError):
+        ssd.forward_into(p, x, dt, A_log, B, B, None, None, None, y, torch.zeros(1, 2, 32, 32))
+    # a split problem needs its workspace, of at least ssd_workspace_size bytes
+    q = ssd.problem(1, 16384, 32, 64, 128, 1, 256, 1, ssd.DTYPE_BF16, 0)
+    need = ssd.workspace_size(q)
+    assert need > 0
+    with pytest.raises(ValueError):
+        ssd._check_workspace(None, need, torch.device("cpu"))
+    with pytest.raises(ValueError):
+        ssd._check_workspace(torch.zeros(need - 1, dtype=torch.uint8), need, torch.device("cpu"))
+    with pytest.raises(ValueError):
+        ssd._check_workspace(torch.zeros(need // 4 + 1, dtype=torch.float32), need, torch.device("cpu"))
+    ssd._check_workspace(torch.zeros(need, dtype=torch.uint8), need, torch.device("cpu"))
+    # backward outputs
+    outs = {"dx": torch.zeros(1, 64, 2, 32), "ddt": torch.zeros(1, 64, 2), "dA_log": torch.zeros(2),
+            "dB": torch.zeros(1, 64, 1, 64), "dC": torch.zeros(1, 64, 1, 32)}      # dC short
+    ws = torch.zeros(ssd.backward_workspace_size(p), dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        ssd.backward_into(p, x, dt, None, A_log, B, B, None, None, y, None, outs, ws)
