@@ -28,7 +28,8 @@
  *    aborts and no C++ exception crosses the ABI.  Argument checks run on the
  *    host before any HIP call, so a rejected call has enqueued nothing.
  *  - The library keeps no per-call state; concurrent calls on different
- *    streams with disjoint outputs and workspaces are safe.
+ *    streams with disjoint outputs and workspaces are safe (except
+ *    ssd_forward_noalloc, whose calls on one GPU share a static scratch array).
  *  - A call only launches kernels on `stream` (no allocation, memset, copy or
  *    synchronisation), so it may be recorded into a HIP graph by stream capture
  *    and replayed; the captured pointers must stay valid for every replay.
@@ -43,7 +44,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 3
+#define SSD_ABI_VERSION 4
 
 /* Element type of x, B and C.  dt, A_log, D, init_state, y and final_state are
  * always fp32.  BF16: bf16 operands, fp32 accumulation; F32: fp32 throughout. */
@@ -78,8 +79,13 @@ enum {
     SSD_ERR_WORKSPACE = 5,      /* workspace NULL or smaller than ssd_workspace_size  */
     SSD_ERR_ALIAS = 6,          /* an output overlaps an input or the other output    */
     SSD_ERR_HIP = 7,            /* a HIP runtime call or kernel launch failed         */
-    SSD_ERR_NO_DEVICE = 8       /* no HIP device is available                         */
+    SSD_ERR_NO_DEVICE = 8,      /* no HIP device is available                         */
+    SSD_ERR_SCRATCH = 9         /* ssd_forward_noalloc: the problem needs more scratch
+                                   than SSD_NOALLOC_SCRATCH_BYTES                      */
 };
+
+/* Size of the static device scratch array of ssd_forward_noalloc (32 MiB). */
+#define SSD_NOALLOC_SCRATCH_BYTES (32u << 20)
 
 typedef struct {
     int64_t batch;      /* b: rows                                                  */
@@ -155,6 +161,32 @@ int ssd_forward(const ssd_problem_t* p,
                 const float* init_state, const int32_t* seq_idx,
                 float* y, float* final_state,
                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* ssd_forward without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, semantics, kernels and results as
+ * ssd_forward, minus workspace / workspace_bytes: when the problem needs a
+ * workspace (ssd_workspace_size(p) > 0: rows split into segments), the
+ * library's own file-scope device array of SSD_NOALLOC_SCRATCH_BYTES stands in
+ * for it.  A problem that needs more (ssd_workspace_size(p) >
+ * ssd_noalloc_scratch_bytes()) is rejected with SSD_ERR_SCRATCH before any HIP
+ * call.  The call itself allocates nothing: no hipMalloc, no hipFree, no
+ * allocating library routine.  Each GPU the library runs on holds its own copy
+ * of the array until the process ends; its device address is looked up once
+ * per device, on the first call that needs it.  Every call on one GPU shares
+ * that GPU's array, and the contents of the previous call are left in it (the
+ * kernels write every scratch element they read, so nothing needs clearing):
+ * calls that overlap in time on one GPU (on different streams, or from
+ * different threads without ordering) race on the scratch and must not be
+ * issued. */
+int ssd_forward_noalloc(const ssd_problem_t* p,
+                        const void* x, const float* dt, const float* dt_bias, const float* A_log,
+                        const void* B, const void* C, const float* D,
+                        const float* init_state, const int32_t* seq_idx,
+                        float* y, float* final_state, void* stream);
+
+/* SSD_NOALLOC_SCRATCH_BYTES, as built into the loaded library. */
+size_t ssd_noalloc_scratch_bytes(void);
 
 /* One token of the recurrence (decoding), for every row and head, on the
  * fp32 state in place:

@@ -21,7 +21,7 @@ import ctypes
 import os
 from typing import Optional
 
-__all__ = ["forward", "forward_into", "step", "backward", "backward_into", "backward_workspace_size", "workspace_size", "validate", "problem", "SSDError",
+__all__ = ["forward", "forward_into", "forward_into_noalloc", "noalloc_scratch_bytes", "step", "backward", "backward_into", "backward_workspace_size", "workspace_size", "validate", "problem", "SSDError",
            "version", "library_path", "load_library", "DTYPE_F32", "DTYPE_BF16", "FLAG_DT_SCALES_X",
            "FLAG_DT_SOFTPLUS", "FLAG_ZOH"]
 
@@ -33,11 +33,11 @@ DTYPE_BF16 = 1
 FLAG_DT_SCALES_X = 1
 FLAG_DT_SOFTPLUS = 2
 FLAG_ZOH = 4
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 SSD_OK = 0
 ERROR_NAMES = {1: "NULL_POINTER", 2: "BAD_SHAPE", 3: "UNSUPPORTED", 4: "ALIGNMENT", 5: "WORKSPACE",
-               6: "ALIAS", 7: "HIP", 8: "NO_DEVICE"}
+               6: "ALIAS", 7: "HIP", 8: "NO_DEVICE", 9: "SCRATCH"}
 
 
 class SSDError(RuntimeError):
@@ -79,6 +79,10 @@ def load_library():
     lib.ssd_workspace_size.restype = sz
     lib.ssd_forward.argtypes = [P] + [vp] * 11 + [vp, sz, vp]
     lib.ssd_forward.restype = ctypes.c_int
+    lib.ssd_forward_noalloc.argtypes = [P] + [vp] * 12
+    lib.ssd_forward_noalloc.restype = ctypes.c_int
+    lib.ssd_noalloc_scratch_bytes.argtypes = []
+    lib.ssd_noalloc_scratch_bytes.restype = sz
     lib.ssd_backward_workspace_size.argtypes = [P]
     lib.ssd_backward_workspace_size.restype = sz
     lib.ssd_backward.argtypes = [P] + [vp] * 19 + [vp, sz, vp]
@@ -263,6 +267,24 @@ def forward_into(p: Problem, x, dt, A_log, B, C, D, init_state, seq_idx, y, fina
     _check(load_library().ssd_forward(ctypes.byref(p), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D),
                                       _ptr(init_state), _ptr(seq_idx), _ptr(y), _ptr(final_state),
                                       _ptr(workspace), wsn, _stream_of(x.device, stream)))
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(load_library().ssd_noalloc_scratch_bytes())
+
+
+def forward_into_noalloc(p: Problem, x, dt, A_log, B, C, D, init_state, seq_idx, y, final_state, stream=None,
+                         dt_bias=None):
+    """``ssd_forward_noalloc`` on caller-provided contiguous tensors: :func:`forward_into`
+    without a workspace (the library's static scratch array stands in for it)."""
+    import torch
+    dev = y.device
+    _check_buffer("y", y, (p.batch, p.seqlen, p.nheads, p.headdim), torch.float32, dev)
+    if final_state is not None:
+        _check_buffer("final_state", final_state, (p.nseqs, p.nheads, p.headdim, p.dstate), torch.float32, dev)
+    _check(load_library().ssd_forward_noalloc(ctypes.byref(p), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A_log),
+                                              _ptr(B), _ptr(C), _ptr(D), _ptr(init_state), _ptr(seq_idx), _ptr(y),
+                                              _ptr(final_state), _stream_of(x.device, stream)))
 
 
 def step(x, dt, A_log, B, C, D, state, y=None, dt_scales_x: bool = False, stream=None, dt_bias=None,

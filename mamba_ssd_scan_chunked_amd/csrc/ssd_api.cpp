@@ -14,6 +14,7 @@
 #include "ssd_launch.hpp"
 
 #include <algorithm>
+#include <mutex>
 
 namespace ssd {
 // Incoming state of every segment from the local pass: for each (row, head) and
@@ -156,15 +157,21 @@ int slices_per_workgroup(const ssd_problem_t* p, bool seq, int nseg) {
     return npt;
 }
 
+// static_ws: the workspace is the library's own scratch array (ssd_forward_noalloc),
+// which no caller buffer can overlap; ws and ws_bytes are then ignored.
 int check_args(const ssd_problem_t* p, const void* x, const float* dt, const float* dt_bias, const float* A_log,
                const void* B,
                const void* C, const float* D, const float* init, const int32_t* seq_idx, const float* y,
-               const float* fin, const void* ws, size_t ws_bytes) {
+               const float* fin, const void* ws, size_t ws_bytes, bool static_ws = false) {
     const int v = ssd_validate(p);
     if (v != SSD_OK) return v;
     const bool empty_tokens = p->batch == 0 || p->seqlen == 0;
     if (!A_log) return SSD_ERR_NULL_POINTER;
-    const int64_t wsb = workspace_bytes(p);
+    const int64_t wsb = static_ws ? 0 : workspace_bytes(p);
+    if (static_ws) {
+        ws = nullptr;
+        ws_bytes = 0;
+    }
     if (!empty_tokens && (!x || !dt || !B || !C || !y)) return SSD_ERR_NULL_POINTER;
     if (wsb > 0 && !ws) return SSD_ERR_WORKSPACE;
     if (!seq_idx && p->nseqs != p->batch) return SSD_ERR_BAD_SHAPE;
@@ -195,6 +202,43 @@ int check_args(const ssd_problem_t* p, const void* x, const float* dt, const flo
     // segments, a later segment's workgroup writes the final state of a
     // sequence whose initial state an earlier segment has yet to read.
     if (fin && fin == init && (seq_idx || segments(p).nseg > 1)) return SSD_ERR_ALIAS;
+    return SSD_OK;
+}
+
+// ---- the allocation-free entry point's scratch: a file-scope device array that
+// each GPU holds for the life of the process.  Host code never uses the array's
+// name as an address (on the host it is only a stand-in for the symbol): the
+// device address of each GPU's copy comes from hipGetSymbolAddress, taken once
+// per device with that device current, and is kept here.
+constexpr int64_t kScratchBytes = int64_t(SSD_NOALLOC_SCRATCH_BYTES);
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[SSD_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// Device address of `scratch` on the device that `stream` belongs to (the
+// current device for the NULL stream).
+int scratch_address(hipStream_t stream, void** out) {
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return SSD_ERR_HIP;
+    int dev = cur;
+    if (stream && hipStreamGetDevice(stream, &dev) != hipSuccess) return SSD_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return SSD_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        if (dev != cur && hipSetDevice(dev) != hipSuccess) return SSD_ERR_HIP;
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (dev != cur) (void)hipSetDevice(cur);
+        if (e != hipSuccess || !ptr || misaligned(ptr, 256)) return SSD_ERR_HIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
     return SSD_OK;
 }
 
@@ -319,6 +363,26 @@ int ssd_forward(const ssd_problem_t* p, const void* x, const float* dt, const fl
                        static_cast<hipStream_t>(stream));
 }
 
+int ssd_forward_noalloc(const ssd_problem_t* p, const void* x, const float* dt, const float* dt_bias,
+                        const float* A_log, const void* B, const void* C, const float* D, const float* init_state,
+                        const int32_t* seq_idx, float* y, float* final_state, void* stream) {
+    const int v = check_args(p, x, dt, dt_bias, A_log, B, C, D, init_state, seq_idx, y, final_state, nullptr, 0,
+                             /*static_ws=*/true);
+    if (v != SSD_OK) return v;
+    if (workspace_bytes(p) > kScratchBytes) return SSD_ERR_SCRATCH;
+    const int d = check_device();
+    if (d != SSD_OK) return d;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    void* ws = nullptr;
+    if (workspace_bytes(p) > 0) {
+        const int r = scratch_address(st, &ws);
+        if (r != SSD_OK) return r;
+    }
+    return launch_scan(p, x, dt, dt_bias, A_log, B, C, D, init_state, seq_idx, y, final_state, ws, st);
+}
+
+size_t ssd_noalloc_scratch_bytes(void) { return static_cast<size_t>(kScratchBytes); }
+
 int ssd_step(const ssd_problem_t* p, const void* x, const float* dt, const float* dt_bias, const float* A_log,
              const void* B,
              const void* C, const float* D, float* state, float* y, void* stream) {
@@ -377,6 +441,9 @@ const char* ssd_strerror(int status) {
         case SSD_ERR_ALIAS: return "an output buffer overlaps an input, the workspace or the other output";
         case SSD_ERR_HIP: return "a HIP runtime call or kernel launch failed";
         case SSD_ERR_NO_DEVICE: return "no HIP device available";
+        case SSD_ERR_SCRATCH:
+            return "the problem needs more scratch than ssd_forward_noalloc's static buffer holds "
+                   "(ssd_workspace_size() > ssd_noalloc_scratch_bytes()); use ssd_forward with a workspace";
         default: return "unknown ssd status code";
     }
 }

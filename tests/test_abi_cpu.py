@@ -31,9 +31,9 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_strerror():
-    assert ssd.version() == 3
+    assert ssd.version() == 4
     lib = ssd.load_library()
-    for code in range(0, 9):
+    for code in range(0, 10):
         assert lib.ssd_strerror(code)
     assert b"unknown" in lib.ssd_strerror(99)
 
@@ -322,3 +322,36 @@ def test_binding_checks_caller_outputs_and_workspace():
     ws = torch.zeros(ssd.backward_workspace_size(p), dtype=torch.uint8)
     with pytest.raises(ValueError):
         ssd.backward_into(p, x, dt, None, A_log, B, B, None, None, y, None, outs, ws)
+
+
+def _forward_noalloc(p, **ptrs):
+    lib = ssd.load_library()
+    names = ["x", "dt", "dt_bias", "A_log", "B", "C", "D", "init", "seq", "y", "fin"]
+    vals = {n: A + (i + 1) * (1 << 30) for i, n in enumerate(names)}
+    vals.update({"dt_bias": None, "D": None, "init": None, "seq": None})
+    vals.update(ptrs)
+    return lib.ssd_forward_noalloc(ctypes.byref(p), *[vals[n] for n in names], None)
+
+
+def test_noalloc_entry_point_checks_and_limit(monkeypatch):
+    """ssd_forward_noalloc runs the argument checks of ssd_forward (no workspace
+    argument) and rejects, before any HIP call, a problem whose workspace would
+    not fit its static scratch array."""
+    assert ssd.noalloc_scratch_bytes() == 32 << 20
+    torch = pytest.importorskip("torch")
+    no_dev = not torch.cuda.is_available()
+    split = prob(batch=1, seqlen=16384, nheads=32)                      # 15.7 MB of segment states
+    assert 0 < ssd.workspace_size(split) <= ssd.noalloc_scratch_bytes()
+    if no_dev:
+        assert _forward_noalloc(split) == 8                             # passes every check
+    assert _forward_noalloc(split, x=None) == 1
+    assert _forward_noalloc(split, y=A + 1) == 4
+    assert _forward_noalloc(split, y=A + 5 * (1 << 30)) == 6           # y on top of B
+    st = A + 20 * (1 << 30)
+    assert _forward_noalloc(split, init=st, fin=st) == 6               # in place on split rows
+    # forced to 64 segments per row, 128 (row, head) items need 258 MB of states
+    monkeypatch.setenv("SSD_SEGMENTS", "64")
+    big = prob(batch=2, seqlen=16384, nheads=64)
+    assert ssd.workspace_size(big) > ssd.noalloc_scratch_bytes()
+    assert _forward_noalloc(big) == 9
+    assert b"scratch" in ssd.load_library().ssd_strerror(9)
