@@ -37,6 +37,16 @@
 
 #include <type_traits>
 
+#ifndef SSD_X_AUX
+#define SSD_X_AUX 0
+#endif
+#ifndef SSD_Y_AUX
+#define SSD_Y_AUX 18
+#endif
+#ifndef SSD_LEADER_SCAN
+#define SSD_LEADER_SCAN 1
+#endif
+
 namespace ssd {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -299,9 +309,10 @@ __device__ inline rsrc_t make_rsrc(const void* base, int64_t bytes) {
     const int64_t lim = bytes < 0 ? 0 : (bytes > 0x7fffffffLL ? 0x7fffffffLL : bytes);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)lim, 0x00020000);
 }
+template <int AUX = 0>
 __device__ inline uint4 buf_load16(rsrc_t r, int off) {
     typedef unsigned int u4 __attribute__((ext_vector_type(4)));
-    const u4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    const u4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX);
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 __device__ inline uint2 buf_load8(rsrc_t r, int off) {
@@ -315,9 +326,10 @@ __device__ inline float buf_load_f32(rsrc_t r, int off) {
 __device__ inline int buf_load_i32(rsrc_t r, int off) {
     return __builtin_bit_cast(int, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
+template <int AUX = 0>
 __device__ inline void buf_store16(f32x4 v, rsrc_t r, int off) {
     typedef unsigned int u4 __attribute__((ext_vector_type(4)));
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, off, 0, AUX);
 }
 
 // Scheduling hint for a straight-line stretch of LDS-fed MFMAs: keep LEAD LDS
@@ -561,6 +573,7 @@ void ssd_scan_kernel(ScanParams prm) {
     constexpr int KSTEP = K::KSTEP, SZ = K::SZ, NK = K::NK, RT = K::RT, MT = K::MT, NW = K::NW;
     constexpr int NH = K::NH, NPT = K::NPT, MTH = K::MTH, NKH = K::NKH, RTH = K::RTH, MLH = K::MLH, XW = K::XW;
     constexpr int NFH = SZ == 2 ? MTH / 2 : 4 * MTH;               // read-out fragments of a state half
+    constexpr bool LEADER_SCAN = SSD_LEADER_SCAN != 0;
     static_assert(NFH == NKH, "fragments of a state half are whole K steps");
     static_assert(QB <= 64 && QB % KSTEP == 0 && QB % 16 == 0, "block length");
     static_assert(N % KSTEP == 0 && N % 16 == 0 && P % 16 == 0, "shape");
@@ -720,12 +733,12 @@ void ssd_scan_kernel(ScanParams prm) {
         const int64_t t0 = (int64_t)blk * QB;
         const rsrc_t rx = make_rsrc(xrow + t0 * xs, xrec - t0 * xs);
         const rsrc_t rd = make_rsrc(drow + t0 * ds, drec - t0 * ds);
-        dtv = buf_load_f32(rd, lane * ds);
+        if (SEQ || !LEADER_SCAN || head_leader) dtv = buf_load_f32(rd, lane * ds);
         if constexpr (SEQ) sqv = buf_load_i32(make_rsrc(seqg + t0, (T - t0) * 4), lane * 4);
 #pragma unroll
         for (int j = 0; j < K::XPT; ++j) {
             const int v = tid + j * NT;
-            if (K::XU % NT == 0 || v < K::XU) xr[j] = buf_load16(rx, (v / (XW / VE)) * xs + (v % (XW / VE)) * 16);
+            if (K::XU % NT == 0 || v < K::XU) xr[j] = buf_load16<SSD_X_AUX>(rx, (v / (XW / VE)) * xs + (v % (XW / VE)) * 16);
         }
     };
     auto issue_bc = [&](int blk) {
@@ -753,6 +766,22 @@ void ssd_scan_kernel(ScanParams prm) {
     //      within-block cumulative decay, segments, X and weighted X.  Every wave
     //      computes the per-token scalars in registers (lane = token); wave 0
     //      publishes them for the MFMA phases.
+    auto prep_x = [&]() {
+        // X (row-major; each thread holds VE channels of one token)
+#pragma unroll
+        for (int j = 0; j < K::XPT; ++j) {
+            const int v = tid + j * NT;
+            if (K::XU % NT == 0 || v < K::XU) {
+                const int t = v / (XW / VE), c = v % (XW / VE);
+                if constexpr (K::SWX) {
+                    *(uint2*)(sXr + unit_off<true>(t, 2 * c, LR)) = make_uint2(xr[j].x, xr[j].y);
+                    *(uint2*)(sXr + unit_off<true>(t, 2 * c + 1, LR)) = make_uint2(xr[j].z, xr[j].w);
+                } else {
+                    *(uint4*)(sXr + t * LR + c * VE) = xr[j];
+                }
+            }
+        }
+    };
     auto prep = [&](int blk) {
         const int rows = (int)min((int64_t)QB, T - (int64_t)blk * QB);
 #pragma unroll
@@ -773,6 +802,9 @@ void ssd_scan_kernel(ScanParams prm) {
                 }
             }
         }
+        // Without sequence ids only the head leaders need the per-token values (they
+        // publish them; the other waves read the block's decay from LDS)
+        if (!SEQ && LEADER_SCAN && !head_leader) return prep_x();
         if (prm.dt_bias || prm.dt_softplus)                        // step size; 0 past the row's end
             dtv = lane < rows ? step_size(dtv + dtb, prm.dt_softplus) : 0.f;
         const cum_t cum = wave_incl_scan((cum_t)dtv * A2);        // dt = 0 past the row's end
@@ -819,20 +851,7 @@ void ssd_scan_kernel(ScanParams prm) {
             if constexpr (XSCALE) sDtf[lane] = dtf;
         }
 
-        // X (row-major; each thread holds VE channels of one token)
-#pragma unroll
-        for (int j = 0; j < K::XPT; ++j) {
-            const int v = tid + j * NT;
-            if (K::XU % NT == 0 || v < K::XU) {
-                const int t = v / (XW / VE), c = v % (XW / VE);
-                if constexpr (K::SWX) {
-                    *(uint2*)(sXr + unit_off<true>(t, 2 * c, LR)) = make_uint2(xr[j].x, xr[j].y);
-                    *(uint2*)(sXr + unit_off<true>(t, 2 * c + 1, LR)) = make_uint2(xr[j].z, xr[j].w);
-                } else {
-                    *(uint4*)(sXr + t * LR + c * VE) = xr[j];
-                }
-            }
-        }
+        prep_x();
     };
 
     // ---- this wave's causal tiles of L o CB: C B^T on MFMA (as (C B^T)^T, rows s,
@@ -951,7 +970,7 @@ void ssd_scan_kernel(ScanParams prm) {
                 }
             }
             // state <- exp(cum_end) state + B^T (weighted X)
-            const float alpha = fast_exp2(cend_f);
+            const float alpha = fast_exp2(!SEQ && LEADER_SCAN ? (float)sCum[QB - 1] : cend_f);
 #pragma unroll
             for (int j = 0; j < MTH; ++j) st[j] *= alpha;
 #pragma unroll
@@ -1093,7 +1112,7 @@ void ssd_scan_kernel(ScanParams prm) {
         const int64_t t0 = (int64_t)blk * QB;
         const rsrc_t ry = make_rsrc(yrow + t0 * ys, yrec - t0 * ys);
 #pragma unroll
-        for (int i = 0; i < RTH; ++i) buf_store16(acc[i], ry, (16 * K::own_tile(nh, i) + lr) * ys + (xc + 4 * lg) * 4);
+        for (int i = 0; i < RTH; ++i) buf_store16<SSD_Y_AUX>(acc[i], ry, (16 * K::own_tile(nh, i) + lr) * ys + (xc + 4 * lg) * 4);
         if constexpr (SEQ) prevseq = lastseq_c;
     };
 
