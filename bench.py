@@ -31,6 +31,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 COPY_BYTES = 1 << 30           # size of the calibration copy (read and written once each)
+SCRUB_BYTES = 1 << 30          # written before each cold timed call: more than L2 and the 256 MB MALL
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense
 
 
@@ -257,17 +258,57 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def committed_traffic(workload: str):
-    """HBM traffic per scan launch from the committed rocprofv3 counter runs, if
-    they were taken on the current kernel sources; otherwise None."""
-    path = os.path.join(ROOT, "profiles", "scan_traffic_%s.json" % workload)
+def committed_counters(workload: str, what: str = "traffic"):
+    """A figure from the committed rocprofv3 counter summaries of the scan kernel
+    (profiles/scan_<what>_<workload>.json), if they were taken on the current kernel
+    sources; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "scan_%s_%s.json" % (what, workload))
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
     if rec.get("kernel_source_sha") != kernel_source_hash():
         return None
-    return rec.get("traffic_bytes_per_launch")
+    return rec
+
+
+def committed_traffic(workload: str):
+    """HBM traffic per scan launch from the committed rocprofv3 counter runs, if
+    they were taken on the current kernel sources; otherwise None."""
+    rec = committed_counters(workload, "traffic")
+    return rec.get("traffic_bytes_per_launch") if rec else None
+
+
+def copy_bandwidth(dev, reps: int = 10):
+    """Achieved HBM bandwidth of a plain device copy of COPY_BYTES (read + write
+    bytes per second), timed with HIP events: the practical ceiling beside the
+    8 TB/s peak."""
+    import torch
+    n = COPY_BYTES // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(reps):
+        dst.copy_(src)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / reps
+    del src, dst
+    return 2.0 * COPY_BYTES / (ms / 1000.0) / 1e9
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(prob, w):
@@ -293,6 +334,8 @@ def cpu_baseline(prob, w):
     dt = time.perf_counter() - t0
     tokens = rows * w.seqlen    # full rows of the workload, every head
     return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(), "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
+            "host_cpus": os.cpu_count(),
             "sample": "%d of %d rows (all %d heads, %d tokens each), fp64 recurrence, %.2f s wall"
                       % (rows, w.batch, w.nheads, w.seqlen, dt)}
 
@@ -380,17 +423,41 @@ def main():
     kms = sorted(e[0].elapsed_time(e[1]) for e in evs)
     median_ms = kms[len(kms) // 2]
     ms_per_step = wall * 1000.0 / args.steps
+
+    # Cold calls: before each, an untimed write of SCRUB_BYTES evicts the inputs
+    # from L2 and the MALL; each call is timed alone between its own events.
+    scrub = torch.empty(SCRUB_BYTES // 4, dtype=torch.float32, device=dev)
+    cold = []
+    for i in range(args.steps):
+        scrub.fill_(float(i))
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        step(e)
+        cold.append(e)
+    torch.cuda.synchronize()
+    cms = sorted(e[0].elapsed_time(e[1]) for e in cold)
+    del scrub
+    pct = lambda v, q: v[min(len(v) - 1, int(round(q * (len(v) - 1))))]
+    cold_med, cold_p10, cold_p90 = pct(cms, 0.5), pct(cms, 0.1), pct(cms, 0.9)
+    copy_gbs = copy_bandwidth(dev)
     tokens = w.batch * w.seqlen
     value = tokens / (ms_per_step / 1000.0)
 
     balg = algorithmic_bytes(w, prob["init"] is not None)
     falg = algorithmic_flops(w)
     achieved = balg / (scan_ms / 1000.0) / 1e9
+    pipe = committed_counters(w.name, "pipe")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": committed_traffic(w.name),
                 "kernel": "ssd_scan_kernel", "kernel_ms": round(scan_ms, 5),
-                "timing": "HIP events around the timed region's back-to-back launches",
+                "timing": "HIP events around the timed region's back-to-back launches (warm)",
                 "single_launch_ms_median": round(median_ms, 5),
+                "cold": {"what": "each call after an untimed %d MiB scrub write, timed alone" % (SCRUB_BYTES >> 20),
+                         "calls": len(cms), "ms_median": round(cold_med, 5), "ms_p10": round(cold_p10, 5),
+                         "ms_p90": round(cold_p90, 5),
+                         "frac_median": round(balg / (cold_med / 1000.0) / 1e9 / HBM_PEAK_GBS, 4)},
+                "copy_gbs": round(copy_gbs, 1), "frac_of_copy": round(achieved / copy_gbs, 4),
+                "mfma_busy": pipe.get("mfma_busy") if pipe else None,
+                "lds_active": pipe.get("lds_active") if pipe else None,
                 "alg_bytes_per_launch": balg, "alg_flops_per_step": falg,
                 "step_frac_of_hbm_roofline": round(balg / (ms_per_step / 1000.0) / 1e9 / HBM_PEAK_GBS, 4)}
 

@@ -103,12 +103,12 @@ typedef struct {
 /* Host-only check of a problem description (no HIP call).  Supported builds:
  *   BF16: headdim in {32, 64}, dstate in {64, 128, 256}
  *   F32 : headdim in {16, 32, 64}, dstate in {16, 32, 64, 128}
- * chunk_len: 32, or any positive multiple of 64.  The chunk length does not
- * change the function computed (every chunking of the sequence gives the same
- * y and final state up to rounding); the kernel evaluates each chunk's
- * quadratic diagonal block in blocks of min(chunk_len, 64) rows, passing the
- * state between those blocks (the past-to-future parts of a diagonal block
- * are low rank, exactly as between chunks). */
+ * chunk_len: 16, 32, or any positive multiple of 64.  The chunk length does
+ * not change the function computed (every chunking of the sequence gives the
+ * same y and final state up to rounding, section 1 of "088 Mamba-2"); the
+ * kernel evaluates the sequence in blocks of 32 rows (chunk_len 16 or 32) or 64
+ * rows (multiples of 64), passing the state between blocks (the past-to-future
+ * parts of a diagonal block are low rank, exactly as between chunks). */
 int ssd_validate(const ssd_problem_t* p);
 
 /* Bytes of device workspace ssd_forward needs for this problem; 0 when it needs

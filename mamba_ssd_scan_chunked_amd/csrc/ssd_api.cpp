@@ -55,7 +55,11 @@ __global__ __launch_bounds__(256) void ssd_combine_kernel(CombineParams prm) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             if (s0 + k < ns) {
-                st = make_float4(c[k] * st.x + l[k].x, c[k] * st.y + l[k].y, c[k] * st.z + l[k].z, c[k] * st.w + l[k].w);
+                // a zero carry (a sequence starts in the segment) replaces the state by a
+                // select, so that an Inf or NaN state of the previous sequence does not leak
+                st = c[k] == 0.f ? l[k]
+                                 : make_float4(c[k] * st.x + l[k].x, c[k] * st.y + l[k].y, c[k] * st.z + l[k].z,
+                                               c[k] * st.w + l[k].w);
                 base[(s0 + k) * stride] = st;
             }
         }
@@ -76,8 +80,12 @@ using namespace ssd_host;
 
 constexpr int64_t kMaxDim = int64_t(1) << 31;
 
+// Tokens per kernel block.  The chunk length does not change the function (every
+// chunking of the sequence gives the same outputs up to rounding), so a chunk of
+// 16 or 32 tokens is evaluated in 32-token blocks and any multiple of 64 in
+// 64-token blocks, with the state passed between blocks inside a chunk.
 int block_len(const ssd_problem_t* p) {
-    if (p->chunk_len == 32) return 32;
+    if (p->chunk_len == 16 || p->chunk_len == 32) return 32;
     if (p->chunk_len >= 64 && p->chunk_len % 64 == 0) return 64;
     return 0;
 }

@@ -239,6 +239,26 @@ template <bool SW = false, typename F>
 __device__ inline float weighted_x_frag(const float* sX, int lp, int ks, int p0, int lr, int lg, F wt) {
     return wt(ks + lg) * x_frag(sX, lp, ks, p0, lr, lg);
 }
+// An operand whose K values are tokens (K = token ks + KPL*(l/16) + e), with the
+// tokens for which keep() is false replaced by zero.  A select, not a product
+// with zero, so that an Inf or NaN of another sequence stays out of the sum.
+template <typename F>
+__device__ inline bf16x8 mask_frag(const bf16x8& v, int ks, int lg, F keep) {
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = keep(ks + 8 * lg + e) ? v[e] : (__bf16)0.f;
+    return r;
+}
+template <typename F>
+__device__ inline float mask_frag(float v, int ks, int lg, F keep) { return keep(ks + lg) ? v : 0.f; }
+// An X operand already in registers, weighted the same way.
+template <typename F>
+__device__ inline bf16x8 weight_frag(const bf16x8& x, int ks, int lg, F wt) {
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = (__bf16)(wt(ks + 8 * lg + e) * (float)x[e]);
+    return r;
+}
 
 // B tile in LDS: row t holds the N values of token t, pitch LB elements: N + 4
 // (8-byte aligned rows), or N with the swizzle above for bf16 and N >= 128.
@@ -807,8 +827,8 @@ void ssd_scan_kernel(ScanParams prm) {
         if (!SEQ && LEADER_SCAN && !head_leader) return prep_x();
         if (prm.dt_bias || prm.dt_softplus)                        // step size; 0 past the row's end
             dtv = lane < rows ? step_size(dtv + dtb, prm.dt_softplus) : 0.f;
-        const cum_t cum = wave_incl_scan((cum_t)dtv * A2);        // dt = 0 past the row's end
-        const cum_t cend = __shfl(cum, QB - 1);
+        const cum_t lv = (cum_t)dtv * A2;
+        cum_t cum = wave_incl_scan(lv);                            // dt = 0 past the row's end
         int nstart = 0;
         cum_t before = 0;
         if constexpr (SEQ) {
@@ -824,9 +844,17 @@ void ssd_scan_kernel(ScanParams prm) {
             const uint64_t upto = (lane == 63) ? ~0ull : ((2ull << lane) - 1ull);
             const uint64_t mine = mask & upto;
             const int segl = __popcll(mine);
-            const int a = mine ? 63 - __clzll(mine) : 0;         // first token of this token's segment
-            const cum_t cprev = __shfl(cum, a > 0 ? a - 1 : 0);
-            before = a > 0 ? cprev : (cum_t)0;
+            if (nstart > 0) {
+                // a block with sequence starts: each segment's cumulative decay from
+                // its own first token, by a scan per segment, so that no step size
+                // (an Inf or NaN one included) crosses a sequence start
+                cum_t cs = 0;
+                for (int j = 0; j <= nstart; ++j) {
+                    const cum_t cj = wave_incl_scan(segl == j ? lv : (cum_t)0);
+                    cs = segl == j ? cj : cs;
+                }
+                cum = cs;
+            }
             if (w == 0) {
                 if (lane < QB) sSeg[lane] = segl;                // all zero for a single-segment block
                 if (start) {
@@ -839,6 +867,7 @@ void ssd_scan_kernel(ScanParams prm) {
                 }
             }
         }
+        const cum_t cend = __shfl(cum, QB - 1);
         nstart_c = nstart;
         cend_f = (float)cend;
         seg_total += cend;
@@ -932,6 +961,13 @@ void ssd_scan_kernel(ScanParams prm) {
     f32x4 acc[RTH];
     constexpr int KS = QB / KSTEP;           // K steps over the tokens of a block
 
+    // X operands of the diagonal product, read before the barrier that ends the MFMA
+    // phase and kept across it (bf16 with paired halves); without sequence ids the
+    // state update reads them first and weights a copy, so each is read once
+    constexpr int DKS = (KSTEP == 32 && NH == 2) ? 2 : 0;
+    constexpr bool XD_SHARED = DKS > 0 && !SEQ && QB / KSTEP == DKS;
+    frag xd[DKS > 0 ? DKS : 1];
+
     // read-out of the carried state over all N (this wave's half from its registers,
     // the partner's from the exchange area) and the update of this wave's half
     auto state_phase = [&]() {
@@ -975,7 +1011,13 @@ void ssd_scan_kernel(ScanParams prm) {
             for (int j = 0; j < MTH; ++j) st[j] *= alpha;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const frag xw = weighted_x_frag<K::SWX>(sXr, LR, ks * KSTEP, xc, lr, lg, [&](int t) { return sWx[t]; });
+                frag xw;
+                if constexpr (XD_SHARED) {
+                    xd[ks] = x_frag<K::SWX>(sXr, LR, ks * KSTEP, xc, lr, lg);
+                    xw = weight_frag(xd[ks], ks * KSTEP, lg, [&](int t) { return sWx[t]; });
+                } else {
+                    xw = weighted_x_frag<K::SWX>(sXr, LR, ks * KSTEP, xc, lr, lg, [&](int t) { return sWx[t]; });
+                }
 #pragma unroll
                 for (int j = 0; j < MTH; ++j) st[j] = MF::mma(bt_frag<N, LB, K::SWB>(sB, mb + j, ks * KSTEP, lr, lg), xw, st[j]);
             }
@@ -1008,8 +1050,10 @@ void ssd_scan_kernel(ScanParams prm) {
 #pragma unroll
                         for (int k = 0; k < NK; ++k) tmp = MF::mma(f[k], c_frag<N>(crw, k, lg), tmp);
                     }
-                    const float sc = (sSeg[t] == j) ? sRow[t] : 0.f;
-                    acc[i] += sc * tmp;
+                    const bool in = sSeg[t] == j;
+                    const float sc = sRow[t];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) acc[i][q] += in ? sc * tmp[q] : 0.f;
                 }
             }
             // (2) state at the end of each segment: a sequence that ends inside
@@ -1027,8 +1071,8 @@ void ssd_scan_kernel(ScanParams prm) {
                     if constexpr (XSCALE) df = sDtf[t];
                     return (sSeg[t] == j) ? fast_exp2((float)(ce - sCum[t])) * df : 0.f;
                 };
-                const cum_t before = (a == 0) ? (cum_t)0 : sCum[a - 1];
-                const float carry = fast_exp2((float)(sCum[e] - before));
+                // (cumulative decays restart at every segment in such a block)
+                const float carry = fast_exp2((float)sCum[e]);
                 f32x4 F[MTH];
                 if (j == 0) {
 #pragma unroll
@@ -1046,9 +1090,13 @@ void ssd_scan_kernel(ScanParams prm) {
                 }
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    const frag xw = weighted_x_frag<K::SWX>(sXr, LR, ks * KSTEP, xc, lr, lg, wseg);
+                    auto keep = [&](int t) { return sSeg[t] == j; };
+                    const frag xw = mask_frag(weighted_x_frag<K::SWX>(sXr, LR, ks * KSTEP, xc, lr, lg, wseg),
+                                              ks * KSTEP, lg, keep);
 #pragma unroll
-                    for (int q = 0; q < MTH; ++q) F[q] = MF::mma(bt_frag<N, LB, K::SWB>(sB, mb + q, ks * KSTEP, lr, lg), xw, F[q]);
+                    for (int q = 0; q < MTH; ++q)
+                        F[q] = MF::mma(mask_frag(bt_frag<N, LB, K::SWB>(sB, mb + q, ks * KSTEP, lr, lg), ks * KSTEP, lg, keep),
+                                       xw, F[q]);
                 }
                 if (j < nstart) {
                     if constexpr (!LOCAL) write_state(F, sSeqOf[j]);
@@ -1069,8 +1117,6 @@ void ssd_scan_kernel(ScanParams prm) {
     // (past-the-end tokens are dropped by the range check).  Everything read from
     // X (the skip term and the X operands) is taken before the barrier that ends
     // the MFMA phase, so the next block's X may be staged right after it.
-    constexpr int DKS = (KSTEP == 32 && NH == 2) ? 2 : 0;          // X operands kept across the barrier
-    frag xd[DKS > 0 ? DKS : 1];
     auto diag_pre = [&]() {
         if (prm.D) {                                             // skip term (none without D)
 #pragma unroll
@@ -1090,23 +1136,56 @@ void ssd_scan_kernel(ScanParams prm) {
                 for (int q = 0; q < 4; ++q) acc[i][q] += Dh * xv[q];
             }
         }
-        if constexpr (DKS > 0) {
+        if constexpr (DKS > 0 && !XD_SHARED) {
 #pragma unroll
             for (int q = 0; q < DKS; ++q) xd[q] = x_frag<K::SWX>(sXr, LR, 32 * q, xc, lr, lg);
         }
     };
     auto diag_phase = [&](int blk) {
+        bool seg_done = false;
+        if constexpr (SEQ) {
+            if (nstart_c > 0) {
+                // A block with sequence starts: one pass per segment, with the other
+                // segments' X rows selected to zero and the result added to the
+                // segment's own tokens only (L o CB is already zero across segments,
+                // but zero times an Inf or NaN of another sequence would not be).
+                for (int j = 0; j <= nstart_c; ++j) {
+                    auto keep = [&](int t) { return sSeg[t] == j; };
 #pragma unroll
-        for (int i = 0; i < RTH; ++i) {
-            const int r = K::own_tile(nh, i);
-            const TI* lrow = sLm + (16 * r + lr) * LQ + KPL * lg;
-            if constexpr (DKS > 0) {
-                // tiles {0, 3} or {1, 2} (or {0} / {1}): one K step for the first, two for the second
+                    for (int i = 0; i < RTH; ++i) {
+                        const int r = K::own_tile(nh, i);
+                        const TI* lrow = sLm + (16 * r + lr) * LQ + KPL * lg;
+                        f32x4 part = f32x4{0.f, 0.f, 0.f, 0.f};
+                        if constexpr (DKS > 0) {
 #pragma unroll
-                for (int q = 0; q < (i == 0 ? 1 : 2); ++q) acc[i] = MF::mma(xd[q], lds_frag<TI>(lrow + 32 * q), acc[i]);
-            } else {
-                for (int ks = 0; ks < 16 * (r + 1); ks += KSTEP)
-                    acc[i] = MF::mma(x_frag<K::SWX>(sXr, LR, ks, xc, lr, lg), lds_frag<TI>(lrow + ks), acc[i]);
+                            for (int q = 0; q < (i == 0 ? 1 : 2); ++q)
+                                part = MF::mma(mask_frag(xd[q], 32 * q, lg, keep), lds_frag<TI>(lrow + 32 * q), part);
+                        } else {
+                            for (int ks = 0; ks < 16 * (r + 1); ks += KSTEP)
+                                part = MF::mma(mask_frag(x_frag<K::SWX>(sXr, LR, ks, xc, lr, lg), ks, lg, keep),
+                                               lds_frag<TI>(lrow + ks), part);
+                        }
+                        const bool in = sSeg[16 * r + lr] == j;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) acc[i][q] += in ? part[q] : 0.f;
+                    }
+                }
+                seg_done = true;
+            }
+        }
+        if (!seg_done) {
+#pragma unroll
+            for (int i = 0; i < RTH; ++i) {
+                const int r = K::own_tile(nh, i);
+                const TI* lrow = sLm + (16 * r + lr) * LQ + KPL * lg;
+                if constexpr (DKS > 0) {
+                    // tiles {0, 3} or {1, 2} (or {0} / {1}): one K step for the first, two for the second
+#pragma unroll
+                    for (int q = 0; q < (i == 0 ? 1 : 2); ++q) acc[i] = MF::mma(xd[q], lds_frag<TI>(lrow + 32 * q), acc[i]);
+                } else {
+                    for (int ks = 0; ks < 16 * (r + 1); ks += KSTEP)
+                        acc[i] = MF::mma(x_frag<K::SWX>(sXr, LR, ks, xc, lr, lg), lds_frag<TI>(lrow + ks), acc[i]);
+                }
             }
         }
         const int64_t t0 = (int64_t)blk * QB;

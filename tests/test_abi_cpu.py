@@ -53,12 +53,14 @@ def test_validate_accepts_the_measured_shapes():
     assert ssd.validate(prob(batch=1, seqlen=8192, nheads=48, ngroups=8, nseqs=16)) == 0
     assert ssd.validate(prob(batch=1, seqlen=256, nheads=2, headdim=16, dstate=16, chunk_len=32,
                              dtype=ssd.DTYPE_F32)) == 0
+    for q in (16, 32, 64, 128, 256, 320):                       # chunk lengths the pages' sweeps use
+        assert ssd.validate(prob(chunk_len=q)) == 0
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(batch=-1), 2), (dict(seqlen=-5), 2), (dict(nheads=0), 2), (dict(headdim=0), 2),
     (dict(ngroups=3), 2), (dict(chunk_len=0), 2), (dict(nseqs=-1), 2),
-    (dict(chunk_len=48), 3), (dict(chunk_len=16), 3), (dict(chunk_len=100), 3),
+    (dict(chunk_len=48), 3), (dict(chunk_len=8), 3), (dict(chunk_len=100), 3),
     (dict(headdim=48), 3), (dict(dstate=96), 3), (dict(dstate=16), 3), (dict(dtype=7), 3), (dict(flags=8), 3),
     (dict(flags=ssd.FLAG_DT_SCALES_X | ssd.FLAG_ZOH), 3),
     (dict(dtype=ssd.DTYPE_F32, dstate=256), 3),

@@ -111,7 +111,7 @@ def test_chunk_length_invariance():
     prob = si.make_problem(1, 300, 2, 64, 128, 1, dtype="bf16", seed=41, d_skip=True, init_std=0.5)
     yr, fr = run_oracle(prob)
     outs = {}
-    for Q in (32, 64, 128, 256):
+    for Q in (16, 32, 64, 128, 256):
         announce("chunk invariance Q=%d" % Q)
         y, f = run_gpu(prob, chunk_len=Q)
         assert_parity(y, yr, TOL["bf16"], "y Q=%d" % Q)
@@ -246,3 +246,62 @@ def test_five_slice_workgroups(case):
     b, T, H, N, G, Q, euler = case
     prob = si.make_problem(b, T, H, 64, N, G, dtype="bf16", seed=H + T, d_skip=True, init_std=0.5)
     check_full(prob, Q, dt_scales_x=euler, label="five slices b=%d H=%d G=%d" % (b, H, G))
+
+
+# ------------------------------------------------------------------ no leak of Inf or NaN
+# "088 Mamba-2", section 5: independent documents packed into one row must not
+# leak into each other.  An Inf or NaN planted in one sequence's inputs may ruin
+# that sequence's outputs, but every other sequence's y and final state must stay
+# finite and bit-identical to the clean run (the kernels select rather than
+# multiply by zero wherever sequences meet inside a block).
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("field,value", [("x", float("inf")), ("x", float("-inf")), ("x", float("nan")),
+                                         ("B", float("inf")), ("C", float("-inf")), ("dt", float("inf")),
+                                         ("dt", float("nan"))])
+@pytest.mark.parametrize("shape", ["blocks", "segments"])
+def test_inf_in_one_sequence_does_not_leak(dtype, field, value, shape):
+    if shape == "blocks":
+        b, T, H, P, N, lens, bad = 2, 200, 2, 32, 64, [[50, 80, 70], [200]], 1     # boundaries inside blocks
+    else:
+        b, T, H, P, N, lens, bad = 1, 1600, 2, 32, 64, [[500, 600, 500]], 1        # rows split into segments
+    if dtype == "f32":
+        P, N = 16, 32
+    prob = si.make_problem(b, T, H, P, N, 1, dtype=dtype, seed=97, d_skip=True, init_std=0.5, seqlens=lens)
+    seq = prob["seq_idx"]
+    announce("inf no-leak %s %s=%s %s" % (dtype, field, value, shape))
+    y0, f0 = run_gpu(prob, chunk_len=64)
+    p2 = dict(prob)
+    t = prob[field].clone()
+    rows, toks = torch.nonzero(seq == bad, as_tuple=True)
+    pick = torch.tensor([0, len(toks) // 2, len(toks) - 1])       # first, a middle and the last token of it
+    r, tk = rows[pick], toks[pick]
+    if field == "dt":
+        t[r, tk, 0] = value
+    else:
+        t[r, tk] = value
+    p2[field] = t
+    y1, f1 = run_gpu(p2, chunk_len=64)
+    others = (seq != bad).numpy()
+    assert np.isfinite(y1[others]).all()
+    np.testing.assert_array_equal(y1[others], y0[others])
+    keep = [k for k in range(prob["nseqs"]) if k != bad]
+    assert np.isfinite(f1[keep]).all()
+    np.testing.assert_array_equal(f1[keep], f0[keep])
+    yr, fr = run_oracle(prob)
+    assert_parity(y0, yr, TOL[dtype], "y (clean)")
+    assert_parity(f0, fr, TOL[dtype], "final (clean)")
+
+
+def test_headline_row_every_head():
+    """At the full 2.7B-layer shape, every head of one row (all 80 heads, so every
+    five-slice workgroup of the row, including those that straddle two heads)
+    against the oracle over the whole 4096-token length."""
+    w = si.WORKLOADS["m2p7_bf16"]
+    prob = si.make_workload(w)
+    announce("m2p7 row 2, all %d heads" % w.nheads)
+    y, f = run_gpu(prob, chunk_len=w.chunk_len)
+    pairs = [(2, h) for h in range(w.nheads)]
+    for (b, h), (yr, fr, seqs) in zip(pairs, oracle_pairs(prob, pairs)):
+        assert_parity(y[b, :, h], yr, TOL["bf16"], "y[%d,:,%d]" % (b, h))
+        assert_parity(f[seqs, h], fr, TOL["bf16"], "final[%d,%d]" % (b, h))
