@@ -124,6 +124,7 @@ def backward_leg(w, prob, d, steps: int, warmup: int):
             "tokens_per_s": round(b * T / (mean / 1000.0), 1),
             "roofline": {"bound": "hbm", "achieved": round(balg / (mean / 1000.0) / 1e9, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(balg / (mean / 1000.0) / 1e9 / HBM_PEAK_GBS, 4),
+                         "traffic": committed_backward_traffic(w.name),
                          "alg_bytes_per_step": balg, "kernels": "all launches of one ssd_backward call"}}
 
 
@@ -256,6 +257,33 @@ def kernel_source_hash() -> str:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
+
+
+def all_source_hash() -> str:
+    """Hash of every kernel and launch source (the backward runs the forward's local
+    pass and combine too)."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mamba_ssd_scan_chunked_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name == "gen_instances.py":
+            continue
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_backward_traffic(workload: str):
+    """HBM bytes moved by one ssd_backward call (FETCH_SIZE and WRITE_SIZE of every
+    launch, scaled by the copy calibration) from profiles/bwd_traffic_<workload>.json,
+    if they were taken on the current sources; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "bwd_traffic_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha") != all_source_hash():
+        return None
+    return rec.get("traffic_bytes_per_call")
 
 
 def committed_counters(workload: str, what: str = "traffic"):

@@ -125,6 +125,26 @@ def test_backward_without_init_dfinal_and_skip():
     check(got, ref, TOL["bf16"], outs=("dx", "ddt", "dA_log", "dB", "dC", "dinit", "dD"))
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_backward_sums_without_cancellation(dt):
+    """With x, B, C, dy, dfinal and the initial states nonnegative, every state H_t
+    and every gradient G_t = dL/dH_t is nonnegative elementwise, so each per-token
+    term of dA_log, ddt_bias (dl_t = <G_t, a_t H_{t-1}>) and dD (x_t . dy_t) has one
+    sign: the sums have no cancellation, and all eight outputs are held to the plain
+    max|ref| rule."""
+    b, T, H, P, N, G = 2, 200, 4, 64, 128 if dt == "bf16" else 64, 2
+    prob = si.make_problem(b, T, H, P, N, G, dtype=dt, seed=41, d_skip=True, init_std=0.5)
+    prob = dict(prob, x=prob["x"].abs(), B=prob["B"].abs(), C=prob["C"].abs(), init=prob["init"].abs())
+    dy, dfinal = cotangents(prob, 42)
+    dtb = si.raw_step_sizes(b, T, H, seed=43, bias_range=(0.0, 0.2))["dt_bias"]
+    announce("backward, sums without cancellation, dtype=%s" % dt)
+    got, ref = run_both(prob, dy.abs(), dfinal.abs(), dt_bias=dtb)
+    for k in SUMS:      # the construction: |sum| equals the sum of the absolute terms
+        assert np.all(np.abs(ref[k]) >= 0.999999 * ref["abs_terms"][k]), k
+    errs = {k: assert_parity(got[k], ref[k], TOL[dt], k) for k in OUTS}
+    print("[errors] " + " ".join("%s=%.2e" % kv for kv in errs.items()), flush=True)
+
+
 def test_backward_no_tokens():
     import mamba_ssd_scan_chunked_amd as ssd
     prob = si.make_problem(2, 0, 2, 64, 128, 1, dtype="bf16", seed=19, d_skip=True, init_std=0.5)
