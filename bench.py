@@ -248,11 +248,12 @@ def fused_step_size_leg(w, prob, d, steps: int, warmup: int):
 
 def kernel_source_hash() -> str:
     """Hash of the sources of the forward path (kernels, instantiations, host
-    launch code); the backward's files and the instance generator are left out."""
+    launch code); the backward's files, the instance generator and the header
+    that only declares the launchers are left out."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "mamba_ssd_scan_chunked_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        if name.startswith("ssd_bwd") or name == "gen_instances.py":
+        if name.startswith("ssd_bwd") or name in ("gen_instances.py", "ssd_launch.hpp"):
             continue
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
