@@ -53,16 +53,16 @@ def gen_bwd(tag, TI, Ps, Ns, QB):
     for P in Ps:
         for N in Ns:
             out.append("    if (P == %d && N == %d) {\n" % (P, N))
-            out.append("        hipLaunchKernelGGL((ssd_bwd_fwd_kernel<%s, %d, %d, %d>), dim3((unsigned)grid), dim3(BwdCfg<%s, %d, %d, %d>::NT), 0, s, prm);\n" % (TI, P, N, QB, TI, P, N, QB))
+            out.append("        hipLaunchKernelGGL((ssd_bwd_fwd_kernel<%s, %d, %d, %d>), dim3((unsigned)grid), dim3(64 * BwdWaves<%s, %d, %d, %d>::FWD), 0, s, prm);\n" % (TI, P, N, QB, TI, P, N, QB))
             out.append("        hipError_t e = hipGetLastError();\n        if (e != hipSuccess) return e;\n")
-            out.append("        hipLaunchKernelGGL((ssd_bwd_rev_kernel<%s, %d, %d, %d>), dim3((unsigned)grid), dim3(BwdCfg<%s, %d, %d, %d>::NT), 0, s, prm);\n" % (TI, P, N, QB, TI, P, N, QB))
+            out.append("        hipLaunchKernelGGL((ssd_bwd_rev_kernel<%s, %d, %d, %d>), dim3((unsigned)grid), dim3(64 * BwdWaves<%s, %d, %d, %d>::REV), 0, s, prm);\n" % (TI, P, N, QB, TI, P, N, QB))
             out.append("        return hipGetLastError();\n    }\n")
     out.append("    return hipErrorInvalidValue;\n}\n\n")
     out.append("hipError_t launch_bwd_klocal_%s(int P, int N, const BwdParams& prm, float* kloc, float* kcarry, int64_t grid, hipStream_t s) {\n" % tag)
     out.append("    if (grid <= 0) return hipSuccess;\n")
     for P in Ps:
         for N in Ns:
-            out.append("    if (P == %d && N == %d) { hipLaunchKernelGGL((ssd_bwd_klocal_kernel<%s, %d, %d, %d>), dim3((unsigned)grid), dim3(BwdCfg<%s, %d, %d, %d>::NT), 0, s, prm, kloc, kcarry); return hipGetLastError(); }\n" % (P, N, TI, P, N, QB, TI, P, N, QB))
+            out.append("    if (P == %d && N == %d) { hipLaunchKernelGGL((ssd_bwd_klocal_kernel<%s, %d, %d, %d>), dim3((unsigned)grid), dim3(64 * BwdWaves<%s, %d, %d, %d>::KLOC), 0, s, prm, kloc, kcarry); return hipGetLastError(); }\n" % (P, N, TI, P, N, QB, TI, P, N, QB))
     out.append("    return hipErrorInvalidValue;\n}\n}  // namespace ssd\n")
     return "".join(out)
 

@@ -207,9 +207,15 @@ __device__ inline float row16_sum(float v) {
     return v;
 }
 
+// Waves per workgroup of each backward kernel.
 template <typename TI, int P, int N, int QB>
+struct BwdWaves {
+    static constexpr int FWD = 16, REV = 8, KLOC = 8;
+};
+
+template <typename TI, int P, int N, int QB, int NW_ = 8>
 struct BwdCfg {
-    static constexpr int NW = 8, NT = 64 * NW;
+    static constexpr int NW = NW_, NT = 64 * NW;
     static constexpr int SZ = sizeof(TI);
     static constexpr int KSTEP = Mfma<TI>::KSTEP;
     static constexpr int PAD = SZ == 2 ? 8 : 4;                 // keeps 16-byte aligned rows
@@ -229,9 +235,9 @@ struct BwdCfg {
 
 // Staging of one block: global loads into registers (issued a block ahead),
 // then into LDS.  dy is converted to the input type for the products.
-template <typename TI, int P, int N, int QB>
+template <typename TI, int P, int N, int QB, int NW_>
 struct BwdStage {
-    using K = BwdCfg<TI, P, N, QB>;
+    using K = BwdCfg<TI, P, N, QB, NW_>;
     uint4 xr[K::XPT], yr[K::YPT], br[K::BPT], cr[K::BPT];
 
     __device__ inline void issue(const char* xrow, int64_t xrec, int xs, const char* yrow, int64_t yrec, int ys,
@@ -288,8 +294,8 @@ struct BwdStage {
 
 // ------------------------------------------------------------ forward pass
 template <typename TI, int P, int N, int QB>
-__global__ __launch_bounds__(512) void ssd_bwd_fwd_kernel(BwdParams prm) {
-    using K = BwdCfg<TI, P, N, QB>;
+__global__ __launch_bounds__((64 * BwdWaves<TI, P, N, QB>::FWD)) void ssd_bwd_fwd_kernel(BwdParams prm) {
+    using K = BwdCfg<TI, P, N, QB, BwdWaves<TI, P, N, QB>::FWD>;
     using M = Mfma<TI>;
     typedef typename CumType<TI>::type cum_t;
     constexpr int NW = K::NW, LP = K::LP, LN = K::LN, LQ = K::LQ, QT = K::QT, PT = K::PT, NTL = K::NTL;
@@ -340,7 +346,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_fwd_kernel(BwdParams prm) {
     else A2 = Anat * 1.4426950408889634f;
     const float dtb = prm.dt_bias ? prm.dt_bias[h] : 0.f;
 
-    BwdStage<TI, P, N, QB> stg;
+    BwdStage<TI, P, N, QB, K::NW> stg;
     float dtn = 0.f;                      // wave 1: the next block's dt (lane = token)
     auto issue = [&](int blk) {
         const int64_t t0 = (int64_t)blk * QB;
@@ -496,8 +502,8 @@ __global__ __launch_bounds__(512) void ssd_bwd_fwd_kernel(BwdParams prm) {
 
 // ------------------------------------------------------------ reverse pass
 template <typename TI, int P, int N, int QB>
-__global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
-    using K = BwdCfg<TI, P, N, QB>;
+__global__ __launch_bounds__((64 * BwdWaves<TI, P, N, QB>::REV)) void ssd_bwd_rev_kernel(BwdParams prm) {
+    using K = BwdCfg<TI, P, N, QB, BwdWaves<TI, P, N, QB>::REV>;
     using M = Mfma<TI>;
     typedef typename CumType<TI>::type cum_t;
     constexpr int NW = K::NW, LP = K::LP, LN = K::LN, LQ = K::LQ, QT = K::QT, PT = K::PT, NTL = K::NTL;
@@ -558,7 +564,7 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
     const float dtb = prm.dt_bias ? prm.dt_bias[h] : 0.f;
     const float Dh = prm.D ? prm.D[h] : 0.f;
 
-    BwdStage<TI, P, N, QB> stg;
+    BwdStage<TI, P, N, QB, K::NW> stg;
     float dtn = 0.f, qn = 0.f;            // the next block's dt (wave 1) and qoff (wave 0), lane = token
     // the block's incoming state at this lane's state-tile positions (4 values per tile)
     typedef typename std::conditional<K::SZ == 2, uint2, uint4>::type h4_t;
@@ -869,8 +875,8 @@ __global__ __launch_bounds__(512) void ssd_bwd_rev_kernel(BwdParams prm) {
 // step then chains the segments from the row's end.  One workgroup per (row,
 // head, segment j > 0); results at (row, head, j - 1).
 template <typename TI, int P, int N, int QB>
-__global__ __launch_bounds__(512) void ssd_bwd_klocal_kernel(BwdParams prm, float* kloc, float* kcarry) {
-    using K = BwdCfg<TI, P, N, QB>;
+__global__ __launch_bounds__((64 * BwdWaves<TI, P, N, QB>::KLOC)) void ssd_bwd_klocal_kernel(BwdParams prm, float* kloc, float* kcarry) {
+    using K = BwdCfg<TI, P, N, QB, BwdWaves<TI, P, N, QB>::KLOC>;
     using M = Mfma<TI>;
     typedef typename CumType<TI>::type cum_t;
     constexpr int NW = K::NW, NT = K::NT, LP = K::LP, LN = K::LN, PT = K::PT, NTL = K::NTL, SZ = K::SZ;
