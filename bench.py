@@ -6,8 +6,13 @@ A step is one full forward (ssd_forward: one launch of the scan kernel) over
 the workload's batch, with inputs and outputs already resident in HBM.
 Prints one JSON line: tokens/s over K timed steps, the roofline of the scan
 kernel from one pair of HIP events around the K back-to-back launches on their
-stream (the median of singly bracketed launches from a separate pass beside
-it), and the CPU oracle timed on the same workload.  The line also carries a "backward" object:
+stream (warm: part of the inputs may still sit in the last-level cache), beside
+it the median of singly bracketed launches and a cold pass (each call timed
+alone after an untimed 1 GiB scrub write: median, p10, p90), the bandwidth of a
+1 GiB device copy and the fraction of it reached, the HBM traffic and pipe
+counters from the committed rocprofv3 summaries (while the kernel sources match
+the hash they were taken on), and the CPU oracle timed on the same workload.
+The line also carries a "backward" object:
 the time of one ssd_backward call (every gradient) on the same workload and its
 fraction of the HBM roofline (skipped with --no-backward); a "step" object: the
 single-token decoding step (ssd_step) at the workload's batch and heads, bound by
