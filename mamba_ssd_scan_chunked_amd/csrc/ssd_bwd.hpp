@@ -565,7 +565,11 @@ __global__ __launch_bounds__((64 * BwdWaves<TI, P, N, QB>::REV)) void ssd_bwd_re
     const float Dh = prm.D ? prm.D[h] : 0.f;
 
     BwdStage<TI, P, N, QB, K::NW> stg;
-    float dtn = 0.f, qn = 0.f;            // the next block's dt (wave 1) and qoff (wave 0), lane = token
+    // the next block's per-token input of waves 0 and 1 (lane = token): qoff for wave 0,
+    // dt for wave 1.  One variable for both: with two, each assigned in its own wave's
+    // branch, the compiler kept them in scratch memory behind a wait for every
+    // outstanding load.
+    float nxt = 0.f;
     // the block's incoming state at this lane's state-tile positions (4 values per tile)
     typedef typename std::conditional<K::SZ == 2, uint2, uint4>::type h4_t;
     // (no branch around the loads, so that nothing waits for them before their use)
@@ -580,13 +584,15 @@ __global__ __launch_bounds__((64 * BwdWaves<TI, P, N, QB>::REV)) void ssd_bwd_re
     auto issue = [&](int blk) {
         const int64_t t0 = (int64_t)blk * QB;
         stg.issue(xrow, xrec, xs, yrow, yrec, ys, brow, crow, brec, bs, t0, tid);
-        if (w == 1) dtn = buf_load_f32(make_rsrc(prm.dt + rh * prm.T + ir.s0 + t0, (T - t0) * 4), lane * 4);
-        if (w == 0) qn = buf_load_f32(make_rsrc(prm.q + rh * prm.T + ir.s0 + t0, (T - t0) * 4), lane * 4);
+        if (w <= 1) {
+            const float* src = w == 1 ? prm.dt : prm.q;
+            nxt = buf_load_f32(make_rsrc(src + rh * prm.T + ir.s0 + t0, (T - t0) * 4), lane * 4);
+        }
     };
     float qcur = 0.f;
     auto scalars = [&](int blk) {
         const int rows = (int)min((int64_t)QB, T - (int64_t)blk * QB);
-        const float pre = dtn + dtb;
+        const float pre = nxt + dtb;          // (wave 1: nxt is dt)
         const float d = lane < rows ? step_size(pre, prm.dt_softplus) : 0.f;
         const cum_t cum = wave_incl_scan((cum_t)d * A2);
         const cum_t cend = __shfl(cum, QB - 1);
@@ -626,7 +632,7 @@ __global__ __launch_bounds__((64 * BwdWaves<TI, P, N, QB>::REV)) void ssd_bwd_re
         issue(nblk - 1);
         stg.store(sX, sDY, sB, sC, tid);
         if (w == 1) scalars(nblk - 1);
-        qcur = qn;
+        qcur = nxt;                       // (wave 0: nxt is qoff)
         block_sync_lds();
     }
 
@@ -831,7 +837,7 @@ __global__ __launch_bounds__((64 * BwdWaves<TI, P, N, QB>::REV)) void ssd_bwd_re
         if (blk > 0) {
             stg.store(sX, sDY, sB, sC, tid);
             if (w == 1) scalars(blk - 1);
-            qcur = qn;
+            qcur = nxt;                       // (wave 0: nxt is qoff)
         }
         block_sync_lds();
     }
