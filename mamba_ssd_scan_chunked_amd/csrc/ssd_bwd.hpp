@@ -190,12 +190,43 @@ __device__ inline f32x4 lds_load4(const __bf16* p) {
     return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
 }
 __device__ inline f32x4 lds_load4(const float* p) { return *(const f32x4*)p; }
-// Sum over the four lane groups (lanes with equal l % 16).
-__device__ inline float group4_sum(float v) {
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
-    return v;
+// Sums across lane rows with gfx950's lane-swap instructions (VALU, no LDS
+// permute).  v_permlane16_swap trades the odd 16-lane rows of its first operand
+// for the even rows of its second; v_permlane32_swap the upper 32 lanes of the
+// first for the lower 32 of the second.  Swapping v with zero leaves v's even rows
+// (resp. lower half) in the first result and its odd rows (resp. upper half) moved
+// down in the second, zero elsewhere, so the two results add to
+//   add_xor16_even: v[l] + v[l + 16] in rows 0 and 2 (lanes 0-15, 32-47),
+//   add_xor32_low:  v[l] + v[l + 32] in lanes 0-31,
+// and to 0 in the other lanes.  The second result passes through an empty asm
+// statement: in a sum of the two results, the compiler's optimizer replaced the
+// second by the first (and added the first to itself).
+__device__ inline float add_swapped(unsigned a, unsigned b) {
+    asm volatile("" : "+v"(b));
+    return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
 }
+__device__ inline float add_xor16_even(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, v), 0u, false, false);
+    return add_swapped(r[0], r[1]);
+}
+__device__ inline float add_xor32_low(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v), 0u, false, false);
+    return add_swapped(r[0], r[1]);
+}
+// The value of lane L (a constant), in every lane.
+template <int L>
+__device__ inline float lane_value(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), L));
+}
+template <int L>
+__device__ inline double lane_value(double v) {
+    const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
+    const unsigned lo = __builtin_amdgcn_readlane((int)(unsigned)u, L), hi = __builtin_amdgcn_readlane((int)(unsigned)(u >> 32), L);
+    return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
+}
+// Sum over the four lane groups (lanes with equal l % 16), valid in lanes 0-15
+// (lane group 0) only: (v[l] + v[l+16]) + (v[l+32] + v[l+48]).
+__device__ inline float group4_sum_lg0(float v) { return add_xor32_low(add_xor16_even(v)); }
 
 // Sum over the 16 lanes of each lane group (lanes with equal l/16), left in the
 // group's last lane (DPP row shifts, as in the wavefront scan).
@@ -358,7 +389,7 @@ __global__ __launch_bounds__((64 * BwdWaves<TI, P, N, QB>::FWD)) void ssd_bwd_fw
         const int rows = (int)min((int64_t)QB, T - (int64_t)blk * QB);
         const float d = lane < rows ? step_size(dtn + dtb, prm.dt_softplus) : 0.f;
         const cum_t cum = wave_incl_scan((cum_t)d * A2);
-        const cum_t cend = __shfl(cum, QB - 1);
+        const cum_t cend = lane_value<QB - 1>(cum);
         const float f = x_factor(d, Anat, prm.x_scale);
         if (lane < QB) {
             sCum[lane] = cum;
@@ -457,7 +488,7 @@ __global__ __launch_bounds__((64 * BwdWaves<TI, P, N, QB>::FWD)) void ssd_bwd_fw
                     const f32x4 off = a3[j] * sDin[t];
                     store_grad4(acc + off, rdc, t * HB * N + n0, prm.h_bf16);
                     const f32x4 c4 = lds_load4(sC + t * LN + n0);
-                    const float qs = group4_sum(off[0] * c4[0] + off[1] * c4[1] + off[2] * c4[2] + off[3] * c4[3]);
+                    const float qs = group4_sum_lg0(off[0] * c4[0] + off[1] * c4[1] + off[2] * c4[2] + off[3] * c4[3]);
                     if (lg == 0) sQp[ni][t] = qs;
                 }
             }
@@ -595,7 +626,7 @@ __global__ __launch_bounds__((64 * BwdWaves<TI, P, N, QB>::REV)) void ssd_bwd_re
         const float pre = nxt + dtb;          // (wave 1: nxt is dt)
         const float d = lane < rows ? step_size(pre, prm.dt_softplus) : 0.f;
         const cum_t cum = wave_incl_scan((cum_t)d * A2);
-        const cum_t cend = __shfl(cum, QB - 1);
+        const cum_t cend = lane_value<QB - 1>(cum);
         if (lane < QB) {
             sCum[lane] = cum;
             sF[lane] = x_factor(d, Anat, prm.x_scale);
@@ -671,8 +702,7 @@ __global__ __launch_bounds__((64 * BwdWaves<TI, P, N, QB>::REV)) void ssd_bwd_re
                     const float zr = row16_sum(z);
                     if (lr == 15) sRz[ti][s] = zr;
                 }
-                zc += __shfl_xor(zc, 16);
-                zc += __shfl_xor(zc, 32);
+                zc = group4_sum_lg0(zc);
                 if (lg == 0) sCz[si][t] = zc;
                 store4(sE + t * LQ + s0, ve[0], ve[1], ve[2], ve[3]);
                 store4(sFm + t * LQ + s0, vf[0], vf[1], vf[2], vf[3]);
@@ -701,8 +731,9 @@ __global__ __launch_bounds__((64 * BwdWaves<TI, P, N, QB>::REV)) void ssd_bwd_re
                     for (int e = 0; e < 4; ++e) kp += kst[j][e] * to_f32(hv[e]);
                 }
             }
+            kp = add_xor32_low(add_xor16_even(kp));          // lanes 0-15 hold the sums of their four lane groups
 #pragma unroll
-            for (int d = 32; d >= 1; d >>= 1) kp += __shfl_xor(kp, d);
+            for (int d = 8; d >= 1; d >>= 1) kp += __shfl_xor(kp, d);      // (within lanes 0-15)
             if (lane == 0) sKap[w] = kp;
         }
         f32x4 a5[K::T_QN];
@@ -737,9 +768,9 @@ __global__ __launch_bounds__((64 * BwdWaves<TI, P, N, QB>::REV)) void ssd_bwd_re
                     const f32x4 gb = acc + gof;
                     const f32x4 dy4 = lds_load4(sDY + t * LP + p0), x4 = lds_load4(sX + t * LP + p0);
                     buf_store16(gb * sF[t] + dy4 * Dh, rdx, (int)((t * H * P + p0) * 4));
-                    const float us = group4_sum(x4[0] * gb[0] + x4[1] * gb[1] + x4[2] * gb[2] + x4[3] * gb[3]);
-                    const float uo = group4_sum(x4[0] * gof[0] + x4[1] * gof[1] + x4[2] * gof[2] + x4[3] * gof[3]);
-                    const float ds = group4_sum(x4[0] * dy4[0] + x4[1] * dy4[1] + x4[2] * dy4[2] + x4[3] * dy4[3]);
+                    const float us = group4_sum_lg0(x4[0] * gb[0] + x4[1] * gb[1] + x4[2] * gb[2] + x4[3] * gb[3]);
+                    const float uo = group4_sum_lg0(x4[0] * gof[0] + x4[1] * gof[1] + x4[2] * gof[2] + x4[3] * gof[3]);
+                    const float ds = group4_sum_lg0(x4[0] * dy4[0] + x4[1] * dy4[1] + x4[2] * dy4[2] + x4[3] * dy4[3]);
                     if (lg == 0) {
                         sUp[pj][t] = us;
                         sUop[pj][t] = uo;
@@ -819,7 +850,7 @@ __global__ __launch_bounds__((64 * BwdWaves<TI, P, N, QB>::REV)) void ssd_bwd_re
             const acc_t qv = valid ? (acc_t)qcur : (acc_t)0;
             const acc_t rv = lane < QB ? (acc_t)f * (acc_t)uo : (acc_t)0;
             const acc_t zi = wave_incl_scan(zv), qi = wave_incl_scan(qv), ri = wave_incl_scan(rv);
-            const acc_t qtot = __shfl(qi, 63);
+            const acc_t qtot = lane_value<63>(qi);
             const acc_t dl = (zi - zv) + (qtot - qi + qv) + (ri - rv) + (acc_t)cend_r * (acc_t)kap;
             if (valid) {
                 const float d = d_r;
@@ -952,7 +983,7 @@ __global__ __launch_bounds__((64 * BwdWaves<TI, P, N, QB>::KLOC)) void ssd_bwd_k
             const int rows = (int)min((int64_t)QB, T - (int64_t)blk * QB);
             const float d = lane < rows ? step_size(dtn + dtb, prm.dt_softplus) : 0.f;
             const cum_t cum = wave_incl_scan((cum_t)d * A2);
-            const cum_t cend = __shfl(cum, QB - 1);
+            const cum_t cend = lane_value<QB - 1>(cum);
             if (lane < QB) sDin[lane] = fast_exp2((float)cum);
             if (lane == 0) sCend = fast_exp2((float)cend);
             total += cend;
