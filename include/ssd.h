@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 4
+#define SSD_ABI_VERSION 5
 
 /* Element type of x, B and C.  dt, A_log, D, init_state, y and final_state are
  * always fp32.  BF16: bf16 operands, fp32 accumulation; F32: fp32 throughout. */
@@ -98,6 +98,12 @@ typedef struct {
     int64_t nseqs;      /* number of sequences: == batch without seq_idx            */
     int32_t dtype;      /* ssd_dtype_t                                              */
     uint32_t flags;     /* SSD_FLAG_*                                               */
+    int32_t segments;   /* segments per row for the split-row path of ssd_forward and
+                           ssd_backward: 0 lets the library choose (the default);
+                           n > 0 forces n (clamped to the row's blocks), 1 no split.
+                           A scheduling choice only: every value gives the same
+                           function.  Must be >= 0                                  */
+    int32_t reserved;   /* must be 0                                                */
 } ssd_problem_t;
 
 /* Host-only check of a problem description (no HIP call).  Supported builds:
@@ -119,9 +125,8 @@ int ssd_validate(const ssd_problem_t* p);
  * each segment's state (fp32 P x N) and carried decay, (batch, nheads,
  * segments - 1) of each.  The chunked algorithm's inter-chunk state passing at
  * segment granularity (section 3 of "088 Mamba-2"; key design 2 on the
- * papernotes page).  Depends on the problem only (and on the SSD_SEGMENTS
- * environment variable, which forces the number of segments per row); the
- * contents need no initialisation. */
+ * papernotes page).  Depends on the problem only (its `segments` field forces
+ * the number of segments per row); the contents need no initialisation. */
 size_t ssd_workspace_size(const ssd_problem_t* p);
 
 /* Full forward on `stream`: one kernel launch, or three when rows are split

@@ -33,7 +33,7 @@ DTYPE_BF16 = 1
 FLAG_DT_SCALES_X = 1
 FLAG_DT_SOFTPLUS = 2
 FLAG_ZOH = 4
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 SSD_OK = 0
 ERROR_NAMES = {1: "NULL_POINTER", 2: "BAD_SHAPE", 3: "UNSUPPORTED", 4: "ALIGNMENT", 5: "WORKSPACE",
@@ -50,7 +50,7 @@ class Problem(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
                 ("headdim", ctypes.c_int64), ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64),
                 ("chunk_len", ctypes.c_int64), ("nseqs", ctypes.c_int64), ("dtype", ctypes.c_int32),
-                ("flags", ctypes.c_uint32)]
+                ("flags", ctypes.c_uint32), ("segments", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 _lib = None
@@ -106,9 +106,12 @@ def _check(code: int):
 
 
 def problem(batch, seqlen, nheads, headdim, dstate, ngroups=1, chunk_len=256, nseqs=None,
-            dtype=DTYPE_BF16, flags=0) -> Problem:
+            dtype=DTYPE_BF16, flags=0, segments=0) -> Problem:
+    """A problem description.  ``segments`` > 0 forces the number of segments each
+    row is cut into on the split-row path (0: the library's choice); it does not
+    change the result."""
     return Problem(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_len,
-                   batch if nseqs is None else nseqs, dtype, flags)
+                   batch if nseqs is None else nseqs, dtype, flags, segments, 0)
 
 
 def validate(p: Problem) -> int:
@@ -130,7 +133,7 @@ def _stream_of(device, stream):
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def _describe(x, B, dt, A_log, chunk_len, seq_idx, nseqs, dt_scales_x, dt_softplus=False, zoh=False):
+def _describe(x, B, dt, A_log, chunk_len, seq_idx, nseqs, dt_scales_x, dt_softplus=False, zoh=False, segments=0):
     import torch
     if x.dim() != 4 or B.dim() != 4:
         raise ValueError("x must be (b,T,H,P) and B, C (b,T,G,N)")
@@ -150,7 +153,7 @@ def _describe(x, B, dt, A_log, chunk_len, seq_idx, nseqs, dt_scales_x, dt_softpl
         ns = int(nseqs)
     flags = (FLAG_DT_SCALES_X if dt_scales_x else 0) | (FLAG_DT_SOFTPLUS if dt_softplus else 0) | \
         (FLAG_ZOH if zoh else 0)
-    return problem(b, T, H, Pd, N, G, chunk_len, ns, dtype, flags)
+    return problem(b, T, H, Pd, N, G, chunk_len, ns, dtype, flags, segments)
 
 
 def _check_tensors(x, dt, A_log, B, C, D, init_state, seq_idx, dt_bias=None):
@@ -210,13 +213,14 @@ def _check_workspace(ws, nbytes, dev):
 def forward(x, dt, A_log, B, C, D=None, chunk_len: int = 256, init_state=None, seq_idx=None,
             nseqs: Optional[int] = None, dt_scales_x: bool = False, y=None, final_state=None,
             workspace=None, return_final: bool = True, stream=None, dt_bias=None, dt_softplus: bool = False,
-            zoh: bool = False):
+            zoh: bool = False, segments: int = 0):
     """SSD forward through ``ssd_forward``.  Returns (y, final_state or None).
 
     The step size is dt + dt_bias (dt_bias None = 0), through softplus when
     ``dt_softplus``; x is written to the state unscaled, times the step size
     (``dt_scales_x``) or times the exact zero-order hold (exp(step A) - 1) / A
-    (``zoh``)."""
+    (``zoh``).  ``segments`` > 0 forces the number of segments per row on the
+    split-row path (a scheduling choice; 0: the library's)."""
     import torch
     _check_tensors(x, dt, A_log, B, C, D, init_state, seq_idx, dt_bias)
     in_place = final_state is not None and init_state is not None and final_state is init_state
@@ -227,7 +231,7 @@ def forward(x, dt, A_log, B, C, D=None, chunk_len: int = 256, init_state=None, s
     dt_bias = dt_bias.contiguous() if dt_bias is not None else None
     init_state = init_state.contiguous() if init_state is not None else None
     seq_idx = seq_idx.contiguous() if seq_idx is not None else None
-    p = _describe(x, B, dt, A_log, chunk_len, seq_idx, nseqs, dt_scales_x, dt_softplus, zoh)
+    p = _describe(x, B, dt, A_log, chunk_len, seq_idx, nseqs, dt_scales_x, dt_softplus, zoh, segments)
     lib = load_library()
     _check(lib.ssd_validate(ctypes.byref(p)))
     dev = x.device
@@ -322,7 +326,7 @@ def backward_workspace_size(p: Problem) -> int:
 
 def backward(x, dt, A_log, B, C, dy, D=None, init_state=None, dfinal=None, chunk_len: int = 256,
              dt_scales_x: bool = False, dt_bias=None, dt_softplus: bool = False, zoh: bool = False,
-             workspace=None, stream=None, seq_idx=None, nseqs: Optional[int] = None):
+             workspace=None, stream=None, seq_idx=None, nseqs: Optional[int] = None, segments: int = 0):
     """Gradients through ``ssd_backward`` of L = <dy, y> + <dfinal, final_state> for the
     forward map of :func:`forward` with the same arguments.  Returns a dict of fp32
     tensors: dx, ddt, dA_log, dB, dC, dD, dinit, ddt_bias (dD, dinit and ddt_bias are
@@ -336,7 +340,7 @@ def backward(x, dt, A_log, B, C, dy, D=None, init_state=None, dfinal=None, chunk
     dt_bias = dt_bias.contiguous() if dt_bias is not None else None
     init_state = init_state.contiguous() if init_state is not None else None
     seq_idx = seq_idx.contiguous() if seq_idx is not None else None
-    p = _describe(x, B, dt, A_log, chunk_len, seq_idx, nseqs, dt_scales_x, dt_softplus, zoh)
+    p = _describe(x, B, dt, A_log, chunk_len, seq_idx, nseqs, dt_scales_x, dt_softplus, zoh, segments)
     lib = load_library()
     _check(lib.ssd_validate(ctypes.byref(p)))
     b, T, H, P = x.shape

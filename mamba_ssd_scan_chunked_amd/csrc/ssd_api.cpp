@@ -101,7 +101,8 @@ int64_t nblocks(const ssd_problem_t* p) {
 // blocks per segment.  (Measured on MI355X: 32 items of 256 blocks run best as
 // 16 segments, or 8 with N = 256; 48 packed-sequence items of 128 blocks as 5;
 // 192 items of 32 blocks run best unsplit.)  A function of the problem alone (no device query),
-// so the workspace size is known on the host; SSD_SEGMENTS=<n> overrides it.
+// so the workspace size is known on the host; the problem's `segments` field, when
+// positive, forces the count.
 struct Segs {
     int nseg, seg_blocks;
 };
@@ -110,9 +111,8 @@ Segs segments(const ssd_problem_t* p) {
     Segs r{1, (int)(nblk > 0 ? nblk : 1)};
     if (nblk <= 1 || p->batch == 0) return r;
     int64_t S = 1;
-    const char* env = std::getenv("SSD_SEGMENTS");
-    if (env && std::atoi(env) > 0) {
-        S = std::atoi(env);
+    if (p->segments > 0) {
+        S = p->segments;
     } else {
         // workgroups the scan keeps resident per CU: one where a single
         // workgroup fills the CU's registers or LDS (bf16 64-channel heads with
@@ -154,11 +154,6 @@ int64_t workspace_bytes(const ssd_problem_t* p) { return ws_layout(p).total; }
 int slices_per_workgroup(const ssd_problem_t* p, bool seq, int nseg) {
     const int npt = (int)(p->headdim / 16);
     const int64_t items = p->batch * p->nheads;
-    const char* env = std::getenv("SSD_SPW");          // forced (measurements and tests)
-    if (env && std::atoi(env) > 0 && p->dtype == SSD_DTYPE_BF16 && p->headdim == 64 && !seq) {
-        const int v = std::atoi(env);
-        if ((v == npt || (v == npt + 1 && nseg == 1)) && ((p->nheads / p->ngroups) * npt) % v == 0) return v;
-    }
     if (p->dtype == SSD_DTYPE_BF16 && p->headdim == 64 && !seq && nseg == 1 && items > 256 && items <= 320 &&
         ((p->nheads / p->ngroups) * npt) % (npt + 1) == 0)
         return npt + 1;
@@ -331,7 +326,8 @@ int ssd_validate(const ssd_problem_t* p) {
     if (p->batch >= kMaxDim || p->seqlen >= kMaxDim || p->nheads >= kMaxDim || p->nseqs >= kMaxDim)
         return SSD_ERR_BAD_SHAPE;
     if (p->nheads % p->ngroups != 0) return SSD_ERR_BAD_SHAPE;
-    if (p->chunk_len <= 0) return SSD_ERR_BAD_SHAPE;
+    if (p->chunk_len <= 0 || p->segments < 0) return SSD_ERR_BAD_SHAPE;
+    if (p->reserved != 0) return SSD_ERR_UNSUPPORTED;
     if (p->dtype != SSD_DTYPE_BF16 && p->dtype != SSD_DTYPE_F32) return SSD_ERR_UNSUPPORTED;
     if (p->flags & ~uint32_t(SSD_FLAG_DT_SCALES_X | SSD_FLAG_DT_SOFTPLUS | SSD_FLAG_ZOH)) return SSD_ERR_UNSUPPORTED;
     if ((p->flags & SSD_FLAG_DT_SCALES_X) && (p->flags & SSD_FLAG_ZOH)) return SSD_ERR_UNSUPPORTED;

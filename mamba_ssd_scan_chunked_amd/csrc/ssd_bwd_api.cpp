@@ -207,7 +207,8 @@ int bwd_block(const ssd_problem_t* p) { return p->dtype == SSD_DTYPE_BF16 ? ssd:
 // S <= 8 that minimises the rounds of workgroups over the 256 CUs per unit of
 // row length, ceil(items S / 256) / S, plus a charge of 0.5 (S - 1) / S for the
 // local passes (measured on MI355X: 320 items run best as 4 segments, 192 unsplit).
-// SSD_BWD_SEGMENTS=<n> forces n.  A function of the problem alone, so the
+// The problem's `segments` field, when positive, forces the count (as for the
+// forward; without sequence ids).  A function of the problem alone, so the
 // workspace size is known on the host.
 struct BwdSegs {
     int nseg;
@@ -218,9 +219,8 @@ BwdSegs bwd_segments(const ssd_problem_t* p) {
     BwdSegs r{1, std::max<int64_t>(p->seqlen, 1)};
     if (nb64 <= 1 || p->batch == 0) return r;
     int64_t S = 1;
-    const char* env = std::getenv("SSD_BWD_SEGMENTS");
-    if (env && std::atoi(env) > 0) {
-        S = std::atoi(env);
+    if (p->segments > 0) {
+        S = p->segments;
     } else {
         const int64_t units = p->batch * p->nheads;
         if (units <= 128) {

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_strerror():
-    assert ssd.version() == 4
+    assert ssd.version() == 5
     lib = ssd.load_library()
     for code in range(0, 10):
         assert lib.ssd_strerror(code)
@@ -86,13 +86,22 @@ def test_workspace_size():
     assert ssd.workspace_size(p) == n * 64 * 128 * 4 + ((n * 4 + 255) // 256) * 256
 
 
-def test_workspace_size_follows_forced_segments(monkeypatch):
-    p = prob(batch=1, seqlen=1000, nheads=2, headdim=32, dstate=64, chunk_len=64)   # 16 blocks
-    monkeypatch.setenv("SSD_SEGMENTS", "1")
+def test_workspace_size_follows_forced_segments():
+    p = prob(batch=1, seqlen=1000, nheads=2, headdim=32, dstate=64, chunk_len=64, segments=1)   # 16 blocks
     assert ssd.workspace_size(p) == 0
-    monkeypatch.setenv("SSD_SEGMENTS", "5")      # 4 blocks per segment -> 4 segments
-    n = 2 * 3
+    p = prob(batch=1, seqlen=1000, nheads=2, headdim=32, dstate=64, chunk_len=64, segments=5)
+    n = 2 * 3                                    # 4 blocks per segment -> 4 segments
     assert ssd.workspace_size(p) == n * 32 * 64 * 4 + 256
+    assert ssd.workspace_size(prob(batch=1, seqlen=1000, nheads=2, headdim=32, dstate=64, chunk_len=64)) > 0
+
+
+def test_segments_and_reserved_fields_are_checked():
+    assert ssd.validate(prob(segments=-1)) == 2                 # SSD_ERR_BAD_SHAPE
+    p = prob()
+    p.reserved = 1
+    assert ssd.validate(p) == 3                                 # SSD_ERR_UNSUPPORTED
+    assert ssd.validate(prob(segments=7)) == 0
+    assert ctypes.sizeof(ssd.Problem) == 80
 
 
 def _forward(p, **ptrs):
@@ -352,8 +361,7 @@ def test_noalloc_entry_point_checks_and_limit(monkeypatch):
     st = A + 20 * (1 << 30)
     assert _forward_noalloc(split, init=st, fin=st) == 6               # in place on split rows
     # forced to 64 segments per row, 128 (row, head) items need 258 MB of states
-    monkeypatch.setenv("SSD_SEGMENTS", "64")
-    big = prob(batch=2, seqlen=16384, nheads=64)
+    big = prob(batch=2, seqlen=16384, nheads=64, segments=64)
     assert ssd.workspace_size(big) > ssd.noalloc_scratch_bytes()
     assert _forward_noalloc(big) == 9
     assert b"scratch" in ssd.load_library().ssd_strerror(9)

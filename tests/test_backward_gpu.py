@@ -39,14 +39,15 @@ def cotangents(prob, seed):
     return f32(rng.standard_normal((b, T, H, P))), f32(rng.standard_normal((ns, H, P, N)))
 
 
-def run_both(prob, dy, dfinal, *, dt_bias=None, dt_softplus=False, zoh=False, dt_scales_x=False, workers=0):
+def run_both(prob, dy, dfinal, *, dt_bias=None, dt_softplus=False, zoh=False, dt_scales_x=False, workers=0,
+             segments=0):
     import mamba_ssd_scan_chunked_amd as ssd
     d = to_device(prob)
     packed = prob["seq_idx"] is not None
     g = ssd.backward(d["x"], d["dt"], d["A_log"], d["B"], d["C"], dy.cuda(), D=d["D"], init_state=d["init"],
                      dfinal=dfinal.cuda() if dfinal is not None else None, dt_scales_x=dt_scales_x,
                      dt_bias=dt_bias.cuda() if dt_bias is not None else None, dt_softplus=dt_softplus, zoh=zoh,
-                     seq_idx=d["seq_idx"], nseqs=prob["nseqs"] if packed else None)
+                     seq_idx=d["seq_idx"], nseqs=prob["nseqs"] if packed else None, segments=segments)
     torch.cuda.synchronize()
     got = {k: v.cpu().double().numpy() for k, v in g.items()}
     ref = oracle.gradients(prob["x"], prob["dt"], prob["A_log"], prob["B"], prob["C"], dy, prob["D"], prob["init"],
@@ -238,23 +239,20 @@ SPLIT = [
 
 
 @pytest.mark.parametrize("case", SPLIT, ids=lambda c: "%s-b%d-T%d-H%d-P%d-N%d-G%d-S%d" % c)
-def test_backward_split_rows(case, monkeypatch):
+def test_backward_split_rows(case):
     """Rows cut into segments (the state entering each segment from the forward's local
     pass and combine step, the gradient leaving each from the reverse local pass and
     combine step): every output against the oracle."""
     dt, b, T, H, P, N, G, S = case
-    if S:
-        monkeypatch.setenv("SSD_BWD_SEGMENTS", str(S))
     prob = si.make_problem(b, T, H, P, N, G, dtype=dt, seed=T + 7, d_skip=True, init_std=0.5)
     dy, dfinal = cotangents(prob, T + 8)
     announce("backward split rows %s" % (case,))
-    got, ref = run_both(prob, dy, dfinal)
+    got, ref = run_both(prob, dy, dfinal, segments=S)
     check(got, ref, TOL[dt])
 
 
 @pytest.mark.parametrize("mode", ["softplus_zoh", "euler"])
-def test_backward_split_rows_step_size_modes(mode, monkeypatch):
-    monkeypatch.setenv("SSD_BWD_SEGMENTS", "4")
+def test_backward_split_rows_step_size_modes(mode):
     kw = dict(MODES[mode])
     kw.pop("bias", None)
     b, T, H = 1, 600, 2
@@ -266,21 +264,20 @@ def test_backward_split_rows_step_size_modes(mode, monkeypatch):
         dtb = raw["dt_bias"]
     dy, dfinal = cotangents(prob, 43)
     announce("backward split rows mode=%s" % mode)
-    got, ref = run_both(prob, dy, dfinal, dt_bias=dtb, **kw)
+    got, ref = run_both(prob, dy, dfinal, dt_bias=dtb, segments=4, **kw)
     check(got, ref, TOL["bf16"])
 
 
-def test_backward_split_equals_unsplit(monkeypatch):
+def test_backward_split_equals_unsplit():
     """The same problem with 1 and 4 segments: equal within the tolerance."""
     import mamba_ssd_scan_chunked_amd as ssd
     prob = si.make_problem(1, 512, 2, 64, 128, 1, dtype="bf16", seed=47, d_skip=True, init_std=0.5)
     dy, dfinal = cotangents(prob, 48)
     d = to_device(prob)
     outs = []
-    for S in ("1", "4"):
-        monkeypatch.setenv("SSD_BWD_SEGMENTS", S)
+    for S in (1, 4):
         g = ssd.backward(d["x"], d["dt"], d["A_log"], d["B"], d["C"], dy.cuda(), D=d["D"], init_state=d["init"],
-                         dfinal=dfinal.cuda())
+                         dfinal=dfinal.cuda(), segments=S)
         torch.cuda.synchronize()
         outs.append({k: v.cpu().double().numpy() for k, v in g.items()})
     for k in OUTS:

@@ -1,12 +1,11 @@
 """Rows split into segments that run in parallel (local pass, combine, scan from
 each segment's incoming state), against the CPU oracle.
 
-The library picks the number of segments from the problem; SSD_SEGMENTS forces
-it, so each case runs unsplit and split into several segments (including a
-ragged last one).  Same tolerance as the other parity tests: max |got - ref| <=
+The library picks the number of segments from the problem; the problem's
+`segments` field forces it, so each case runs unsplit and split into several
+segments (including a ragged last one).  Same tolerance as the other parity tests: max |got - ref| <=
 tol * max |ref|, tol = 2e-2 for bf16 inputs and 1e-5 for fp32.
 """
-import os
 import sys
 
 import numpy as np
@@ -25,11 +24,7 @@ def announce(msg):
 
 
 def run_split(prob, chunk_len, nseg, dt_scales_x=False):
-    os.environ["SSD_SEGMENTS"] = str(nseg)
-    try:
-        return run_gpu(prob, chunk_len=chunk_len, dt_scales_x=dt_scales_x)
-    finally:
-        del os.environ["SSD_SEGMENTS"]
+    return run_gpu(prob, chunk_len=chunk_len, dt_scales_x=dt_scales_x, segments=nseg)
 
 
 CASES = [
