@@ -37,17 +37,15 @@
 
 #include <type_traits>
 
-#ifndef SSD_X_AUX
-#define SSD_X_AUX 0
-#endif
-#ifndef SSD_Y_AUX
-#define SSD_Y_AUX 18
-#endif
-#ifndef SSD_LEADER_SCAN
-#define SSD_LEADER_SCAN 1
-#endif
-
 namespace ssd {
+
+// Cache-policy bits of the buffer loads and stores (gfx950: 1 = sc0, 2 = nt,
+// 16 = sc1).  y is written once and never read back by the kernel: its stores are
+// non-temporal at device scope (nt | sc1), so its stream does not displace the B
+// and C rows that the heads of a row share in L2.  x loads keep the default policy
+// (a sweep of nt, sc0 and sc1 on them changed nothing measurable).
+constexpr int kXLoadPolicy = 0;
+constexpr int kYStorePolicy = 18;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -593,7 +591,7 @@ void ssd_scan_kernel(ScanParams prm) {
     constexpr int KSTEP = K::KSTEP, SZ = K::SZ, NK = K::NK, RT = K::RT, MT = K::MT, NW = K::NW;
     constexpr int NH = K::NH, NPT = K::NPT, MTH = K::MTH, NKH = K::NKH, RTH = K::RTH, MLH = K::MLH, XW = K::XW;
     constexpr int NFH = SZ == 2 ? MTH / 2 : 4 * MTH;               // read-out fragments of a state half
-    constexpr bool LEADER_SCAN = SSD_LEADER_SCAN != 0;
+    constexpr bool LEADER_SCAN = true;     // without sequence ids only the head leaders run the per-token scan
     static_assert(NFH == NKH, "fragments of a state half are whole K steps");
     static_assert(QB <= 64 && QB % KSTEP == 0 && QB % 16 == 0, "block length");
     static_assert(N % KSTEP == 0 && N % 16 == 0 && P % 16 == 0, "shape");
@@ -758,7 +756,7 @@ void ssd_scan_kernel(ScanParams prm) {
 #pragma unroll
         for (int j = 0; j < K::XPT; ++j) {
             const int v = tid + j * NT;
-            if (K::XU % NT == 0 || v < K::XU) xr[j] = buf_load16<SSD_X_AUX>(rx, (v / (XW / VE)) * xs + (v % (XW / VE)) * 16);
+            if (K::XU % NT == 0 || v < K::XU) xr[j] = buf_load16<kXLoadPolicy>(rx, (v / (XW / VE)) * xs + (v % (XW / VE)) * 16);
         }
     };
     auto issue_bc = [&](int blk) {
@@ -1191,7 +1189,7 @@ void ssd_scan_kernel(ScanParams prm) {
         const int64_t t0 = (int64_t)blk * QB;
         const rsrc_t ry = make_rsrc(yrow + t0 * ys, yrec - t0 * ys);
 #pragma unroll
-        for (int i = 0; i < RTH; ++i) buf_store16<SSD_Y_AUX>(acc[i], ry, (16 * K::own_tile(nh, i) + lr) * ys + (xc + 4 * lg) * 4);
+        for (int i = 0; i < RTH; ++i) buf_store16<kYStorePolicy>(acc[i], ry, (16 * K::own_tile(nh, i) + lr) * ys + (xc + 4 * lg) * 4);
         if constexpr (SEQ) prevseq = lastseq_c;
     };
 
