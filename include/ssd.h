@@ -114,7 +114,9 @@ typedef struct {
  * same y and final state up to rounding, section 1 of "088 Mamba-2"); the
  * kernel evaluates the sequence in blocks of 32 rows (chunk_len 16 or 32) or 64
  * rows (multiples of 64), passing the state between blocks (the past-to-future
- * parts of a diagonal block are low rank, exactly as between chunks). */
+ * parts of a diagonal block are low rank, exactly as between chunks).
+ * A negative `segments` gives SSD_ERR_BAD_SHAPE, a nonzero `reserved`
+ * SSD_ERR_UNSUPPORTED. */
 int ssd_validate(const ssd_problem_t* p);
 
 /* Bytes of device workspace ssd_forward needs for this problem; 0 when it needs
