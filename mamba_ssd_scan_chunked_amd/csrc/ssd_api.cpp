@@ -95,12 +95,13 @@ int64_t nblocks(const ssd_problem_t* p) {
     return q ? (p->seqlen + q - 1) / q : 0;
 }
 
-// Segments per row.  With at most 128 (row, head) items, rows are split into
+// Segments per row.  With at most 128 (row, head) items and rows of at least 16
+// blocks, rows are split into
 // up to 512 / items segments (256 / items where one workgroup fills a CU) that run in parallel (a local pass, a combine
 // step, then the scan of every segment from its incoming state), down to 4
 // blocks per segment.  (Measured on MI355X: 32 items of 256 blocks run best as
 // 16 segments, or 8 with N = 256; 48 packed-sequence items of 128 blocks as 5;
-// 192 items of 32 blocks run best unsplit.)  A function of the problem alone (no device query),
+// 192 items of 32 blocks run best unsplit; rows of 8 blocks ran faster unsplit.)  A function of the problem alone (no device query),
 // so the workspace size is known on the host; the problem's `segments` field, when
 // positive, forces the count.
 struct Segs {
@@ -121,7 +122,9 @@ Segs segments(const ssd_problem_t* p) {
                                 (p->nseqs != p->batch || p->dstate == 256);
         const int64_t slots = (one_per_cu ? 1 : 2) * 256;
         const int64_t units = p->batch * p->nheads;
-        if (units <= 128) S = std::min<int64_t>(slots / units, nblk / 4);
+        // (rows under 16 blocks stay whole: the local pass and the combine cost
+        // more than the shorter walk saves)
+        if (units <= 128 && nblk >= 16) S = std::min<int64_t>(slots / units, nblk / 4);
     }
     S = std::max<int64_t>(1, std::min<int64_t>(S, nblk));
     const int64_t sb = (nblk + S - 1) / S;

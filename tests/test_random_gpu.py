@@ -153,7 +153,8 @@ def draw_split(seed):
     r = random.Random(seed)
     c = draw(seed)
     G = r.choice([1, 2])
-    c.update(b=r.randint(1, 2), G=G, H=G * r.randint(1, 2), T=r.randint(520, 2000),
+    blk = 64 if c["chunk"] >= 64 else 32           # rows under 16 blocks are not split
+    c.update(b=r.randint(1, 2), G=G, H=G * r.randint(1, 2), T=r.randint(16 * blk + 8, 2000),
              packed=(r.randint(2, 5) if r.random() < 0.3 else 0))
     return c
 

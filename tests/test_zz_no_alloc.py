@@ -44,7 +44,7 @@ def test_noalloc_equals_forward_on_two_calls_in_a_row():
     cases = [
         # b, T, H, P, N, G, seqlens: the first call larger than the second
         (2, 2000, 4, 64, 128, 2, None),                 # 8 items: 8 segments of 4 blocks per row
-        (1, 700, 2, 32, 64, 1, [[300, 1, 399]]),        # packed sequences, 2 items: 2 segments
+        (1, 1100, 2, 32, 64, 1, [[450, 1, 649]]),       # packed sequences, 2 items: 4 segments
     ]
     sizes = []
     for i, (b, T, H, P, N, G, lens) in enumerate(cases):
